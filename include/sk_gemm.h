@@ -1,0 +1,217 @@
+/*
+ * sk_gemm.h -- Stream-K dense GEMM for one AMD Instinct MI355X (gfx950).
+ *
+ * Computes C = alpha * A * B + beta * C (the GEMM definition of the Stream-K
+ * page, "Stream-K: Work-centric Parallel Decomposition for Dense
+ * Matrix-Matrix Multiplication on the GPU", section 3 background) with the
+ * work-centric decomposition of that page's section 4 (Algorithm 5) and the
+ * "two-tile Stream-K + data-parallel" hybrid of its section 5.2, optionally
+ * with threadblock-level ABFT checksums ("Anatomy of High-Performance GEMM
+ * with Online Fault Tolerance on GPUs", threadblock-level scheme, Figs. 5-7).
+ *
+ * Conventions shared by every entry point:
+ *  - A is m x k, B is k x n, C is m x n.  Storage order of A and B is given by
+ *    sk_layout; C is always row-major (element (i, j) at C[i * ldc + j]).
+ *    Leading dimensions are in elements.  Row-major A needs lda >= k,
+ *    column-major A needs lda >= m; row-major B needs ldb >= n, column-major
+ *    B needs ldb >= k; ldc >= n.
+ *  - A, B and C are device pointers owned by the caller; the library never
+ *    frees them.  A and B are read only; C is read only when beta != 0.
+ *  - Calls are asynchronous: work is enqueued on `stream` (0 = the default
+ *    stream) and the call returns; results are valid once the stream has been
+ *    synchronised.  No host synchronisation happens inside a call, except
+ *    that the first call on a (device, stream) pair allocates the library's
+ *    workspace (partial tiles and flags for the cross-workgroup fixup).
+ *  - Two host threads must not issue calls on the same stream at the same
+ *    time (they would share one workspace).
+ *  - Return value: SK_OK (0) or a negative sk_status.  No exception crosses
+ *    this interface.  Errors found on the device (a fixup wait that timed
+ *    out) are reported by sk_device_status().
+ */
+#ifndef SK_GEMM_H
+#define SK_GEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types.  SK_F32: fp32 in and out, fp32 accumulation (SGEMM).
+ * SK_F16 / SK_BF16: fp16 / bf16 in and out, fp32 accumulation (HGEMM);
+ * alpha and beta are applied in fp32 and the result is rounded once to the
+ * output type (round to nearest even). */
+typedef enum { SK_F32 = 0, SK_F16 = 1, SK_BF16 = 2 } sk_dtype;
+
+/* Storage order of A and B ("ROW": the second index is contiguous).
+ * SK_A_ROW_B_COL keeps both operands contiguous along k. */
+typedef enum {
+  SK_A_ROW_B_ROW = 0,
+  SK_A_ROW_B_COL = 1,
+  SK_A_COL_B_ROW = 2,
+  SK_A_COL_B_COL = 3
+} sk_layout;
+
+typedef enum {
+  SK_OK = 0,
+  SK_ERR_INVALID_ARG = -1,   /* negative size, leading dimension too small, NULL pointer with nonzero size, bad enum */
+  SK_ERR_UNSUPPORTED = -2,   /* combination the library does not implement (e.g. an operand row over 8 MiB) */
+  SK_ERR_NO_MEMORY = -3,     /* workspace allocation failed */
+  SK_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed; sk_last_hip_error() has the text */
+  SK_ERR_FIXUP_TIMEOUT = -5, /* device: a workgroup gave up waiting for a peer's partial tile */
+  SK_ERR_NO_DEVICE = -6      /* no usable gfx950 device */
+} sk_status;
+
+/* Work decompositions (Stream-K page):
+ *  SK_SCHED_AUTO      two-tile hybrid when the tile count spans at least one
+ *                     full wave and is not a multiple of the CU slots; plain
+ *                     data-parallel when it is a multiple; basic Stream-K with
+ *                     a model-chosen grid when it is below one wave.
+ *  SK_SCHED_DP        data-parallel (Algorithm 2), persistent over the slots.
+ *  SK_SCHED_SK_BASIC  basic Stream-K (Algorithm 5) over all tiles.
+ *  SK_SCHED_SK_HYBRID2 "two-tile Stream-K + data-parallel" (section 5.2).
+ *  SK_SCHED_SK_HYBRID1 "data-parallel + one-tile Stream-K" (section 5.2). */
+typedef enum {
+  SK_SCHED_AUTO = 0,
+  SK_SCHED_DP = 1,
+  SK_SCHED_SK_BASIC = 2,
+  SK_SCHED_SK_HYBRID2 = 3,
+  SK_SCHED_SK_HYBRID1 = 4
+} sk_schedule;
+
+/* One GEMM. */
+typedef struct {
+  int64_t m, n, k;
+  float alpha;
+  const void *A;
+  int64_t lda;
+  const void *B;
+  int64_t ldb;
+  float beta;
+  void *C;
+  int64_t ldc;
+  sk_dtype dtype;
+  sk_layout layout;
+} sk_gemm_desc;
+
+/* A fault to inject in ABFT mode (testing only).  The fault is applied to the
+ * fp32 accumulator of element (row, col) of C in the work segment whose
+ * k-iteration range (within the element's output tile) contains `iter`,
+ * just before that segment is verified.  kind 0: add `value`; kind 1: flip
+ * bit `bit` (0..31) of the fp32 accumulator. */
+typedef struct {
+  int64_t row, col;
+  int32_t iter;
+  int32_t kind;
+  int32_t bit;
+  float value;
+} sk_fault;
+
+#define SK_ABFT_MAX_RECORDS 64
+
+/* One corrected (or uncorrectable) element found by ABFT. */
+typedef struct {
+  int64_t row, col;  /* element of C; -1 when not locatable */
+  float delta;       /* faulty value minus corrected value */
+  int32_t status;    /* 1 corrected, 2 uncorrectable (mismatch not located to one element) */
+  int32_t tile;      /* output tile */
+  int32_t seg_begin; /* first k-iteration of the verified segment */
+} sk_abft_record;
+
+/* ABFT report, written on the device (caller-owned device memory; the
+ * library zeroes it at the start of each sk_gemm_ex call that passes it). */
+typedef struct {
+  int32_t detected;      /* verification domains with any mismatch */
+  int32_t corrected;     /* elements corrected */
+  int32_t uncorrectable; /* domains whose mismatch could not be located */
+  int32_t n_records;     /* records written (at most SK_ABFT_MAX_RECORDS) */
+  sk_abft_record records[SK_ABFT_MAX_RECORDS];
+} sk_abft_report;
+
+/* Options for sk_gemm_ex.  Zero-initialised options mean: AUTO schedule, no
+ * forced grid, ABFT off, default model constants. */
+typedef struct {
+  int32_t schedule;         /* sk_schedule */
+  int32_t forced_grid;      /* > 0: basic Stream-K with exactly this many workgroups */
+  int32_t abft;             /* nonzero: ABFT mode (checksums, verify, correct); SK_F32 only */
+  int32_t hybrid_min_waves; /* full waves needed before the two-tile hybrid is used (default 1) */
+  const sk_fault *faults;   /* device array of injected faults (testing), or NULL */
+  int32_t n_faults;
+  float abft_tau;           /* detection threshold factor c_tau (default 1) */
+  /* grid-size model constants in units of one MAC iteration (0 = default):
+   * fixed cost a, partial-output cost b, per-iteration cost c, per-peer cost d */
+  float model_a, model_b, model_c, model_d;
+  int32_t spin_limit_us;    /* fixup wait time-out in microseconds (0 = 2 s) */
+  int32_t reserved;
+} sk_options;
+
+/* Plan of one call, for inspection (host only, needs no GPU when
+ * sk_plan_query is given an explicit slot count). */
+typedef struct {
+  int32_t tile_m, tile_n, tile_k; /* BLK_M, BLK_N, BLK_K of the kernel */
+  int32_t slots;                  /* p: workgroups resident at once */
+  int32_t grid;                   /* g: workgroups launched */
+  int32_t schedule;               /* resolved sk_schedule (never AUTO) */
+  int64_t tiles_m, tiles_n, tiles;/* t = tiles_m * tiles_n */
+  int64_t iters_per_tile;         /* ceil(k / BLK_K) */
+  int64_t total_iters;            /* t * iters_per_tile */
+  int64_t sk_tiles;               /* tiles [0, sk_tiles) form the Stream-K region */
+  int64_t sk_iters_q;             /* floor(sk_tiles * ipt / grid) */
+  int64_t sk_iters_r;             /* (sk_tiles * ipt) mod grid: the first r workgroups take one more */
+  int64_t dp_tiles;               /* tiles after the Stream-K region, dealt round-robin */
+  int32_t full_waves;             /* w = floor(t / slots) */
+  int32_t tail_tiles;             /* r = t mod slots */
+  int32_t max_peers;              /* most partials any owner adds */
+  int32_t packs;                  /* bit 0: A is repacked, bit 1: B is repacked */
+} sk_plan;
+
+/* One work segment of a workgroup. */
+typedef struct {
+  int64_t tile;
+  int64_t iter_begin, iter_end; /* k-iterations within the tile, [begin, end) */
+  int32_t started;              /* holds iteration 0: the workgroup writes the tile */
+  int32_t ended;                /* holds the tile's last iteration */
+  int64_t last_peer;            /* owner that did not end the tile: highest peer it sums; else -1 */
+} sk_segment;
+
+/* C = alpha*A*B + beta*C with the AUTO schedule.  m == 0 or n == 0 returns
+ * SK_OK without launching anything; k == 0 or alpha == 0 scales C by beta
+ * (beta == 0 writes zeros without reading C). */
+int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t lda,
+            const void *B, int64_t ldb, float beta, void *C, int64_t ldc, sk_dtype dtype,
+            sk_layout layout, hipStream_t stream);
+
+/* Same as sk_gemm with options.  `opts` may be NULL.  `report` is a device
+ * pointer to an sk_abft_report (required when opts->abft is set, else
+ * ignored). */
+int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
+               hipStream_t stream);
+
+/* Plan the call would use.  slots > 0 plans for that many resident
+ * workgroups without touching the GPU; slots == 0 asks the current device. */
+int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slots, sk_plan *out);
+
+/* Segments of workgroup `wg` under `plan`, in execution order.  Writes at
+ * most `cap` entries and returns the number of segments (which may exceed
+ * cap), or a negative sk_status. */
+int64_t sk_plan_segments(const sk_plan *plan, int64_t wg, sk_segment *out, int64_t cap);
+
+/* Device-side status word of the current device's workspaces: SK_OK or
+ * SK_ERR_FIXUP_TIMEOUT; reading it synchronises the device and clears it. */
+int sk_device_status(void);
+
+/* Text of a status code, and of the last HIP error seen by the library. */
+const char *sk_strerror(int status);
+const char *sk_last_hip_error(void);
+
+/* Frees every workspace of the calling process (synchronises the device). */
+int sk_release_workspace(void);
+
+/* Library version string. */
+const char *sk_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SK_GEMM_H */

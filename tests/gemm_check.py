@@ -1,0 +1,130 @@
+"""Helpers for the GPU parity tests: seeded inputs, upload through torch, one
+call through the C ABI, and the comparison with the oracle.
+
+Error metric: max over elements of |C_gpu - C_ref| / D, where C_ref is the
+oracle's unrounded fp64 value and D = |alpha| |A||B| + |beta| |C_in| is the
+componentwise bound (elements with D == 0 must match exactly).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import sk_synth as S
+import work_centric_decomposition_amd as sk
+
+TOL = {sk.F32: 1e-5, sk.F16: 5e-3, sk.BF16: 5e-3}
+TORCH_DT = {sk.F32: torch.float32, sk.F16: torch.float16, sk.BF16: torch.bfloat16}
+
+
+def orders(layout):
+    a = "row" if layout in (sk.A_ROW_B_ROW, sk.A_ROW_B_COL) else "col"
+    b = "row" if layout in (sk.A_ROW_B_ROW, sk.A_COL_B_ROW) else "col"
+    return a, b
+
+
+def to_dev(arr: np.ndarray, dtype: int) -> torch.Tensor:
+    if dtype == sk.F32:
+        return torch.from_numpy(np.ascontiguousarray(arr)).cuda()
+    t = torch.from_numpy(np.ascontiguousarray(arr).view(np.int16))
+    return t.view(TORCH_DT[dtype]).cuda()
+
+
+def from_dev(t: torch.Tensor, dtype: int) -> np.ndarray:
+    if dtype == sk.F32:
+        return t.cpu().numpy()
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def decode(arr: np.ndarray, dtype: int) -> np.ndarray:
+    if dtype == sk.F32:
+        return arr.astype(np.float64)
+    if dtype == sk.F16:
+        return arr.view(np.float16).astype(np.float64)
+    return (arr.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+class Case:
+    """Seeded inputs of one GEMM, on the host (storage arrays) and device."""
+
+    def __init__(self, m, n, k, dtype, layout, seed, dist="uniform", scale=1.0, pad=0,
+                 with_c=True):
+        self.m, self.n, self.k, self.dtype, self.layout = m, n, k, dtype, layout
+        ao, bo = orders(layout)
+        self.lda = max(1, (k if ao == "row" else m) + pad)
+        self.ldb = max(1, (n if bo == "row" else k) + pad)
+        self.ldc = max(1, n + pad)
+        self.A = S.matrix(seed, S.STREAM_A, m, k, dtype, dist, ao, self.lda, scale)
+        self.B = S.matrix(seed, S.STREAM_B, k, n, dtype, dist, bo, self.ldb, scale)
+        if with_c:
+            self.Cin = S.matrix(seed, S.STREAM_C, m, n, dtype, dist, "row", self.ldc, scale)
+        else:  # beta = 0 cases: C_in is never read, a zero buffer is enough
+            size = (m - 1) * self.ldc + n if m > 0 and n > 0 else 0
+            self.Cin = np.zeros(size, np.float32 if dtype == sk.F32 else np.uint16)
+        # device buffers sized to the storage (at least one element)
+        self.dA = to_dev(self.A if self.A.size else np.zeros(1, self.A.dtype), dtype)
+        self.dB = to_dev(self.B if self.B.size else np.zeros(1, self.B.dtype), dtype)
+        self.dC = to_dev(self.Cin if self.Cin.size else np.zeros(1, self.Cin.dtype), dtype)
+
+    def reset_c(self):
+        self.dC.copy_(to_dev(self.Cin if self.Cin.size else np.zeros(1, self.Cin.dtype),
+                             self.dtype))
+
+    def run(self, alpha=1.0, beta=0.0, opts=None, report=None):
+        d = sk.make_desc(self.m, self.n, self.k, alpha, self.dA, self.lda, self.dB, self.ldb, beta,
+                         self.dC, self.ldc, self.dtype, self.layout)
+        if opts is None and report is None:
+            sk.gemm(self.m, self.n, self.k, alpha, self.dA, self.lda, self.dB, self.ldb, beta,
+                    self.dC, self.ldc, self.dtype, self.layout)
+        else:
+            sk.gemm_ex(d, opts, report)
+        torch.cuda.synchronize()
+        return self.result()
+
+    def result(self) -> np.ndarray:
+        """C as an (m, n) storage array."""
+        flat = from_dev(self.dC, self.dtype)
+        if self.m == 0 or self.n == 0:
+            return flat[:0].reshape(self.m, self.n)
+        view = np.lib.stride_tricks.as_strided(flat, shape=(self.m, self.n),
+                                               strides=(self.ldc * flat.itemsize, flat.itemsize))
+        return view.copy()
+
+    def reference(self, alpha=1.0, beta=0.0):
+        out64, bound, _ = oracle.gemm(self.m, self.n, self.k, alpha, self.A, self.lda, self.B,
+                                      self.ldb, beta, self.Cin, self.ldc, self.dtype, self.layout,
+                                      want_round=False)
+        return out64, bound
+
+    def reference_entries(self, rows, cols, alpha=1.0, beta=0.0):
+        return oracle.gemm_entries(self.m, self.n, self.k, alpha, self.A, self.lda, self.B,
+                                   self.ldb, beta, self.Cin, self.ldc, self.dtype, self.layout,
+                                   rows, cols)
+
+    def freivalds(self, C_out: np.ndarray, alpha=1.0, beta=0.0, seed=99, nvec=2) -> float:
+        X = np.stack([S.signs(seed, v, self.n) for v in range(nvec)])
+        return oracle.freivalds(self.m, self.n, self.k, alpha, self.A, self.lda, self.B, self.ldb,
+                                beta, self.Cin, self.ldc, np.ascontiguousarray(C_out), self.n,
+                                self.dtype, self.layout, X)
+
+
+def rel_err(got: np.ndarray, dtype: int, ref64: np.ndarray, bound: np.ndarray) -> float:
+    g = decode(got, dtype)
+    diff = np.abs(g - ref64)
+    zero = bound == 0
+    if np.any(zero & (diff != 0)) or np.any(~np.isfinite(g)):
+        return float("inf")
+    with np.errstate(invalid="ignore", divide="ignore"):
+        r = np.where(zero, 0.0, diff / np.where(zero, 1.0, bound))
+    return float(r.max()) if r.size else 0.0
+
+
+def sample_indices(m, n, count, seed):
+    u = S.u64(seed, 555, 0, 2 * count)
+    rows = (u[:count] % np.uint64(m)).astype(np.int64)
+    cols = (u[count:] % np.uint64(n)).astype(np.int64)
+    # always include the corners and the last tile's edge
+    rows = np.concatenate([rows, [0, 0, m - 1, m - 1]])
+    cols = np.concatenate([cols, [0, n - 1, 0, n - 1]])
+    return rows, cols

@@ -1,0 +1,204 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Tolerances (max |C - C_ref| / (|alpha||A||B| + |beta||C_in|)): 1e-5 for
+fp32, 5e-3 for fp16/bf16 inputs with fp32 accumulation.  Schedule
+equivalences are bitwise.
+"""
+import numpy as np
+import pytest
+
+import sk_synth as S
+import work_centric_decomposition_amd as sk
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+from gemm_check import TOL, Case, decode, rel_err, sample_indices  # noqa: E402
+
+DTYPES = [sk.F32, sk.F16, sk.BF16]
+LAYOUTS = [sk.A_ROW_B_ROW, sk.A_ROW_B_COL, sk.A_COL_B_ROW, sk.A_COL_B_COL]
+
+
+@pytest.fixture(autouse=True)
+def _gpu_available():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    yield
+    assert sk.device_status() == sk.OK
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------ the SGEMM correctness case
+
+@pytest.mark.parametrize("forced", [0, 4])
+def test_sgemm_384_uniform_auto_and_forced_grid4(forced):
+    """384x384x128 fp32, row-major A and B, U[-1,1], alpha=1 beta=0; AUTO and a
+    forced Stream-K grid of 4 workgroups (partial-tile fixup)."""
+    _say("case sgemm 384^2x128 forced", forced)
+    c = Case(384, 384, 128, sk.F32, sk.A_ROW_B_ROW, S.SEED_SGEMM_SMALL)
+    opts = sk.make_options(forced_grid=forced) if forced else None
+    got = c.run(1.0, 0.0, opts)
+    ref, bound = c.reference()
+    assert rel_err(got, sk.F32, ref, bound) <= TOL[sk.F32]
+
+
+# ------------------------------------- ragged shapes, all types and layouts
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_ragged_shapes_all_layouts(dtype, layout):
+    for (m, n, k, pad, alpha, beta) in [(300, 520, 200, 0, 1.0, 0.0), (513, 257, 1000, 8, 0.5, -1.5),
+                                        (17, 33, 48, 0, 1.0, 1.0), (1, 1, 8, 0, 2.0, 0.0)]:
+        _say("case ragged", dtype, layout, m, n, k, pad)
+        c = Case(m, n, k, dtype, layout, 7 + m + layout, pad=pad)
+        got = c.run(alpha, beta)
+        ref, bound = c.reference(alpha, beta)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_k_not_multiple_of_vector_width_and_odd_ld(dtype):
+    for (m, n, k, pad) in [(129, 130, 131, 1), (64, 300, 77, 3), (260, 70, 5, 0)]:
+        _say("case odd", dtype, m, n, k, pad)
+        c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 40 + k, pad=pad)
+        got = c.run(1.0, 0.5)
+        ref, bound = c.reference(1.0, 0.5)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
+
+
+# ----------------------------------------------------------------- edges
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_quick_returns(dtype):
+    c = Case(40, 24, 16, dtype, sk.A_ROW_B_ROW, 3)
+    before = c.result()
+    sk.gemm(0, 24, 16, 1.0, c.dA, c.lda, c.dB, c.ldb, 1.0, c.dC, c.ldc, dtype, 0)
+    torch.cuda.synchronize()
+    assert np.array_equal(c.result().view(np.uint8), before.view(np.uint8))
+    # k == 0: C = beta * C
+    sk.gemm(40, 24, 0, 1.0, c.dA, c.lda, c.dB, c.ldb, -2.0, c.dC, c.ldc, dtype, 0)
+    torch.cuda.synchronize()
+    want = -2.0 * decode(before, dtype)  # exact: a power-of-two scale
+    assert np.array_equal(decode(c.result(), dtype), want)
+    # alpha == 0 and beta == 0 writes zeros without reading C (NaN in C)
+    c.dC.fill_(float("nan"))
+    sk.gemm(40, 24, 16, 0.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc, dtype, 0)
+    torch.cuda.synchronize()
+    assert np.all(decode(c.result(), dtype) == 0.0)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_beta_zero_does_not_read_c(dtype):
+    c = Case(300, 300, 64, dtype, sk.A_ROW_B_COL, 5)
+    c.dC.fill_(float("nan"))
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+
+
+# ------------------------------------------------- schedule equivalences
+
+@pytest.mark.parametrize("dtype", [sk.F32, sk.F16])
+def test_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype):
+    m, n, k = (1024, 768, 2048) if dtype != sk.F32 else (640, 512, 1024)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 11)
+    p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
+                                   sk.A_ROW_B_COL))
+    t = p.tiles
+    dp = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP))
+    c.reset_c()
+    skg = c.run(1.0, 0.0, sk.make_options(forced_grid=t))
+    assert np.array_equal(dp.view(np.uint8), skg.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_every_grid_size_exact_on_integer_inputs(dtype):
+    """Small integers make every partial sum exact in fp32, so every
+    decomposition gives the same bits."""
+    m, n, k = (700, 600, 1024) if dtype == sk.F32 else (600, 520, 2048)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 12, dist="int")
+    ref = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP))
+    for g in [1, 2, 3, 5, 7, 13, 31, 100, 255, 256, 300]:
+        c.reset_c()
+        got = c.run(1.0, 0.0, sk.make_options(forced_grid=g))
+        assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), g
+    for sched in (sk.SCHED_SK_HYBRID1, sk.SCHED_SK_HYBRID2, sk.SCHED_SK_BASIC):
+        c.reset_c()
+        got = c.run(1.0, 0.0, sk.make_options(schedule=sched))
+        assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), sched
+    # the fp32 sums are exact, so the one rounding to the output type must
+    # give the oracle's rounded value bit for bit
+    import oracle
+    _, _, rnd = oracle.gemm(m, n, k, 1.0, c.A, c.lda, c.B, c.ldb, 0.0, None, c.ldc, dtype,
+                            c.layout)
+    assert np.array_equal(ref.view(np.uint8), rnd.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_forced_grids_against_oracle(dtype):
+    m, n, k = 520, 600, 3000
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL if dtype else sk.A_ROW_B_ROW, 13)
+    ref, bound = c.reference(1.0, 1.0)
+    for g in [1, 3, 7, 64, 200]:
+        _say("case forced grid", dtype, g)
+        c.reset_c()
+        got = c.run(1.0, 1.0, sk.make_options(forced_grid=g))
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], g
+
+
+def test_hybrid_schedule_hgemm_against_oracle():
+    """17 x 16 = 272 tiles of 256 x 256: one full wave plus 16 tiles -> the
+    two-tile Stream-K + DP hybrid."""
+    m, n, k = 256 * 17, 256 * 16, 256
+    c = Case(m, n, k, sk.F16, sk.A_ROW_B_COL, 14, dist="normal", scale=1 / 16)
+    p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, sk.F16,
+                                   sk.A_ROW_B_COL))
+    assert p.schedule == sk.SCHED_SK_HYBRID2
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference()
+    assert rel_err(got, sk.F16, ref, bound) <= TOL[sk.F16]
+    again = c.run(1.0, 0.0)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8))  # run-to-run bitwise
+
+
+def test_hybrid_schedule_sgemm_against_oracle():
+    m, n, k = 128 * 23, 128 * 23, 128  # 529 tiles on 512 slots
+    c = Case(m, n, k, sk.F32, sk.A_ROW_B_ROW, 15)
+    got = c.run(1.0, 1.0)
+    ref, bound = c.reference(1.0, 1.0)
+    assert rel_err(got, sk.F32, ref, bound) <= TOL[sk.F32]
+
+
+# ------------------------------------------ full-size workloads (sampled)
+
+@pytest.mark.parametrize("nsq", [1024, 2048, 3072, 4096, 5120, 6144])
+def test_sgemm_square_sweep_sampled(nsq):
+    """Square SGEMM, row-major, U[-1,1], C_in U[-1,1], alpha=1 beta=1."""
+    _say("case sgemm square", nsq)
+    c = Case(nsq, nsq, nsq, sk.F32, sk.A_ROW_B_ROW, S.SEED_SGEMM_SQUARE)
+    got = c.run(1.0, 1.0)
+    rows, cols = sample_indices(nsq, nsq, 1500, nsq)
+    ref, bound = c.reference_entries(rows, cols, 1.0, 1.0)
+    g = decode(got[rows, cols], sk.F32)
+    assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F32]
+    assert c.freivalds(got, 1.0, 1.0) <= TOL[sk.F32]
+
+
+@pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
+def test_hgemm_8192_sampled(dtype):
+    """8192^3, A row-major and B column-major (both k-contiguous), entries
+    N(0,1)/sqrt(k), alpha=1 beta=0, fp32 accumulation."""
+    _say("case hgemm 8192", dtype)
+    n = 8192
+    c = Case(n, n, n, dtype, sk.A_ROW_B_COL, S.SEED_HGEMM_LARGE, dist="normal",
+             scale=1 / np.sqrt(n), with_c=False)
+    got = c.run(1.0, 0.0)
+    rows, cols = sample_indices(n, n, 1500, 8192 + dtype)
+    ref, bound = c.reference_entries(rows, cols)
+    g = decode(got[rows, cols], dtype)
+    assert np.max(np.abs(g - ref) / bound) <= TOL[dtype]
+    assert c.freivalds(got) <= TOL[dtype]

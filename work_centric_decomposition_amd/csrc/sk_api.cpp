@@ -1,0 +1,371 @@
+// sk_api.cpp -- the C ABI of the Stream-K GEMM library (host side).
+//
+// Validates arguments, handles the BLAS quick returns, plans the work
+// decomposition, manages the per-(device, stream) workspace that holds the
+// partial tiles and flags of the cross-workgroup fixup, repacks operands the
+// kernels cannot read directly, and launches the kernels.  Every arithmetic
+// step of the GEMM runs in the HIP kernels of sk_kernels.hip.
+#include <hip/hip_runtime.h>
+
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <utility>
+#include <vector>
+
+#include "sk_internal.h"
+
+namespace sk {
+namespace {
+
+thread_local std::string g_last_hip_error = "no error";
+
+int hip_fail(hipError_t e, const char *what) {
+  char buf[256];
+  std::snprintf(buf, sizeof(buf), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  g_last_hip_error = buf;
+  return SK_ERR_HIP;
+}
+
+struct DeviceInfo {
+  bool ok = false;
+  int cus = 0;
+  int slots[3] = {0, 0, 0};  // per dtype
+  int64_t wall_khz = 100000;
+};
+
+struct Workspace {
+  float *partials = nullptr;
+  size_t partial_bytes = 0;
+  uint32_t *flags = nullptr;
+  int flag_count = 0;
+  int32_t *status = nullptr;
+  uint32_t epoch = 0;
+};
+
+std::mutex g_mu;
+std::map<int, DeviceInfo> g_dev;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int device_info(int dev, DeviceInfo **out) {
+  auto it = g_dev.find(dev);
+  if (it != g_dev.end()) {
+    *out = &it->second;
+    return it->second.ok ? SK_OK : SK_ERR_NO_DEVICE;
+  }
+  DeviceInfo &d = g_dev[dev];
+  *out = &d;
+  struct Forget {  // a failed probe is retried on the next call
+    int dev;
+    bool armed = true;
+    ~Forget() { if (armed) g_dev.erase(dev); }
+  } forget{dev};
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) {
+    g_last_hip_error = std::string("device is ") + prop.gcnArchName + ", the kernels are built for gfx950";
+    return SK_ERR_NO_DEVICE;
+  }
+  d.cus = prop.multiProcessorCount;
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    d.wall_khz = khz;
+  for (int dt = 0; dt < 3; ++dt) {
+    int occ = 0;
+    e = (hipError_t)kernel_occupancy(dt, &occ);
+    if (e != hipSuccess) return hip_fail(e, "occupancy query");
+    const int want = tile_cfg(dt).occupancy;
+    if (occ < 1) {
+      g_last_hip_error = "kernel does not fit on a CU";
+      return SK_ERR_HIP;
+    }
+    d.slots[dt] = d.cus * (occ < want ? occ : want);
+  }
+  d.ok = true;
+  forget.armed = false;
+  return SK_OK;
+}
+
+__global__ void init_flags_kernel(uint32_t *flags, int n, int32_t *status) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0;
+  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+}
+
+// Workspace of (dev, stream) with room for `slots` partial tiles of
+// `tile_bytes` each.  Caller holds g_mu.
+int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes, Workspace **out) {
+  Workspace &w = g_ws[{dev, stream}];
+  const size_t need = (size_t)slots * tile_bytes;
+  const size_t base = (size_t)256 * 256 * 256 * 4;  // 256 slots of the largest tile: 64 MiB
+  if (w.partials == nullptr || w.partial_bytes < need || w.flag_count < slots) {
+    if (w.partials) {  // growth: wait for work that may still use the old buffers
+      hipError_t e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipFree(w.partials);
+      (void)hipFree(w.flags);
+      (void)hipFree(w.status);
+      w = Workspace{};
+    }
+    size_t bytes = need > base ? need : base;
+    int nflags = slots > 1024 ? (int)slots : 1024;
+    hipError_t e = hipMalloc(&w.partials, bytes);
+    if (e != hipSuccess) { w = Workspace{}; (void)hipGetLastError(); return SK_ERR_NO_MEMORY; }
+    e = hipMalloc(&w.flags, sizeof(uint32_t) * nflags);
+    if (e == hipSuccess) e = hipMalloc(&w.status, sizeof(int32_t));
+    if (e != hipSuccess) {
+      (void)hipFree(w.partials);
+      (void)hipFree(w.flags);
+      w = Workspace{};
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
+    w.partial_bytes = bytes;
+    w.flag_count = nflags;
+    w.epoch = 0;
+    hipLaunchKernelGGL(init_flags_kernel, dim3(4), dim3(256), 0, stream, w.flags, nflags, w.status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "workspace init");
+  }
+  *out = &w;
+  return SK_OK;
+}
+
+bool a_kmajor_of(int layout) { return layout == SK_A_ROW_B_ROW || layout == SK_A_ROW_B_COL; }
+bool b_kmajor_of(int layout) { return layout == SK_A_ROW_B_COL || layout == SK_A_COL_B_COL; }
+
+int validate(const sk_gemm_desc &d, const sk_options &o, const sk_abft_report *report) {
+  if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
+  if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
+  if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_SK_HYBRID1) return SK_ERR_INVALID_ARG;
+  if (o.forced_grid < 0 || o.hybrid_min_waves < 0 || o.n_faults < 0 || o.spin_limit_us < 0)
+    return SK_ERR_INVALID_ARG;
+  if (o.n_faults > 0 && o.faults == nullptr) return SK_ERR_INVALID_ARG;
+  if (o.abft && d.dtype != SK_F32) return SK_ERR_UNSUPPORTED;
+  if (o.abft && report == nullptr) return SK_ERR_INVALID_ARG;
+  if (d.m == 0 || d.n == 0) return SK_OK;
+  if (d.C == nullptr || d.ldc < d.n) return SK_ERR_INVALID_ARG;
+  if (d.k > 0 && d.alpha != 0.f) {
+    if (d.A == nullptr || d.B == nullptr) return SK_ERR_INVALID_ARG;
+    const int64_t a_min = a_kmajor_of(d.layout) ? d.k : d.m;
+    const int64_t b_min = b_kmajor_of(d.layout) ? d.k : d.n;
+    if (d.lda < (a_min > 1 ? a_min : 1) || d.ldb < (b_min > 1 ? b_min : 1)) return SK_ERR_INVALID_ARG;
+  }
+  return SK_OK;
+}
+
+int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report, hipStream_t stream) {
+  int rc = validate(d, o, report);
+  if (rc != SK_OK) return rc;
+  if (d.m == 0 || d.n == 0) return SK_OK;  // nothing to compute or write
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  std::lock_guard<std::mutex> lock(g_mu);
+  DeviceInfo *info = nullptr;
+  rc = device_info(dev, &info);
+  if (rc != SK_OK) return rc;
+  if (o.abft) {
+    rc = launch_zero_report(report, stream);
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "report reset");
+  }
+  if (d.k == 0 || d.alpha == 0.f) {  // C = beta * C
+    rc = launch_scale(d.dtype, d.m, d.n, d.beta, d.C, d.ldc, stream);
+    return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "scale kernel");
+  }
+  Plan P;
+  rc = make_plan(d, o, info->slots[d.dtype], P);
+  if (rc != SK_OK) return rc;
+  const int es = d.dtype == SK_F32 ? 4 : 2;
+  const bool ak = a_kmajor_of(d.layout), bk = b_kmajor_of(d.layout);
+
+  // operands: direct, or repacked into a k-contiguous copy
+  const int64_t kp = (d.k + 63) / 64 * 64;
+  void *pa = nullptr, *pb = nullptr;
+  KernelArgs a;
+  std::memset(&a, 0, sizeof(a));
+  a.A = d.A; a.lda = d.lda; a.a_kmajor = ak; a.a_kext = (int32_t)d.k;
+  a.B = d.B; a.ldb = d.ldb; a.b_kmajor = bk; a.b_kext = (int32_t)d.k;
+  if (P.pack_a) {
+    e = hipMallocAsync(&pa, (size_t)d.m * kp * es, stream);
+    if (e != hipSuccess) { (void)hipGetLastError(); return SK_ERR_NO_MEMORY; }
+    rc = launch_pack(d.dtype, d.A, d.lda, ak, d.m, d.k, pa, kp, stream);
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack A");
+    a.A = pa; a.lda = kp; a.a_kmajor = 1; a.a_kext = (int32_t)kp;
+  }
+  if (P.pack_b) {
+    e = hipMallocAsync(&pb, (size_t)d.n * kp * es, stream);
+    if (e != hipSuccess) {
+      if (pa) (void)hipFreeAsync(pa, stream);
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
+    rc = launch_pack(d.dtype, d.B, d.ldb, bk, d.n, d.k, pb, kp, stream);
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack B");
+    a.B = pb; a.ldb = kp; a.b_kmajor = 1; a.b_kext = (int32_t)kp;
+  }
+  // 32-bit buffer offsets inside a k-major tile: rows * ld * es must fit
+  const TileCfg &c = P.cfg;
+  auto offsets_fit = [&](bool kmaj, int64_t ld, int rows) {
+    const int64_t span = kmaj ? (int64_t)rows * ld * es : (int64_t)c.bk * ld * es;
+    return span + 1024 < 0x7FFFFFFF;
+  };
+  if (!offsets_fit(a.a_kmajor, a.lda, c.bm) || !offsets_fit(a.b_kmajor, a.ldb, c.bn)) {
+    if (pa) (void)hipFreeAsync(pa, stream);
+    if (pb) (void)hipFreeAsync(pb, stream);
+    return SK_ERR_UNSUPPORTED;
+  }
+
+  Workspace *ws = nullptr;
+  const int64_t slots_needed = P.grid;
+  rc = get_workspace(dev, stream, slots_needed, (size_t)c.bm * c.bn * 4, &ws);
+  if (rc != SK_OK) {
+    if (pa) (void)hipFreeAsync(pa, stream);
+    if (pb) (void)hipFreeAsync(pb, stream);
+    return rc;
+  }
+  if (++ws->epoch == 0) ws->epoch = 1;
+
+  a.C = d.C; a.ldc = d.ldc;
+  a.m = (int32_t)d.m; a.n = (int32_t)d.n; a.k = (int32_t)d.k;
+  a.alpha = d.alpha; a.beta = d.beta;
+  a.tiles_m = (int32_t)P.tiles_m; a.tiles_n = (int32_t)P.tiles_n;
+  a.tiles = (int32_t)P.tiles; a.ipt = (int32_t)P.ipt;
+  a.grid = P.grid; a.sk_tiles = (int32_t)P.sk_tiles;
+  a.sk_q = P.sk_q; a.sk_r = P.sk_r;
+  a.partials = ws->partials; a.flags = ws->flags; a.epoch = ws->epoch; a.status = ws->status;
+  const int64_t us = o.spin_limit_us > 0 ? o.spin_limit_us : 2000000;
+  a.spin_limit = us * info->wall_khz / 1000;
+  a.abft = o.abft; a.n_faults = o.n_faults; a.faults = o.faults; a.report = report;
+  a.abft_tau = o.abft_tau > 0 ? o.abft_tau : 1.0f;
+
+  rc = launch_gemm(P, a, stream);
+  if (pa) (void)hipFreeAsync(pa, stream);
+  if (pb) (void)hipFreeAsync(pb, stream);
+  if (rc != hipSuccess) return hip_fail((hipError_t)rc, "GEMM kernel launch");
+  return SK_OK;
+}
+
+const sk_options kDefaultOpts = {};
+
+}  // namespace
+}  // namespace sk
+
+using namespace sk;
+
+extern "C" {
+
+int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t lda, const void *B,
+            int64_t ldb, float beta, void *C, int64_t ldc, sk_dtype dtype, sk_layout layout,
+            hipStream_t stream) {
+  sk_gemm_desc d{m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, dtype, layout};
+  try {
+    return gemm_impl(d, kDefaultOpts, nullptr, stream);
+  } catch (...) {
+    return SK_ERR_NO_MEMORY;
+  }
+}
+
+int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
+               hipStream_t stream) {
+  if (!desc) return SK_ERR_INVALID_ARG;
+  try {
+    return gemm_impl(*desc, opts ? *opts : kDefaultOpts, report, stream);
+  } catch (...) {
+    return SK_ERR_NO_MEMORY;
+  }
+}
+
+int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slots, sk_plan *out) {
+  if (!desc || !out || slots < 0) return SK_ERR_INVALID_ARG;
+  const sk_options &o = opts ? *opts : kDefaultOpts;
+  try {
+    if (slots == 0) {
+      int dev = 0;
+      hipError_t e = hipGetDevice(&dev);
+      if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+      std::lock_guard<std::mutex> lock(g_mu);
+      DeviceInfo *info = nullptr;
+      int rc = device_info(dev, &info);
+      if (rc != SK_OK) return rc;
+      if (desc->dtype < 0 || desc->dtype > 2) return SK_ERR_INVALID_ARG;
+      slots = info->slots[desc->dtype];
+    }
+    Plan P;
+    int rc = make_plan(*desc, o, slots, P);
+    if (rc != SK_OK) return rc;
+    std::memset(out, 0, sizeof(*out));
+    out->tile_m = P.cfg.bm; out->tile_n = P.cfg.bn; out->tile_k = P.cfg.bk;
+    out->slots = P.slots; out->grid = P.grid; out->schedule = P.schedule;
+    out->tiles_m = P.tiles_m; out->tiles_n = P.tiles_n; out->tiles = P.tiles;
+    out->iters_per_tile = P.ipt; out->total_iters = P.total;
+    out->sk_tiles = P.sk_tiles; out->sk_iters_q = P.sk_q; out->sk_iters_r = P.sk_r;
+    out->dp_tiles = P.dp_tiles; out->full_waves = P.w; out->tail_tiles = P.r;
+    out->max_peers = P.max_peers;
+    out->packs = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
+    return SK_OK;
+  } catch (...) {
+    return SK_ERR_NO_MEMORY;
+  }
+}
+
+int sk_device_status(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
+  hipError_t e = hipDeviceSynchronize();
+  if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
+  int result = SK_OK;
+  for (auto &kv : g_ws) {
+    if (kv.first.first != dev || !kv.second.status) continue;
+    int32_t v = 0;
+    e = hipMemcpy(&v, kv.second.status, sizeof(v), hipMemcpyDeviceToHost);
+    if (e != hipSuccess) return hip_fail(e, "status read");
+    if (v & 1) result = SK_ERR_FIXUP_TIMEOUT;
+    if (v) {
+      const int32_t zero = 0;
+      e = hipMemcpy(kv.second.status, &zero, sizeof(zero), hipMemcpyHostToDevice);
+      if (e != hipSuccess) return hip_fail(e, "status clear");
+    }
+  }
+  return result;
+}
+
+const char *sk_strerror(int status) {
+  switch (status) {
+    case SK_OK: return "success";
+    case SK_ERR_INVALID_ARG: return "invalid argument";
+    case SK_ERR_UNSUPPORTED: return "unsupported argument combination";
+    case SK_ERR_NO_MEMORY: return "workspace allocation failed";
+    case SK_ERR_HIP: return "HIP runtime error";
+    case SK_ERR_FIXUP_TIMEOUT: return "a workgroup timed out waiting for a partial tile";
+    case SK_ERR_NO_DEVICE: return "no usable gfx950 device";
+    default: return "unknown status";
+  }
+}
+
+const char *sk_last_hip_error(void) { return g_last_hip_error.c_str(); }
+
+int sk_release_workspace(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_ws.empty()) return SK_OK;
+  hipError_t e = hipDeviceSynchronize();
+  for (auto &kv : g_ws) {
+    int cur = 0;
+    (void)hipGetDevice(&cur);
+    (void)hipSetDevice(kv.first.first);
+    (void)hipFree(kv.second.partials);
+    (void)hipFree(kv.second.flags);
+    (void)hipFree(kv.second.status);
+    (void)hipSetDevice(cur);
+  }
+  g_ws.clear();
+  return e == hipSuccess ? SK_OK : hip_fail(e, "hipDeviceSynchronize");
+}
+
+const char *sk_version(void) { return "sk_gemm 0.1 (gfx950)"; }
+
+}  // extern "C"
