@@ -1,0 +1,240 @@
+#!/usr/bin/env python3
+"""Benchmark of the Stream-K GEMM on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload sgemm-sweep|hgemm-8192]
+
+A step is one pass of the whole hot path over one batch of synthetic inputs:
+  sgemm-sweep (default): the fp32 square sweep m = n = k in {1024, 2048, 3072,
+      4096, 5120, 6144}, row-major A and B, entries U[-1, 1], C pre-filled
+      U[-1, 1], alpha = 1, beta = 1 -- six GEMM calls;
+  hgemm-8192: one 8192^3 fp16 GEMM, A row-major and B column-major, entries
+      N(0, 1)/sqrt(k), fp32 accumulation, alpha = 1, beta = 0.
+Inputs are generated on the host from the seeded counter-based generator and
+are resident in HBM before the timed region.  W untimed steps, then K timed
+steps between synchronisations; one JSON line is printed.
+
+The line carries
+  roofline: the GEMM kernel's achieved rate (algorithmic flops per launch over
+      its mean launch time, from HIP events on the launch stream) against
+      MI355X's dense peak for the data type;
+  cpu_baseline: the CPU oracle timed on a bounded sample of the workload;
+  hgemm / sgemm: the other workload's throughput, measured in the same run.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+METRIC = "GEMM TFLOPS + % of MI355X MFMA peak (fp32, fp16) over shape sweep"
+SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
+# HBM bytes per dispatch measured with rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, scaled by the copy-kernel calibration); None when not measured
+# for the current kernel.
+TRAFFIC_BYTES = {"sgemm-sweep": None, "hgemm-8192": None}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="sgemm-sweep", choices=["sgemm-sweep", "hgemm-8192"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extra", action="store_true", help="skip the other workload")
+    return p.parse_args()
+
+
+def make_sweep_inputs(torch, sk, S):
+    cases = []
+    for n in SWEEP:
+        A = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_A, n, n, S.F32)
+        B = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_B, n, n, S.F32)
+        C = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_C, n, n, S.F32)
+        cases.append(dict(n=n, host=(A, B, C), A=torch.from_numpy(A).cuda(),
+                          B=torch.from_numpy(B).cuda(), C=torch.from_numpy(C).cuda()))
+    return cases
+
+
+def make_hgemm_inputs(torch, sk, S, dtype):
+    import numpy as np
+    n = 8192
+    tdt = torch.float16 if dtype == sk.F16 else torch.bfloat16
+    A = S.matrix(S.SEED_HGEMM_LARGE, S.STREAM_A, n, n, dtype, "normal", "row", None, 1 / math.sqrt(n))
+    B = S.matrix(S.SEED_HGEMM_LARGE, S.STREAM_B, n, n, dtype, "normal", "col", None, 1 / math.sqrt(n))
+    dA = torch.from_numpy(A.view(np.int16)).view(tdt).cuda()
+    dB = torch.from_numpy(B.view(np.int16)).view(tdt).cuda()
+    dC = torch.zeros(n * n, dtype=tdt, device="cuda")
+    return dict(n=n, dtype=dtype, A=dA, B=dB, C=dC)
+
+
+def sweep_step(sk, cases, events=None):
+    for i, c in enumerate(cases):
+        n = c["n"]
+        if events is not None:
+            events[i][0].record()
+        sk.gemm(n, n, n, 1.0, c["A"], n, c["B"], n, 1.0, c["C"], n, sk.F32, sk.A_ROW_B_ROW)
+        if events is not None:
+            events[i][1].record()
+
+
+def hgemm_step(sk, h, events=None):
+    n = h["n"]
+    if events is not None:
+        events[0][0].record()
+    sk.gemm(n, n, n, 1.0, h["A"], n, h["B"], n, 0.0, h["C"], n, h["dtype"], sk.A_ROW_B_COL)
+    if events is not None:
+        events[0][1].record()
+
+
+def timed(torch, step, n_launch, steps, warmup):
+    """Runs warmup + timed steps; returns (ms per step, mean ms per launch
+    for each launch index of the step)."""
+    for _ in range(warmup):
+        step(None)
+    torch.cuda.synchronize()
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(n_launch)] for _ in range(steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record()
+    for s in range(steps):
+        step(ev[s])
+    t1.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - wall0) * 1e3
+    total_ms = t0.elapsed_time(t1)
+    per_launch = [sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(steps)) / steps
+                  for i in range(n_launch)]
+    return max(total_ms, 0.0) / steps, per_launch, wall / steps
+
+
+def cpu_baseline(S, budget_s=25.0):
+    """The oracle (six-loop fp64 GEMM, full output) on the fp32 sweep's
+    shapes, smallest first, on the host's cores, stopping once about
+    `budget_s` seconds of CPU work have been spent."""
+    import oracle
+    flops, secs = 0.0, 0.0
+    sample = []
+    prev, last_t = None, 0.0
+    for n in SWEEP:
+        if prev is not None and secs + last_t * (n / prev) ** 3 > budget_s:
+            break
+        A = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_A, n, n, S.F32)
+        B = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_B, n, n, S.F32)
+        C = S.matrix(S.SEED_SGEMM_SQUARE, S.STREAM_C, n, n, S.F32)
+        t0 = time.perf_counter()
+        oracle.gemm(n, n, n, 1.0, A, n, B, n, 1.0, C, n, oracle.F32, oracle.A_ROW_B_ROW)
+        last_t = time.perf_counter() - t0
+        secs += last_t
+        prev = n
+        flops += 2.0 * n ** 3
+        sample.append(f"{n}^3")
+    return {"value": round(flops / secs / 1e12, 6), "unit": "TFLOP/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "full oracle (fp64 six-loop, alpha=1 beta=1) on the " + ", ".join(sample) +
+                      " shapes of the fp32 square sweep; " + f"{secs:.1f} s of CPU work"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); this path has no "
+              "multi-GPU mode: run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import sk_synth as S
+    import work_centric_decomposition_amd as sk
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(3)
+    torch.cuda.set_device(0)
+
+    results = {}
+    order = [args.workload] + ([] if args.no_extra else
+                               [w for w in ("sgemm-sweep", "hgemm-8192") if w != args.workload])
+    for wl in order:
+        main_wl = wl == args.workload
+        steps = args.steps if main_wl else max(3, args.steps // 4)
+        warmup = args.warmup if main_wl else 2
+        if wl == "sgemm-sweep":
+            cases = make_sweep_inputs(torch, sk, S)
+            ms, per_launch, wall = timed(torch, lambda ev: sweep_step(sk, cases, ev), len(cases),
+                                         steps, warmup)
+            flops = [2.0 * c["n"] ** 3 for c in cases]
+            # algorithmic flops: 2mnk MACs plus the alpha/beta epilogue (3mn)
+            step_flops = sum(2.0 * c["n"] ** 3 + 3.0 * c["n"] ** 2 for c in cases)
+            kern_ms = sum(per_launch)
+            achieved = sum(flops) / (kern_ms * 1e-3) / 1e12
+            results[wl] = dict(
+                value=step_flops / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype="f32",
+                per_shape={str(c["n"]): round(f / (t * 1e-3) / 1e12, 2)
+                           for c, f, t in zip(cases, flops, per_launch)},
+                roofline={"bound": "mfma", "achieved": round(achieved, 2),
+                          "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                          "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
+                          "traffic": TRAFFIC_BYTES[wl],
+                          "kernel": "sgemm_kernel<k-major A, n-major B>",
+                          "launch_ms": round(kern_ms / len(cases), 4)},
+                config={"workload": "SGEMM fp32 square sweep m=n=k in {1024,2048,3072,4096,5120,6144},"
+                                    " row-major A and B, U[-1,1] inputs, C pre-filled U[-1,1],"
+                                    " alpha=1 beta=1", "shapes": SWEEP, "schedule": "AUTO"})
+            del cases
+        else:
+            out = {}
+            for dt, name in ((sk.F16, "f16"), (sk.BF16, "bf16")):
+                h = make_hgemm_inputs(torch, sk, S, dt)
+                ms, per_launch, wall = timed(torch, lambda ev: hgemm_step(sk, h, ev), 1, steps, warmup)
+                fl = 2.0 * 8192 ** 3
+                achieved = fl / (per_launch[0] * 1e-3) / 1e12
+                out[name] = dict(value=fl / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype=name,
+                                 roofline={"bound": "mfma", "achieved": round(achieved, 2),
+                                           "peak": PEAK_TFLOPS[name], "unit": "TFLOP/s",
+                                           "frac": round(achieved / PEAK_TFLOPS[name], 4),
+                                           "traffic": TRAFFIC_BYTES[wl],
+                                           "kernel": f"hgemm_kernel<{name}>",
+                                           "launch_ms": round(per_launch[0], 4)})
+                del h
+                torch.cuda.empty_cache()
+            r = out["f16"]
+            r["bf16"] = {k: out["bf16"][k] for k in ("value", "ms", "roofline")} if "bf16" in out else None
+            r["config"] = {"workload": "HGEMM 8192^3, fp16 in/out (bf16 also timed), fp32 accumulate,"
+                                       " A row-major, B column-major, N(0,1)/sqrt(k), alpha=1 beta=0",
+                           "schedule": "AUTO"}
+            results[wl] = r
+        torch.cuda.empty_cache()
+
+    m = results[args.workload]
+    line = {"metric": METRIC, "value": round(m["value"], 3), "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms"], 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": m["dtype"], "data": "synthetic", "config": m["config"],
+            "roofline": m["roofline"]}
+    if "per_shape" in m:
+        line["per_shape_tflops"] = m["per_shape"]
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(S)
+    for wl, r in results.items():
+        if wl == args.workload:
+            continue
+        extra = {"value": round(r["value"], 3), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
+                 "dtype": r["dtype"], "roofline": r["roofline"], "config": r["config"]}
+        if r.get("bf16"):
+            extra["bf16"] = {"value": round(r["bf16"]["value"], 3), "roofline": r["bf16"]["roofline"]}
+        if "per_shape" in r:
+            extra["per_shape_tflops"] = r["per_shape"]
+        line["hgemm" if wl == "hgemm-8192" else "sgemm"] = extra
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
