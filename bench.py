@@ -49,7 +49,21 @@ def parse():
     p.add_argument("--workload", default="sgemm-sweep", choices=["sgemm-sweep", "hgemm-8192"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workload")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
+                        "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
     return p.parse_args()
+
+
+def calibrate_copy(torch):
+    n = (1 << 30) // 4  # 1 GiB of fp32
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "copy", "bytes_read_per_dispatch": 1 << 30,
+                      "bytes_written_per_dispatch": 1 << 30, "dispatches": 5}), flush=True)
 
 
 def make_sweep_inputs(torch, sk, S):
@@ -158,6 +172,9 @@ def main():
         print("no GPU visible", file=sys.stderr)
         sys.exit(3)
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        calibrate_copy(torch)
+        return
 
     results = {}
     order = [args.workload] + ([] if args.no_extra else

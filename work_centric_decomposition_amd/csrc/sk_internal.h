@@ -10,8 +10,8 @@ namespace sk {
 
 // Tile shape and launch shape of each kernel instance.
 //   HGEMM (fp16/bf16): 256 x 256 x 64 tiles, 512 threads (8 wave64s laid out
-//   2 x 4, each wave owns a 128 x 64 block of C), two LDS stages of 64 KiB,
-//   one workgroup per CU.
+//   2 x 4, two per SIMD, each owning a 128 x 64 block of C), two LDS stages
+//   of 64 KiB, one workgroup per CU.
 //   SGEMM (fp32): 128 x 128 x 32 tiles, 256 threads (4 wave64s, 2 x 2, each
 //   64 x 64), two LDS stages of 32 KiB, two workgroups per CU.
 struct TileCfg {
@@ -23,9 +23,22 @@ struct TileCfg {
   float a, b, c, d;
 };
 
+// k-depth of an HGEMM tile iteration and number of LDS stages (a build-time
+// choice; the default is two stages of 64).
+#ifndef SK_HGEMM_BK
+#define SK_HGEMM_BK 64
+#endif
+#ifndef SK_HGEMM_STAGES
+#define SK_HGEMM_STAGES 2
+#endif
+
 inline TileCfg tile_cfg(int dtype) {
   if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 0.25f, 1.f, 0.25f};
-  return TileCfg{256, 256, 64, 512, 1, 2 * 2 * 256 * 64 * 2, 4.f, 2.f, 1.f, 2.f};
+  // model constants in units of one iteration: a 256 x 256 fp32 partial costs
+  // about two 64-deep iterations to write or to read and add
+  const float it = SK_HGEMM_BK / 64.f;
+  return TileCfg{256, 256, SK_HGEMM_BK, 512, 1, SK_HGEMM_STAGES * 2 * 256 * SK_HGEMM_BK * 2,
+                 4.f / it, 2.f / it, 1.f, 2.f / it};
 }
 
 // Resolved work decomposition (integers only).

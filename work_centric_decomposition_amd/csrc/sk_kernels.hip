@@ -129,12 +129,12 @@ template <> struct Elem<SK_F32> {
 // owner reads the flag with agent-scope acquire semantics (invalidating its
 // own stale cached copies) before any thread loads the partial.
 
-template <int NT, int NACC>
-__device__ __forceinline__ void store_partial(const KernelArgs &a, int x, const f4_t (&acc)[NACC]) {
-  f4_t *slot = reinterpret_cast<f4_t *>(a.partials) + (int64_t)x * NACC * NT;
+template <class P>
+__device__ __forceinline__ void store_partial(const KernelArgs &a, int x, const typename P::Acc &acc) {
+  f4_t *slot = reinterpret_cast<f4_t *>(a.partials) + (int64_t)x * P::NACC4 * P::NT;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < NACC; ++i) slot[i * NT + t] = acc[i];
+  for (int i = 0; i < P::NACC4; ++i) slot[i * P::NT + t] = P::get4(acc, i);
   __syncthreads();
   if (t == 0) __hip_atomic_store(a.flags + x, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -160,45 +160,34 @@ __device__ __forceinline__ bool wait_flag(const KernelArgs &a, int peer) {
   return ok_s != 0;
 }
 
-template <int NT, int NACC>
-__device__ __forceinline__ void add_partial(const KernelArgs &a, int peer, f4_t (&acc)[NACC]) {
-  const f4_t *slot = reinterpret_cast<const f4_t *>(a.partials) + (int64_t)peer * NACC * NT;
+template <class P>
+__device__ __forceinline__ void add_partial(const KernelArgs &a, int peer, typename P::Acc &acc) {
+  const f4_t *slot = reinterpret_cast<const f4_t *>(a.partials) + (int64_t)peer * P::NACC4 * P::NT;
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < NACC; ++i) acc[i] += slot[i * NT + t];
+  for (int i = 0; i < P::NACC4; ++i) P::add4(acc, i, slot[i * P::NT + t]);
 }
 
 // ------------------------------------------------------------ epilogue
 //
-// Lane (l) of a wave holds, for accumulator block (mb, nb), row
-// r0 + mb*16 + (l & 15) and columns c0 + nb*16 + 4*(l >> 4) + {0..3}.
-template <int DT, int MB, int NB>
-__device__ __forceinline__ void epilogue(const KernelArgs &a, bool vec_ok, int row0, int col0,
-                                         const f4_t (&acc)[MB * NB]) {
+// Stores alpha * v + beta * C for the four consecutive columns j..j+3 of row
+// i (columns at or beyond n are skipped; C is not read when beta == 0).
+template <int DT>
+__device__ __forceinline__ void store4(const KernelArgs &a, bool vec_ok, int i, int j, f4_t v) {
   using E = Elem<DT>;
-  const int lane = threadIdx.x & 63;
+  if (i >= a.m || j >= a.n) return;
+  const int64_t off = (int64_t)i * a.ldc + j;
+  v *= a.alpha;
+  if (vec_ok && j + 3 < a.n) {
+    if (a.beta != 0.f) v += a.beta * E::ld4(a.C, off);
+    E::st4(a.C, off, v);
+  } else {
 #pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int i = row0 + mb * 16 + (lane & 15);
-    if (i >= a.m) continue;
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) {
-      const int j = col0 + nb * 16 + 4 * (lane >> 4);
-      if (j >= a.n) continue;
-      const int64_t off = (int64_t)i * a.ldc + j;
-      f4_t v = acc[mb * NB + nb] * a.alpha;
-      if (vec_ok && j + 3 < a.n) {
-        if (a.beta != 0.f) v += a.beta * E::ld4(a.C, off);
-        E::st4(a.C, off, v);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (j + e < a.n) {
-            float o = v[e];
-            if (a.beta != 0.f) o += a.beta * E::ld(a.C, off + e);
-            E::st(a.C, off + e, o);
-          }
-        }
+    for (int e = 0; e < 4; ++e) {
+      if (j + e < a.n) {
+        float o = v[e];
+        if (a.beta != 0.f) o += a.beta * E::ld(a.C, off + e);
+        E::st(a.C, off + e, o);
       }
     }
   }
@@ -252,77 +241,249 @@ __device__ __forceinline__ void load_mnmajor_f32x128(int lds_off, const char *ba
   }
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (LDS/scalar and export counters unchecked).
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+typedef float f16v_t __attribute__((ext_vector_type(16)));
+
 // ============================================================== HGEMM
-// 256 x 256 x 64 tiles, 8 waves as 2 (m) x 4 (n), wave tile 128 x 64,
-// v_mfma_f32_16x16x32_{f16,bf16}: 8 x 4 blocks per wave.
-struct HCfg {
-  static constexpr int BM = 256, BN = 256, BK = 64, NT = 512;
-  static constexpr int WTM = 128, WTN = 64, MB = 8, NB = 4, NACC = MB * NB;
-  static constexpr int A_BYTES = BM * BK * 2, B_BYTES = BN * BK * 2;
+// 256 x 256 x BK tiles (BK = 64 by default), 8 waves (two per SIMD) as
+// 2 (m) x 4 (n), wave tile 128 x 64 = 4 x 2 blocks of
+// v_mfma_f32_32x32x16_{f16,bf16} (16 fp32 per lane per block, 128 per lane).
+// A k-iteration is BK/16 k-substeps; the fragments of one substep are 6 LDS
+// reads (24 VGPRs).  NSTAGE LDS stages (two of 64 KiB by default): loads are
+// issued NSTAGE-1 iterations ahead of their use.
+// 32x32 block layout, with the product formed as C^T = B^T A^T: register r
+// of lane l holds row (l & 31) and column 8*(r/4) + 4*(l >> 5) + (r & 3) of
+// the block, i.e. four consecutive columns per register quad.
+template <int DT>
+struct HPolicy {
+  static constexpr int BM = 256, BN = 256, BK = SK_HGEMM_BK, NT = 512, NSTAGE = SK_HGEMM_STAGES;
+  static constexpr int SUBS = BK / 16;  // k-substeps of one iteration
+  static_assert(SUBS % 2 == 0 && NSTAGE >= 2 && NSTAGE <= 5, "pipeline shape");
+  static constexpr int WTM = 128, WTN = 64, MB = 4, NB = 2;
+  static constexpr int WAVES_N = BN / WTN;
+  static constexpr int NACC4 = MB * NB * 4;
+  static constexpr int ROW = BK * 2;  // bytes of one LDS row (k-contiguous)
+  static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LOADS = A_BYTES / 1024 / (NT / 64);  // per operand per wave and stage
+  static constexpr int ROWS_PER_LOAD = 1024 / ROW;
+  // 16-byte chunk c of LDS row r is stored at chunk position c ^ swz(r):
+  // the 16 lanes of one LDS cycle (rows r..r+15, one chunk) then touch 16
+  // distinct 16-byte bank groups of gfx950's 64 banks (256 bytes hold
+  // 256/ROW rows; consecutive groups of them get distinct XOR masks).
+  static __device__ __forceinline__ int swz(int r) { return (r / (256 / ROW)) % (ROW / 16); }
+  struct Acc { f16v_t v[MB * NB]; };
+  static __device__ __forceinline__ f4_t get4(const Acc &c, int i) {
+    const f16v_t &b = c.v[i >> 2];
+    const int g = i & 3;
+    return f4_t{b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
+  }
+  static __device__ __forceinline__ void add4(Acc &c, int i, f4_t x) {
+    f16v_t &b = c.v[i >> 2];
+    const int g = i & 3;
+    b[4 * g] += x[0]; b[4 * g + 1] += x[1]; b[4 * g + 2] += x[2]; b[4 * g + 3] += x[3];
+  }
+  static __device__ __forceinline__ void zero(Acc &c) {
+#pragma unroll
+    for (int i = 0; i < MB * NB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c.v[i][e] = 0.f;
+  }
 };
 
+// Direct-to-LDS loads of one tile's A and B k-slices.  The per-lane byte
+// offsets (row * ld + swizzled chunk, or an out-of-range offset for rows
+// past the matrix) are computed once per tile; each k-iteration only adds
+// the scalar offset k0 * 2.  In the iteration that holds the end of k,
+// chunks at or past k are fetched out of range (zeros).
 template <int DT>
-__device__ __forceinline__ void h_load(const KernelArgs &a, int stage, int m0, int n0, int kit) {
-  constexpr int ES = 2;
-  const int k0 = kit * HCfg::BK;
-  const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
-  const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * lda_b + (int64_t)k0 * ES;
-  const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * ldb_b + (int64_t)k0 * ES;
-  const int64_t a_total = (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)(a.a_kext - k0) * ES;
-  const int64_t b_total = (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)(a.b_kext - k0) * ES;
-  const int kb = (a.k - k0) * ES;
-  load_kmajor_128<HCfg::BM, HCfg::NT>(stage * HCfg::STAGE, Ab, lda_b, a.m - m0, kb, a_total);
-  load_kmajor_128<HCfg::BN, HCfg::NT>(stage * HCfg::STAGE + HCfg::A_BYTES, Bb, ldb_b, a.n - n0, kb,
-                                      b_total);
+struct HLoader {
+  using P = HPolicy<DT>;
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[P::LOADS], vb[P::LOADS];
+  int chunk[P::LOADS];  // 16-byte k-chunk each load fetches (same for A and B)
+  int lds_a;            // LDS byte offset of this wave's first A load (stage 0)
+
+  __device__ __forceinline__ void init(const KernelArgs &a, int m0, int n0) {
+    constexpr int ES = 2;
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
+    const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * lda_b;
+    const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * ldb_b;
+    ra = make_rsrc(Ab, (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)a.a_kext * ES);
+    rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
+    constexpr int CPR = P::ROW / 16;  // chunks per row
+#pragma unroll
+    for (int j = 0; j < P::LOADS; ++j) {
+      const int row = (w * P::LOADS + j) * P::ROWS_PER_LOAD + lane / CPR;
+      const int c = (lane % CPR) ^ P::swz(row);
+      chunk[j] = c;
+      va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
+      vb[j] = row < a.n - n0 ? (uint32_t)(row * ldb_b + c * 16) : kOOB;
+    }
+    lds_a = w * P::LOADS * 1024;
+  }
+
+  __device__ __forceinline__ void load(const KernelArgs &a, int stage, int kit) const {
+    const int k0b = kit * P::BK * 2;
+    const int left = (a.k - kit * P::BK) * 2;  // bytes of k from k0
+    const int base = stage * P::STAGE + lds_a;
+    if (left >= P::BK * 2) {
+#pragma unroll
+      for (int j = 0; j < P::LOADS; ++j) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + base + j * 1024), 16, va[j], k0b, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + base + P::A_BYTES + j * 1024), 16,
+                                                 vb[j], k0b, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < P::LOADS; ++j) {
+        const bool ok = chunk[j] * 16 < left;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + base + j * 1024), 16,
+                                                 ok ? va[j] : kOOB, k0b, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + base + P::A_BYTES + j * 1024), 16,
+                                                 ok ? vb[j] : kOOB, k0b, 0, 0);
+      }
+    }
+  }
+};
+
+// Fragments of k-substep `sub` (16 values of k) of an LDS stage: lane l
+// holds row (l & 31) of each 32-row block and k chunk 2*sub + (l >> 5).
+template <int DT>
+__device__ __forceinline__ void h_frags(int stage, int sub, int wm, int wn,
+                                        typename Elem<DT>::V8 (&af)[HPolicy<DT>::MB],
+                                        typename Elem<DT>::V8 (&bf)[HPolicy<DT>::NB]) {
+  using P = HPolicy<DT>;
+  using V8 = typename Elem<DT>::V8;
+  const int lane = threadIdx.x & 63;
+  const int As = stage * P::STAGE, Bs = As + P::A_BYTES;
+  const int c = sub * 2 + (lane >> 5);
+#pragma unroll
+  for (int nb = 0; nb < P::NB; ++nb) {
+    const int row = wn * P::WTN + nb * 32 + (lane & 31);
+    bf[nb] = *reinterpret_cast<const V8 *>(smem + Bs + row * P::ROW + ((c ^ P::swz(row)) << 4));
+  }
+#pragma unroll
+  for (int mb = 0; mb < P::MB; ++mb) {
+    const int row = wm * P::WTM + mb * 32 + (lane & 31);
+    af[mb] = *reinterpret_cast<const V8 *>(smem + As + row * P::ROW + ((c ^ P::swz(row)) << 4));
+  }
 }
 
 template <int DT>
-__device__ __forceinline__ void h_compute(int stage, int wm, int wn, f4_t (&acc)[HCfg::NACC]) {
-  using E = Elem<DT>;
-  using V8 = typename E::V8;
-  const int lane = threadIdx.x & 63;
-  const int As = stage * HCfg::STAGE, Bs = As + HCfg::A_BYTES;
+__device__ __forceinline__ f16v_t h_mfma(typename Elem<DT>::V8 a, typename Elem<DT>::V8 b, f16v_t c);
+template <>
+__device__ __forceinline__ f16v_t h_mfma<SK_F16>(h8_t a, h8_t b, f16v_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ f16v_t h_mfma<SK_BF16>(b8_t a, b8_t b, f16v_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int DT>
+__device__ __forceinline__ void h_mfmas(const typename Elem<DT>::V8 (&af)[HPolicy<DT>::MB],
+                                        const typename Elem<DT>::V8 (&bf)[HPolicy<DT>::NB],
+                                        typename HPolicy<DT>::Acc &acc) {
+  using P = HPolicy<DT>;
 #pragma unroll
-  for (int ks = 0; ks < HCfg::BK / 32; ++ks) {
-    V8 bf[HCfg::NB], af[HCfg::MB];
-    const int c = ks * 4 + (lane >> 4);
+  for (int mb = 0; mb < P::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < HCfg::NB; ++nb) {
-      const int row = wn * HCfg::WTN + nb * 16 + (lane & 15);
-      bf[nb] = *reinterpret_cast<const V8 *>(smem + Bs + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-    }
-#pragma unroll
-    for (int mb = 0; mb < HCfg::MB; ++mb) {
-      const int row = wm * HCfg::WTM + mb * 16 + (lane & 15);
-      af[mb] = *reinterpret_cast<const V8 *>(smem + As + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-    }
-#pragma unroll
-    for (int mb = 0; mb < HCfg::MB; ++mb)
-#pragma unroll
-      for (int nb = 0; nb < HCfg::NB; ++nb)
-        acc[mb * HCfg::NB + nb] = E::mfma(bf[nb], af[mb], acc[mb * HCfg::NB + nb]);
-  }
+    for (int nb = 0; nb < P::NB; ++nb)
+      acc.v[mb * P::NB + nb] = h_mfma<DT>(bf[nb], af[mb], acc.v[mb * P::NB + nb]);
+}
+
+// s_waitcnt immediate: at most n vector-memory operations of this wave
+// outstanding and no LDS read outstanding.
+constexpr int vmcnt_le_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Waits until at most `stages` stages of this wave's loads are outstanding
+// (and all of its LDS reads have completed).  A wave's vector-memory
+// operations complete in issue order.
+template <int LPS>
+__device__ __forceinline__ void wait_stages(int stages) {
+  if (stages >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(3 * LPS));
+  else if (stages == 2) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(2 * LPS));
+  else if (stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(LPS));
+  else __builtin_amdgcn_s_waitcnt(0);
 }
 
 // MacLoop over iterations [lb, le) of the tile at (m0, n0).
+//
+// Software pipeline: NSTAGE LDS stages and two register sets of fragments.
+// While the MFMAs of substep s run, the fragments of substep s+1 are read.
+// Before the last substep: wait until this wave's loads of stage i+1 have
+// landed, barrier (every wave has also finished reading stage i), issue the
+// loads of iteration i+NSTAGE into stage i's buffer, and read substep 0 of
+// stage i+1 while the MFMAs of the last substep run.  A load thus has
+// NSTAGE-1 iterations to land, and LDS latency is covered by MFMAs.
 template <int DT>
 __device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
-                                          f4_t (&acc)[HCfg::NACC]) {
+                                          typename HPolicy<DT>::Acc &acc) {
+  using P = HPolicy<DT>;
+  using V8 = typename Elem<DT>::V8;
+  constexpr int NS = P::NSTAGE, LPS = 2 * P::LOADS;
   const int w = wave_id();
-  const int wm = w / 4, wn = w % 4;
+  const int wm = w / P::WAVES_N, wn = w % P::WAVES_N;
+  P::zero(acc);
+  const int n = le - lb;
+  if (n <= 0) return;
+  HLoader<DT> ld;
+  ld.init(a, m0, n0);
+  const int pre = n < NS ? n : NS;
+  for (int s = 0; s < pre; ++s) ld.load(a, s, lb + s);
+  wait_stages<LPS>(pre - 1);
+  __syncthreads();
+  V8 fa0[P::MB], fb0[P::NB], fa1[P::MB], fb1[P::NB];
+  h_frags<DT>(0, 0, wm, wn, fa0, fb0);
+  int buf = 0;
+  for (int i = 0; i < n; ++i) {
 #pragma unroll
-  for (int i = 0; i < HCfg::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
-  if (lb >= le) return;
-  h_load<DT>(a, 0, m0, n0, lb);
-  for (int it = lb; it < le; ++it) {
-    const int cur = (it - lb) & 1;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of stage `cur` have landed
+    for (int sub = 0; sub + 1 < P::SUBS; ++sub) {
+      if (sub % 2 == 0) {
+        h_frags<DT>(buf, sub + 1, wm, wn, fa1, fb1);
+        __builtin_amdgcn_sched_barrier(0);
+        h_mfmas<DT>(fa0, fb0, acc);
+      } else {
+        h_frags<DT>(buf, sub + 1, wm, wn, fa0, fb0);
+        __builtin_amdgcn_sched_barrier(0);
+        h_mfmas<DT>(fa1, fb1, acc);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // last substep: switch stages.  Stages issued beyond i+1:
+    // min(i+NS-1, n-1) - (i+1).
+    const int last = i + NS - 1 < n - 1 ? i + NS - 1 : n - 1;
+    wait_stages<LPS>(last - (i + 1));
     __syncthreads();
-    if (it + 1 < le) h_load<DT>(a, cur ^ 1, m0, n0, it + 1);
-    h_compute<DT>(cur, wm, wn, acc);
+    if (i + NS < n) ld.load(a, buf, lb + i + NS);
+    const int nbuf = buf + 1 == NS ? 0 : buf + 1;
+    if (i + 1 < n) h_frags<DT>(nbuf, 0, wm, wn, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    h_mfmas<DT>(fa1, fb1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    buf = nbuf;
   }
-  __syncthreads();  // the next segment's loads reuse the stages
+}
+
+template <int DT>
+__device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
+                                           const typename HPolicy<DT>::Acc &acc) {
+  using P = HPolicy<DT>;
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int r0 = m0 + (w / P::WAVES_N) * P::WTM, c0 = n0 + (w % P::WAVES_N) * P::WTN;
+#pragma unroll
+  for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        store4<DT>(a, vec_ok, r0 + mb * 32 + (lane & 31), c0 + nb * 32 + 8 * g + 4 * (lane >> 5),
+                   P::get4(acc, (mb * P::NB + nb) * 4 + g));
 }
 
 // ============================================================== SGEMM
@@ -436,30 +597,56 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   __syncthreads();
 }
 
+template <bool AK, bool BKM>
+struct SPolicy {
+  static constexpr int BM = SCfg::BM, BN = SCfg::BN, NT = SCfg::NT;
+  static constexpr int NACC4 = SCfg::NACC;
+  struct Acc { f4_t v[SCfg::NACC]; };
+  static __device__ __forceinline__ f4_t get4(const Acc &c, int i) { return c.v[i]; }
+  static __device__ __forceinline__ void add4(Acc &c, int i, f4_t x) { c.v[i] += x; }
+};
+
+// 16x16 block layout (SGEMM): lane l of a wave holds, for block (mb, nb),
+// row (l & 15) and columns 4*(l >> 4) + {0..3} of the block.
+template <bool AK, bool BKM>
+__device__ __forceinline__ void s_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
+                                           const typename SPolicy<AK, BKM>::Acc &acc) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  constexpr int WN = SCfg::BN / SCfg::WTN;
+  const int r0 = m0 + (w / WN) * SCfg::WTM, c0 = n0 + (w % WN) * SCfg::WTN;
+#pragma unroll
+  for (int mb = 0; mb < SCfg::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < SCfg::NB; ++nb)
+      store4<SK_F32>(a, vec_ok, r0 + mb * 16 + (lane & 15), c0 + nb * 16 + 4 * (lane >> 4),
+                     acc.v[mb * SCfg::NB + nb]);
+}
+
 // ======================================================= work iteration
 
-// Runs one segment: MacLoop, then partial store or fixup + epilogue.
-template <class Cfg, class MacLoop, int DT>
-__device__ __forceinline__ void run_segment(const KernelArgs &a, bool vec_ok, int x, int tile, int lb,
-                                            int le, bool started, int last_peer, MacLoop macloop) {
-  f4_t acc[Cfg::NACC];
+// Runs one segment: MacLoop, then partial store, or fixup + epilogue.
+template <class P, class MacLoop, class Epilogue>
+__device__ __forceinline__ void run_segment(const KernelArgs &a, int x, int tile, int lb, int le,
+                                            bool started, int last_peer, MacLoop macloop,
+                                            Epilogue epilogue) {
+  typename P::Acc acc;
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int m0 = tm * P::BM, n0 = tn * P::BN;
   macloop(m0, n0, lb, le, acc);
   if (!started) {
-    store_partial<Cfg::NT, Cfg::NACC>(a, x, acc);
+    store_partial<P>(a, x, acc);
     return;
   }
   for (int p = x + 1; p <= last_peer; ++p) {
-    if (wait_flag(a, p)) add_partial<Cfg::NT, Cfg::NACC>(a, p, acc);
+    if (wait_flag(a, p)) add_partial<P>(a, p, acc);
   }
-  const int w = wave_id();
-  constexpr int WN = Cfg::BN / Cfg::WTN;
-  epilogue<DT, Cfg::MB, Cfg::NB>(a, vec_ok, m0 + (w / WN) * Cfg::WTM, n0 + (w % WN) * Cfg::WTN, acc);
+  epilogue(m0, n0, acc);
 }
 
-template <class Cfg, int DT, class MacLoop>
-__device__ __forceinline__ void run_workgroup(const KernelArgs &a, bool vec_ok, MacLoop macloop) {
+// All segments of workgroup blockIdx.x: its Stream-K range (Algorithm 5 on
+// tiles [0, sk_tiles)), then its data-parallel tiles.
+template <class P, class MacLoop, class Epilogue>
+__device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop macloop, Epilogue epilogue) {
   const int x = blockIdx.x;
   if (a.sk_tiles > 0) {
     int64_t it = (int64_t)x * a.sk_q + (x < a.sk_r ? x : a.sk_r);
@@ -474,26 +661,29 @@ __device__ __forceinline__ void run_workgroup(const KernelArgs &a, bool vec_ok, 
         const int64_t big = a.sk_r * (a.sk_q + 1), l = te - 1;
         last_peer = (int)(l < big ? l / (a.sk_q + 1) : a.sk_r + (l - big) / a.sk_q);
       }
-      run_segment<Cfg, MacLoop, DT>(a, vec_ok, x, tile, lb, le, started, last_peer, macloop);
+      run_segment<P>(a, x, tile, lb, le, started, last_peer, macloop, epilogue);
       it = te;
     }
   }
   for (int tile = a.sk_tiles + x; tile < a.tiles; tile += a.grid)
-    run_segment<Cfg, MacLoop, DT>(a, vec_ok, x, tile, 0, a.ipt, true, -1, macloop);
+    run_segment<P>(a, x, tile, 0, a.ipt, true, -1, macloop, epilogue);
 }
 
 template <int DT>
-__global__ __launch_bounds__(HCfg::NT) void hgemm_kernel(KernelArgs a, int vec_ok) {
-  run_workgroup<HCfg, DT>(a, vec_ok != 0, [&](int m0, int n0, int lb, int le, f4_t(&acc)[HCfg::NACC]) {
-    h_macloop<DT>(a, m0, n0, lb, le, acc);
-  });
+__global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, int vec_ok) {
+  using P = HPolicy<DT>;
+  run_workgroup<P>(
+      a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { h_macloop<DT>(a, m0, n0, lb, le, acc); },
+      [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<DT>(a, vec_ok != 0, m0, n0, acc); });
 }
 
 template <bool AK, bool BKM>
 __global__ __launch_bounds__(SCfg::NT) void sgemm_kernel(KernelArgs a, int vec_ok) {
-  run_workgroup<SCfg, SK_F32>(a, vec_ok != 0, [&](int m0, int n0, int lb, int le, f4_t(&acc)[SCfg::NACC]) {
-    s_macloop<AK, BKM>(a, m0, n0, lb, le, acc);
-  });
+  using P = SPolicy<AK, BKM>;
+  run_workgroup<P>(
+      a,
+      [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { s_macloop<AK, BKM>(a, m0, n0, lb, le, acc.v); },
+      [&](int m0, int n0, const typename P::Acc &acc) { s_epilogue<AK, BKM>(a, vec_ok != 0, m0, n0, acc); });
 }
 
 // ========================================================= small kernels
