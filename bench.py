@@ -132,6 +132,38 @@ def timed(torch, step, n_launch, steps, warmup):
     return max(total_ms, 0.0) / steps, per_launch, wall / steps
 
 
+def abft_overhead(torch, sk, S, steps=10):
+    """4096^3 fp32 GEMM (row-major, U[-1,1], alpha=1, beta=0) with and without
+    ABFT (no faults), each timed over `steps` launches."""
+    import ctypes
+    n = 4096
+    A = torch.from_numpy(S.matrix(S.SEED_ABFT, S.STREAM_A, n, n, S.F32)).cuda()
+    B = torch.from_numpy(S.matrix(S.SEED_ABFT, S.STREAM_B, n, n, S.F32)).cuda()
+    C = torch.zeros(n * n, dtype=torch.float32, device="cuda")
+    rep = torch.zeros(ctypes.sizeof(sk.AbftReport), dtype=torch.uint8, device="cuda")
+    d = sk.make_desc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, sk.F32, sk.A_ROW_B_ROW)
+    out = {}
+    for name, opts in (("plain", sk.make_options()), ("abft", sk.make_options(abft=True))):
+        def one():
+            sk.gemm_ex(d, opts, rep if name == "abft" else None)
+        for _ in range(2):
+            one()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            one()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name] = {"ms": round(ms, 4), "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 2)}
+    r = sk.read_report(rep)
+    out["overhead"] = round(out["abft"]["ms"] / out["plain"]["ms"] - 1.0, 4)
+    out["false_positives"] = int(r.detected)
+    out["config"] = "fp32 4096^3 row-major U[-1,1], alpha=1 beta=0, no faults injected"
+    return out
+
+
 def cpu_baseline(S, budget_s=25.0):
     """The oracle (six-loop fp64 GEMM, full output) on the fp32 sweep's
     shapes, smallest first, on the host's cores, stopping once about
@@ -240,6 +272,8 @@ def main():
         line["per_shape_tflops"] = m["per_shape"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(S)
+    if not args.no_extra:
+        line["abft"] = abft_overhead(torch, sk, S)
     for wl, r in results.items():
         if wl == args.workload:
             continue

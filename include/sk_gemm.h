@@ -125,7 +125,7 @@ typedef struct {
   int32_t detected;      /* verification domains with any mismatch */
   int32_t corrected;     /* elements corrected */
   int32_t uncorrectable; /* domains whose mismatch could not be located */
-  int32_t n_records;     /* records written (at most SK_ABFT_MAX_RECORDS) */
+  int32_t n_records;     /* records produced; the first SK_ABFT_MAX_RECORDS are stored */
   sk_abft_record records[SK_ABFT_MAX_RECORDS];
 } sk_abft_report;
 

@@ -614,9 +614,9 @@ int or_sk_execute(int64_t m, int64_t n, int64_t k, double alpha, const void *A, 
  *     rc_i = sum_l A_il (B e)_l        (row checksum,  C e   = A (B e))
  *     cc_j = sum_l (e^T A)_l B_lj      (column checksum, e^T C = (e^T A) B)
  * and absolute versions ra, ca with |A|, |B| for the detection threshold
- * tau = c_tau * 2^-24 * ra_i (rows), c_tau * 2^-24 * ca_j (columns)
- * (reading: the pages give no threshold; this scales with the rounding error
- * of an fp32 accumulation).
+ * tau = c_tau * 2^-24 * sqrt(kk) * ra_i (rows), likewise with ca_j (columns)
+ * (reading: the pages give no threshold; the rounding error of an fp32 dot
+ * product of length kk grows like sqrt(kk) * 2^-24 * sum |a||b|).
  * Verify: row residual dr_i = sum_j C_ij - rc_i, column residual dc_j likewise;
  * a row/column mismatches when |residual| > tau or the residual is not finite.
  * Locate: the intersection of the single mismatching row and column.
@@ -638,7 +638,7 @@ int or_abft_check(int64_t rows, int64_t cols, int64_t kk, const double *A_blk, c
     for (int64_t j = 0; j < cols; ++j) { be[l] += B_blk[l * cols + j]; bea[l] += fabs(B_blk[l * cols + j]); }
     for (int64_t i = 0; i < rows; ++i) { ea[l] += A_blk[i * kk + l]; eaa[l] += fabs(A_blk[i * kk + l]); }
   }
-  const double u = ldexp(1.0, -24);
+  const double u = ldexp(1.0, -24) * sqrt((double)(kk > 0 ? kk : 1));
   int64_t bad_r = -1, bad_c = -1, n_bad_r = 0, n_bad_c = 0;
   for (int64_t i = 0; i < rows; ++i) {
     double rc = 0, ra = 0, s = 0;

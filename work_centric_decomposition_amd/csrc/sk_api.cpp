@@ -33,6 +33,7 @@ struct DeviceInfo {
   bool ok = false;
   int cus = 0;
   int slots[3] = {0, 0, 0};  // per dtype
+  int slots_abft = 0;        // fp32 with ABFT
   int64_t wall_khz = 100000;
 };
 
@@ -73,16 +74,17 @@ int device_info(int dev, DeviceInfo **out) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     d.wall_khz = khz;
-  for (int dt = 0; dt < 3; ++dt) {
+  for (int dt = 0; dt < 4; ++dt) {  // 3: fp32 with ABFT
     int occ = 0;
-    e = (hipError_t)kernel_occupancy(dt, &occ);
+    const int dtype = dt == 3 ? SK_F32 : dt;
+    e = (hipError_t)kernel_occupancy(dtype, dt == 3, &occ);
     if (e != hipSuccess) return hip_fail(e, "occupancy query");
-    const int want = tile_cfg(dt).occupancy;
+    const int want = tile_cfg(dtype).occupancy;
     if (occ < 1) {
       g_last_hip_error = "kernel does not fit on a CU";
       return SK_ERR_HIP;
     }
-    d.slots[dt] = d.cus * (occ < want ? occ : want);
+    (dt == 3 ? d.slots_abft : d.slots[dt]) = d.cus * (occ < want ? occ : want);
   }
   d.ok = true;
   forget.armed = false;
@@ -177,7 +179,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "scale kernel");
   }
   Plan P;
-  rc = make_plan(d, o, info->slots[d.dtype], P);
+  rc = make_plan(d, o, o.abft ? info->slots_abft : info->slots[d.dtype], P);
   if (rc != SK_OK) return rc;
   const int es = d.dtype == SK_F32 ? 4 : 2;
   const bool ak = a_kmajor_of(d.layout), bk = b_kmajor_of(d.layout);
@@ -292,7 +294,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       int rc = device_info(dev, &info);
       if (rc != SK_OK) return rc;
       if (desc->dtype < 0 || desc->dtype > 2) return SK_ERR_INVALID_ARG;
-      slots = info->slots[desc->dtype];
+      slots = o.abft && desc->dtype == SK_F32 ? info->slots_abft : info->slots[desc->dtype];
     }
     Plan P;
     int rc = make_plan(*desc, o, slots, P);

@@ -112,7 +112,7 @@ int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t l
 int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_t rows,
                 int64_t k, void *dst, int64_t ldd, hipStream_t stream);
 int launch_zero_report(sk_abft_report *report, hipStream_t stream);
-// Occupancy query for the GEMM kernel of `dtype`.
-int kernel_occupancy(int dtype, int *blocks_per_cu);
+// Occupancy query for the GEMM kernel of `dtype` (fp32: with or without ABFT).
+int kernel_occupancy(int dtype, bool abft, int *blocks_per_cu);
 
 }  // namespace sk

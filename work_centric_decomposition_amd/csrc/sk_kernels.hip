@@ -578,7 +578,244 @@ __device__ __forceinline__ void s_compute(int stage, int wm, int wn, f4_t (&acc)
   }
 }
 
+// ---------------------------------------------------------------- ABFT
+//
+// Threadblock-level ABFT of the fault-tolerant GEMM page, per work segment.
+// Each k-iteration, from the tiles already staged in LDS:
+//   encodings   (e^T A)_k = sum_i A_ik,  (B e)_k = sum_j B_kj   (and |.| sums)
+//   checksums   rc_i += sum_k A_ik (B e)_k     -- row checksum of C = A B
+//               cc_j += sum_k (e^T A)_k B_kj   -- column checksum
+//               ra_i, ca_j: the same with |A|, |B| (detection threshold).
+// At the end of the segment (before its partial store, or before the owner
+// adds its peers' partials) the row and column sums of the accumulators are
+// compared with the checksums: a row mismatches when |sum - rc_i| exceeds
+// tau * 2^-24 * sqrt(k_seg) * ra_i or is not finite (likewise columns), where
+// k_seg is the number of k values the segment accumulated: the rounding
+// error of an fp32 dot product of length k grows like sqrt(k) u sum|a||b|.  One mismatching
+// row and one mismatching column locate the fault; the element is recomputed
+// from its row checksum, c_ij = rc_i - sum_{l != j} c_il.  Any other pattern
+// is reported as uncorrectable.  All reductions run in a fixed order.
+struct AbftLds {
+  float enc[4][8][SCfg::BK];  // per-part encodings: e^T A, e^T|A|, B e, |B| e
+  float e[4][SCfg::BK];       // encodings of the iteration
+  float part[4][2][128];      // rc, ra, cc, ca: two k-halves
+  float sums[2][2][128];      // row sums per wave column, column sums per wave row
+  float others[SCfg::NT / 64];
+  int bad[4];                 // mismatching rows, one such row, columns, one such column
+};
+
+struct AbftPart {
+  float rc, ra, cc, ca;
+};
+
+// The ABFT working set in LDS (allocated only in kernels that use it).
+__device__ __forceinline__ AbftLds &abft_lds() {
+  __shared__ AbftLds L;
+  return L;
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ float s_elem(int base_off, int mn, int k) {
+  if (KMAJOR) {
+    const int c = k >> 2;
+    return *reinterpret_cast<const float *>(smem + base_off + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4) + (k & 3) * 4);
+  }
+  return s_mn_elem(base_off, mn, k);
+}
+
 template <bool AK, bool BKM>
+__device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, int n_valid, int k_valid,
+                                            AbftPart &pt) {
+  const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
+  const int t = threadIdx.x;
+  {  // encodings: thread t covers k = t % 32 over 16 rows / columns
+    const int k = t & (SCfg::BK - 1), part = t / SCfg::BK;
+    float ea = 0.f, eaa = 0.f, eb = 0.f, eba = 0.f;
+    if (k < k_valid) {
+#pragma unroll 4
+      for (int r = 0; r < 16; ++r) {
+        const int i = part * 16 + r;
+        if (i < m_valid) { const float v = s_elem<AK>(As, i, k); ea += v; eaa += fabsf(v); }
+        if (i < n_valid) { const float v = s_elem<BKM>(Bs, i, k); eb += v; eba += fabsf(v); }
+      }
+    }
+    L.enc[0][part][k] = ea; L.enc[1][part][k] = eaa; L.enc[2][part][k] = eb; L.enc[3][part][k] = eba;
+  }
+  __syncthreads();
+  if (t < 4 * SCfg::BK) {
+    const int q = t / SCfg::BK, k = t % SCfg::BK;
+    float v = 0.f;
+#pragma unroll
+    for (int p = 0; p < 8; ++p) v += L.enc[q][p][k];
+    L.e[q][k] = v;
+  }
+  __syncthreads();
+  {  // checksums: thread t covers row / column t % 128 over half of the k range
+    const int i = t & 127, h = t >> 7;
+    const bool row_ok = i < m_valid, col_ok = i < n_valid;
+#pragma unroll 4
+    for (int kk = 0; kk < SCfg::BK / 2; ++kk) {
+      const int k = h * (SCfg::BK / 2) + kk;
+      if (k < k_valid) {
+        if (row_ok) {
+          const float v = s_elem<AK>(As, i, k);
+          pt.rc += v * L.e[2][k];
+          pt.ra += fabsf(v) * L.e[3][k];
+        }
+        if (col_ok) {
+          const float v = s_elem<BKM>(Bs, i, k);
+          pt.cc += L.e[0][k] * v;
+          pt.ca += L.e[1][k] * fabsf(v);
+        }
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ void abft_record(const KernelArgs &a, int64_t row, int64_t col, float delta,
+                                            int status, int tile, int seg_begin) {
+  const int idx = atomicAdd(&a.report->n_records, 1);
+  if (idx < SK_ABFT_MAX_RECORDS) {
+    sk_abft_record &r = a.report->records[idx];
+    r.row = row; r.col = col; r.delta = delta; r.status = status; r.tile = tile; r.seg_begin = seg_begin;
+  }
+}
+
+// Verification of one segment; acc in the 16x16 block layout of the SGEMM
+// kernel (lane l of wave (wm, wn) holds row wm*64 + mb*16 + (l & 15) and
+// columns wn*64 + nb*16 + 4*(l >> 4) + e of the tile).
+__device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, const AbftPart &pt,
+                                            f4_t (&acc)[SCfg::NACC], int m0, int n0, int lb, int le) {
+  const int t = threadIdx.x, w = wave_id(), lane = t & 63;
+  const int wm = w / 2, wn = w % 2;
+  const int m_valid = a.m - m0, n_valid = a.n - n0;
+  {
+    const int i = t & 127, h = t >> 7;
+    L.part[0][h][i] = pt.rc; L.part[1][h][i] = pt.ra; L.part[2][h][i] = pt.cc; L.part[3][h][i] = pt.ca;
+  }
+  if (t < 4) L.bad[t] = t == 0 || t == 2 ? 0 : -1;
+  // injected faults (testing): applied to the accumulator before verification
+  for (int f = 0; f < a.n_faults; ++f) {
+    const sk_fault F = a.faults[f];
+    if (F.row < m0 || F.row >= m0 + SCfg::BM || F.col < n0 || F.col >= n0 + SCfg::BN) continue;
+    if (F.iter < lb || F.iter >= le) continue;
+    const int li = (int)(F.row - m0) - wm * SCfg::WTM, lj = (int)(F.col - n0) - wn * SCfg::WTN;
+    if (li < 0 || li >= SCfg::WTM || lj < 0 || lj >= SCfg::WTN) continue;
+    if ((lane & 15) != (li & 15) || (lane >> 4) != ((lj & 15) >> 2)) continue;
+    f4_t &v = acc[(li >> 4) * SCfg::NB + (lj >> 4)];
+    const int e = lj & 3;
+    if (F.kind == 0) {
+      v[e] += F.value;
+    } else {
+      uint32_t u = __float_as_uint(v[e]) ^ (1u << (F.bit & 31));
+      v[e] = __uint_as_float(u);
+    }
+  }
+  // row and column sums of the accumulators (valid elements only)
+#pragma unroll
+  for (int mb = 0; mb < SCfg::MB; ++mb) {
+    float sr = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < SCfg::NB; ++nb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int j = wn * SCfg::WTN + nb * 16 + 4 * (lane >> 4) + e;
+        if (j < n_valid) sr += acc[mb * SCfg::NB + nb][e];
+      }
+    sr += __shfl_xor(sr, 16);
+    sr += __shfl_xor(sr, 32);
+    if ((lane >> 4) == 0) L.sums[0][wn][wm * SCfg::WTM + mb * 16 + lane] = sr;
+  }
+#pragma unroll
+  for (int nb = 0; nb < SCfg::NB; ++nb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float sc = 0.f;
+#pragma unroll
+      for (int mb = 0; mb < SCfg::MB; ++mb) {
+        const int i = wm * SCfg::WTM + mb * 16 + (lane & 15);
+        if (i < m_valid) sc += acc[mb * SCfg::NB + nb][e];
+      }
+      sc += __shfl_xor(sc, 1);
+      sc += __shfl_xor(sc, 2);
+      sc += __shfl_xor(sc, 4);
+      sc += __shfl_xor(sc, 8);
+      if ((lane & 15) == 0) L.sums[1][wm][wn * SCfg::WTN + nb * 16 + 4 * (lane >> 4) + e] = sc;
+    }
+  __syncthreads();
+  const int kseg = ((le * SCfg::BK < a.k ? le * SCfg::BK : a.k) - lb * SCfg::BK);
+  const float u = 5.9604644775390625e-08f * sqrtf((float)kseg);  // 2^-24 sqrt(k_seg)
+  {
+    const int x = t & 127;
+    const bool is_row = t < 128;
+    const bool valid = is_row ? x < m_valid : x < n_valid;
+    if (valid) {
+      const int q = is_row ? 0 : 2;
+      const float ck = L.part[q][0][x] + L.part[q][1][x];
+      const float ab = L.part[q + 1][0][x] + L.part[q + 1][1][x];
+      const float sm = L.sums[is_row ? 0 : 1][0][x] + L.sums[is_row ? 0 : 1][1][x];
+      const float r = sm - ck;
+      if (!(fabsf(r) <= a.abft_tau * u * ab)) {
+        atomicAdd(&L.bad[q], 1);
+        L.bad[q + 1] = x;
+      }
+    }
+  }
+  __syncthreads();
+  const int nbr = L.bad[0], nbc = L.bad[2];
+  if (nbr == 0 && nbc == 0) return;
+  const int tile = (m0 / SCfg::BM) * a.tiles_n + n0 / SCfg::BN;
+  if (nbr == 1 && nbc == 1) {
+    const int bi = L.bad[1], bj = L.bad[3];
+    // sum of the bad row without the bad element, in a fixed order
+    float s = 0.f;
+    const int li = bi - wm * SCfg::WTM;
+    if (li >= 0 && li < SCfg::WTM && (lane & 15) == (li & 15)) {
+#pragma unroll
+      for (int mb = 0; mb < SCfg::MB; ++mb) {
+        if (mb != (li >> 4)) continue;
+#pragma unroll
+        for (int nb = 0; nb < SCfg::NB; ++nb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int j = wn * SCfg::WTN + nb * 16 + 4 * (lane >> 4) + e;
+            if (j < n_valid && j != bj) s += acc[mb * SCfg::NB + nb][e];
+          }
+      }
+    }
+    s += __shfl_xor(s, 16);
+    s += __shfl_xor(s, 32);
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    if (lane == 0) L.others[w] = s;
+    __syncthreads();
+    const int lj = bj - wn * SCfg::WTN;
+    if (li >= 0 && li < SCfg::WTM && lj >= 0 && lj < SCfg::WTN && (lane & 15) == (li & 15) &&
+        (lane >> 4) == ((lj & 15) >> 2)) {
+      float others = 0.f;
+#pragma unroll
+      for (int v = 0; v < SCfg::NT / 64; ++v) others += L.others[v];
+      const float rc = L.part[0][0][bi] + L.part[0][1][bi];
+      f4_t &val = acc[(li >> 4) * SCfg::NB + (lj >> 4)];
+      const float fixed = rc - others;
+      const float delta = val[lj & 3] - fixed;
+      val[lj & 3] = fixed;
+      atomicAdd(&a.report->detected, 1);
+      atomicAdd(&a.report->corrected, 1);
+      abft_record(a, (int64_t)m0 + bi, (int64_t)n0 + bj, delta, 1, tile, lb);
+    }
+  } else if (t == 0) {
+    atomicAdd(&a.report->detected, 1);
+    atomicAdd(&a.report->uncorrectable, 1);
+    abft_record(a, nbr == 1 ? (int64_t)m0 + L.bad[1] : -1, nbc == 1 ? (int64_t)n0 + L.bad[3] : -1, 0.f, 2,
+                tile, lb);
+  }
+  __syncthreads();
+}
+
+template <bool AK, bool BKM, bool ABFT>
 __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
                                           f4_t (&acc)[SCfg::NACC]) {
   const int w = wave_id();
@@ -586,6 +823,7 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
 #pragma unroll
   for (int i = 0; i < SCfg::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
   if (lb >= le) return;
+  AbftPart pt{0.f, 0.f, 0.f, 0.f};
   s_load<AK, BKM>(a, 0, m0, n0, lb);
   for (int it = lb; it < le; ++it) {
     const int cur = (it - lb) & 1;
@@ -593,8 +831,13 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     __syncthreads();
     if (it + 1 < le) s_load<AK, BKM>(a, cur ^ 1, m0, n0, it + 1);
     s_compute<AK, BKM>(cur, wm, wn, acc);
+    if constexpr (ABFT) {
+      const int kv = a.k - it * SCfg::BK;
+      abft_update<AK, BKM>(abft_lds(), cur, a.m - m0, a.n - n0, kv < SCfg::BK ? kv : SCfg::BK, pt);
+    }
   }
   __syncthreads();
+  if constexpr (ABFT) abft_verify(a, abft_lds(), pt, acc, m0, n0, lb, le);
 }
 
 template <bool AK, bool BKM>
@@ -677,12 +920,14 @@ __global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, in
       [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<DT>(a, vec_ok != 0, m0, n0, acc); });
 }
 
-template <bool AK, bool BKM>
+template <bool AK, bool BKM, bool ABFT>
 __global__ __launch_bounds__(SCfg::NT) void sgemm_kernel(KernelArgs a, int vec_ok) {
   using P = SPolicy<AK, BKM>;
   run_workgroup<P>(
       a,
-      [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { s_macloop<AK, BKM>(a, m0, n0, lb, le, acc.v); },
+      [&](int m0, int n0, int lb, int le, typename P::Acc &acc) {
+        s_macloop<AK, BKM, ABFT>(a, m0, n0, lb, le, acc.v);
+      },
       [&](int m0, int n0, const typename P::Acc &acc) { s_epilogue<AK, BKM>(a, vec_ok != 0, m0, n0, acc); });
 }
 
@@ -741,6 +986,21 @@ static bool c_vec_ok(const KernelArgs &a, int dtype) {
   return (reinterpret_cast<uintptr_t>(a.C) % align == 0) && (a.ldc % 4 == 0);
 }
 
+// Entry point of the fp32 kernel for the operands' storage orders and mode.
+static const void *sgemm_entry(bool ak, bool bk, bool abft) {
+  using namespace dev;
+  if (abft) {
+    if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<true, true, true>);
+    if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<true, false, true>);
+    if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<false, true, true>);
+    return reinterpret_cast<const void *>(&sgemm_kernel<false, false, true>);
+  }
+  if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<true, true, false>);
+  if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<true, false, false>);
+  if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<false, true, false>);
+  return reinterpret_cast<const void *>(&sgemm_kernel<false, false, false>);
+}
+
 int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   dim3 grid(p.grid), block(p.cfg.threads);
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
@@ -750,14 +1010,9 @@ int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   } else if (p.dtype == SK_BF16) {
     hipLaunchKernelGGL(dev::hgemm_kernel<SK_BF16>, grid, block, lds, stream, a, vec_ok);
   } else {
-    if (a.a_kmajor && a.b_kmajor)
-      hipLaunchKernelGGL((dev::sgemm_kernel<true, true>), grid, block, lds, stream, a, vec_ok);
-    else if (a.a_kmajor)
-      hipLaunchKernelGGL((dev::sgemm_kernel<true, false>), grid, block, lds, stream, a, vec_ok);
-    else if (a.b_kmajor)
-      hipLaunchKernelGGL((dev::sgemm_kernel<false, true>), grid, block, lds, stream, a, vec_ok);
-    else
-      hipLaunchKernelGGL((dev::sgemm_kernel<false, false>), grid, block, lds, stream, a, vec_ok);
+    const void *f = sgemm_entry(a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
+    void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
+    return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
   }
   return (int)hipGetLastError();
 }
@@ -798,20 +1053,21 @@ int launch_zero_report(sk_abft_report *report, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
-int kernel_occupancy(int dtype, int *blocks_per_cu) {
+int kernel_occupancy(int dtype, bool abft, int *blocks_per_cu) {
   const TileCfg c = tile_cfg(dtype);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   int nb = 0;
   if (dtype == SK_F32) {
-    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&dev::sgemm_kernel<true, false>),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, dev::sgemm_kernel<true, false>, c.threads,
-                                                       c.lds_bytes);
-    for (auto f : {reinterpret_cast<const void *>(&dev::sgemm_kernel<true, true>),
-                   reinterpret_cast<const void *>(&dev::sgemm_kernel<false, true>),
-                   reinterpret_cast<const void *>(&dev::sgemm_kernel<false, false>)})
-      (void)hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
+    // the four storage-order instances of the mode: the slot count is the
+    // smallest occupancy among them
+    nb = 1 << 20;
+    for (int i = 0; i < 4 && e == hipSuccess; ++i) {
+      const void *f = sgemm_entry(i & 1, (i >> 1) & 1, abft);
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
+      int o = 0;
+      if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, f, c.threads, c.lds_bytes);
+      if (o < nb) nb = o;
+    }
   } else {
     const void *f16 = reinterpret_cast<const void *>(&dev::hgemm_kernel<SK_F16>);
     const void *bf16 = reinterpret_cast<const void *>(&dev::hgemm_kernel<SK_BF16>);
