@@ -49,6 +49,10 @@ def parse():
     p.add_argument("--workload", default="sgemm-sweep", choices=["sgemm-sweep", "hgemm-8192"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workload")
+    p.add_argument("--sweep", type=int, default=0, metavar="COUNT",
+                   help="run the Stream-K shape sweep (first COUNT of the 2000 seeded fp16 "
+                        "shapes), Stream-K (AUTO) vs data-parallel, and print its summary")
+    p.add_argument("--sweep-out", default="", help="CSV file for the per-shape sweep results")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
@@ -164,6 +168,93 @@ def abft_overhead(torch, sk, S, steps=10):
     return out
 
 
+def shape_sweep(torch, sk, S, count, out_path, reps=5):
+    """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
+    contiguous along k; alpha=1, beta=0) on the seeded shape list; each shape
+    runs the AUTO schedule and the data-parallel schedule of the same kernel.
+
+    Per shape: median time of `reps` launches after one warm-up; roofline time
+    T_min = max(2mnk / P_fp16, 2(mk + kn + mn) / BW_HBM); utilisation =
+    T_min / T.  Inputs: N(0,1)/sqrt(k)-scaled normal values drawn on the GPU
+    from a generator seeded with the sweep seed (timing only; parity of sweep
+    shapes is covered by the tests)."""
+    import statistics
+    probe = sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, sk.F16, sk.A_ROW_B_COL)
+    tile = sk.plan_query(probe)
+    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, tile.tile_m, tile.tile_n, tile.slots)[:count]
+    mx = max(max(m * k, k * n, m * n) for _, m, n, k in shapes)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(S.SEED_SWEEP)
+    A = torch.randn(mx, generator=g, device="cuda", dtype=torch.float32).to(torch.float16)
+    B = torch.randn(mx, generator=g, device="cuda", dtype=torch.float32).to(torch.float16)
+    C = torch.empty(mx, device="cuda", dtype=torch.float16)
+    peak, bw = PEAK_TFLOPS["f16"] * 1e12, 8.0e12
+    rows = []
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for idx, (kind, m, n, k) in enumerate(shapes):
+        d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+        res = {}
+        for sched_name, opts in (("sk", sk.make_options()),
+                                 ("dp", sk.make_options(schedule=sk.SCHED_DP))):
+            sk.gemm_ex(d, opts)
+            for e0, e1 in ev:
+                e0.record()
+                sk.gemm_ex(d, opts)
+                e1.record()
+            torch.cuda.synchronize()
+            res[sched_name] = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3
+        p = sk.plan_query(d)
+        fl = 2.0 * m * n * k
+        by = 2.0 * (m * k + k * n + m * n)
+        tmin = max(fl / peak, by / bw)
+        t, slots = p.tiles, p.slots
+        rows.append(dict(kind=kind, m=m, n=n, k=k, tiles=t, schedule=p.schedule, grid=p.grid,
+                         t_sk_us=res["sk"] * 1e6, t_dp_us=res["dp"] * 1e6,
+                         tflops_sk=fl / res["sk"] / 1e12, tflops_dp=fl / res["dp"] / 1e12,
+                         util_sk=tmin / res["sk"], util_dp=tmin / res["dp"],
+                         dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak)))
+        if idx % 100 == 0:
+            print(f"sweep {idx}/{len(shapes)}", file=sys.stderr, flush=True)
+    if out_path:
+        with open(out_path, "w") as f:
+            f.write(",".join(rows[0].keys()) + "\n")
+            for r in rows:
+                f.write(",".join(f"{v:.6g}" if isinstance(v, float) else str(v) for v in r.values()) + "\n")
+
+    def cv(xs):
+        mu = statistics.fmean(xs)
+        return statistics.pstdev(xs) / mu if mu > 0 else float("nan")
+
+    def summary(sel):
+        if not sel:
+            return None
+        sp = [r["t_dp_us"] / r["t_sk_us"] for r in sel]
+        return {"shapes": len(sel),
+                "speedup_sk_over_dp": {"mean": round(statistics.fmean(sp), 4),
+                                       "geomean": round(math.exp(statistics.fmean(math.log(x) for x in sp)), 4),
+                                       "median": round(statistics.median(sp), 4),
+                                       "max": round(max(sp), 3), "min": round(min(sp), 3),
+                                       "frac_sk_not_slower": round(sum(x >= 0.98 for x in sp) / len(sp), 4)},
+                "util_sk": {"mean": round(statistics.fmean(r["util_sk"] for r in sel), 4),
+                            "cv": round(cv([r["util_sk"] for r in sel]), 4)},
+                "util_dp": {"mean": round(statistics.fmean(r["util_dp"] for r in sel), 4),
+                            "cv": round(cv([r["util_dp"] for r in sel]), 4)},
+                "tflops_sk_mean": round(statistics.fmean(r["tflops_sk"] for r in sel), 2),
+                "tflops_dp_mean": round(statistics.fmean(r["tflops_dp"] for r in sel), 2),
+                "dp_quant_eff_mean": round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)}
+
+    return {"sweep": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0",
+            "all": summary(rows),
+            "compute_bound": summary([r for r in rows if not r["mem_bound"]]),
+            "memory_bound": summary([r for r in rows if r["mem_bound"]]),
+            "random": summary([r for r in rows if r["kind"] == "random"]),
+            "skinny": summary([r for r in rows if r["kind"] == "skinny"]),
+            "adversarial": summary([r for r in rows if r["kind"] == "adversarial"]),
+            "roofline": {"peak_tflops": PEAK_TFLOPS["f16"], "hbm_tb_s": 8.0,
+                         "t_min": "max(2mnk/peak, 2(mk+kn+mn)/bw)"}}
+
+
 def cpu_baseline(S, budget_s=25.0):
     """The oracle (six-loop fp64 GEMM, full output) on the fp32 sweep's
     shapes, smallest first, on the host's cores, stopping once about
@@ -206,6 +297,9 @@ def main():
     torch.cuda.set_device(0)
     if args.calibrate_copy:
         calibrate_copy(torch)
+        return
+    if args.sweep:
+        print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out)), flush=True)
         return
 
     results = {}

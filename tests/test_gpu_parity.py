@@ -202,3 +202,38 @@ def test_hgemm_8192_sampled(dtype):
     g = decode(got[rows, cols], dtype)
     assert np.max(np.abs(g - ref) / bound) <= TOL[dtype]
     assert c.freivalds(got) <= TOL[dtype]
+
+
+# ------------------------------------------------- Stream-K sweep shapes
+
+def _sweep_subset(per_kind=8, max_elems=None):
+    # adversarial shapes have more than one full wave of 256 x 256 tiles, so
+    # their output alone is ~17M elements
+    max_elems = max_elems or {"random": 1.2e7, "skinny": 1.2e7, "adversarial": 4.5e7}
+    probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, sk.F16,
+                                       sk.A_ROW_B_COL))
+    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, probe.tile_m, probe.tile_n, probe.slots)
+    out, seen = [], {}
+    for kind, m, n, k in shapes:
+        if m * k + k * n + m * n > max_elems[kind] or seen.get(kind, 0) >= per_kind:
+            continue
+        seen[kind] = seen.get(kind, 0) + 1
+        out.append((kind, m, n, k))
+    return out
+
+
+def test_sweep_shapes_auto_and_dp_against_oracle():
+    """A seeded subset of the Stream-K sweep (random, skinny and tile-count
+    adversarial kinds): AUTO and data-parallel schedules both match the oracle
+    on sampled entries and pass a Freivalds check."""
+    for kind, m, n, k in _sweep_subset():
+        _say("case sweep", kind, m, n, k)
+        c = Case(m, n, k, sk.F16, sk.A_ROW_B_COL, S.SEED_SWEEP + m + n + k, dist="normal",
+                 scale=1 / np.sqrt(k), with_c=False)
+        rows, cols = sample_indices(m, n, 400, m * 7 + n)
+        ref, bound = c.reference_entries(rows, cols)
+        for opts in (None, sk.make_options(schedule=sk.SCHED_DP)):
+            got = c.run(1.0, 0.0, opts)
+            g = decode(got[rows, cols], sk.F16)
+            assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F16], (kind, m, n, k)
+            assert c.freivalds(got) <= TOL[sk.F16]

@@ -306,7 +306,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
     out->iters_per_tile = P.ipt; out->total_iters = P.total;
     out->sk_tiles = P.sk_tiles; out->sk_iters_q = P.sk_q; out->sk_iters_r = P.sk_r;
     out->dp_tiles = P.dp_tiles; out->full_waves = P.w; out->tail_tiles = P.r;
-    out->max_peers = P.max_peers;
+    out->max_peers = plan_max_peers(P);
     out->packs = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
     return SK_OK;
   } catch (...) {

@@ -54,12 +54,14 @@ struct Plan {
   int64_t sk_q, sk_r;   // even split of sk_tiles*ipt over g: first sk_r get sk_q+1
   int64_t dp_tiles;     // tiles [sk_tiles, tiles), round-robin over g
   int w, r;             // full waves and leftover tiles
-  int max_peers;
+  int max_peers;        // filled by plan_max_peers (inspection only)
   bool pack_a, pack_b;  // operand repacked to k-contiguous before the GEMM
 };
 
-// Fills `plan`; returns SK_OK or an sk_status.  slots > 0.
+// Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots > 0.
 int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &plan);
+// Most partials any owner adds under `plan` (O(tiles); for inspection).
+int plan_max_peers(const Plan &plan);
 
 // First Stream-K iteration of workgroup x (x == grid gives the region's end).
 inline int64_t sk_first_iter(int64_t q, int64_t r, int64_t x) { return x * q + (x < r ? x : r); }

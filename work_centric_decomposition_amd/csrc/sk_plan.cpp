@@ -68,6 +68,11 @@ static int split_peers(int64_t tiles, int64_t ipt, int64_t g, bool *any_split) {
   return peers;
 }
 
+// Grid size of basic Stream-K from the runtime model (evaluated in O(1) per
+// candidate, so planning stays cheap next to a small kernel): a tile is
+// split unless every workgroup boundary falls on a tile boundary, and a tile
+// of ipt iterations meets at most ceil((ipt - 1) / q) + 1 workgroups whose
+// ranges hold at least q iterations.
 static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, float c, float d) {
   const int64_t total = t * ipt;
   int64_t hi = std::min<int64_t>(slots, total);
@@ -75,9 +80,10 @@ static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, f
   double best = 1e300;
   int64_t best_g = t;
   for (int64_t g = t; g <= hi; ++g) {
-    bool split = false;
-    int peers = split_peers(t, ipt, g, &split);
-    double T = a + (split ? b : 0.0) + c * (double)cdiv(total, g) + d * peers;
+    const int64_t q = total / g, r = total % g;
+    const bool split = !(r == 0 && q % ipt == 0);
+    const int64_t peers = split ? std::max<int64_t>(1, cdiv(ipt - 1, q)) : 0;
+    const double T = a + (split ? b : 0.0) + c * (double)cdiv(total, g) + d * (double)peers;
     if (T < best - 1e-9) { best = T; best_g = g; }
   }
   return best_g;
@@ -160,9 +166,12 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
     const int64_t I = sk_tiles * P.ipt;
     P.sk_q = I / grid;
     P.sk_r = I % grid;
-    P.max_peers = split_peers(sk_tiles, P.ipt, grid, nullptr);
   }
   return SK_OK;
+}
+
+int plan_max_peers(const Plan &P) {
+  return P.sk_tiles > 0 ? split_peers(P.sk_tiles, P.ipt, P.grid, nullptr) : 0;
 }
 
 }  // namespace sk
