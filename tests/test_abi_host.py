@@ -57,9 +57,13 @@ def test_auto_plan_matches_oracle_decomposition(shape, dtype, slots):
     if r == 0:
         assert p.schedule == sk.SCHED_DP and p.sk_tiles == 0
         mode, param = oracle.DP_PERSISTENT, p.grid
-    elif w >= 1:
-        assert p.schedule == sk.SCHED_SK_HYBRID2 and p.grid == slots and p.sk_tiles == r + slots
+    elif w >= 1 and p.schedule == sk.SCHED_SK_HYBRID2:
+        assert p.grid == slots and p.sk_tiles == r + slots
         mode, param = oracle.HYBRID2, slots
+    elif w >= 1:
+        # the model judged the hybrid's fixup too costly for this k
+        assert p.schedule == sk.SCHED_DP and p.sk_tiles == 0
+        mode, param = oracle.DP_PERSISTENT, p.grid
     else:
         assert p.schedule in (sk.SCHED_SK_BASIC,) and t <= p.grid <= slots
         mode, param = oracle.SK, p.grid
@@ -103,6 +107,15 @@ def test_page_example_plan_through_the_library():
     assert work == [9, 9, 9, 9]
     partials = sum(1 for x in range(4) for s in sk.plan_segments(p, x) if not s[3])
     assert partials == 3
+
+
+def test_auto_takes_the_hybrid_only_when_k_pays_for_the_fixup():
+    """t = 272 tiles on 256 slots: the hybrid saves 15/16 of a tile's
+    iterations per workgroup, which beats one partial + one peer only when
+    the tile has enough iterations."""
+    short = sk.plan_query(_desc(256 * 17, 256 * 16, 256), None, 256)
+    long_ = sk.plan_query(_desc(256 * 17, 256 * 16, 8192), None, 256)
+    assert short.schedule == sk.SCHED_DP and long_.schedule == sk.SCHED_SK_HYBRID2
 
 
 def test_two_tile_hybrid_owner_has_one_peer():

@@ -155,20 +155,36 @@ def test_hybrid_schedule_hgemm_against_oracle():
     two-tile Stream-K + DP hybrid."""
     m, n, k = 256 * 17, 256 * 16, 256
     c = Case(m, n, k, sk.F16, sk.A_ROW_B_COL, 14, dist="normal", scale=1 / 16)
+    opts = sk.make_options(schedule=sk.SCHED_SK_HYBRID2)
     p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, sk.F16,
+                                   sk.A_ROW_B_COL), opts)
+    assert p.schedule == sk.SCHED_SK_HYBRID2 and p.max_peers == 1
+    got = c.run(1.0, 0.0, opts)
+    ref, bound = c.reference()
+    assert rel_err(got, sk.F16, ref, bound) <= TOL[sk.F16]
+    again = c.run(1.0, 0.0, opts)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8))  # run-to-run bitwise
+
+
+def test_auto_hybrid_on_a_long_k_shape_against_oracle():
+    """272 tiles with k = 8192: AUTO picks the two-tile hybrid."""
+    m, n, k = 256 * 17, 256 * 16, 8192
+    c = Case(m, n, k, sk.BF16, sk.A_ROW_B_COL, 16, dist="normal", scale=1 / np.sqrt(8192),
+             with_c=False)
+    p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, sk.BF16,
                                    sk.A_ROW_B_COL))
     assert p.schedule == sk.SCHED_SK_HYBRID2
     got = c.run(1.0, 0.0)
-    ref, bound = c.reference()
-    assert rel_err(got, sk.F16, ref, bound) <= TOL[sk.F16]
-    again = c.run(1.0, 0.0)
-    assert np.array_equal(got.view(np.uint8), again.view(np.uint8))  # run-to-run bitwise
+    rows, cols = sample_indices(m, n, 1500, 16)
+    ref, bound = c.reference_entries(rows, cols)
+    assert np.max(np.abs(decode(got[rows, cols], sk.BF16) - ref) / bound) <= TOL[sk.BF16]
+    assert c.freivalds(got) <= TOL[sk.BF16]
 
 
 def test_hybrid_schedule_sgemm_against_oracle():
     m, n, k = 128 * 23, 128 * 23, 128  # 529 tiles on 512 slots
     c = Case(m, n, k, sk.F32, sk.A_ROW_B_ROW, 15)
-    got = c.run(1.0, 1.0)
+    got = c.run(1.0, 1.0, sk.make_options(schedule=sk.SCHED_SK_HYBRID2))
     ref, bound = c.reference(1.0, 1.0)
     assert rel_err(got, sk.F32, ref, bound) <= TOL[sk.F32]
 

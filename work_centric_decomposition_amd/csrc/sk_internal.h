@@ -33,12 +33,15 @@ struct TileCfg {
 #endif
 
 inline TileCfg tile_cfg(int dtype) {
-  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 0.25f, 1.f, 0.25f};
-  // model constants in units of one iteration: a 256 x 256 fp32 partial costs
-  // about two 64-deep iterations to write or to read and add
+  // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
+  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f};
+  // model constants in units of one iteration, fitted to the fp16 shape
+  // sweep on MI355X: a 256 x 256 fp32 partial (256 KiB) costs about five
+  // 64-deep iterations to write and four to read and add when every
+  // workgroup exchanges one at the same time
   const float it = SK_HGEMM_BK / 64.f;
   return TileCfg{256, 256, SK_HGEMM_BK, 512, 1, SK_HGEMM_STAGES * 2 * 256 * SK_HGEMM_BK * 2,
-                 4.f / it, 2.f / it, 1.f, 2.f / it};
+                 4.f / it, 5.f / it, 1.f, 4.f / it};
 }
 
 // Resolved work decomposition (integers only).

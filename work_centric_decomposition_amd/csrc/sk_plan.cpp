@@ -28,9 +28,11 @@
 //  * the Stream-K region is the first tiles in linear order; each workgroup
 //    runs its Stream-K segments first and then its data-parallel tiles,
 //    which are dealt round-robin (tile sk_tiles + x + j*g);
-//  * the two-tile hybrid applies when w >= hybrid_min_waves (default 1) and
-//    r > 0; r == 0 is plain data-parallel; w == 0 is basic Stream-K with the
-//    model's grid size.
+//  * AUTO: r == 0 is plain data-parallel; w == 0 is basic Stream-K with the
+//    model's grid size; w >= hybrid_min_waves (default 1) and r > 0 is the
+//    two-tile hybrid when the model predicts it beats data-parallel (the
+//    iterations it saves exceed the cost of one partial and one peer), else
+//    data-parallel.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -132,9 +134,20 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
     sk_tiles = P.tiles;
   } else {
     if (sched == SK_SCHED_AUTO) {
-      if (P.r == 0) sched = SK_SCHED_DP;
-      else if (P.w >= min_waves) sched = SK_SCHED_SK_HYBRID2;
-      else sched = SK_SCHED_SK_BASIC;
+      if (P.r == 0) {
+        sched = SK_SCHED_DP;
+      } else if (P.w >= min_waves) {
+        // the same model decides whether giving back a wave pays for the
+        // fixup: DP runs ceil(t/p) full tiles, the two-tile hybrid
+        // ceil((r+p)*ipt/p) Stream-K iterations plus w-1 tiles, one partial
+        // and one peer per workgroup
+        const double t_dp = (double)(P.w + 1) * P.ipt;
+        const double t_h2 = (double)cdiv((P.r + slots) * P.ipt, slots) + (double)(P.w - 1) * P.ipt +
+                            (mb + md) / mc;
+        sched = t_h2 < t_dp ? SK_SCHED_SK_HYBRID2 : SK_SCHED_DP;
+      } else {
+        sched = SK_SCHED_SK_BASIC;
+      }
     }
     if (sched == SK_SCHED_SK_HYBRID2 && (P.w < 1 || P.r == 0))
       sched = P.r == 0 ? SK_SCHED_DP : SK_SCHED_SK_BASIC;
