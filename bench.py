@@ -45,7 +45,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default="sgemm-sweep", choices=["sgemm-sweep", "hgemm-8192"])
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workload")
@@ -307,8 +307,9 @@ def main():
                                [w for w in ("sgemm-sweep", "hgemm-8192") if w != args.workload])
     for wl in order:
         main_wl = wl == args.workload
-        steps = args.steps if main_wl else max(3, args.steps // 4)
-        warmup = args.warmup if main_wl else 2
+        # the clock needs ~10 ms of load to settle: extra legs get 10 warm-up steps
+        steps = args.steps if main_wl else max(10, args.steps // 2)
+        warmup = args.warmup if main_wl else 10
         if wl == "sgemm-sweep":
             cases = make_sweep_inputs(torch, sk, S)
             ms, per_launch, wall = timed(torch, lambda ev: sweep_step(sk, cases, ev), len(cases),

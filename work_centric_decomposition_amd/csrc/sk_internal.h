@@ -31,6 +31,11 @@ struct TileCfg {
 #ifndef SK_HGEMM_STAGES
 #define SK_HGEMM_STAGES 2
 #endif
+// waves per HGEMM workgroup: 8 (two per SIMD, 128 x 64 wave tiles) or 4 (one
+// per SIMD, 128 x 128 wave tiles)
+#ifndef SK_HGEMM_WAVES
+#define SK_HGEMM_WAVES 8
+#endif
 
 inline TileCfg tile_cfg(int dtype) {
   // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
@@ -40,7 +45,7 @@ inline TileCfg tile_cfg(int dtype) {
   // 64-deep iterations to write and four to read and add when every
   // workgroup exchanges one at the same time
   const float it = SK_HGEMM_BK / 64.f;
-  return TileCfg{256, 256, SK_HGEMM_BK, 512, 1, SK_HGEMM_STAGES * 2 * 256 * SK_HGEMM_BK * 2,
+  return TileCfg{256, 256, SK_HGEMM_BK, 64 * SK_HGEMM_WAVES, 1, SK_HGEMM_STAGES * 2 * 256 * SK_HGEMM_BK * 2,
                  4.f / it, 5.f / it, 1.f, 4.f / it};
 }
 

@@ -49,10 +49,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, in
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, n, kRsrcWord3);
 }
 
-__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, int lds_off, uint32_t voff) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(smem + lds_off), 16, voff, 0, 0, 0);
-}
-
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 }
@@ -193,54 +189,6 @@ __device__ __forceinline__ void store4(const KernelArgs &a, bool vec_ok, int i, 
   }
 }
 
-// --------------------------------------------------------- tile loaders
-//
-// K-major operand tile: R rows (m or n) x BKB bytes of k per row, row-major
-// in LDS with 16-byte chunk c of row r stored at chunk position
-// c ^ ((r >> 1) & 7) (8 chunks per 128-byte row).  One 1 KiB direct-to-LDS
-// instruction per wave covers 8 rows; lane L writes position L & 7 of row
-// L >> 3 and therefore fetches the chunk that belongs there.
-//   base: element (row0, k0) of the operand; rows_left = rows of the operand
-//   from row0; kbytes_left = bytes of k from k0; total: bytes from base to
-//   the end of the operand.
-template <int R, int NT>
-__device__ __forceinline__ void load_kmajor_128(int lds_off, const char *base, int64_t ld_bytes,
-                                                int rows_left, int kbytes_left, int64_t total) {
-  static_assert(R * 128 % (NT / 64 * 1024) == 0, "tile must split evenly over the waves");
-  constexpr int PER_WAVE = R * 128 / 1024 / (NT / 64);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, total);
-  const int w = wave_id(), lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int inst = w * PER_WAVE + j;
-    const int row = inst * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row >> 1) & 7);
-    const bool ok = row < rows_left && c * 16 < kbytes_left;
-    const uint32_t voff = ok ? (uint32_t)(row * ld_bytes + c * 16) : kOOB;
-    dma16(rs, lds_off + inst * 1024, voff);
-  }
-}
-
-// MN-major fp32 operand tile: BK rows (k) x 128 floats (512 bytes) per row,
-// 16-byte chunk c of row k stored at position c ^ (4 * ((k >> 2) & 3)).  One
-// instruction covers two rows.
-template <int BK, int NT>
-__device__ __forceinline__ void load_mnmajor_f32x128(int lds_off, const char *base, int64_t ld_bytes,
-                                                     int krows_left, int mn_left, int64_t total) {
-  constexpr int PER_WAVE = BK * 512 / 1024 / (NT / 64);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(base, total);
-  const int w = wave_id(), lane = threadIdx.x & 63;
-#pragma unroll
-  for (int j = 0; j < PER_WAVE; ++j) {
-    const int inst = w * PER_WAVE + j;
-    const int kr = inst * 2 + (lane >> 5);
-    const int c = (lane & 31) ^ (4 * ((kr >> 2) & 3));
-    const bool ok = kr < krows_left && c * 4 < mn_left;
-    const uint32_t voff = ok ? (uint32_t)(kr * ld_bytes + c * 16) : kOOB;
-    dma16(rs, lds_off + inst * 1024, voff);
-  }
-}
-
 // s_waitcnt immediate that waits until at most n vector-memory operations
 // of this wave are outstanding (LDS/scalar and export counters unchecked).
 constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
@@ -259,10 +207,12 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // the block, i.e. four consecutive columns per register quad.
 template <int DT>
 struct HPolicy {
-  static constexpr int BM = 256, BN = 256, BK = SK_HGEMM_BK, NT = 512, NSTAGE = SK_HGEMM_STAGES;
+  static constexpr int BM = 256, BN = 256, BK = SK_HGEMM_BK, NSTAGE = SK_HGEMM_STAGES;
+  static constexpr int WAVES = SK_HGEMM_WAVES, NT = 64 * WAVES;
   static constexpr int SUBS = BK / 16;  // k-substeps of one iteration
   static_assert(SUBS % 2 == 0 && NSTAGE >= 2 && NSTAGE <= 5, "pipeline shape");
-  static constexpr int WTM = 128, WTN = 64, MB = 4, NB = 2;
+  static_assert(WAVES == 4 || WAVES == 8, "2 x 2 or 2 x 4 waves");
+  static constexpr int WTM = 128, WTN = BN / (WAVES / 2), MB = WTM / 32, NB = WTN / 32;
   static constexpr int WAVES_N = BN / WTN;
   static constexpr int NACC4 = MB * NB * 4;
   static constexpr int ROW = BK * 2;  // bytes of one LDS row (k-contiguous)
@@ -412,6 +362,40 @@ __device__ __forceinline__ void wait_stages(int stages) {
   else __builtin_amdgcn_s_waitcnt(0);
 }
 
+// Instruction-scheduling knobs of the HGEMM main loop (build-time):
+//  SK_HGEMM_INTERLEAVE: let the scheduler interleave the LDS reads of
+//    substep s+1 one by one with the MFMAs of substep s (instead of issuing
+//    all reads first);
+//  SK_HGEMM_SETPRIO: raise the wave's issue priority while it issues MFMAs,
+//    so that of the two waves sharing a SIMD the one with MFMAs ready wins.
+#ifndef SK_HGEMM_INTERLEAVE
+#define SK_HGEMM_INTERLEAVE 1
+#endif
+#ifndef SK_HGEMM_SETPRIO
+#define SK_HGEMM_SETPRIO 0
+#endif
+#if SK_HGEMM_INTERLEAVE
+#define H_PHASE_SPLIT() ((void)0)
+#define H_INTERLEAVE()                                                  \
+  do {                                                                  \
+    _Pragma("unroll") for (int q = 0; q < P::MB + P::NB; ++q) {         \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
+    }                                                                   \
+    __builtin_amdgcn_sched_group_barrier(0x008, P::MB * P::NB, 0);      \
+  } while (0)
+#else
+#define H_PHASE_SPLIT() __builtin_amdgcn_sched_barrier(0)
+#define H_INTERLEAVE() ((void)0)
+#endif
+#if SK_HGEMM_SETPRIO
+#define H_PRIO_UP() __builtin_amdgcn_s_setprio(1)
+#define H_PRIO_DOWN() __builtin_amdgcn_s_setprio(0)
+#else
+#define H_PRIO_UP() ((void)0)
+#define H_PRIO_DOWN() ((void)0)
+#endif
+
 // MacLoop over iterations [lb, le) of the tile at (m0, n0).
 //
 // Software pipeline: NSTAGE LDS stages and two register sets of fragments.
@@ -446,13 +430,17 @@ __device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, i
     for (int sub = 0; sub + 1 < P::SUBS; ++sub) {
       if (sub % 2 == 0) {
         h_frags<DT>(buf, sub + 1, wm, wn, fa1, fb1);
-        __builtin_amdgcn_sched_barrier(0);
+        H_PHASE_SPLIT();
+        H_PRIO_UP();
         h_mfmas<DT>(fa0, fb0, acc);
       } else {
         h_frags<DT>(buf, sub + 1, wm, wn, fa0, fb0);
-        __builtin_amdgcn_sched_barrier(0);
+        H_PHASE_SPLIT();
+        H_PRIO_UP();
         h_mfmas<DT>(fa1, fb1, acc);
       }
+      H_INTERLEAVE();
+      H_PRIO_DOWN();
       __builtin_amdgcn_sched_barrier(0);
     }
     // last substep: switch stages.  Stages issued beyond i+1:
@@ -499,83 +487,129 @@ struct SCfg {
   static constexpr int STAGE = A_BYTES + B_BYTES;
 };
 
+// Direct-to-LDS loads of one operand's tile slices (fp32), with per-lane
+// offsets computed once per tile; each k-iteration advances a scalar base.
+//  k-major: BM rows (m or n) of BK fp32 (128 bytes), chunk c of row r at
+//    position c ^ ((r >> 1) & 7); one 1 KiB load covers 8 rows; the base
+//    of iteration kit is kit * BK * 4 bytes further.
+//  mn-major: BK rows (k) of 128 fp32 (512 bytes), chunk c of row k at
+//    position c ^ (4 * ((k >> 2) & 3)); one load covers 2 rows; the base
+//    advances kit * BK * ld * 4 bytes.
+// Rows past the matrix (and, in the iteration holding the end of k, k
+// chunks or rows at or past k) are fetched out of range, i.e. as zeros.
 template <bool KMAJOR>
-__device__ __forceinline__ void s_load_operand(int lds_off, const void *ptr, int64_t ld, int mn0,
-                                               int mn_total, int k0, int k_total, int k_ext) {
-  constexpr int ES = 4;
-  const int64_t ldb = ld * ES;
-  const char *p = static_cast<const char *>(ptr);
-  if (KMAJOR) {
-    const char *base = p + (int64_t)mn0 * ldb + (int64_t)k0 * ES;
-    const int64_t total = (int64_t)(mn_total - 1 - mn0) * ldb + (int64_t)(k_ext - k0) * ES;
-    load_kmajor_128<SCfg::BM, SCfg::NT>(lds_off, base, ldb, mn_total - mn0, (k_total - k0) * ES, total);
-  } else {
-    const char *base = p + (int64_t)k0 * ldb + (int64_t)mn0 * ES;
-    const int64_t total = (int64_t)(k_total - 1 - k0) * ldb + (int64_t)(mn_total - mn0) * ES;
-    load_mnmajor_f32x128<SCfg::BK, SCfg::NT>(lds_off, base, ldb, k_total - k0, mn_total - mn0, total);
+struct SLoader {
+  static constexpr int LOADS = SCfg::BM * SCfg::BK * 4 / 1024 / (SCfg::NT / 64);
+  const char *base;     // element (mn0, 0) of the operand
+  int64_t range;        // bytes from base to the end of the operand
+  int64_t kstep;        // bytes the slice advances per k-iteration
+  uint32_t v[LOADS];
+  int key[LOADS];       // k-major: chunk index; mn-major: k row within the slice
+  int lds_first;        // LDS offset of this wave's first load within the operand's stage area
+
+  __device__ __forceinline__ void init(const void *ptr, int64_t ld, int mn0, int mn_total, int k_total,
+                                       int k_ext) {
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    const int64_t ldb = ld * 4;
+    lds_first = w * LOADS * 1024;
+    if (KMAJOR) {
+      base = static_cast<const char *>(ptr) + (int64_t)mn0 * ldb;
+      range = (int64_t)(mn_total - 1 - mn0) * ldb + (int64_t)k_ext * 4;
+      kstep = SCfg::BK * 4;
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        const int row = (w * LOADS + j) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((row >> 1) & 7);
+        key[j] = c;
+        v[j] = row < mn_total - mn0 ? (uint32_t)(row * ldb + c * 16) : kOOB;
+      }
+    } else {
+      base = static_cast<const char *>(ptr) + (int64_t)mn0 * 4;
+      range = (int64_t)(k_total - 1) * ldb + (int64_t)(mn_total - mn0) * 4;
+      kstep = SCfg::BK * ldb;
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        const int kr = (w * LOADS + j) * 2 + (lane >> 5);
+        const int c = (lane & 31) ^ (4 * ((kr >> 2) & 3));
+        key[j] = kr;
+        v[j] = c * 4 < mn_total - mn0 ? (uint32_t)(kr * ldb + c * 16) : kOOB;
+      }
+    }
   }
-}
 
-template <bool AK, bool BKM>
-__device__ __forceinline__ void s_load(const KernelArgs &a, int stage, int m0, int n0, int kit) {
-  const int k0 = kit * SCfg::BK;
-  s_load_operand<AK>(stage * SCfg::STAGE, a.A, a.lda, m0, a.m, k0, a.k, a.a_kext);
-  s_load_operand<BKM>(stage * SCfg::STAGE + SCfg::A_BYTES, a.B, a.ldb, n0, a.n, k0, a.k, a.b_kext);
-}
+  // Slice of k-iteration kit into the operand's area at LDS offset lds_off.
+  // The buffer descriptor is rebuilt from the advanced base (scalar work),
+  // so the hardware range check ends exactly at the operand's last element.
+  __device__ __forceinline__ void load(int lds_off, int kit, int k_total) const {
+    const int64_t adv = (int64_t)kit * kstep;
+    const __amdgpu_buffer_rsrc_t r = make_rsrc(base + adv, range - adv);
+    const int left = k_total - kit * SCfg::BK;  // k values from the slice start
+    const int dst = lds_off + lds_first;
+    if (left >= SCfg::BK) {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(smem + dst + j * 1024), 16, v[j], 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int j = 0; j < LOADS; ++j) {
+        const bool ok = KMAJOR ? key[j] * 4 < left : key[j] < left;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(smem + dst + j * 1024), 16, ok ? v[j] : kOOB,
+                                                 0, 0, 0);
+      }
+    }
+  }
+};
 
-// Value of operand element (mn_local, k_local) for MFMA step q, lane group h.
-template <bool KMAJOR>
-__device__ __forceinline__ f4_t s_frag4(int base_off, int row, int g) {
-  // k-major: row `row`, chunk 4g + h (the caller's lane group is folded into
-  // `row`'s lane part and into the chunk below)
-  const int lane = threadIdx.x & 63;
-  const int c = 4 * g + (lane >> 4);
-  return *reinterpret_cast<const f4_t *>(smem + base_off + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-}
-
+// Element (mn, k) of an mn-major fp32 stage area.
 __device__ __forceinline__ float s_mn_elem(int base_off, int mn, int k) {
   const int c = mn >> 2, e = mn & 3;
   const int p = c ^ (4 * ((k >> 2) & 3));
   return *reinterpret_cast<const float *>(smem + base_off + k * 512 + p * 16 + e * 4);
 }
 
+// Fragments of k-group g (16 values of k) of an LDS stage.  Within the
+// group, MFMA step q of lane group h = lane >> 4 multiplies k = 16 g + 4 h + q
+// for both operands: a k-major operand reads its four values with one
+// 128-bit LDS read, an mn-major operand with one 32-bit read per step.
 template <bool AK, bool BKM>
-__device__ __forceinline__ void s_compute(int stage, int wm, int wn, f4_t (&acc)[SCfg::NACC]) {
+__device__ __forceinline__ void s_frags(int stage, int g, int wm, int wn, f4_t (&av)[SCfg::MB],
+                                        f4_t (&bv)[SCfg::NB]) {
   const int lane = threadIdx.x & 63;
   const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
   const int h = lane >> 4, li = lane & 15;
+  const int c = 4 * g + h;
 #pragma unroll
-  for (int g = 0; g < SCfg::BK / 16; ++g) {
-    f4_t av[SCfg::MB], bv[SCfg::NB];
+  for (int mb = 0; mb < SCfg::MB; ++mb) {
+    const int mn = wm * SCfg::WTM + mb * 16 + li;
+    if (AK) {
+      av[mb] = *reinterpret_cast<const f4_t *>(smem + As + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4));
+    } else {
 #pragma unroll
-    for (int mb = 0; mb < SCfg::MB; ++mb) {
-      const int mn = wm * SCfg::WTM + mb * 16 + li;
-      if (AK) {
-        av[mb] = s_frag4<true>(As, mn, g);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) av[mb][q] = s_mn_elem(As, mn, 16 * g + 4 * h + q);
-      }
+      for (int q = 0; q < 4; ++q) av[mb][q] = s_mn_elem(As, mn, 16 * g + 4 * h + q);
     }
-#pragma unroll
-    for (int nb = 0; nb < SCfg::NB; ++nb) {
-      const int mn = wn * SCfg::WTN + nb * 16 + li;
-      if (BKM) {
-        bv[nb] = s_frag4<true>(Bs, mn, g);
-      } else {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) bv[nb][q] = s_mn_elem(Bs, mn, 16 * g + 4 * h + q);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-#pragma unroll
-      for (int mb = 0; mb < SCfg::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < SCfg::NB; ++nb)
-          acc[mb * SCfg::NB + nb] =
-              __builtin_amdgcn_mfma_f32_16x16x4f32(bv[nb][q], av[mb][q], acc[mb * SCfg::NB + nb], 0, 0, 0);
   }
+#pragma unroll
+  for (int nb = 0; nb < SCfg::NB; ++nb) {
+    const int mn = wn * SCfg::WTN + nb * 16 + li;
+    if (BKM) {
+      bv[nb] = *reinterpret_cast<const f4_t *>(smem + Bs + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4));
+    } else {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) bv[nb][q] = s_mn_elem(Bs, mn, 16 * g + 4 * h + q);
+    }
+  }
+}
+
+__device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (&bv)[SCfg::NB],
+                                        f4_t (&acc)[SCfg::NACC]) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int mb = 0; mb < SCfg::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < SCfg::NB; ++nb)
+        acc[mb * SCfg::NB + nb] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(bv[nb][q], av[mb][q], acc[mb * SCfg::NB + nb], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- ABFT
@@ -815,6 +849,12 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
   __syncthreads();
 }
 
+// MacLoop of the fp32 kernel, same two-stage pipeline as the HGEMM one:
+// the fragments of k-group 1 are read while the MFMAs of group 0 run; then
+// (ABFT: the checksum update of this stage;) wait for this wave's loads of
+// the next stage, barrier, issue the loads of iteration i+2 into this
+// stage's buffer and read group 0 of the next stage while the MFMAs of
+// group 1 run.
 template <bool AK, bool BKM, bool ABFT>
 __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
                                           f4_t (&acc)[SCfg::NACC]) {
@@ -822,21 +862,46 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   const int wm = w / 2, wn = w % 2;
 #pragma unroll
   for (int i = 0; i < SCfg::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
-  if (lb >= le) return;
+  const int n = le - lb;
+  if (n <= 0) return;
   AbftPart pt{0.f, 0.f, 0.f, 0.f};
-  s_load<AK, BKM>(a, 0, m0, n0, lb);
-  for (int it = lb; it < le; ++it) {
-    const int cur = (it - lb) & 1;
+  SLoader<AK> la;
+  SLoader<BKM> lbd;
+  la.init(a.A, a.lda, m0, a.m, a.k, a.a_kext);
+  lbd.init(a.B, a.ldb, n0, a.n, a.k, a.b_kext);
+  auto load = [&](int stage, int kit) {
+    la.load(stage * SCfg::STAGE, kit, a.k);
+    lbd.load(stage * SCfg::STAGE + SCfg::A_BYTES, kit, a.k);
+  };
+  load(0, lb);
+  if (n > 1) {
+    load(1, lb + 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(SLoader<AK>::LOADS + SLoader<BKM>::LOADS));
+  } else {
     __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (it + 1 < le) s_load<AK, BKM>(a, cur ^ 1, m0, n0, it + 1);
-    s_compute<AK, BKM>(cur, wm, wn, acc);
-    if constexpr (ABFT) {
-      const int kv = a.k - it * SCfg::BK;
-      abft_update<AK, BKM>(abft_lds(), cur, a.m - m0, a.n - n0, kv < SCfg::BK ? kv : SCfg::BK, pt);
-    }
   }
   __syncthreads();
+  f4_t a0[SCfg::MB], b0[SCfg::NB], a1[SCfg::MB], b1[SCfg::NB];
+  s_frags<AK, BKM>(0, 0, wm, wn, a0, b0);
+  int buf = 0;
+  for (int i = 0; i < n; ++i) {
+    s_frags<AK, BKM>(buf, 1, wm, wn, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    s_mfmas(a0, b0, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    if constexpr (ABFT) {
+      const int kv = a.k - (lb + i) * SCfg::BK;
+      abft_update<AK, BKM>(abft_lds(), buf, a.m - m0, a.n - n0, kv < SCfg::BK ? kv : SCfg::BK, pt);
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (i + 2 < n) load(buf, lb + i + 2);
+    if (i + 1 < n) s_frags<AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    s_mfmas(a1, b1, acc);
+    __builtin_amdgcn_sched_barrier(0);
+    buf ^= 1;
+  }
   if constexpr (ABFT) abft_verify(a, abft_lds(), pt, acc, m0, n0, lb, le);
 }
 
@@ -921,7 +986,7 @@ __global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, in
 }
 
 template <bool AK, bool BKM, bool ABFT>
-__global__ __launch_bounds__(SCfg::NT) void sgemm_kernel(KernelArgs a, int vec_ok) {
+__global__ __launch_bounds__(SCfg::NT, ABFT ? 1 : 2) void sgemm_kernel(KernelArgs a, int vec_ok) {
   using P = SPolicy<AK, BKM>;
   run_workgroup<P>(
       a,
