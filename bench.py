@@ -171,7 +171,10 @@ def abft_overhead(torch, sk, S, steps=10):
 def shape_sweep(torch, sk, S, count, out_path, reps=5):
     """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
     contiguous along k; alpha=1, beta=0) on the seeded shape list; each shape
-    runs the AUTO schedule and the data-parallel schedule of the same kernel.
+    runs three schedules of the same kernel: AUTO (the XCD-aware split), the
+    page's own choice (two-tile hybrid with a wave or more of tiles, basic
+    Stream-K below a wave, data-parallel when the tiles fill whole waves) and
+    data-parallel in linear tile order.
 
     Per shape: median time of `reps` launches after one warm-up; roofline time
     T_min = max(2mnk / P_fp16, 2(mk + kn + mn) / BW_HBM); utilisation =
@@ -194,8 +197,13 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
           for _ in range(reps)]
     for idx, (kind, m, n, k) in enumerate(shapes):
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+        p = sk.plan_query(d)
+        t, slots = p.tiles, p.slots
+        w, r = divmod(t, slots)
+        page = sk.SCHED_DP if r == 0 else sk.SCHED_SK_HYBRID2 if w >= 1 else sk.SCHED_SK_BASIC
         res = {}
-        for sched_name, opts in (("sk", sk.make_options()),
+        for sched_name, opts in (("auto", sk.make_options()),
+                                 ("page", sk.make_options(schedule=page)),
                                  ("dp", sk.make_options(schedule=sk.SCHED_DP))):
             sk.gemm_ex(d, opts)
             for e0, e1 in ev:
@@ -204,15 +212,17 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
                 e1.record()
             torch.cuda.synchronize()
             res[sched_name] = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3
-        p = sk.plan_query(d)
         fl = 2.0 * m * n * k
         by = 2.0 * (m * k + k * n + m * n)
         tmin = max(fl / peak, by / bw)
-        t, slots = p.tiles, p.slots
         rows.append(dict(kind=kind, m=m, n=n, k=k, tiles=t, schedule=p.schedule, grid=p.grid,
-                         t_sk_us=res["sk"] * 1e6, t_dp_us=res["dp"] * 1e6,
-                         tflops_sk=fl / res["sk"] / 1e12, tflops_dp=fl / res["dp"] / 1e12,
-                         util_sk=tmin / res["sk"], util_dp=tmin / res["dp"],
+                         sk_tiles=p.sk_tiles, phase_div=p.phase_div, page_schedule=page,
+                         t_auto_us=res["auto"] * 1e6, t_page_us=res["page"] * 1e6,
+                         t_dp_us=res["dp"] * 1e6,
+                         tflops_auto=fl / res["auto"] / 1e12, tflops_page=fl / res["page"] / 1e12,
+                         tflops_dp=fl / res["dp"] / 1e12,
+                         util_auto=tmin / res["auto"], util_page=tmin / res["page"],
+                         util_dp=tmin / res["dp"],
                          dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak)))
         if idx % 100 == 0:
             print(f"sweep {idx}/{len(shapes)}", file=sys.stderr, flush=True)
@@ -226,23 +236,26 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
         mu = statistics.fmean(xs)
         return statistics.pstdev(xs) / mu if mu > 0 else float("nan")
 
+    def speed(sel, name):
+        sp = [r["t_dp_us"] / r[f"t_{name}_us"] for r in sel]
+        return {"mean": round(statistics.fmean(sp), 4),
+                "geomean": round(math.exp(statistics.fmean(math.log(x) for x in sp)), 4),
+                "median": round(statistics.median(sp), 4),
+                "max": round(max(sp), 3), "min": round(min(sp), 3),
+                "frac_not_slower": round(sum(x >= 0.98 for x in sp) / len(sp), 4)}
+
     def summary(sel):
         if not sel:
             return None
-        sp = [r["t_dp_us"] / r["t_sk_us"] for r in sel]
-        return {"shapes": len(sel),
-                "speedup_sk_over_dp": {"mean": round(statistics.fmean(sp), 4),
-                                       "geomean": round(math.exp(statistics.fmean(math.log(x) for x in sp)), 4),
-                                       "median": round(statistics.median(sp), 4),
-                                       "max": round(max(sp), 3), "min": round(min(sp), 3),
-                                       "frac_sk_not_slower": round(sum(x >= 0.98 for x in sp) / len(sp), 4)},
-                "util_sk": {"mean": round(statistics.fmean(r["util_sk"] for r in sel), 4),
-                            "cv": round(cv([r["util_sk"] for r in sel]), 4)},
-                "util_dp": {"mean": round(statistics.fmean(r["util_dp"] for r in sel), 4),
-                            "cv": round(cv([r["util_dp"] for r in sel]), 4)},
-                "tflops_sk_mean": round(statistics.fmean(r["tflops_sk"] for r in sel), 2),
-                "tflops_dp_mean": round(statistics.fmean(r["tflops_dp"] for r in sel), 2),
-                "dp_quant_eff_mean": round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)}
+        out = {"shapes": len(sel)}
+        for name in ("auto", "page"):
+            out[f"speedup_{name}_over_dp"] = speed(sel, name)
+        for name in ("auto", "page", "dp"):
+            out[f"util_{name}"] = {"mean": round(statistics.fmean(r[f"util_{name}"] for r in sel), 4),
+                                   "cv": round(cv([r[f"util_{name}"] for r in sel]), 4)}
+            out[f"tflops_{name}_mean"] = round(statistics.fmean(r[f"tflops_{name}"] for r in sel), 2)
+        out["dp_quant_eff_mean"] = round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)
+        return out
 
     return {"sweep": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0",
             "all": summary(rows),

@@ -63,21 +63,30 @@ typedef enum {
   SK_ERR_NO_DEVICE = -6      /* no usable gfx950 device */
 } sk_status;
 
-/* Work decompositions (Stream-K page):
- *  SK_SCHED_AUTO      two-tile hybrid when the tile count spans at least one
- *                     full wave and is not a multiple of the CU slots; plain
- *                     data-parallel when it is a multiple; basic Stream-K with
- *                     a model-chosen grid when it is below one wave.
+/* Work decompositions.  The first four are the Stream-K page's, with tiles in
+ * linear m -> n order:
  *  SK_SCHED_DP        data-parallel (Algorithm 2), persistent over the slots.
  *  SK_SCHED_SK_BASIC  basic Stream-K (Algorithm 5) over all tiles.
  *  SK_SCHED_SK_HYBRID2 "two-tile Stream-K + data-parallel" (section 5.2).
- *  SK_SCHED_SK_HYBRID1 "data-parallel + one-tile Stream-K" (section 5.2). */
+ *  SK_SCHED_SK_HYBRID1 "data-parallel + one-tile Stream-K" (section 5.2).
+ * SK_SCHED_XCD_ALIGNED is this library's MI355X form of the same work-centric
+ * split: the Stream-K region (all tiles when there are fewer than the slots,
+ * else one full wave plus the leftover tiles, as in the two-tile hybrid) is
+ * split in quanta of ipt / D iterations so that the workgroups resident on
+ * one XCD run at equal k offsets on a compact block of tiles (they then share
+ * the A and B slices they read in that XCD's L2), and data-parallel tiles are
+ * dealt in compact per-XCD blocks.  With no leftover tiles it is
+ * data-parallel in that XCD-aware order.
+ *  SK_SCHED_AUTO      SK_SCHED_XCD_ALIGNED with the quantum and grid chosen by
+ *                     the runtime model, or its data-parallel form when the
+ *                     model predicts the split does not pay. */
 typedef enum {
   SK_SCHED_AUTO = 0,
   SK_SCHED_DP = 1,
   SK_SCHED_SK_BASIC = 2,
   SK_SCHED_SK_HYBRID2 = 3,
-  SK_SCHED_SK_HYBRID1 = 4
+  SK_SCHED_SK_HYBRID1 = 4,
+  SK_SCHED_XCD_ALIGNED = 5
 } sk_schedule;
 
 /* One GEMM. */
@@ -157,18 +166,25 @@ typedef struct {
   int64_t iters_per_tile;         /* ceil(k / BLK_K) */
   int64_t total_iters;            /* t * iters_per_tile */
   int64_t sk_tiles;               /* tiles [0, sk_tiles) form the Stream-K region */
-  int64_t sk_iters_q;             /* floor(sk_tiles * ipt / grid) */
+  int64_t sk_iters_q;             /* floor(sk_tiles * ipt / grid) (XCD_ALIGNED: floor(s * ipt / D)) */
   int64_t sk_iters_r;             /* (sk_tiles * ipt) mod grid: the first r workgroups take one more */
   int64_t dp_tiles;               /* tiles after the Stream-K region, dealt round-robin */
   int32_t full_waves;             /* w = floor(t / slots) */
   int32_t tail_tiles;             /* r = t mod slots */
   int32_t max_peers;              /* most partials any owner adds */
   int32_t packs;                  /* bit 0: A is repacked, bit 1: B is repacked */
+  /* SK_SCHED_XCD_ALIGNED only (else 0): workgroup x covers region iterations
+   * [floor(x*sk_blocks*ipt/phase_div), floor((x+1)*sk_blocks*ipt/phase_div));
+   * tiles are ordered in bands of group_rows tile rows */
+  int32_t phase_div;              /* D: quanta per tile (a multiple of 8) */
+  int32_t sk_blocks;              /* s: quanta per workgroup */
+  int32_t group_rows;             /* G */
+  int32_t reserved;
 } sk_plan;
 
 /* One work segment of a workgroup. */
 typedef struct {
-  int64_t tile;
+  int64_t tile;                 /* linear tile index: tile row * tiles_n + tile column */
   int64_t iter_begin, iter_end; /* k-iterations within the tile, [begin, end) */
   int32_t started;              /* holds iteration 0: the workgroup writes the tile */
   int32_t ended;                /* holds the tile's last iteration */

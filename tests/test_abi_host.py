@@ -43,33 +43,132 @@ SHAPES = [(384, 384, 128), (8192, 8192, 8192), (6144, 6144, 6144), (1000, 3000, 
           (3000, 200, 64)]
 
 
+def _check_schedule(p):
+    """Invariants every schedule must keep: each (tile, k-iteration) is
+    covered exactly once; the segment holding a tile's k = 0 iteration is its
+    owner and, when it does not also hold the last iteration, adds the
+    partials of exactly workgroups owner+1 .. last_peer, which cover the rest
+    of the tile; a partial is always its workgroup's first segment (so an
+    owner never waits on a peer that must first finish other work)."""
+    t, ipt = p.tiles, p.iters_per_tile
+    cover = {}
+    for x in range(p.grid):
+        segs = sk.plan_segments(p, x)
+        for i, (tile, lb, le, st, en, lp) in enumerate(segs):
+            assert 0 <= lb < le <= ipt
+            assert st == (lb == 0) and en == (le == ipt)
+            if not st:
+                assert i == 0, (x, segs)
+            cover.setdefault(tile, []).append((lb, le, x, st, en, lp))
+    assert sorted(cover) == list(range(t))
+    for tile, segs in cover.items():
+        segs.sort()
+        assert segs[0][0] == 0 and segs[-1][1] == ipt
+        assert all(a[1] == b[0] for a, b in zip(segs, segs[1:])), (tile, segs)
+        owner = segs[0]
+        peers = sorted(s_[2] for s_ in segs[1:])
+        if owner[4]:
+            assert peers == [] and owner[5] == -1
+        else:
+            assert peers == list(range(owner[2] + 1, owner[5] + 1)), (tile, segs)
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("dtype", [sk.F16, sk.F32])
-@pytest.mark.parametrize("slots", [256, 512, 7])
-def test_auto_plan_matches_oracle_decomposition(shape, dtype, slots):
+@pytest.mark.parametrize("slots", [256, 512, 8])
+def test_page_schedules_match_oracle_decomposition(shape, dtype, slots):
+    """The page's decompositions, chosen explicitly, against the oracle's own
+    construction of Algorithms 2 and 5 and section 5.2's hybrids."""
+    m, n, k = shape
+    d = _desc(m, n, k, dtype)
+    for sched, mode in [(sk.SCHED_DP, oracle.DP_PERSISTENT), (sk.SCHED_SK_BASIC, oracle.SK),
+                        (sk.SCHED_SK_HYBRID2, oracle.HYBRID2), (sk.SCHED_SK_HYBRID1, oracle.HYBRID1)]:
+        p = sk.plan_query(d, sk.make_options(schedule=sched), slots)
+        t, ipt = p.tiles, p.iters_per_tile
+        assert t == -(-m // p.tile_m) * -(-n // p.tile_n) and ipt == -(-k // p.tile_k)
+        w, r = t // slots, t % slots
+        assert (p.full_waves, p.tail_tiles) == (w, r)
+        assert p.group_rows == 0 and p.phase_div == 0
+        if sched == sk.SCHED_SK_HYBRID2 and (w < 1 or r == 0):
+            continue  # resolved to another schedule (checked below)
+        if sched == sk.SCHED_DP:
+            param = p.grid
+        elif sched == sk.SCHED_SK_BASIC:
+            assert min(t, slots) <= p.grid <= slots
+            param = p.grid
+        else:
+            param = slots
+        assert p.schedule == sched
+        want = _oracle_records(m, n, k, p.tile_m, p.tile_n, p.tile_k, mode, param)
+        assert _lib_plan_records(p) == want
+        _check_schedule(p)
+
+
+@pytest.mark.parametrize("shape", SHAPES + [(4352, 4096, 4096), (9392, 2976, 14144), (3808, 4624, 720),
+                                            (2048, 2048, 8192), (512, 512, 30000), (256 * 17, 256 * 16, 256)])
+@pytest.mark.parametrize("dtype", [sk.F16, sk.F32])
+@pytest.mark.parametrize("slots", [256, 512, 8])
+def test_auto_xcd_aligned_schedule_invariants(shape, dtype, slots):
     m, n, k = shape
     d = _desc(m, n, k, dtype)
     p = sk.plan_query(d, None, slots)
-    t, ipt = p.tiles, p.iters_per_tile
-    assert t == -(-m // p.tile_m) * -(-n // p.tile_n) and ipt == -(-k // p.tile_k)
-    w, r = t // slots, t % slots
-    assert (p.full_waves, p.tail_tiles) == (w, r)
-    if r == 0:
-        assert p.schedule == sk.SCHED_DP and p.sk_tiles == 0
-        mode, param = oracle.DP_PERSISTENT, p.grid
-    elif w >= 1 and p.schedule == sk.SCHED_SK_HYBRID2:
-        assert p.grid == slots and p.sk_tiles == r + slots
-        mode, param = oracle.HYBRID2, slots
-    elif w >= 1:
-        # the model judged the hybrid's fixup too costly for this k
-        assert p.schedule == sk.SCHED_DP and p.sk_tiles == 0
-        mode, param = oracle.DP_PERSISTENT, p.grid
+    assert p.schedule == sk.SCHED_XCD_ALIGNED and p.group_rows == 8
+    t, w, r = p.tiles, p.tiles // slots, p.tiles % slots
+    if w >= 1 and r == 0:
+        assert p.sk_tiles == 0 and p.grid == slots
+    if p.sk_tiles:
+        D, s = p.phase_div, p.sk_blocks
+        assert D % 8 == 0 and slots % D == 0 and s >= 1
+        assert p.sk_tiles in (t, slots + r)
+        assert p.grid <= slots and p.grid % 8 == 0
+        assert (p.sk_iters_q, p.sk_iters_r) == divmod(s * p.iters_per_tile, D)
+        if w >= 1:
+            assert p.grid == slots and s >= D and p.max_peers <= 1
     else:
-        assert p.schedule in (sk.SCHED_SK_BASIC,) and t <= p.grid <= slots
-        mode, param = oracle.SK, p.grid
-    got = _lib_plan_records(p)
-    want = _oracle_records(m, n, k, p.tile_m, p.tile_n, p.tile_k, mode, param)
-    assert got == want
+        assert p.phase_div == 0 and p.grid == min(t, slots)
+    _check_schedule(p)
+    for x in range(p.grid):
+        assert sum(e - b for _, b, e, *_ in sk.plan_segments(p, x)) <= \
+            (-(-p.sk_blocks * p.iters_per_tile // p.phase_div) if p.sk_tiles else 0) + \
+            -(-(t - p.sk_tiles) // p.grid) * p.iters_per_tile
+
+
+@pytest.mark.parametrize("shape", [(4352, 4096, 4096), (9392, 2976, 14144), (3808, 4624, 720),
+                                   (2048, 2048, 8192), (1024, 6144, 4096), (6000, 5000, 3000)])
+def test_xcd_aligned_workgroups_of_one_class_run_in_lock_step(shape):
+    """Workgroups x and x + D (D = phase_div, a multiple of 8, so both sit on
+    the same XCD) start at the same k offset and cross tile boundaries at the
+    same times: their Stream-K segments have identical k ranges, and at every
+    step they work on tiles of one 8-row band."""
+    m, n, k = shape
+    p = sk.plan_query(_desc(m, n, k), sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256)
+    assert p.sk_tiles > 0
+    D = p.phase_div
+    J = -(-p.sk_tiles // p.sk_blocks)
+    region = p.sk_tiles * p.iters_per_tile
+    for c in range(D):
+        members = [c + D * j for j in range(J) if c + D * j < p.grid]
+        full = [x for x in members
+                if (x + 1) * p.sk_blocks * p.iters_per_tile // D <= region]
+        shapes = {tuple((b, e) for _, b, e, *_ in sk.plan_segments(p, x)[:_n_sk(p, x)]) for x in full}
+        assert len(shapes) == 1, (c, shapes)
+        # tiles processed at the same step: contiguous block of the band order
+        nseg = _n_sk(p, full[0])
+        for i in range(nseg):
+            tiles = [sk.plan_segments(p, x)[i][0] for x in full]
+            rows = {tl // p.tiles_n for tl in tiles}
+            cols = {tl % p.tiles_n for tl in tiles}
+            assert len(rows) + len(cols) <= len(tiles) // 2 + 10, (c, i, rows, cols)
+
+
+def _n_sk(p, x):
+    """Number of Stream-K segments of workgroup x (the rest are whole tiles
+    dealt after the region)."""
+    b = x * p.sk_blocks * p.iters_per_tile // p.phase_div
+    e = min((x + 1) * p.sk_blocks * p.iters_per_tile // p.phase_div, p.sk_tiles * p.iters_per_tile)
+    if e <= b:
+        return 0
+    return (e - 1) // p.iters_per_tile - b // p.iters_per_tile + 1
 
 
 @pytest.mark.parametrize("shape", SHAPES[:6])
@@ -109,20 +208,23 @@ def test_page_example_plan_through_the_library():
     assert partials == 3
 
 
-def test_auto_takes_the_hybrid_only_when_k_pays_for_the_fixup():
-    """t = 272 tiles on 256 slots: the hybrid saves 15/16 of a tile's
+def test_auto_keeps_the_stream_k_region_only_when_k_pays_for_the_fixup():
+    """t = 272 tiles on 256 slots: the region saves most of a tile's
     iterations per workgroup, which beats one partial + one peer only when
     the tile has enough iterations."""
     short = sk.plan_query(_desc(256 * 17, 256 * 16, 256), None, 256)
     long_ = sk.plan_query(_desc(256 * 17, 256 * 16, 8192), None, 256)
-    assert short.schedule == sk.SCHED_DP and long_.schedule == sk.SCHED_SK_HYBRID2
+    assert short.schedule == long_.schedule == sk.SCHED_XCD_ALIGNED
+    assert short.sk_tiles == 0 and long_.sk_tiles == 272 and long_.grid == 256
 
 
 def test_two_tile_hybrid_owner_has_one_peer():
     for t_m, t_n in [(17, 17), (23, 12), (16, 17)]:
         d = _desc(256 * t_m, 256 * t_n, 4096, sk.F16)
-        p = sk.plan_query(d, None, 256)
+        p = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_HYBRID2), 256)
         assert p.schedule == sk.SCHED_SK_HYBRID2 and p.max_peers == 1
+        p = sk.plan_query(d, None, 256)
+        assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles > 0 and p.max_peers == 1
 
 
 def test_grid_model_regimes():
@@ -130,14 +232,22 @@ def test_grid_model_regimes():
     short-wide shapes use every slot, a medium-k 64-tile shape stays at the
     tile count, a single tile with a huge k stops at a small grid."""
     model = (4.0, 2.0, 1.0, 2.0)
+    basic = sk.SCHED_SK_BASIC
     # T(g) ~ c*I/g + d*g/t is minimised near sqrt(c*I*t/d); with t = 16 tiles
     # and I = 16 * 1024 iterations that lies beyond the 256 slots
-    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model), 256)
+    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model, schedule=basic), 256)
     assert p.grid == 256
     # 64 tiles of 4 iterations: splitting saves at most 2 iterations per
     # workgroup but costs b + d = 4
-    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model), 256)
+    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model, schedule=basic), 256)
     assert p.grid == 64
+    p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model, schedule=basic), 256)
+    assert 1 < p.grid <= 16
+    # the same regimes under the XCD-aware split (grid = D * ceil(t / s))
+    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model), 256)
+    assert p.sk_tiles == 16 and p.grid == 256
+    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model), 256)
+    assert p.sk_tiles == 0 and p.grid == 64
     p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model), 256)
     assert 1 < p.grid <= 16
 
@@ -169,6 +279,10 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
                       check=False) == sk.ERR_INVALID_ARG
     assert sk.gemm(8, 8, 8, 1.0, 16, 7, 16, 8, 0.0, 16, 8, sk.F32, 0, stream=0,
                    check=False) == sk.ERR_INVALID_ARG  # lda < k
+    assert sk.gemm_ex(d, sk.make_options(schedule=sk.SCHED_XCD_ALIGNED + 1), stream=0,
+                      check=False) == sk.ERR_INVALID_ARG
+    assert sk.plan_query(d, sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256).schedule == \
+        sk.SCHED_XCD_ALIGNED
 
 
 def test_strerror_texts():

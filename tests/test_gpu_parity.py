@@ -126,7 +126,8 @@ def test_every_grid_size_exact_on_integer_inputs(dtype):
         c.reset_c()
         got = c.run(1.0, 0.0, sk.make_options(forced_grid=g))
         assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), g
-    for sched in (sk.SCHED_SK_HYBRID1, sk.SCHED_SK_HYBRID2, sk.SCHED_SK_BASIC):
+    for sched in (sk.SCHED_SK_HYBRID1, sk.SCHED_SK_HYBRID2, sk.SCHED_SK_BASIC, sk.SCHED_XCD_ALIGNED,
+                  sk.SCHED_AUTO):
         c.reset_c()
         got = c.run(1.0, 0.0, sk.make_options(schedule=sched))
         assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), sched
@@ -167,18 +168,49 @@ def test_hybrid_schedule_hgemm_against_oracle():
 
 
 def test_auto_hybrid_on_a_long_k_shape_against_oracle():
-    """272 tiles with k = 8192: AUTO picks the two-tile hybrid."""
+    """272 tiles with k = 8192: AUTO keeps a Stream-K region of one wave plus
+    the 16 leftover tiles, split in XCD lock-step quanta."""
     m, n, k = 256 * 17, 256 * 16, 8192
     c = Case(m, n, k, sk.BF16, sk.A_ROW_B_COL, 16, dist="normal", scale=1 / np.sqrt(8192),
              with_c=False)
     p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, sk.BF16,
                                    sk.A_ROW_B_COL))
-    assert p.schedule == sk.SCHED_SK_HYBRID2
+    assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles == 272 and p.phase_div > 0
     got = c.run(1.0, 0.0)
     rows, cols = sample_indices(m, n, 1500, 16)
     ref, bound = c.reference_entries(rows, cols)
     assert np.max(np.abs(decode(got[rows, cols], sk.BF16) - ref) / bound) <= TOL[sk.BF16]
     assert c.freivalds(got) <= TOL[sk.BF16]
+
+
+XCD_CASES = [
+    # (m, n, k, dtype, layout): a wave or more of tiles (two-tile region plus
+    # data-parallel tiles), ragged edges, and below one wave
+    (256 * 17, 256 * 16, 256, sk.F16, sk.A_ROW_B_COL),
+    (256 * 17 - 37, 256 * 16 - 5, 300, sk.BF16, sk.A_ROW_B_COL),
+    (256 * 23, 256 * 24, 192, sk.F16, sk.A_ROW_B_COL),
+    (1000, 1000, 5000, sk.F16, sk.A_ROW_B_COL),
+    (3000, 2960, 200, sk.F32, sk.A_ROW_B_ROW),
+    (128 * 47, 128 * 23, 96, sk.F32, sk.A_COL_B_COL),
+    (600, 520, 3000, sk.F32, sk.A_COL_B_ROW),
+]
+
+
+@pytest.mark.parametrize("case", XCD_CASES)
+def test_xcd_aligned_schedule_against_oracle(case):
+    m, n, k, dtype, layout = case
+    _say("case xcd aligned", case)
+    c = Case(m, n, k, dtype, layout, 21, dist="normal", scale=1 / np.sqrt(k))
+    opts = sk.make_options(schedule=sk.SCHED_XCD_ALIGNED)
+    p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
+                                   layout), opts)
+    assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles > 0
+    got = c.run(1.0, 1.0, opts)
+    ref, bound = c.reference(1.0, 1.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+    c.reset_c()
+    again = c.run(1.0, 1.0, opts)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8))  # run-to-run bitwise
 
 
 def test_hybrid_schedule_sgemm_against_oracle():

@@ -24,6 +24,7 @@ HEADER_PATH = os.path.join(HERE, "..", "include", "sk_gemm.h")
 F32, F16, BF16 = 0, 1, 2
 A_ROW_B_ROW, A_ROW_B_COL, A_COL_B_ROW, A_COL_B_COL = 0, 1, 2, 3
 SCHED_AUTO, SCHED_DP, SCHED_SK_BASIC, SCHED_SK_HYBRID2, SCHED_SK_HYBRID1 = 0, 1, 2, 3, 4
+SCHED_XCD_ALIGNED = 5
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT, ERR_NO_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 ABFT_MAX_RECORDS = 64
@@ -77,7 +78,8 @@ class Plan(ctypes.Structure):
                 ("schedule", i32), ("tiles_m", i64), ("tiles_n", i64), ("tiles", i64),
                 ("iters_per_tile", i64), ("total_iters", i64), ("sk_tiles", i64),
                 ("sk_iters_q", i64), ("sk_iters_r", i64), ("dp_tiles", i64), ("full_waves", i32),
-                ("tail_tiles", i32), ("max_peers", i32), ("packs", i32)]
+                ("tail_tiles", i32), ("max_peers", i32), ("packs", i32), ("phase_div", i32),
+                ("sk_blocks", i32), ("group_rows", i32), ("reserved", i32)]
 
 
 class Segment(ctypes.Structure):

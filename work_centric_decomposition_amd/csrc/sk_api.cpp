@@ -142,7 +142,7 @@ int validate(const sk_gemm_desc &d, const sk_options &o, const sk_abft_report *r
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
   if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
   if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
-  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_SK_HYBRID1) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
   if (o.forced_grid < 0 || o.hybrid_min_waves < 0 || o.n_faults < 0 || o.spin_limit_us < 0)
     return SK_ERR_INVALID_ARG;
   if (o.n_faults > 0 && o.faults == nullptr) return SK_ERR_INVALID_ARG;
@@ -236,8 +236,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   a.alpha = d.alpha; a.beta = d.beta;
   a.tiles_m = (int32_t)P.tiles_m; a.tiles_n = (int32_t)P.tiles_n;
   a.tiles = (int32_t)P.tiles; a.ipt = (int32_t)P.ipt;
-  a.grid = P.grid; a.sk_tiles = (int32_t)P.sk_tiles;
-  a.sk_q = P.sk_q; a.sk_r = P.sk_r;
+  a.sched = P.sched();
   a.partials = ws->partials; a.flags = ws->flags; a.epoch = ws->epoch; a.status = ws->status;
   const int64_t us = o.spin_limit_us > 0 ? o.spin_limit_us : 2000000;
   a.spin_limit = us * info->wall_khz / 1000;
@@ -308,6 +307,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
     out->dp_tiles = P.dp_tiles; out->full_waves = P.w; out->tail_tiles = P.r;
     out->max_peers = plan_max_peers(P);
     out->packs = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
+    out->phase_div = P.phase_div; out->sk_blocks = P.blocks; out->group_rows = P.group_rows;
     return SK_OK;
   } catch (...) {
     return SK_ERR_NO_MEMORY;

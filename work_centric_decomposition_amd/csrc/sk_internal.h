@@ -49,6 +49,130 @@ inline TileCfg tile_cfg(int dtype) {
                  4.f / it, 5.f / it, 1.f, 4.f / it};
 }
 
+// How the kernels walk the work (shared by the kernels and the host's
+// segment listing, so both enumerate exactly the same segments).
+//
+// Tiles are visited in "region order" u = 0 .. tiles-1: the Stream-K region
+// is u < sk_tiles, the data-parallel tiles follow.  With group_rows == 0,
+// region order is the linear m -> n order and data-parallel tile j of
+// workgroup x is u = sk_tiles + x + j * grid (the page's layout).
+//
+// With group_rows = G > 0 (the XCD-aware schedule), u is mapped to tiles in
+// bands of G tile rows, column by column within a band, and
+//  * workgroup x's data-parallel tiles are u = sk_tiles + slot + j * grid
+//    with slot = (x % 8) * (grid / 8) + x / 8: the workgroups that the
+//    dispatcher places on one XCD (x mod 8 equal) take a run of grid / 8
+//    consecutive u, a compact block of tiles sharing A rows and B columns;
+//  * the Stream-K region is split in quanta of ipt / D iterations
+//    (D = phase_div, a multiple of 8): workgroup x covers
+//    [floor(x s ipt / D), floor((x+1) s ipt / D)) of the region's
+//    iterations, cut at sk_tiles * ipt.  Workgroups with equal x mod D then
+//    work at the same k offset at the same time, and the region's tile index
+//    L is mapped so that those workgroups also work on neighbouring tiles:
+//    L = j s + v (v < s) is tile u = prefix(v) + j, where block v holds the
+//    block_len (or block_len - 1 for v >= block_cut) tiles L = v, v + s, ....
+struct Sched {
+  int64_t ipt, tiles, tiles_m, tiles_n;
+  int64_t sk_tiles;
+  int64_t sk_q, sk_r;   // even split (group_rows == 0): the first sk_r get sk_q + 1
+  int64_t grid;
+  int64_t phase_div;    // D (XCD-aware schedule with a Stream-K region), else 0
+  int64_t blocks;       // s: quanta per workgroup
+  int64_t block_len;    // J = ceil(sk_tiles / s)
+  int64_t block_cut;    // sk_tiles - (J - 1) * s
+  int64_t group_rows;   // G, 0 for the page's linear order
+};
+
+#define SK_HD __host__ __device__ __forceinline__
+
+SK_HD int64_t sched_min(int64_t a, int64_t b) { return a < b ? a : b; }
+
+// Tile (linear m -> n index) of region-order position u.
+SK_HD int64_t sched_tile_of_u(const Sched &S, int64_t u) {
+  if (S.group_rows <= 0) return u;
+  const int64_t band = S.group_rows * S.tiles_n;
+  const int64_t b = u / band, rem = u - b * band;
+  const int64_t rows = sched_min(S.group_rows, S.tiles_m - b * S.group_rows);
+  return (b * S.group_rows + rem % rows) * S.tiles_n + rem / rows;
+}
+
+// Tile of Stream-K region position L.
+SK_HD int64_t sched_sk_tile(const Sched &S, int64_t L) {
+  if (S.phase_div <= 0) return sched_tile_of_u(S, L);
+  const int64_t v = L % S.blocks, j = L / S.blocks;
+  const int64_t over = v - S.block_cut;
+  return sched_tile_of_u(S, v * S.block_len - (over > 0 ? over : 0) + j);
+}
+
+// First Stream-K iteration of workgroup x (x == grid gives the region's end).
+SK_HD int64_t sched_first_iter(const Sched &S, int64_t x) {
+  if (S.phase_div > 0) return sched_min(x * S.blocks * S.ipt / S.phase_div, S.sk_tiles * S.ipt);
+  return x * S.sk_q + (x < S.sk_r ? x : S.sk_r);
+}
+
+// Workgroup whose Stream-K range holds iteration `it`.
+SK_HD int64_t sched_owner_of(const Sched &S, int64_t it) {
+  if (S.phase_div > 0) return ((it + 1) * S.phase_div - 1) / (S.blocks * S.ipt);
+  const int64_t big = S.sk_r * (S.sk_q + 1);
+  return it < big ? it / (S.sk_q + 1) : S.sk_r + (it - big) / S.sk_q;
+}
+
+// Segments of workgroup x in execution order: its Stream-K range (Algorithm
+// 5: a workgroup that holds a tile's k = 0 iteration but not its last one
+// adds the partials of workgroups x+1 .. last_peer), then its data-parallel
+// tiles.  The iterator keeps three integers of state, so that a kernel that
+// runs a whole MAC loop per segment keeps little alive across it (the
+// kernels call next() from a single site).
+struct SegIter {
+  int64_t it, end;  // remaining Stream-K range
+  int64_t d;        // next data-parallel index
+};
+struct Segment {
+  int64_t tile, lb, le, last_peer;
+  bool started, ended;
+};
+
+SK_HD SegIter sched_begin(const Sched &S, int64_t x) {
+  SegIter I;
+  I.it = S.sk_tiles > 0 ? sched_first_iter(S, x) : 0;
+  I.end = S.sk_tiles > 0 ? sched_first_iter(S, x + 1) : 0;
+  I.d = (S.group_rows > 0 && S.grid % 8 == 0) ? (x % 8) * (S.grid / 8) + x / 8 : x;
+  return I;
+}
+
+SK_HD bool sched_next(const Sched &S, SegIter &I, Segment &g) {
+  if (I.it < I.end) {
+    const int64_t L = I.it / S.ipt, ts = L * S.ipt, te = ts + S.ipt;
+    g.lb = I.it - ts;
+    g.le = (I.end < te ? I.end : te) - ts;
+    g.started = g.lb == 0;
+    g.ended = I.end >= te;
+    g.last_peer = (g.started && !g.ended) ? sched_owner_of(S, te - 1) : -1;
+    g.tile = sched_sk_tile(S, L);
+    I.it = te;
+    return true;
+  }
+  if (I.d < S.tiles - S.sk_tiles) {
+    g.tile = sched_tile_of_u(S, S.sk_tiles + I.d);
+    g.lb = 0;
+    g.le = S.ipt;
+    g.started = g.ended = true;
+    g.last_peer = -1;
+    I.d += S.grid;
+    return true;
+  }
+  return false;
+}
+
+// Calls f(tile, lb, le, started, ended, last_peer) for each segment of
+// workgroup x (host-side listing).
+template <class F>
+SK_HD void sched_segments(const Sched &S, int64_t x, F &&f) {
+  SegIter I = sched_begin(S, x);
+  Segment g;
+  while (sched_next(S, I, g)) f(g.tile, g.lb, g.le, g.started, g.ended, g.last_peer);
+}
+
 // Resolved work decomposition (integers only).
 struct Plan {
   int64_t m, n, k;
@@ -58,26 +182,30 @@ struct Plan {
   int grid;             // g
   int schedule;         // resolved sk_schedule
   int64_t tiles_m, tiles_n, tiles, ipt, total;
-  int64_t sk_tiles;     // Stream-K region: tiles [0, sk_tiles)
+  int64_t sk_tiles;     // Stream-K region: tiles [0, sk_tiles) of region order
   int64_t sk_q, sk_r;   // even split of sk_tiles*ipt over g: first sk_r get sk_q+1
-  int64_t dp_tiles;     // tiles [sk_tiles, tiles), round-robin over g
+  int64_t dp_tiles;     // the remaining tiles, dealt over g
   int w, r;             // full waves and leftover tiles
+  int phase_div, blocks, group_rows;  // XCD-aware schedule (see Sched)
   int max_peers;        // filled by plan_max_peers (inspection only)
   bool pack_a, pack_b;  // operand repacked to k-contiguous before the GEMM
+  Sched sched() const {
+    Sched S{};
+    S.ipt = ipt; S.tiles = tiles; S.tiles_m = tiles_m; S.tiles_n = tiles_n;
+    S.sk_tiles = sk_tiles; S.sk_q = sk_q; S.sk_r = sk_r; S.grid = grid;
+    S.phase_div = phase_div; S.blocks = blocks; S.group_rows = group_rows;
+    if (phase_div > 0 && blocks > 0) {
+      S.block_len = (sk_tiles + blocks - 1) / blocks;
+      S.block_cut = sk_tiles - (S.block_len - 1) * blocks;
+    }
+    return S;
+  }
 };
 
 // Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots > 0.
 int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &plan);
 // Most partials any owner adds under `plan` (O(tiles); for inspection).
 int plan_max_peers(const Plan &plan);
-
-// First Stream-K iteration of workgroup x (x == grid gives the region's end).
-inline int64_t sk_first_iter(int64_t q, int64_t r, int64_t x) { return x * q + (x < r ? x : r); }
-// Workgroup whose Stream-K range holds iteration `it`.
-inline int64_t sk_owner_of(int64_t q, int64_t r, int64_t it) {
-  int64_t big = r * (q + 1);
-  return it < big ? it / (q + 1) : r + (it - big) / q;
-}
 
 // Does the kernel read this operand directly (true), or from a repacked
 // k-contiguous copy (false)?  `kmajor` = operand contiguous along k.
@@ -97,8 +225,7 @@ struct KernelArgs {
   int32_t a_kext, b_kext;
   float alpha, beta;
   int32_t tiles_m, tiles_n, tiles, ipt;
-  int32_t grid, sk_tiles;
-  int64_t sk_q, sk_r;
+  Sched sched;
   float *partials;     // grid slots of BM*BN floats
   uint32_t *flags;     // grid flags
   uint32_t epoch;

@@ -35,6 +35,7 @@ namespace dev {
 typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_vptr;
@@ -48,6 +49,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const char *base, in
   int32_t n = bytes <= 0 ? 0 : (bytes > 0x7FFFFFFF ? 0x7FFFFFFF : (int32_t)bytes);
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char *>(base), (short)0, n, kRsrcWord3);
 }
+
+// s_waitcnt immediate that waits until at most n vector-memory operations
+// of this wave are outstanding (LDS/scalar and export counters unchecked).
+constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -119,20 +124,34 @@ template <> struct Elem<SK_F32> {
 // Partial tiles live in the workgroup's slot in the same per-lane order as
 // the accumulators (float4 i of thread t at slot[i * NT + t]), so the store
 // and the owner's load are both fully coalesced 16-byte accesses.
-// Ordering: every thread's stores complete before the workgroup barrier; the
-// flag is then published with an agent-scope release (which writes the
-// XCD's L2 back, so that a workgroup on another XCD sees the data), and the
-// owner reads the flag with agent-scope acquire semantics (invalidating its
-// own stale cached copies) before any thread loads the partial.
+// Ordering without whole-cache maintenance.  The L2 of each XCD is not
+// coherent with the others, and an agent-scope release or acquire in the
+// language memory model writes back or invalidates the entire L2 of the XCD
+// (disturbing every workgroup that shares it, and costing tens of
+// microseconds per fixup on a busy chip).  Instead, the partial tile is
+// written and read with agent-coherent (sc1) 128-bit buffer accesses, which
+// the L2 passes through to the memory side, so only the order of the
+// accesses matters:
+//   producer: sc1 stores; wait for this wave's stores to complete; workgroup
+//     barrier; thread 0 stores the flag (relaxed, agent scope, also sc1);
+//   owner: thread 0 reads the flag (relaxed, agent scope) until it holds the
+//     epoch; workgroup barrier; sc1 loads of the partial.
+constexpr int kAuxSc1 = 16;  // cache-policy operand: sc1 (agent coherence)
 
 template <class P>
 __device__ __forceinline__ void store_partial(const KernelArgs &a, int x, const typename P::Acc &acc) {
-  f4_t *slot = reinterpret_cast<f4_t *>(a.partials) + (int64_t)x * P::NACC4 * P::NT;
+  constexpr int BYTES = P::NACC4 * P::NT * 16;
+  const __amdgpu_buffer_rsrc_t r = make_rsrc(reinterpret_cast<const char *>(a.partials) + (int64_t)x * BYTES, BYTES);
   const int t = threadIdx.x;
 #pragma unroll
-  for (int i = 0; i < P::NACC4; ++i) slot[i * P::NT + t] = P::get4(acc, i);
+  for (int i = 0; i < P::NACC4; ++i) {
+    const f4_t v = P::get4(acc, i);
+    // lane offset in a register, slice offset as a scalar constant
+    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4_t, v), r, t * 16, i * P::NT * 16, kAuxSc1);
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
   __syncthreads();
-  if (t == 0) __hip_atomic_store(a.flags + x, a.epoch, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) __hip_atomic_store(a.flags + x, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Returns false if the wait timed out (the status word is set).
@@ -149,19 +168,41 @@ __device__ __forceinline__ bool wait_flag(const KernelArgs &a, int peer) {
         break;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     ok_s = ok;
   }
   __syncthreads();
   return ok_s != 0;
 }
 
+// The owner's loads go through LDS: every wave fetches its own lanes' 16-byte
+// entries of up to LDS_BYTES of the partial with direct-to-LDS loads (no
+// registers held while they are in flight, so they all overlap), waits for
+// its own loads only (no other wave reads them) and adds them from LDS.  The
+// caller has passed a workgroup barrier since the last MAC-loop LDS read; a
+// barrier at the end keeps the next segment's tile loads from overwriting
+// entries another wave has not read yet.
 template <class P>
 __device__ __forceinline__ void add_partial(const KernelArgs &a, int peer, typename P::Acc &acc) {
-  const f4_t *slot = reinterpret_cast<const f4_t *>(a.partials) + (int64_t)peer * P::NACC4 * P::NT;
-  const int t = threadIdx.x;
+  constexpr int SLICE = P::NT * 16;                       // bytes of one accumulator slice
+  constexpr int BYTES = P::NACC4 * SLICE;
+  constexpr int CHUNK = P::LDS_BYTES / SLICE < P::NACC4 ? P::LDS_BYTES / SLICE : P::NACC4;
+  static_assert(CHUNK > 0 && P::NACC4 % CHUNK == 0, "partial staging");
+  const __amdgpu_buffer_rsrc_t r =
+      make_rsrc(reinterpret_cast<const char *>(a.partials) + (int64_t)peer * BYTES, BYTES);
+  const int t = threadIdx.x, wbase = wave_id() * 1024;
 #pragma unroll
-  for (int i = 0; i < P::NACC4; ++i) P::add4(acc, i, slot[i * P::NT + t]);
+  for (int c0 = 0; c0 < P::NACC4; c0 += CHUNK) {
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(smem + i * SLICE + wbase), 16, t * 16,
+                                               (c0 + i) * SLICE, 0, kAuxSc1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+#pragma unroll
+    for (int i = 0; i < CHUNK; ++i)
+      P::add4(acc, c0 + i, *reinterpret_cast<const f4_t *>(smem + i * SLICE + t * 16));
+    if (c0 + CHUNK < P::NACC4) __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this chunk read
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------ epilogue
@@ -189,9 +230,6 @@ __device__ __forceinline__ void store4(const KernelArgs &a, bool vec_ok, int i, 
   }
 }
 
-// s_waitcnt immediate that waits until at most n vector-memory operations
-// of this wave are outstanding (LDS/scalar and export counters unchecked).
-constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 
@@ -218,6 +256,7 @@ struct HPolicy {
   static constexpr int ROW = BK * 2;  // bytes of one LDS row (k-contiguous)
   static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int LDS_BYTES = NSTAGE * STAGE;
   static constexpr int LOADS = A_BYTES / 1024 / (NT / 64);  // per operand per wave and stage
   static constexpr int ROWS_PER_LOAD = 1024 / ROW;
   // 16-byte chunk c of LDS row r is stored at chunk position c ^ swz(r):
@@ -909,6 +948,7 @@ template <bool AK, bool BKM>
 struct SPolicy {
   static constexpr int BM = SCfg::BM, BN = SCfg::BN, NT = SCfg::NT;
   static constexpr int NACC4 = SCfg::NACC;
+  static constexpr int LDS_BYTES = 2 * SCfg::STAGE;
   struct Acc { f4_t v[SCfg::NACC]; };
   static __device__ __forceinline__ f4_t get4(const Acc &c, int i) { return c.v[i]; }
   static __device__ __forceinline__ void add4(Acc &c, int i, f4_t x) { c.v[i] += x; }
@@ -951,30 +991,15 @@ __device__ __forceinline__ void run_segment(const KernelArgs &a, int x, int tile
   epilogue(m0, n0, acc);
 }
 
-// All segments of workgroup blockIdx.x: its Stream-K range (Algorithm 5 on
-// tiles [0, sk_tiles)), then its data-parallel tiles.
+// All segments of workgroup blockIdx.x, in the order the schedule gives
+// them: its Stream-K range, then its data-parallel tiles.
 template <class P, class MacLoop, class Epilogue>
 __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop macloop, Epilogue epilogue) {
   const int x = blockIdx.x;
-  if (a.sk_tiles > 0) {
-    int64_t it = (int64_t)x * a.sk_q + (x < a.sk_r ? x : a.sk_r);
-    const int64_t end = (int64_t)(x + 1) * a.sk_q + (x + 1 < a.sk_r ? x + 1 : a.sk_r);
-    while (it < end) {
-      const int tile = (int)(it / a.ipt);
-      const int64_t ts = (int64_t)tile * a.ipt, te = ts + a.ipt;
-      const int lb = (int)(it - ts), le = (int)((end < te ? end : te) - ts);
-      const bool started = lb == 0, ended = end >= te;
-      int last_peer = -1;
-      if (started && !ended) {
-        const int64_t big = a.sk_r * (a.sk_q + 1), l = te - 1;
-        last_peer = (int)(l < big ? l / (a.sk_q + 1) : a.sk_r + (l - big) / a.sk_q);
-      }
-      run_segment<P>(a, x, tile, lb, le, started, last_peer, macloop, epilogue);
-      it = te;
-    }
-  }
-  for (int tile = a.sk_tiles + x; tile < a.tiles; tile += a.grid)
-    run_segment<P>(a, x, tile, 0, a.ipt, true, -1, macloop, epilogue);
+  SegIter I = sched_begin(a.sched, x);
+  Segment g;
+  while (sched_next(a.sched, I, g))
+    run_segment<P>(a, x, (int)g.tile, (int)g.lb, (int)g.le, g.started, (int)g.last_peer, macloop, epilogue);
 }
 
 template <int DT>

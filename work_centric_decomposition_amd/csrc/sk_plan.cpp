@@ -28,11 +28,28 @@
 //  * the Stream-K region is the first tiles in linear order; each workgroup
 //    runs its Stream-K segments first and then its data-parallel tiles,
 //    which are dealt round-robin (tile sk_tiles + x + j*g);
-//  * AUTO: r == 0 is plain data-parallel; w == 0 is basic Stream-K with the
-//    model's grid size; w >= hybrid_min_waves (default 1) and r > 0 is the
-//    two-tile hybrid when the model predicts it beats data-parallel (the
-//    iterations it saves exceed the cost of one partial and one peer), else
-//    data-parallel.
+//
+// XCD-aware schedule (this library's design for MI355X, not the page's): on
+// a chip whose 256 CUs sit in 8 XCDs with one L2 each, a workgroup reads
+// 2 * 256 * 64 * 2 bytes per 64-deep fp16 iteration, so the 256 workgroups
+// together ask for about 10 TB/s and the L2s must serve most of it.  Under
+// the page's even split every workgroup starts at a different k offset and
+// the L2 hit rate falls from about 0.6-0.7 (data-parallel) to under 0.2
+// (measured with TCC_HIT / TCC_MISS), which makes the Stream-K region slower
+// per iteration than data-parallel.  The XCD-aware schedule (see Sched)
+// quantises the split to ipt / D so that the workgroups of one XCD run in
+// lock-step on a compact block of tiles.  Its planning:
+//  * the Stream-K region is all tiles when w < hybrid_min_waves (w == 0
+//    included), else one full wave plus the r leftover tiles (two-tile
+//    hybrid); r == 0 with w >= 1 leaves no region (XCD-ordered DP);
+//  * with a wave or more, D is 8, 16 or 32, whichever gives the shortest
+//    per-workgroup work s * ipt / D (s = ceil(D * sk_tiles / p)), each
+//    doubling of D charged 3 % since it halves the workgroups in lock-step;
+//  * below a wave, D (a multiple of 8 up to p) and s are chosen by the
+//    runtime model with g = D * ceil(t / s), the same 3 % charge per doubling
+//    of D beyond 16;
+//  * AUTO keeps the region only when the model predicts it beats the
+//    XCD-ordered data-parallel form.
 #include <algorithm>
 #include <cmath>
 #include <cstring>
@@ -58,6 +75,10 @@ bool operand_direct(int dtype, bool kmajor, const void *ptr, int64_t ld, int64_t
 // whether any tile is split.
 static int split_peers(int64_t tiles, int64_t ipt, int64_t g, bool *any_split) {
   const int64_t I = tiles * ipt, q = I / g, r = I % g;
+  auto sk_owner_of = [](int64_t q, int64_t r, int64_t it) {
+    const int64_t big = r * (q + 1);
+    return it < big ? it / (q + 1) : r + (it - big) / q;
+  };
   int peers = 0;
   bool split = false;
   for (int64_t t = 0; t < tiles; ++t) {
@@ -91,12 +112,51 @@ static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, f
   return best_g;
 }
 
+// Charge for the phase classes that share one XCD's L2 (D / 8 of them).
+static double phase_charge(int64_t D) {
+  double f = 1.0;
+  for (int64_t d = 16; d < D; d *= 2) f *= 1.03;
+  return f;
+}
+
+// XCD-aware schedule over a Stream-K region of sk_tiles tiles with the whole
+// grid (a wave or more): D in {8, 16, 32} and s = ceil(D * sk_tiles / p).
+static void aligned_wave(int64_t sk_tiles, int64_t ipt, int slots, int *D_out, int *s_out) {
+  double best = 1e300;
+  for (int64_t D = 8; D <= 32 && D <= slots; D *= 2) {
+    if (slots % D) continue;
+    const int64_t s = cdiv(D * sk_tiles, slots);
+    const double T = (double)cdiv(s * ipt, D) * (D > 8 ? 1.03 * phase_charge(D) : 1.0);
+    if (T < best - 1e-9) { best = T; *D_out = (int)D; *s_out = (int)s; }
+  }
+}
+
+// XCD-aware schedule below one wave: D (multiple of 8 dividing p) and s by
+// the runtime model with g = D * ceil(t / s) workgroups.
+static double aligned_small(int64_t t, int64_t ipt, int slots, float a, float b, float c, float d, int *D_out,
+                            int *s_out) {
+  double best = 1e300;
+  for (int64_t D = 8; D <= slots; D *= 2) {
+    if (slots % D) continue;
+    for (int64_t s = 1; s <= D; ++s) {
+      const int64_t J = cdiv(t, s);
+      if (D * J > slots) continue;
+      const bool split = s % D != 0 || (s * ipt) % D != 0;
+      const int64_t work = cdiv(s * ipt, D);
+      const int64_t peers = split ? std::max<int64_t>(1, cdiv(D - 1, s)) : 0;
+      const double T = (a + (split ? b : 0.0) + c * (double)work + d * (double)peers) * phase_charge(D);
+      if (T < best - 1e-9) { best = T; *D_out = (int)D; *s_out = (int)s; }
+    }
+  }
+  return best;
+}
+
 int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
   std::memset(&P, 0, sizeof(P));
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
   if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
   if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
-  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_SK_HYBRID1) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
   if (o.forced_grid < 0 || slots <= 0) return SK_ERR_INVALID_ARG;
   // 32-bit indices inside the kernels
   if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
@@ -133,22 +193,7 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
     grid = o.forced_grid;
     sk_tiles = P.tiles;
   } else {
-    if (sched == SK_SCHED_AUTO) {
-      if (P.r == 0) {
-        sched = SK_SCHED_DP;
-      } else if (P.w >= min_waves) {
-        // the same model decides whether giving back a wave pays for the
-        // fixup: DP runs ceil(t/p) full tiles, the two-tile hybrid
-        // ceil((r+p)*ipt/p) Stream-K iterations plus w-1 tiles, one partial
-        // and one peer per workgroup
-        const double t_dp = (double)(P.w + 1) * P.ipt;
-        const double t_h2 = (double)cdiv((P.r + slots) * P.ipt, slots) + (double)(P.w - 1) * P.ipt +
-                            (mb + md) / mc;
-        sched = t_h2 < t_dp ? SK_SCHED_SK_HYBRID2 : SK_SCHED_DP;
-      } else {
-        sched = SK_SCHED_SK_BASIC;
-      }
-    }
+    if (sched == SK_SCHED_AUTO) sched = SK_SCHED_XCD_ALIGNED;
     if (sched == SK_SCHED_SK_HYBRID2 && (P.w < 1 || P.r == 0))
       sched = P.r == 0 ? SK_SCHED_DP : SK_SCHED_SK_BASIC;
     switch (sched) {
@@ -168,6 +213,33 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
         grid = slots;
         sk_tiles = P.r;
         break;
+      case SK_SCHED_XCD_ALIGNED: {
+        P.group_rows = 8;
+        int D = 0, s = 0;
+        if (P.w == 0) {
+          const double t_al = aligned_small(P.tiles, P.ipt, slots, ma, mb, mc, md, &D, &s);
+          // the data-parallel form: one tile per workgroup
+          const double t_dp = ma + mc * (double)P.ipt;
+          if (o.schedule == SK_SCHED_AUTO && t_dp <= t_al) D = 0;
+        } else if (P.r > 0) {
+          sk_tiles = P.w >= min_waves ? P.r + slots : P.tiles;
+          aligned_wave(sk_tiles, P.ipt, slots, &D, &s);
+          const double t_al = (double)cdiv((int64_t)s * P.ipt, D) +
+                              (double)((P.tiles - sk_tiles) / slots) * P.ipt + (mb + md) / mc;
+          const double t_dp = (double)(P.w + 1) * P.ipt;
+          if (o.schedule == SK_SCHED_AUTO && t_dp <= t_al) D = 0;
+        }
+        if (D > 0) {
+          if (P.w == 0) sk_tiles = P.tiles;
+          P.phase_div = D;
+          P.blocks = s;
+          grid = P.w == 0 ? (int64_t)D * cdiv(P.tiles, s) : slots;
+        } else {
+          sk_tiles = 0;
+          grid = std::min<int64_t>(P.tiles, slots);
+        }
+        break;
+      }
     }
   }
   if (grid > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
@@ -175,7 +247,10 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
   P.grid = (int)grid;
   P.sk_tiles = sk_tiles;
   P.dp_tiles = P.tiles - sk_tiles;
-  if (sk_tiles > 0) {
+  if (sk_tiles > 0 && P.phase_div > 0) {
+    P.sk_q = (int64_t)P.blocks * P.ipt / P.phase_div;
+    P.sk_r = (int64_t)P.blocks * P.ipt % P.phase_div;
+  } else if (sk_tiles > 0) {
     const int64_t I = sk_tiles * P.ipt;
     P.sk_q = I / grid;
     P.sk_r = I % grid;
@@ -184,7 +259,15 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
 }
 
 int plan_max_peers(const Plan &P) {
-  return P.sk_tiles > 0 ? split_peers(P.sk_tiles, P.ipt, P.grid, nullptr) : 0;
+  if (P.sk_tiles <= 0) return 0;
+  if (P.phase_div <= 0) return split_peers(P.sk_tiles, P.ipt, P.grid, nullptr);
+  const Sched S = P.sched();
+  int64_t peers = 0;
+  for (int64_t x = 0; x < P.grid; ++x)
+    sched_segments(S, x, [&](int64_t, int64_t, int64_t, bool, bool, int64_t lp) {
+      if (lp >= 0 && lp - x > peers) peers = lp - x;
+    });
+  return (int)peers;
 }
 
 }  // namespace sk
@@ -194,23 +277,22 @@ using namespace sk;
 extern "C" int64_t sk_plan_segments(const sk_plan *plan, int64_t x, sk_segment *out, int64_t cap) {
   if (!plan || x < 0 || cap < 0 || (cap > 0 && !out)) return SK_ERR_INVALID_ARG;
   if (x >= plan->grid) return 0;
-  int64_t n = 0;
-  auto push = [&](int64_t tile, int64_t lb, int64_t le, int st, int en, int64_t lp) {
-    if (n < cap) out[n] = sk_segment{tile, lb, le, st, en, lp};
-    ++n;
-  };
-  const int64_t ipt = plan->iters_per_tile, q = plan->sk_iters_q, r = plan->sk_iters_r;
-  if (plan->sk_tiles > 0) {
-    int64_t it = sk_first_iter(q, r, x), end = sk_first_iter(q, r, x + 1);
-    while (it < end) {
-      int64_t tile = it / ipt, ts = tile * ipt, te = ts + ipt;
-      int64_t lb = it - ts, le = std::min(end, te) - ts;
-      int st = it == ts, en = end >= te;
-      int64_t lp = (st && !en) ? sk_owner_of(q, r, te - 1) : -1;
-      push(tile, lb, le, st, en, lp);
-      it = te;
-    }
+  if (plan->iters_per_tile <= 0 || plan->tiles <= 0) return 0;
+  if (plan->phase_div > 0 && plan->sk_blocks <= 0) return SK_ERR_INVALID_ARG;
+  Sched S{};
+  S.ipt = plan->iters_per_tile; S.tiles = plan->tiles;
+  S.tiles_m = plan->tiles_m; S.tiles_n = plan->tiles_n;
+  S.sk_tiles = plan->sk_tiles; S.sk_q = plan->sk_iters_q; S.sk_r = plan->sk_iters_r;
+  S.grid = plan->grid; S.phase_div = plan->phase_div; S.blocks = plan->sk_blocks;
+  S.group_rows = plan->group_rows;
+  if (S.phase_div > 0) {
+    S.block_len = (S.sk_tiles + S.blocks - 1) / S.blocks;
+    S.block_cut = S.sk_tiles - (S.block_len - 1) * S.blocks;
   }
-  for (int64_t t = plan->sk_tiles + x; t < plan->tiles; t += plan->grid) push(t, 0, ipt, 1, 1, -1);
+  int64_t n = 0;
+  sched_segments(S, x, [&](int64_t tile, int64_t lb, int64_t le, bool st, bool en, int64_t lp) {
+    if (n < cap) out[n] = sk_segment{tile, lb, le, st ? 1 : 0, en ? 1 : 0, lp};
+    ++n;
+  });
   return n;
 }
