@@ -38,7 +38,27 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # HBM bytes per dispatch measured with rocprofv3 counters (FETCH_SIZE and
 # WRITE_SIZE, scaled by the copy-kernel calibration); None when not measured
 # for the current kernel.
-TRAFFIC_BYTES = {"sgemm-sweep": None, "hgemm-8192": None}
+# HBM traffic per launch of the dominant kernel (bytes), from rocprofv3 --pmc
+# FETCH_SIZE and WRITE_SIZE runs of this script scaled by the copy-kernel
+# calibration (read and written bytes per counter KiB).  Valid only for the
+# kernel sources whose hash is recorded: after any kernel change the field
+# reports null until the counters are taken again.
+KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
+                  "work_centric_decomposition_amd/csrc/sk_internal.h")
+TRAFFIC = {"kernel_hash": None, "sgemm-sweep": None, "hgemm-8192": None}
+
+
+def kernel_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(wl):
+    return TRAFFIC[wl] if TRAFFIC["kernel_hash"] == kernel_hash() else None
 
 
 def parse():
@@ -53,10 +73,50 @@ def parse():
                    help="run the Stream-K shape sweep (first COUNT of the 2000 seeded fp16 "
                         "shapes), Stream-K (AUTO) vs data-parallel, and print its summary")
     p.add_argument("--sweep-out", default="", help="CSV file for the per-shape sweep results")
+    p.add_argument("--compare-schedules", action="store_true",
+                   help="time AUTO, the page's schedules and data-parallel on a few fp16 shapes "
+                        "(one launch each with --steps 1, e.g. under rocprofv3 --pmc)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
     return p.parse_args()
+
+
+COMPARE_SHAPES = [(9392, 2976, 14144), (4352, 4096, 4096), (3808, 4624, 720), (2048, 2048, 8192)]
+
+
+def compare_schedules(torch, sk, S, steps):
+    """Each shape of COMPARE_SHAPES (fp16, A row-major, B column-major) under
+    the data-parallel schedule, the page's two-tile hybrid (basic Stream-K
+    below one wave) and AUTO, in that order; `steps` timed launches each after
+    one warm-up (with steps == 1 the launches are easy to pick out of a
+    counter trace: dispatches come in pairs per schedule)."""
+    out = []
+    g = torch.Generator(device="cuda")
+    g.manual_seed(S.SEED_SWEEP)
+    for m, n, k in COMPARE_SHAPES:
+        A = (torch.randn(m * k, generator=g, device="cuda") / math.sqrt(k)).to(torch.float16)
+        B = torch.randn(k * n, generator=g, device="cuda").to(torch.float16)
+        C = torch.empty(m * n, device="cuda", dtype=torch.float16)
+        d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+        t = sk.plan_query(d).tiles
+        page = sk.SCHED_SK_HYBRID2 if t >= sk.plan_query(d).slots else sk.SCHED_SK_BASIC
+        for name, opts in (("dp", sk.make_options(schedule=sk.SCHED_DP)),
+                           ("page", sk.make_options(schedule=page)), ("auto", sk.make_options())):
+            sk.gemm_ex(d, opts)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                sk.gemm_ex(d, opts)
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) / steps * 1e3
+            p = sk.plan_query(d, opts)
+            out.append({"shape": [m, n, k], "schedule": name, "resolved": p.schedule, "grid": p.grid,
+                        "sk_tiles": p.sk_tiles, "phase_div": p.phase_div, "us": round(us, 1),
+                        "tflops": round(2.0 * m * n * k / us / 1e6, 1)})
+        del A, B, C
+    return out
 
 
 def calibrate_copy(torch):
@@ -202,9 +262,11 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
         w, r = divmod(t, slots)
         page = sk.SCHED_DP if r == 0 else sk.SCHED_SK_HYBRID2 if w >= 1 else sk.SCHED_SK_BASIC
         res = {}
-        for sched_name, opts in (("auto", sk.make_options()),
-                                 ("page", sk.make_options(schedule=page)),
-                                 ("dp", sk.make_options(schedule=sk.SCHED_DP))):
+        legs = [("auto", sk.make_options()), ("page", sk.make_options(schedule=page)),
+                ("dp", sk.make_options(schedule=sk.SCHED_DP))]
+        # rotate the order per shape so that clock ramps do not favour one leg
+        legs = legs[idx % 3:] + legs[:idx % 3]
+        for sched_name, opts in legs:
             sk.gemm_ex(d, opts)
             for e0, e1 in ev:
                 e0.record()
@@ -314,6 +376,10 @@ def main():
     if args.sweep:
         print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out)), flush=True)
         return
+    if args.compare_schedules:
+        for r in compare_schedules(torch, sk, S, args.steps):
+            print(json.dumps(r), flush=True)
+        return
 
     results = {}
     order = [args.workload] + ([] if args.no_extra else
@@ -339,7 +405,7 @@ def main():
                 roofline={"bound": "mfma", "achieved": round(achieved, 2),
                           "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                           "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
-                          "traffic": TRAFFIC_BYTES[wl],
+                          "traffic": traffic_for(wl),
                           "kernel": "sgemm_kernel<k-major A, n-major B>",
                           "launch_ms": round(kern_ms / len(cases), 4)},
                 config={"workload": "SGEMM fp32 square sweep m=n=k in {1024,2048,3072,4096,5120,6144},"
@@ -357,7 +423,7 @@ def main():
                                  roofline={"bound": "mfma", "achieved": round(achieved, 2),
                                            "peak": PEAK_TFLOPS[name], "unit": "TFLOP/s",
                                            "frac": round(achieved / PEAK_TFLOPS[name], 4),
-                                           "traffic": TRAFFIC_BYTES[wl],
+                                           "traffic": traffic_for(wl),
                                            "kernel": f"hgemm_kernel<{name}>",
                                            "launch_ms": round(per_launch[0], 4)})
                 del h
