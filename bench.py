@@ -386,9 +386,9 @@ def main():
                                [w for w in ("sgemm-sweep", "hgemm-8192") if w != args.workload])
     for wl in order:
         main_wl = wl == args.workload
-        # the clock needs ~10 ms of load to settle: extra legs get 10 warm-up steps
+        # the clock needs tens of ms of load to settle: extra legs get 30 warm-up steps
         steps = args.steps if main_wl else max(10, args.steps // 2)
-        warmup = args.warmup if main_wl else 10
+        warmup = args.warmup if main_wl else 30
         if wl == "sgemm-sweep":
             cases = make_sweep_inputs(torch, sk, S)
             ms, per_launch, wall = timed(torch, lambda ev: sweep_step(sk, cases, ev), len(cases),

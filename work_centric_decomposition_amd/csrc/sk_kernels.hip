@@ -497,6 +497,88 @@ __device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, i
   }
 }
 
+#ifndef SK_HGEMM_LOOKAHEAD
+#define SK_HGEMM_LOOKAHEAD 2
+#endif
+
+// MacLoop with fragments read two substeps ahead (three fragment sets in
+// rotation) for the two-stage, four-substep configuration.  The stage
+// switch moves to the middle of each iteration: after substep 1 every
+// fragment of stage i has been read, so after this wave's loads of stage
+// i+1 have landed and its LDS reads have returned, one workgroup barrier
+// both publishes stage i+1 and frees stage i for the loads of iteration
+// i+2.  The barrier is kept in the last iteration too, so a following
+// segment may overwrite either stage.
+template <int DT>
+struct HFrag {
+  typename Elem<DT>::V8 a[HPolicy<DT>::MB], b[HPolicy<DT>::NB];
+};
+
+template <int DT, int PH>
+__device__ __forceinline__ void h_iter_la2(const KernelArgs &a, const HLoader<DT> &ld, int i, int n, int lb,
+                                           int wm, int wn, HFrag<DT> (&F)[3], typename HPolicy<DT>::Acc &acc) {
+  using P = HPolicy<DT>;
+  const int buf = i & 1;
+  // global substep g = 4 i + s uses F[g % 3]; with i = PH (mod 3),
+  // 4 i = PH (mod 3)
+  constexpr int f0 = (PH + 0) % 3, f1 = (PH + 1) % 3, f2 = (PH + 2) % 3;
+  h_frags<DT>(buf, 2, wm, wn, F[f2].a, F[f2].b);
+  h_mfmas<DT>(F[f0].a, F[f0].b, acc);
+  H_INTERLEAVE();
+  __builtin_amdgcn_sched_barrier(0);
+  h_frags<DT>(buf, 3, wm, wn, F[f0].a, F[f0].b);
+  h_mfmas<DT>(F[f1].a, F[f1].b, acc);
+  H_INTERLEAVE();
+  __builtin_amdgcn_sched_barrier(0);
+  // stage switch: stage i+1 complete (its loads were the only ones in
+  // flight) and every read of stage i returned
+  __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(0));
+  __syncthreads();
+  if (i + 2 < n) ld.load(a, buf, lb + i + 2);
+  if (i + 1 < n) h_frags<DT>(buf ^ 1, 0, wm, wn, F[f1].a, F[f1].b);
+  h_mfmas<DT>(F[f2].a, F[f2].b, acc);
+  H_INTERLEAVE();
+  __builtin_amdgcn_sched_barrier(0);
+  if (i + 1 < n) h_frags<DT>(buf ^ 1, 1, wm, wn, F[f2].a, F[f2].b);
+  h_mfmas<DT>(F[f0].a, F[f0].b, acc);
+  H_INTERLEAVE();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int DT>
+__device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n0, int lb, int le,
+                                              typename HPolicy<DT>::Acc &acc) {
+  using P = HPolicy<DT>;
+  static_assert(P::NSTAGE == 2 && P::SUBS == 4, "lookahead-2 loop: two stages of four substeps");
+  constexpr int LPS = 2 * P::LOADS;
+  const int w = wave_id();
+  const int wm = w / P::WAVES_N, wn = w % P::WAVES_N;
+  P::zero(acc);
+  const int n = le - lb;
+  if (n <= 0) return;
+  HLoader<DT> ld;
+  ld.init(a, m0, n0);
+  ld.load(a, 0, lb);
+  if (n > 1) {
+    ld.load(a, 1, lb + 1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(LPS));
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(0));
+  }
+  __syncthreads();
+  HFrag<DT> F[3];
+  h_frags<DT>(0, 0, wm, wn, F[0].a, F[0].b);
+  h_frags<DT>(0, 1, wm, wn, F[1].a, F[1].b);
+  int i = 0;
+  for (; i + 3 <= n; i += 3) {
+    h_iter_la2<DT, 0>(a, ld, i, n, lb, wm, wn, F, acc);
+    h_iter_la2<DT, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
+    h_iter_la2<DT, 2>(a, ld, i + 2, n, lb, wm, wn, F, acc);
+  }
+  if (i < n) h_iter_la2<DT, 0>(a, ld, i, n, lb, wm, wn, F, acc);
+  if (i + 1 < n) h_iter_la2<DT, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
+}
+
 template <int DT>
 __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
                                            const typename HPolicy<DT>::Acc &acc) {
@@ -1006,7 +1088,14 @@ template <int DT>
 __global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, int vec_ok) {
   using P = HPolicy<DT>;
   run_workgroup<P>(
-      a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { h_macloop<DT>(a, m0, n0, lb, le, acc); },
+      a,
+      [&](int m0, int n0, int lb, int le, typename P::Acc &acc) {
+#if SK_HGEMM_LOOKAHEAD == 2
+        h_macloop_la2<DT>(a, m0, n0, lb, le, acc);
+#else
+        h_macloop<DT>(a, m0, n0, lb, le, acc);
+#endif
+      },
       [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<DT>(a, vec_ok != 0, m0, n0, acc); });
 }
 
