@@ -857,13 +857,19 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
     const int li = (int)(F.row - m0) - wm * SCfg::WTM, lj = (int)(F.col - n0) - wn * SCfg::WTN;
     if (li < 0 || li >= SCfg::WTM || lj < 0 || lj >= SCfg::WTN) continue;
     if ((lane & 15) != (li & 15) || (lane >> 4) != ((lj & 15) >> 2)) continue;
-    f4_t &v = acc[(li >> 4) * SCfg::NB + (lj >> 4)];
-    const int e = lj & 3;
-    if (F.kind == 0) {
-      v[e] += F.value;
-    } else {
-      uint32_t u = __float_as_uint(v[e]) ^ (1u << (F.bit & 31));
-      v[e] = __uint_as_float(u);
+    // every accumulator index stays a compile-time constant (a runtime index
+    // would move the whole accumulator array to scratch memory)
+#pragma unroll
+    for (int b = 0; b < SCfg::NACC; ++b) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (b != (li >> 4) * SCfg::NB + (lj >> 4) || e != (lj & 3)) continue;
+        if (F.kind == 0) {
+          acc[b][e] += F.value;
+        } else {
+          acc[b][e] = __uint_as_float(__float_as_uint(acc[b][e]) ^ (1u << (F.bit & 31)));
+        }
+      }
     }
   }
   // row and column sums of the accumulators (valid elements only)
@@ -953,10 +959,17 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
 #pragma unroll
       for (int v = 0; v < SCfg::NT / 64; ++v) others += L.others[v];
       const float rc = L.part[0][0][bi] + L.part[0][1][bi];
-      f4_t &val = acc[(li >> 4) * SCfg::NB + (lj >> 4)];
       const float fixed = rc - others;
-      const float delta = val[lj & 3] - fixed;
-      val[lj & 3] = fixed;
+      float delta = 0.f;
+#pragma unroll
+      for (int b = 0; b < SCfg::NACC; ++b) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (b != (li >> 4) * SCfg::NB + (lj >> 4) || e != (lj & 3)) continue;
+          delta = acc[b][e] - fixed;
+          acc[b][e] = fixed;
+        }
+      }
       atomicAdd(&a.report->detected, 1);
       atomicAdd(&a.report->corrected, 1);
       abft_record(a, (int64_t)m0 + bi, (int64_t)n0 + bj, delta, 1, tile, lb);
@@ -1100,7 +1113,7 @@ __global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, in
 }
 
 template <bool AK, bool BKM, bool ABFT>
-__global__ __launch_bounds__(SCfg::NT, ABFT ? 1 : 2) void sgemm_kernel(KernelArgs a, int vec_ok) {
+__global__ __launch_bounds__(SCfg::NT, 2) void sgemm_kernel(KernelArgs a, int vec_ok) {
   using P = SPolicy<AK, BKM>;
   run_workgroup<P>(
       a,
