@@ -752,7 +752,7 @@ __device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (
 // is reported as uncorrectable.  All reductions run in a fixed order.
 struct AbftLds {
   float enc[4][8][SCfg::BK];  // per-part encodings: e^T A, e^T|A|, B e, |B| e
-  float e[4][SCfg::BK];       // encodings of the iteration
+  alignas(16) float e[4][SCfg::BK];  // encodings of the iteration
   float part[4][2][128];      // rc, ra, cc, ca: two k-halves
   float sums[2][2][128];      // row sums per wave column, column sums per wave row
   float others[SCfg::NT / 64];
@@ -776,6 +776,25 @@ __device__ __forceinline__ float s_elem(int base_off, int mn, int k) {
     return *reinterpret_cast<const float *>(smem + base_off + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4) + (k & 3) * 4);
   }
   return s_mn_elem(base_off, mn, k);
+}
+
+// The 16 k values 16 h .. 16 h + 15 of row (m or n) `mn` of a staged tile:
+// four 128-bit reads in the k-major format, sixteen 32-bit reads in the
+// mn-major one.
+template <bool KMAJOR>
+__device__ __forceinline__ void s_row16(int base_off, int mn, int h, float (&v)[16]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    if (KMAJOR) {
+      const int cc = 4 * h + c;
+      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + mn * 128 + ((cc ^ ((mn >> 1) & 7)) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * c + e] = x[e];
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[4 * c + e] = s_mn_elem(base_off, mn, 16 * h + 4 * c + e);
+    }
+  }
 }
 
 template <bool AK, bool BKM>
@@ -806,21 +825,33 @@ __device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, 
   }
   __syncthreads();
   {  // checksums: thread t covers row / column t % 128 over half of the k range
+    // (entries past k_valid are zero in the staged tiles)
     const int i = t & 127, h = t >> 7;
-    const bool row_ok = i < m_valid, col_ok = i < n_valid;
-#pragma unroll 4
-    for (int kk = 0; kk < SCfg::BK / 2; ++kk) {
-      const int k = h * (SCfg::BK / 2) + kk;
-      if (k < k_valid) {
-        if (row_ok) {
-          const float v = s_elem<AK>(As, i, k);
-          pt.rc += v * L.e[2][k];
-          pt.ra += fabsf(v) * L.e[3][k];
+    if (i < m_valid) {
+      float v[16];
+      s_row16<AK>(As, i, h, v);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[2][16 * h + 4 * c]);
+        const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[3][16 * h + 4 * c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pt.rc += v[4 * c + e] * eb[e];
+          pt.ra += fabsf(v[4 * c + e]) * eba[e];
         }
-        if (col_ok) {
-          const float v = s_elem<BKM>(Bs, i, k);
-          pt.cc += L.e[0][k] * v;
-          pt.ca += L.e[1][k] * fabsf(v);
+      }
+    }
+    if (i < n_valid) {
+      float v[16];
+      s_row16<BKM>(Bs, i, h, v);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[0][16 * h + 4 * c]);
+        const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[1][16 * h + 4 * c]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          pt.cc += ea[e] * v[4 * c + e];
+          pt.ca += eaa[e] * fabsf(v[4 * c + e]);
         }
       }
     }
