@@ -751,7 +751,7 @@ __device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (
 // from its row checksum, c_ij = rc_i - sum_{l != j} c_il.  Any other pattern
 // is reported as uncorrectable.  All reductions run in a fixed order.
 struct AbftLds {
-  float enc[4][8][SCfg::BK];  // per-part encodings: e^T A, e^T|A|, B e, |B| e
+  alignas(16) float enc[4][16][SCfg::BK];  // per-part encodings: e^T A, e^T|A|, B e, |B| e
   alignas(16) float e[4][SCfg::BK];  // encodings of the iteration
   float part[4][2][128];      // rc, ra, cc, ca: two k-halves
   float sums[2][2][128];      // row sums per wave column, column sums per wave row
@@ -797,30 +797,67 @@ __device__ __forceinline__ void s_row16(int base_off, int mn, int h, float (&v)[
   }
 }
 
+// Partial encodings of one staged operand tile (128 rows of the operand by
+// BK = 32 values of k): sums over the rows and of their absolute values, by
+// 128 threads u, written to L.enc[q0] and L.enc[q0 + 1] as [part][k].
+//  k-major: part p = u >> 3 sums rows 8p .. 8p+7 of 16-byte chunk c = u & 7
+//    (k = 4c .. 4c+3) with 128-bit reads (16 parts); rows past the matrix
+//    were loaded as zeros.
+//  mn-major: thread u sums row k = u & 31 over columns 32p .. 32p+31
+//    (p = u >> 5, 4 parts); each lane starts at a different chunk so that the
+//    32 rows read at once fall in distinct bank groups; columns past the
+//    matrix in a partial chunk are masked.
+template <bool KMAJOR>
+__device__ __forceinline__ void enc_part(AbftLds &L, int q0, int base, int u, int valid) {
+  if (KMAJOR) {
+    const int c = u & 7, p = u >> 3;
+    f4_t sm = {0.f, 0.f, 0.f, 0.f}, sa = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+      const int row = 8 * p + r;
+      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) { sm[e] += x[e]; sa[e] += fabsf(x[e]); }
+    }
+    *reinterpret_cast<f4_t *>(&L.enc[q0][p][4 * c]) = sm;
+    *reinterpret_cast<f4_t *>(&L.enc[q0 + 1][p][4 * c]) = sa;
+  } else {
+    const int k = u & 31, p = u >> 5;
+    float sm = 0.f, sa = 0.f;
+#pragma unroll
+    for (int cc = 0; cc < 8; ++cc) {
+      const int c = 8 * p + ((cc + k) & 7);
+      const int pos = c ^ (4 * ((k >> 2) & 3));
+      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base + k * 512 + pos * 16);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        if (4 * c + e < valid) { sm += x[e]; sa += fabsf(x[e]); }
+    }
+    L.enc[q0][p][k] = sm;
+    L.enc[q0 + 1][p][k] = sa;
+  }
+}
+
 template <bool AK, bool BKM>
 __device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, int n_valid, int k_valid,
                                             AbftPart &pt) {
   const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
   const int t = threadIdx.x;
-  {  // encodings: thread t covers k = t % 32 over 16 rows / columns
-    const int k = t & (SCfg::BK - 1), part = t / SCfg::BK;
-    float ea = 0.f, eaa = 0.f, eb = 0.f, eba = 0.f;
-    if (k < k_valid) {
-#pragma unroll 4
-      for (int r = 0; r < 16; ++r) {
-        const int i = part * 16 + r;
-        if (i < m_valid) { const float v = s_elem<AK>(As, i, k); ea += v; eaa += fabsf(v); }
-        if (i < n_valid) { const float v = s_elem<BKM>(Bs, i, k); eb += v; eba += fabsf(v); }
-      }
-    }
-    L.enc[0][part][k] = ea; L.enc[1][part][k] = eaa; L.enc[2][part][k] = eb; L.enc[3][part][k] = eba;
+  {  // encodings: threads 0-127 form e^T A and e^T|A|, threads 128-255 B e and |B| e
+    const int u = t & 127;
+    const bool is_b = t >= 128;
+    if (is_b) enc_part<BKM>(L, 2, Bs, u, n_valid);
+    else enc_part<AK>(L, 0, As, u, m_valid);
   }
   __syncthreads();
   if (t < 4 * SCfg::BK) {
     const int q = t / SCfg::BK, k = t % SCfg::BK;
+    const bool kmaj = q < 2 ? AK : BKM;
+    const int parts = kmaj ? 16 : 4;
     float v = 0.f;
 #pragma unroll
-    for (int p = 0; p < 8; ++p) v += L.enc[q][p][k];
+    for (int p = 0; p < 16; ++p)
+      if (p < parts) v += L.enc[q][p][k];
     L.e[q][k] = v;
   }
   __syncthreads();
