@@ -218,6 +218,19 @@ def test_auto_keeps_the_stream_k_region_only_when_k_pays_for_the_fixup():
     assert short.sk_tiles == 0 and long_.sk_tiles == 272 and long_.grid == 256
 
 
+def test_auto_below_a_wave_needs_a_clear_iteration_gain():
+    """228 tiles of 229 iterations on 256 slots: the split would save about
+    11 % of the iterations, less than the single data-parallel wave gains
+    from its 28 idle CUs (higher clock), so AUTO keeps the wave; 64 tiles
+    split four ways save 75 % and keep the split."""
+    near = sk.plan_query(_desc(2896, 4816, 14608), None, 256)
+    assert near.tiles == 228 and near.sk_tiles == 0 and near.grid == 228
+    forced = sk.plan_query(_desc(2896, 4816, 14608), sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256)
+    assert forced.sk_tiles == 228
+    far = sk.plan_query(_desc(2048, 2048, 8192), None, 256)
+    assert far.sk_tiles == 64 and far.grid == 256
+
+
 def test_two_tile_hybrid_owner_has_one_peer():
     for t_m, t_n in [(17, 17), (23, 12), (16, 17)]:
         d = _desc(256 * t_m, 256 * t_n, 4096, sk.F16)

@@ -47,7 +47,8 @@
 //    doubling of D charged 3 % since it halves the workgroups in lock-step;
 //  * below a wave, D (a multiple of 8 up to p) and s are chosen by the
 //    runtime model with g = D * ceil(t / s), the same 3 % charge per doubling
-//    of D beyond 16;
+//    of D beyond 16, and AUTO also asks for at least 15 % fewer iterations
+//    per workgroup than the single data-parallel wave (kSmallGain);
 //  * AUTO keeps the region only when the model predicts it beats the
 //    XCD-ordered data-parallel form.
 #include <algorithm>
@@ -111,6 +112,10 @@ static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, f
   }
   return best_g;
 }
+
+// Below one wave, the smallest iteration gain of the split over the single
+// data-parallel wave that AUTO accepts.
+static constexpr double kSmallGain = 1.15;
 
 // Charge for the phase classes that share one XCD's L2 (D / 8 of them).
 static double phase_charge(int64_t D) {
@@ -218,9 +223,14 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
         int D = 0, s = 0;
         if (P.w == 0) {
           const double t_al = aligned_small(P.tiles, P.ipt, slots, ma, mb, mc, md, &D, &s);
-          // the data-parallel form: one tile per workgroup
+          // the data-parallel form: one tile per workgroup.  Below a wave it
+          // leaves p - t CUs idle and the busy ones then run at a higher
+          // clock, so the split must also promise at least 15 % fewer
+          // iterations per workgroup (measured on the fp16 shape sweep:
+          // splits promising 10 % ran 7 % slower than the single wave)
           const double t_dp = ma + mc * (double)P.ipt;
-          if (o.schedule == SK_SCHED_AUTO && t_dp <= t_al) D = 0;
+          const double work = (double)cdiv((int64_t)s * P.ipt, D);
+          if (o.schedule == SK_SCHED_AUTO && (t_dp <= t_al || (double)P.ipt < kSmallGain * work)) D = 0;
         } else if (P.r > 0) {
           sk_tiles = P.w >= min_waves ? P.r + slots : P.tiles;
           aligned_wave(sk_tiles, P.ipt, slots, &D, &s);
