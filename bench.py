@@ -232,6 +232,19 @@ def abft_overhead(torch, sk, S, steps=10):
     return out
 
 
+def _spin_cycles(torch, seconds):
+    """Argument of torch.cuda._sleep that keeps the GPU busy for about
+    `seconds` (calibrated on a 1e6-cycle spin)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda._sleep(1000)
+    e0.record()
+    torch.cuda._sleep(1000000)
+    e1.record()
+    torch.cuda.synchronize()
+    per_cycle = e0.elapsed_time(e1) * 1e-3 / 1e6
+    return max(1000, int(seconds / per_cycle))
+
+
 def shape_sweep(torch, sk, S, count, out_path, reps=5):
     """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
     contiguous along k; alpha=1, beta=0) on the seeded shape list; each shape
@@ -240,7 +253,11 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
     Stream-K below a wave, data-parallel when the tiles fill whole waves) and
     data-parallel in linear tile order.
 
-    Per shape: median time of `reps` launches after one warm-up; roofline time
+    Per shape: median time of `reps` launches after one warm-up; a spin
+    kernel queued ahead of the timed launches keeps the GPU busy while the
+    host enqueues them, so each event pair brackets the GEMM alone and not
+    the host's launch cost (which for the smallest shapes exceeds the kernel
+    time; it is reported separately as the plan+launch latency); roofline time
     T_min = max(2mnk / P_fp16, 2(mk + kn + mn) / BW_HBM); utilisation =
     T_min / T.  Inputs: N(0,1)/sqrt(k)-scaled normal values drawn on the GPU
     from a generator seeded with the sweep seed (timing only; parity of sweep
@@ -259,6 +276,7 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
     rows = []
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(reps)]
+    spin = _spin_cycles(torch, 40e-6 * (reps + 1))
     for idx, (kind, m, n, k) in enumerate(shapes):
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
         p = sk.plan_query(d)
@@ -272,12 +290,17 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
         legs = legs[idx % 3:] + legs[:idx % 3]
         for sched_name, opts in legs:
             sk.gemm_ex(d, opts)
+            torch.cuda._sleep(spin)
+            host = []
             for e0, e1 in ev:
                 e0.record()
+                h0 = time.perf_counter()
                 sk.gemm_ex(d, opts)
+                host.append(time.perf_counter() - h0)
                 e1.record()
             torch.cuda.synchronize()
             res[sched_name] = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3
+            res["host_" + sched_name] = statistics.median(host)
         fl = 2.0 * m * n * k
         by = 2.0 * (m * k + k * n + m * n)
         tmin = max(fl / peak, by / bw)
@@ -289,7 +312,8 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
                          tflops_dp=fl / res["dp"] / 1e12,
                          util_auto=tmin / res["auto"], util_page=tmin / res["page"],
                          util_dp=tmin / res["dp"],
-                         dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak)))
+                         dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak),
+                         host_auto_us=res["host_auto"] * 1e6, host_dp_us=res["host_dp"] * 1e6))
         if idx % 100 == 0:
             print(f"sweep {idx}/{len(shapes)}", file=sys.stderr, flush=True)
     if out_path:
@@ -321,6 +345,9 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
                                    "cv": round(cv([r[f"util_{name}"] for r in sel]), 4)}
             out[f"tflops_{name}_mean"] = round(statistics.fmean(r[f"tflops_{name}"] for r in sel), 2)
         out["dp_quant_eff_mean"] = round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)
+        # host time of one sk_gemm call from Python (plan + launch)
+        out["host_launch_us_median"] = {name: round(statistics.median(r[f"host_{name}_us"] for r in sel), 2)
+                                        for name in ("auto", "dp")}
         return out
 
     return {"sweep": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0",

@@ -179,7 +179,12 @@ typedef struct {
   int32_t phase_div;              /* D: quanta per tile (a multiple of 8) */
   int32_t sk_blocks;              /* s: quanta per workgroup */
   int32_t group_rows;             /* G */
-  int32_t reserved;
+  /* 1: the partials of a tile split over workgroups owner .. owner+P-1 are
+   * combined in a binary tree: with r = x - owner, at level l = 0, 1, ... a
+   * workgroup with bit l of r set stores the sum of its subtree and stops,
+   * otherwise it adds the subtree of r + 2^l (if r + 2^l < P); the owner
+   * (r = 0) writes the tile.  0: the owner adds the P-1 partials in order. */
+  int32_t fixup_tree;
 } sk_plan;
 
 /* One work segment of a workgroup. */
@@ -200,7 +205,11 @@ int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t
 
 /* Same as sk_gemm with options.  `opts` may be NULL.  `report` is a device
  * pointer to an sk_abft_report (required when opts->abft is set, else
- * ignored). */
+ * ignored).  The kernels walk a schedule in 32-bit integers: a schedule
+ * chosen explicitly whose positions or quanta products would reach 2^31
+ * (k of several million with the XCD-aware schedule) returns
+ * SK_ERR_UNSUPPORTED; AUTO then takes the two-tile hybrid, else the
+ * data-parallel order. */
 int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
                hipStream_t stream);
 

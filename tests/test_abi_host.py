@@ -88,7 +88,7 @@ def test_page_schedules_match_oracle_decomposition(shape, dtype, slots):
         assert t == -(-m // p.tile_m) * -(-n // p.tile_n) and ipt == -(-k // p.tile_k)
         w, r = t // slots, t % slots
         assert (p.full_waves, p.tail_tiles) == (w, r)
-        assert p.group_rows == 0 and p.phase_div == 0
+        assert p.group_rows == 0 and p.phase_div == 0 and p.fixup_tree == 0
         if sched == sk.SCHED_SK_HYBRID2 and (w < 1 or r == 0):
             continue  # resolved to another schedule (checked below)
         if sched == sk.SCHED_DP:
@@ -131,6 +131,31 @@ def test_auto_xcd_aligned_schedule_invariants(shape, dtype, slots):
         assert sum(e - b for _, b, e, *_ in sk.plan_segments(p, x)) <= \
             (-(-p.sk_blocks * p.iters_per_tile // p.phase_div) if p.sk_tiles else 0) + \
             -(-(t - p.sk_tiles) // p.grid) * p.iters_per_tile
+
+
+@pytest.mark.parametrize("tiles", [(17, 16), (20, 15), (9, 9), (33, 9), (16, 16), (24, 11)])
+@pytest.mark.parametrize("slots", [256, 512])
+def test_xcd_aligned_data_parallel_waves_spread_over_all_xcds(tiles, slots):
+    """Each data-parallel wave, the partial last one too, gives the eight
+    XCDs (workgroups x with equal x mod 8) runs of consecutive tiles whose
+    lengths differ by at most one."""
+    t_m, t_n = tiles
+    d = _desc(256 * t_m, 256 * t_n, 64 * 8, sk.F16)
+    p = sk.plan_query(d, None, slots)
+    # short k: AUTO keeps a partial last wave data-parallel
+    assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles == 0 and p.group_rows == 8
+    waves = -(-p.tiles // p.grid)
+    per_wave = [[[] for _ in range(8)] for _ in range(waves)]
+    for x in range(p.grid):
+        segs = sk.plan_segments(p, x)
+        assert len(segs) in (waves - 1, waves)
+        for wave, (tile, lb, le, st, en, lp) in enumerate(segs):
+            assert (lb, le, lp) == (0, p.iters_per_tile, -1)
+            per_wave[wave][x % 8].append(tile)
+    for runs in per_wave:
+        sizes = [len(r) for r in runs]
+        assert max(sizes) - min(sizes) <= 1, sizes
+    _check_schedule(p)
 
 
 @pytest.mark.parametrize("shape", [(4352, 4096, 4096), (9392, 2976, 14144), (3808, 4624, 720),
@@ -218,6 +243,88 @@ def test_auto_keeps_the_stream_k_region_only_when_k_pays_for_the_fixup():
     assert short.sk_tiles == 0 and long_.sk_tiles == 272 and long_.grid == 256
 
 
+def _simulate_tree_fixup(p):
+    """Runs the binary-tree combine of sk_gemm.h (fixup_tree) over the plan's
+    segments on sets of (workgroup, tile) pieces: every owner must end with
+    each piece of its tile exactly once, every stored partial must be
+    consumed exactly once, and a workgroup may only wait for a higher one."""
+    t, ipt = p.tiles, p.iters_per_tile
+    pieces_of = {}
+    for x in range(p.grid):
+        for tile, lb, le, st, en, lp in sk.plan_segments(p, x):
+            pieces_of.setdefault(tile, []).append((lb, x))
+    owners = {}
+    for tile, lst in pieces_of.items():
+        lst.sort()
+        xs = [x for _, x in lst]
+        assert xs == list(range(xs[0], xs[0] + len(xs))), (tile, xs)  # contiguous workgroups
+        owners[tile] = xs
+    stored, consumed, final = {}, [], {}
+    # process in decreasing workgroup order: every wait targets a higher one
+    for tile, xs in owners.items():
+        first, n = xs[0], len(xs)
+        sums = {x: {(x, tile)} for x in xs}
+        for r in reversed(range(n)):
+            x = first + r
+            l = 0
+            while (1 << l) < n:
+                if r & (1 << l):
+                    stored[(x, tile)] = sums[x]
+                    break
+                child = r + (1 << l)
+                if child < n:
+                    assert first + child > x
+                    consumed.append((first + child, tile))
+                    sums[x] |= stored[(first + child, tile)]
+                l += 1
+            else:
+                final[tile] = sums[x]
+                assert r == 0
+    assert sorted(final) == list(range(t))
+    for tile, xs in owners.items():
+        assert final[tile] == {(x, tile) for x in xs}
+    assert sorted(consumed) == sorted(stored)
+    # one stored partial per workgroup at most (one slot each)
+    assert len({x for x, _ in stored}) == len(stored)
+
+
+@pytest.mark.parametrize("shape", [(256, 4096, 65536), (1000, 1000, 5000), (144, 208, 11952), (600, 520, 3000),
+                                   (4352, 4096, 4096), (2048, 2048, 8192), (9392, 2976, 14144)])
+@pytest.mark.parametrize("dtype", [sk.F16, sk.F32])
+def test_xcd_aligned_tree_fixup_combines_every_piece_once(shape, dtype):
+    m, n, k = shape
+    slots = 256 if dtype != sk.F32 else 512
+    p = sk.plan_query(_desc(m, n, k, dtype), sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), slots)
+    assert p.fixup_tree == 1
+    _simulate_tree_fixup(p)
+
+
+def test_schedules_beyond_32_bit_arithmetic():
+    """The kernels walk schedules in 32-bit integers.  With 2^20 iterations
+    per tile (k = 2^26) the XCD-aware quanta products of a 272-tile region
+    pass 2^31: the explicit schedule is refused and AUTO takes the two-tile
+    hybrid.  With 2^24 - 1 iterations even that region passes 2^31 and AUTO
+    runs data-parallel.  Every plan handed out still covers each iteration
+    once."""
+    d = _desc(256 * 17, 256 * 16, 1 << 26)
+    with pytest.raises(sk.SkError):
+        sk.plan_query(d, sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256)
+    p = sk.plan_query(d, None, 256)
+    assert p.schedule == sk.SCHED_SK_HYBRID2 and p.sk_tiles == 272
+    _check_schedule(p)
+    d = _desc(256 * 17, 256 * 16, (1 << 30) - 64)
+    for sched in (sk.SCHED_SK_BASIC, sk.SCHED_SK_HYBRID2, sk.SCHED_XCD_ALIGNED):
+        with pytest.raises(sk.SkError):
+            sk.plan_query(d, sk.make_options(schedule=sched), 256)
+    p = sk.plan_query(d, None, 256)
+    assert p.schedule == sk.SCHED_DP and p.sk_tiles == 0
+    _check_schedule(p)
+    # just inside the limit the aligned schedule is kept
+    p = sk.plan_query(_desc(256 * 17, 256 * 16, 1 << 20), None, 256)
+    assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles > 0
+    _check_schedule(p)
+
+
 def test_auto_below_a_wave_needs_a_clear_iteration_gain():
     """228 tiles of 229 iterations on 256 slots: the split would save about
     11 % of the iterations, less than the single data-parallel wave gains
@@ -261,8 +368,10 @@ def test_grid_model_regimes():
     assert p.sk_tiles == 16 and p.grid == 256
     p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model), 256)
     assert p.sk_tiles == 0 and p.grid == 64
+    # one tile: its partials meet in a binary tree, so the owner waits for
+    # only log2(pieces) of them and a deeper split than the page's pays
     p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model), 256)
-    assert 1 < p.grid <= 16
+    assert 16 <= p.grid <= 64 and p.fixup_tree == 1
 
 
 def test_repack_flags():

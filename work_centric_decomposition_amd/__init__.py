@@ -79,7 +79,7 @@ class Plan(ctypes.Structure):
                 ("iters_per_tile", i64), ("total_iters", i64), ("sk_tiles", i64),
                 ("sk_iters_q", i64), ("sk_iters_r", i64), ("dp_tiles", i64), ("full_waves", i32),
                 ("tail_tiles", i32), ("max_peers", i32), ("packs", i32), ("phase_div", i32),
-                ("sk_blocks", i32), ("group_rows", i32), ("reserved", i32)]
+                ("sk_blocks", i32), ("group_rows", i32), ("fixup_tree", i32)]
 
 
 class Segment(ctypes.Structure):

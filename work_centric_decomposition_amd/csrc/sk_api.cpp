@@ -308,6 +308,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
     out->max_peers = plan_max_peers(P);
     out->packs = (P.pack_a ? 1 : 0) | (P.pack_b ? 2 : 0);
     out->phase_div = P.phase_div; out->sk_blocks = P.blocks; out->group_rows = P.group_rows;
+    out->fixup_tree = P.sched().tree ? 1 : 0;
     return SK_OK;
   } catch (...) {
     return SK_ERR_NO_MEMORY;

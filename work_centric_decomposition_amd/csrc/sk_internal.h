@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "../../include/sk_gemm.h"
 
 namespace sk {
@@ -59,10 +61,11 @@ inline TileCfg tile_cfg(int dtype) {
 //
 // With group_rows = G > 0 (the XCD-aware schedule), u is mapped to tiles in
 // bands of G tile rows, column by column within a band, and
-//  * workgroup x's data-parallel tiles are u = sk_tiles + slot + j * grid
-//    with slot = (x % 8) * (grid / 8) + x / 8: the workgroups that the
-//    dispatcher places on one XCD (x mod 8 equal) take a run of grid / 8
-//    consecutive u, a compact block of tiles sharing A rows and B columns;
+//  * the data-parallel tiles go in waves of `grid`; a wave's R tiles are cut
+//    into 8 runs of consecutive u (lengths R / 8 or R / 8 + 1) and run c goes to the
+//    workgroups the dispatcher places on XCD c (x mod 8 = c, in order of
+//    x / 8): each XCD works on a compact block of tiles sharing A rows and B
+//    columns, and a partial last wave still spreads over all eight XCDs;
 //  * the Stream-K region is split in quanta of ipt / D iterations
 //    (D = phase_div, a multiple of 8): workgroup x covers
 //    [floor(x s ipt / D), floor((x+1) s ipt / D)) of the region's
@@ -71,94 +74,135 @@ inline TileCfg tile_cfg(int dtype) {
 //    L is mapped so that those workgroups also work on neighbouring tiles:
 //    L = j s + v (v < s) is tile u = prefix(v) + j, where block v holds the
 //    block_len (or block_len - 1 for v >= block_cut) tiles L = v, v + s, ....
+// All fields and every value the helpers below form (products included)
+// are below 2^31: the planner only hands such plans to the kernels
+// (sched_fits), so the device walks the schedule in 32-bit arithmetic; a
+// 64-bit division would expand to a long dependent instruction chain at
+// every segment.
 struct Sched {
-  int64_t ipt, tiles, tiles_m, tiles_n;
-  int64_t sk_tiles;
-  int64_t sk_q, sk_r;   // even split (group_rows == 0): the first sk_r get sk_q + 1
-  int64_t grid;
-  int64_t phase_div;    // D (XCD-aware schedule with a Stream-K region), else 0
-  int64_t blocks;       // s: quanta per workgroup
-  int64_t block_len;    // J = ceil(sk_tiles / s)
-  int64_t block_cut;    // sk_tiles - (J - 1) * s
-  int64_t group_rows;   // G, 0 for the page's linear order
+  int32_t ipt, tiles, tiles_m, tiles_n;
+  int32_t sk_tiles;
+  int32_t sk_q, sk_r;   // even split (group_rows == 0): the first sk_r get sk_q + 1
+  int32_t grid;
+  int32_t phase_div;    // D (XCD-aware schedule with a Stream-K region), else 0
+  int32_t blocks;       // s: quanta per workgroup
+  int32_t block_len;    // J = ceil(sk_tiles / s)
+  int32_t block_cut;    // sk_tiles - (J - 1) * s
+  int32_t group_rows;   // G, 0 for the page's linear order
+  int32_t tree;         // 1: the partials of a split tile are combined in a binary tree
 };
 
 #define SK_HD __host__ __device__ __forceinline__
 
-SK_HD int64_t sched_min(int64_t a, int64_t b) { return a < b ? a : b; }
+SK_HD int32_t sched_min(int32_t a, int32_t b) { return a < b ? a : b; }
+
+// Quotient of non-negative a and positive b.
+SK_HD int32_t sched_div(int32_t a, int32_t b) { return (int32_t)((uint32_t)a / (uint32_t)b); }
 
 // Tile (linear m -> n index) of region-order position u.
-SK_HD int64_t sched_tile_of_u(const Sched &S, int64_t u) {
+SK_HD int32_t sched_tile_of_u(const Sched &S, int32_t u) {
   if (S.group_rows <= 0) return u;
-  const int64_t band = S.group_rows * S.tiles_n;
-  const int64_t b = u / band, rem = u - b * band;
-  const int64_t rows = sched_min(S.group_rows, S.tiles_m - b * S.group_rows);
-  return (b * S.group_rows + rem % rows) * S.tiles_n + rem / rows;
+  const int32_t band = S.group_rows * S.tiles_n;
+  const int32_t b = sched_div(u, band), rem = u - b * band;
+  const int32_t rows = sched_min(S.group_rows, S.tiles_m - b * S.group_rows);
+  const int32_t col = sched_div(rem, rows);
+  return (b * S.group_rows + rem - col * rows) * S.tiles_n + col;
 }
 
 // Tile of Stream-K region position L.
-SK_HD int64_t sched_sk_tile(const Sched &S, int64_t L) {
+SK_HD int32_t sched_sk_tile(const Sched &S, int32_t L) {
   if (S.phase_div <= 0) return sched_tile_of_u(S, L);
-  const int64_t v = L % S.blocks, j = L / S.blocks;
-  const int64_t over = v - S.block_cut;
+  const int32_t j = sched_div(L, S.blocks), v = L - j * S.blocks;
+  const int32_t over = v - S.block_cut;
   return sched_tile_of_u(S, v * S.block_len - (over > 0 ? over : 0) + j);
 }
 
 // First Stream-K iteration of workgroup x (x == grid gives the region's end).
-SK_HD int64_t sched_first_iter(const Sched &S, int64_t x) {
-  if (S.phase_div > 0) return sched_min(x * S.blocks * S.ipt / S.phase_div, S.sk_tiles * S.ipt);
+SK_HD int32_t sched_first_iter(const Sched &S, int32_t x) {
+  if (S.phase_div > 0) return sched_min(sched_div(x * S.blocks * S.ipt, S.phase_div), S.sk_tiles * S.ipt);
   return x * S.sk_q + (x < S.sk_r ? x : S.sk_r);
 }
 
 // Workgroup whose Stream-K range holds iteration `it`.
-SK_HD int64_t sched_owner_of(const Sched &S, int64_t it) {
-  if (S.phase_div > 0) return ((it + 1) * S.phase_div - 1) / (S.blocks * S.ipt);
-  const int64_t big = S.sk_r * (S.sk_q + 1);
-  return it < big ? it / (S.sk_q + 1) : S.sk_r + (it - big) / S.sk_q;
+SK_HD int32_t sched_owner_of(const Sched &S, int32_t it) {
+  if (S.phase_div > 0) return sched_div((it + 1) * S.phase_div - 1, S.blocks * S.ipt);
+  const int32_t big = S.sk_r * (S.sk_q + 1);
+  return it < big ? sched_div(it, S.sk_q + 1) : S.sk_r + sched_div(it - big, S.sk_q);
 }
 
 // Segments of workgroup x in execution order: its Stream-K range (Algorithm
 // 5: a workgroup that holds a tile's k = 0 iteration but not its last one
 // adds the partials of workgroups x+1 .. last_peer), then its data-parallel
-// tiles.  The iterator keeps three integers of state, so that a kernel that
+// tiles.  The iterator keeps four integers of state, so that a kernel that
 // runs a whole MAC loop per segment keeps little alive across it (the
 // kernels call next() from a single site).
 struct SegIter {
-  int64_t it, end;  // remaining Stream-K range
-  int64_t d;        // next data-parallel index
+  int32_t it, end;  // remaining Stream-K range
+  int32_t d;        // next data-parallel index (XCD-aware order: wave)
+  int32_t x;        // the workgroup
 };
+// first / last: the workgroups holding the tile's first and last iteration,
+// -1 where that is x itself.
 struct Segment {
-  int64_t tile, lb, le, last_peer;
+  int32_t tile, lb, le, last_peer, first, last;
   bool started, ended;
 };
 
-SK_HD SegIter sched_begin(const Sched &S, int64_t x) {
+SK_HD SegIter sched_begin(const Sched &S, int32_t x) {
   SegIter I;
   I.it = S.sk_tiles > 0 ? sched_first_iter(S, x) : 0;
   I.end = S.sk_tiles > 0 ? sched_first_iter(S, x + 1) : 0;
-  I.d = (S.group_rows > 0 && S.grid % 8 == 0) ? (x % 8) * (S.grid / 8) + x / 8 : x;
+  I.d = 0;  // XCD-aware order: data-parallel wave index; else the next index
+  if (!(S.group_rows > 0 && S.grid % 8 == 0)) I.d = x;
+  I.x = x;
   return I;
+}
+
+// Data-parallel tile u (region order) of wave `wave` for workgroup x in the
+// XCD-aware order, or -1: the wave's R tiles are cut into 8 runs of
+// consecutive tiles whose lengths differ by at most one, run c going to the
+// workgroups of XCD c.
+SK_HD int32_t sched_dp_xcd(const Sched &S, int32_t wave, int32_t x) {
+  const int32_t dp = S.tiles - S.sk_tiles;
+  const int32_t base = wave * S.grid;
+  if (base >= dp) return -1;
+  const int32_t R = sched_min(S.grid, dp - base);
+  const int32_t q = R >> 3, e = R & 7;
+  const int32_t c = x & 7, pos = x >> 3;
+  if (pos >= q + (c < e)) return -1;
+  return S.sk_tiles + base + c * q + sched_min(c, e) + pos;
 }
 
 SK_HD bool sched_next(const Sched &S, SegIter &I, Segment &g) {
   if (I.it < I.end) {
-    const int64_t L = I.it / S.ipt, ts = L * S.ipt, te = ts + S.ipt;
+    const int32_t L = sched_div(I.it, S.ipt), ts = L * S.ipt, te = ts + S.ipt;
     g.lb = I.it - ts;
     g.le = (I.end < te ? I.end : te) - ts;
     g.started = g.lb == 0;
     g.ended = I.end >= te;
-    g.last_peer = (g.started && !g.ended) ? sched_owner_of(S, te - 1) : -1;
+    g.first = g.started ? -1 : sched_owner_of(S, ts);
+    g.last = g.ended ? -1 : sched_owner_of(S, te - 1);
+    g.last_peer = (g.started && !g.ended) ? g.last : -1;
     g.tile = sched_sk_tile(S, L);
     I.it = te;
     return true;
   }
-  if (I.d < S.tiles - S.sk_tiles) {
-    g.tile = sched_tile_of_u(S, S.sk_tiles + I.d);
+  int32_t u = -1;
+  if (S.group_rows > 0 && S.grid % 8 == 0) {
+    // full waves give every workgroup a tile; only the last wave can leave
+    // one without, and nothing follows it
+    const int32_t waves = sched_div(S.tiles - S.sk_tiles + S.grid - 1, S.grid);
+    while (u < 0 && I.d < waves) u = sched_dp_xcd(S, I.d++, I.x);
+  } else if (I.d < S.tiles - S.sk_tiles) {
+    u = S.sk_tiles + I.d;
+    I.d += S.grid;
+  }
+  if (u >= 0) {
+    g.tile = sched_tile_of_u(S, u);
     g.lb = 0;
     g.le = S.ipt;
     g.started = g.ended = true;
-    g.last_peer = -1;
-    I.d += S.grid;
+    g.last_peer = g.first = g.last = -1;
     return true;
   }
   return false;
@@ -167,10 +211,31 @@ SK_HD bool sched_next(const Sched &S, SegIter &I, Segment &g) {
 // Calls f(tile, lb, le, started, ended, last_peer) for each segment of
 // workgroup x (host-side listing).
 template <class F>
-SK_HD void sched_segments(const Sched &S, int64_t x, F &&f) {
+SK_HD void sched_segments(const Sched &S, int32_t x, F &&f) {
   SegIter I = sched_begin(S, x);
   Segment g;
   while (sched_next(S, I, g)) f(g.tile, g.lb, g.le, g.started, g.ended, g.last_peer);
+}
+
+// Fills the fields of S that follow from the others (block_len, block_cut).
+inline void sched_derive(Sched &S) {
+  if (S.phase_div > 0 && S.blocks > 0) {
+    S.block_len = (S.sk_tiles + S.blocks - 1) / S.blocks;
+    S.block_cut = S.sk_tiles - (S.block_len - 1) * S.blocks;
+  }
+}
+
+// Do all of a plan's schedule values, and the products the helpers form
+// from them (tile positions up to tiles + grid, x s ipt up to x = grid,
+// (it + 1) D, sk_r (sk_q + 1)), stay below 2^31?
+inline bool sched_fits(int64_t tiles, int64_t tiles_m, int64_t tiles_n, int64_t ipt, int64_t grid,
+                       int64_t sk_tiles, int64_t phase_div, int64_t blocks) {
+  const int64_t lim = (int64_t)1 << 31;
+  if (tiles_m >= lim || tiles_n >= lim || ipt >= lim) return false;
+  const int64_t D = phase_div > 0 ? phase_div : 1;
+  const int64_t big = std::max({tiles + grid, (sk_tiles * ipt + 1) * D, (grid + 1) * blocks * ipt,
+                                sk_tiles * ipt + grid, (int64_t)8 * tiles_n});
+  return big < lim;
 }
 
 // Resolved work decomposition (integers only).
@@ -191,13 +256,11 @@ struct Plan {
   bool pack_a, pack_b;  // operand repacked to k-contiguous before the GEMM
   Sched sched() const {
     Sched S{};
-    S.ipt = ipt; S.tiles = tiles; S.tiles_m = tiles_m; S.tiles_n = tiles_n;
-    S.sk_tiles = sk_tiles; S.sk_q = sk_q; S.sk_r = sk_r; S.grid = grid;
+    S.ipt = (int32_t)ipt; S.tiles = (int32_t)tiles; S.tiles_m = (int32_t)tiles_m; S.tiles_n = (int32_t)tiles_n;
+    S.sk_tiles = (int32_t)sk_tiles; S.sk_q = (int32_t)sk_q; S.sk_r = (int32_t)sk_r; S.grid = grid;
     S.phase_div = phase_div; S.blocks = blocks; S.group_rows = group_rows;
-    if (phase_div > 0 && blocks > 0) {
-      S.block_len = (sk_tiles + blocks - 1) / blocks;
-      S.block_cut = sk_tiles - (S.block_len - 1) * blocks;
-    }
+    S.tree = phase_div > 0 ? 1 : 0;
+    sched_derive(S);
     return S;
   }
 };

@@ -1137,21 +1137,45 @@ __device__ __forceinline__ void s_epilogue(const KernelArgs &a, bool vec_ok, int
 
 // Runs one segment: MacLoop, then partial store, or fixup + epilogue.
 template <class P, class MacLoop, class Epilogue>
-__device__ __forceinline__ void run_segment(const KernelArgs &a, int x, int tile, int lb, int le,
-                                            bool started, int last_peer, MacLoop macloop,
+__device__ __forceinline__ void run_segment(const KernelArgs &a, int x, const Segment &g, MacLoop macloop,
                                             Epilogue epilogue) {
   typename P::Acc acc;
+  const int tile = (int)g.tile;
   const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
   const int m0 = tm * P::BM, n0 = tn * P::BN;
-  macloop(m0, n0, lb, le, acc);
-  if (!started) {
+  macloop(m0, n0, (int)g.lb, (int)g.le, acc);
+  // One call site each for the partial store, the partial add and the
+  // epilogue (a second inlined copy of them doubles the live accumulators).
+  //  page order: a non-owner stores; the owner adds x+1 .. last_peer;
+  //  tree (sk_gemm.h, fixup_tree): with r = x - first, at level l a
+  //  workgroup with bit l of r set stores, else adds the subtree of r + 2^l.
+  const bool tree = a.sched.tree != 0;
+  const int first = g.first < 0 ? x : (int)g.first, last = g.last < 0 ? x : (int)g.last;
+  const int pieces = last - first + 1, r = x - first;
+  bool publish = false;
+  for (int step = 0;; ++step) {
+    int child;
+    if (tree) {
+      if ((1 << step) >= pieces) break;
+      if (r & (1 << step)) {
+        publish = true;
+        break;
+      }
+      child = r + (1 << step) < pieces ? first + r + (1 << step) : -1;
+    } else {
+      if (!g.started) {
+        publish = true;
+        break;
+      }
+      child = x + 1 + step;
+      if (child > (int)g.last_peer) break;
+    }
+    if (child >= 0 && wait_flag(a, child)) add_partial<P>(a, child, acc);
+  }
+  if (publish)
     store_partial<P>(a, x, acc);
-    return;
-  }
-  for (int p = x + 1; p <= last_peer; ++p) {
-    if (wait_flag(a, p)) add_partial<P>(a, p, acc);
-  }
-  epilogue(m0, n0, acc);
+  else
+    epilogue(m0, n0, acc);
 }
 
 // All segments of workgroup blockIdx.x, in the order the schedule gives
@@ -1161,8 +1185,7 @@ __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop maclo
   const int x = blockIdx.x;
   SegIter I = sched_begin(a.sched, x);
   Segment g;
-  while (sched_next(a.sched, I, g))
-    run_segment<P>(a, x, (int)g.tile, (int)g.lb, (int)g.le, g.started, (int)g.last_peer, macloop, epilogue);
+  while (sched_next(a.sched, I, g)) run_segment<P>(a, x, g, macloop, epilogue);
 }
 
 template <int DT>

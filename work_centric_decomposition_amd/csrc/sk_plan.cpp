@@ -54,6 +54,7 @@
 #include <algorithm>
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "sk_internal.h"
 
@@ -148,12 +149,62 @@ static double aligned_small(int64_t t, int64_t ipt, int slots, float a, float b,
       if (D * J > slots) continue;
       const bool split = s % D != 0 || (s * ipt) % D != 0;
       const int64_t work = cdiv(s * ipt, D);
-      const int64_t peers = split ? std::max<int64_t>(1, cdiv(D - 1, s)) : 0;
-      const double T = (a + (split ? b : 0.0) + c * (double)work + d * (double)peers) * phase_charge(D);
+      // the partials of a tile meet in a binary tree: on its critical path
+      // each of the ceil(log2(pieces)) levels stores a partial (b) and adds
+      // it (d) one after the other.  Workgroup x of a class covers
+      // [floor(x s ipt / D), floor((x + 1) s ipt / D)); the widest of its s
+      // tiles sets the depth.
+      int64_t pieces = 1;
+      for (int64_t j = 0; split && j < s; ++j) {
+        const int64_t f = ((j * ipt + 1) * D - 1) / (s * ipt), l = (((j + 1) * ipt) * D - 1) / (s * ipt);
+        pieces = std::max(pieces, l - f + 1);
+      }
+      int64_t levels = 0;
+      while (((int64_t)1 << levels) < pieces) ++levels;
+      const double T = (a + c * (double)work + (b + d) * (double)levels) * phase_charge(D);
       if (T < best - 1e-9) { best = T; *D_out = (int)D; *s_out = (int)s; }
     }
   }
   return best;
+}
+
+struct DecisionKey {
+  int dtype;
+  int64_t tiles_m, tiles_n, ipt;
+  int slots, schedule, forced_grid, min_waves;
+  float ma, mb, mc, md;
+  bool operator==(const DecisionKey &o) const {
+    return dtype == o.dtype && tiles_m == o.tiles_m && tiles_n == o.tiles_n && ipt == o.ipt && slots == o.slots &&
+           schedule == o.schedule && forced_grid == o.forced_grid && min_waves == o.min_waves && ma == o.ma &&
+           mb == o.mb && mc == o.mc && md == o.md;
+  }
+};
+struct Decision {
+  DecisionKey key;
+  int schedule, grid, phase_div, blocks, group_rows;
+  int64_t sk_tiles, sk_q, sk_r;
+  bool valid;
+};
+static std::mutex g_decision_mu;
+static Decision g_decisions[64];
+static unsigned g_decision_next = 0;
+
+static bool lookup_decision(const DecisionKey &k, Plan &P) {
+  std::lock_guard<std::mutex> lock(g_decision_mu);
+  for (const Decision &e : g_decisions) {
+    if (!e.valid || !(e.key == k)) continue;
+    P.schedule = e.schedule; P.grid = e.grid; P.phase_div = e.phase_div; P.blocks = e.blocks;
+    P.group_rows = e.group_rows; P.sk_tiles = e.sk_tiles; P.sk_q = e.sk_q; P.sk_r = e.sk_r;
+    P.dp_tiles = P.tiles - P.sk_tiles;
+    return true;
+  }
+  return false;
+}
+
+static void store_decision(const DecisionKey &k, const Plan &P) {
+  std::lock_guard<std::mutex> lock(g_decision_mu);
+  Decision &e = g_decisions[g_decision_next++ % 64];
+  e = Decision{k, P.schedule, P.grid, P.phase_div, P.blocks, P.group_rows, P.sk_tiles, P.sk_q, P.sk_r, true};
 }
 
 int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
@@ -190,6 +241,13 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
   const float mc = o.model_c > 0 ? o.model_c : c.c;
   const float md = o.model_d > 0 ? o.model_d : c.d;
   const int min_waves = o.hybrid_min_waves > 0 ? o.hybrid_min_waves : 1;
+
+  // The schedule depends only on these integers and the options; a small
+  // cache keeps its search (a few microseconds below a wave) off the launch
+  // path of repeated shapes.
+  const DecisionKey key{d.dtype, P.tiles_m, P.tiles_n, P.ipt, slots, o.schedule, o.forced_grid, min_waves,
+                        ma, mb, mc, md};
+  if (lookup_decision(key, P)) return SK_OK;
 
   int sched = o.schedule;
   int64_t grid = 0, sk_tiles = 0;
@@ -265,6 +323,21 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
     P.sk_q = I / grid;
     P.sk_r = I % grid;
   }
+  if (!sched_fits(P.tiles, P.tiles_m, P.tiles_n, P.ipt, P.grid, P.sk_tiles, P.phase_div, P.blocks)) {
+    // the kernels walk schedules in 32-bit arithmetic; beyond it (k in the
+    // millions with the XCD-aware quanta) AUTO takes the page's hybrid,
+    // whose Stream-K region is smaller, else the data-parallel order
+    if (o.schedule != SK_SCHED_AUTO) return SK_ERR_UNSUPPORTED;
+    sk_options o2 = o;
+    o2.schedule = SK_SCHED_SK_HYBRID2;
+    int rc = make_plan(d, o2, slots, P);
+    if (rc == SK_ERR_UNSUPPORTED) {
+      o2.schedule = SK_SCHED_DP;
+      rc = make_plan(d, o2, slots, P);
+    }
+    if (rc != SK_OK) return rc;
+  }
+  store_decision(key, P);
   return SK_OK;
 }
 
@@ -272,9 +345,9 @@ int plan_max_peers(const Plan &P) {
   if (P.sk_tiles <= 0) return 0;
   if (P.phase_div <= 0) return split_peers(P.sk_tiles, P.ipt, P.grid, nullptr);
   const Sched S = P.sched();
-  int64_t peers = 0;
-  for (int64_t x = 0; x < P.grid; ++x)
-    sched_segments(S, x, [&](int64_t, int64_t, int64_t, bool, bool, int64_t lp) {
+  int32_t peers = 0;
+  for (int32_t x = 0; x < P.grid; ++x)
+    sched_segments(S, x, [&](int32_t, int32_t, int32_t, bool, bool, int32_t lp) {
       if (lp >= 0 && lp - x > peers) peers = lp - x;
     });
   return (int)peers;
@@ -289,18 +362,19 @@ extern "C" int64_t sk_plan_segments(const sk_plan *plan, int64_t x, sk_segment *
   if (x >= plan->grid) return 0;
   if (plan->iters_per_tile <= 0 || plan->tiles <= 0) return 0;
   if (plan->phase_div > 0 && plan->sk_blocks <= 0) return SK_ERR_INVALID_ARG;
+  if (!sched_fits(plan->tiles, plan->tiles_m, plan->tiles_n, plan->iters_per_tile, plan->grid, plan->sk_tiles,
+                  plan->phase_div, plan->sk_blocks))
+    return SK_ERR_INVALID_ARG;
   Sched S{};
-  S.ipt = plan->iters_per_tile; S.tiles = plan->tiles;
-  S.tiles_m = plan->tiles_m; S.tiles_n = plan->tiles_n;
-  S.sk_tiles = plan->sk_tiles; S.sk_q = plan->sk_iters_q; S.sk_r = plan->sk_iters_r;
+  S.ipt = (int32_t)plan->iters_per_tile; S.tiles = (int32_t)plan->tiles;
+  S.tiles_m = (int32_t)plan->tiles_m; S.tiles_n = (int32_t)plan->tiles_n;
+  S.sk_tiles = (int32_t)plan->sk_tiles; S.sk_q = (int32_t)plan->sk_iters_q; S.sk_r = (int32_t)plan->sk_iters_r;
   S.grid = plan->grid; S.phase_div = plan->phase_div; S.blocks = plan->sk_blocks;
   S.group_rows = plan->group_rows;
-  if (S.phase_div > 0) {
-    S.block_len = (S.sk_tiles + S.blocks - 1) / S.blocks;
-    S.block_cut = S.sk_tiles - (S.block_len - 1) * S.blocks;
-  }
+  S.tree = plan->fixup_tree ? 1 : 0;
+  sched_derive(S);
   int64_t n = 0;
-  sched_segments(S, x, [&](int64_t tile, int64_t lb, int64_t le, bool st, bool en, int64_t lp) {
+  sched_segments(S, (int32_t)x, [&](int32_t tile, int32_t lb, int32_t le, bool st, bool en, int32_t lp) {
     if (n < cap) out[n] = sk_segment{tile, lb, le, st ? 1 : 0, en ? 1 : 0, lp};
     ++n;
   });
