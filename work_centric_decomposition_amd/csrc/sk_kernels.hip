@@ -316,6 +316,20 @@ struct HLoader {
     lds_a = w * P::LOADS * 1024;
   }
 
+  // Load q of this wave's share of iteration kit (q even: A, q odd: B,
+  // block q / 2), without a branch: chunks at or past k, and every chunk
+  // when `live` is false, are fetched out of range, i.e. written to LDS as
+  // zeros.
+  __device__ __forceinline__ void load_one(const KernelArgs &a, int stage, int kit, bool live, int q) const {
+    const int j = q >> 1;
+    const int k0b = kit * P::BK * 2;
+    const int left = live ? (a.k - kit * P::BK) * 2 : 0;
+    const bool ok = chunk[j] * 16 < left;
+    const int dst = stage * P::STAGE + lds_a + (q & 1) * P::A_BYTES + j * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds((q & 1) ? rb : ra, (lds_vptr)(smem + dst), 16,
+                                             ok ? ((q & 1) ? vb[j] : va[j]) : kOOB, k0b, 0, 0);
+  }
+
   __device__ __forceinline__ void load(const KernelArgs &a, int stage, int kit) const {
     const int k0b = kit * P::BK * 2;
     const int left = (a.k - kit * P::BK) * 2;  // bytes of k from k0
@@ -507,42 +521,79 @@ __device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, i
 // fragment of stage i has been read, so after this wave's loads of stage
 // i+1 have landed and its LDS reads have returned, one workgroup barrier
 // both publishes stage i+1 and frees stage i for the loads of iteration
-// i+2.  The barrier is kept in the last iteration too, so a following
-// segment may overwrite either stage.
+// i+2.
 template <int DT>
 struct HFrag {
   typename Elem<DT>::V8 a[HPolicy<DT>::MB], b[HPolicy<DT>::NB];
 };
 
+// One fragment read (q < NB: B block q, else A block q - NB) and one MFMA
+// (block row q / NB, column q % NB) of a substep, for the pinned
+// interleaving below.
+template <int DT>
+__device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, int q, HFrag<DT> &F) {
+  using P = HPolicy<DT>;
+  using V8 = typename Elem<DT>::V8;
+  const int lane = threadIdx.x & 63;
+  const int As = stage * P::STAGE, Bs = As + P::A_BYTES;
+  const int c = sub * 2 + (lane >> 5);
+  if (q < P::NB) {
+    const int row = wn * P::WTN + q * 32 + (lane & 31);
+    F.b[q] = *reinterpret_cast<const V8 *>(smem + Bs + row * P::ROW + ((c ^ P::swz(row)) << 4));
+  } else {
+    const int row = wm * P::WTM + (q - P::NB) * 32 + (lane & 31);
+    F.a[q - P::NB] = *reinterpret_cast<const V8 *>(smem + As + row * P::ROW + ((c ^ P::swz(row)) << 4));
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void h_mfma_one(const HFrag<DT> &F, typename HPolicy<DT>::Acc &acc, int q) {
+  using P = HPolicy<DT>;
+  const int mb = q / P::NB, nb = q % P::NB;
+  acc.v[q] = h_mfma<DT>(F.b[nb], F.a[mb], acc.v[q]);
+}
+
+// One substep: the MFMAs of fragment set M, each followed (in this exact
+// order: the scheduler may not regroup them) by one fragment read of
+// substep `sub` of stage `stage` into set R and, while q < nl, by load q of
+// this wave's share of iteration `kit` into stage `lstage`.  Spreading the
+// reads and loads this way keeps a single wave issuing MFMAs back to back:
+// grouped loads stall its issue for longer than an MFMA takes.
+template <int DT>
+__device__ __forceinline__ void h_substep(const KernelArgs &a, const HLoader<DT> &ld, const HFrag<DT> &M,
+                                          HFrag<DT> &R, int stage, int sub, int wm, int wn,
+                                          typename HPolicy<DT>::Acc &acc, int nl, int lstage, int kit, bool live) {
+  using P = HPolicy<DT>;
+  constexpr int NM = P::MB * P::NB, NR = P::MB + P::NB;
+  static_assert(NR <= NM && 2 * P::LOADS <= NM, "one read and one load per MFMA at most");
+#pragma unroll
+  for (int q = 0; q < NM; ++q) {
+    h_mfma_one<DT>(M, acc, q);
+    __builtin_amdgcn_sched_barrier(0);
+    if (q < nl) ld.load_one(a, lstage, kit, live, q);
+    if (q < NR) h_frag_one<DT>(stage, sub, wm, wn, q, R);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// Iteration i of the lookahead-2 loop.  Global substep g = 4 i + s uses
+// fragment set F[g % 3]; with i = PH (mod 3), 4 i = PH (mod 3).
 template <int DT, int PH>
 __device__ __forceinline__ void h_iter_la2(const KernelArgs &a, const HLoader<DT> &ld, int i, int n, int lb,
                                            int wm, int wn, HFrag<DT> (&F)[3], typename HPolicy<DT>::Acc &acc) {
-  using P = HPolicy<DT>;
-  const int buf = i & 1;
-  // global substep g = 4 i + s uses F[g % 3]; with i = PH (mod 3),
-  // 4 i = PH (mod 3)
   constexpr int f0 = (PH + 0) % 3, f1 = (PH + 1) % 3, f2 = (PH + 2) % 3;
-  h_frags<DT>(buf, 2, wm, wn, F[f2].a, F[f2].b);
-  h_mfmas<DT>(F[f0].a, F[f0].b, acc);
-  H_INTERLEAVE();
-  __builtin_amdgcn_sched_barrier(0);
-  h_frags<DT>(buf, 3, wm, wn, F[f0].a, F[f0].b);
-  h_mfmas<DT>(F[f1].a, F[f1].b, acc);
-  H_INTERLEAVE();
-  __builtin_amdgcn_sched_barrier(0);
+  const int buf = i & 1;
+  h_substep<DT>(a, ld, F[f0], F[f2], buf, 2, wm, wn, acc, 0, 0, 0, false);
+  h_substep<DT>(a, ld, F[f1], F[f0], buf, 3, wm, wn, acc, 0, 0, 0, false);
   // stage switch: stage i+1 complete (its loads were the only ones in
   // flight) and every read of stage i returned
   __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(0));
   __syncthreads();
-  if (i + 2 < n) ld.load(a, buf, lb + i + 2);
-  if (i + 1 < n) h_frags<DT>(buf ^ 1, 0, wm, wn, F[f1].a, F[f1].b);
-  h_mfmas<DT>(F[f2].a, F[f2].b, acc);
-  H_INTERLEAVE();
-  __builtin_amdgcn_sched_barrier(0);
-  if (i + 1 < n) h_frags<DT>(buf ^ 1, 1, wm, wn, F[f2].a, F[f2].b);
-  h_mfmas<DT>(F[f0].a, F[f0].b, acc);
-  H_INTERLEAVE();
-  __builtin_amdgcn_sched_barrier(0);
+  // no branches from here to the next stage switch: in the last two
+  // iterations the loads fetch nothing (zeros into the stage just freed)
+  // and the last iteration's reads of stage i+1 go unused
+  h_substep<DT>(a, ld, F[f2], F[f1], buf ^ 1, 0, wm, wn, acc, 2 * HPolicy<DT>::LOADS, buf, lb + i + 2, i + 2 < n);
+  h_substep<DT>(a, ld, F[f0], F[f2], buf ^ 1, 1, wm, wn, acc, 0, 0, 0, false);
 }
 
 template <int DT>
@@ -577,6 +628,10 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
   }
   if (i < n) h_iter_la2<DT, 0>(a, ld, i, n, lb, wm, wn, F, acc);
   if (i + 1 < n) h_iter_la2<DT, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
+  // the last iterations' (empty) loads and reads have landed in every wave
+  // before the caller reuses LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
 template <int DT>
