@@ -80,6 +80,10 @@ def parse():
     p.add_argument("--compare-schedules", action="store_true",
                    help="time AUTO, the page's schedules and data-parallel on a few fp16 shapes "
                         "(one launch each with --steps 1, e.g. under rocprofv3 --pmc)")
+    p.add_argument("--library-gemm", action="store_true",
+                   help="time only the vendor GEMM behind torch.mm on the 8192^3 fp16 and bf16 "
+                        "inputs of the hgemm workload (context for the kernel's counters; not "
+                        "this library's path)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
@@ -120,6 +124,31 @@ def compare_schedules(torch, sk, S, steps):
                         "sk_tiles": p.sk_tiles, "phase_div": p.phase_div, "us": round(us, 1),
                         "tflops": round(2.0 * m * n * k / us / 1e6, 1)})
         del A, B, C
+    return out
+
+
+def library_gemm(torch, sk, S, steps, warmup):
+    """The vendor GEMM (torch.mm) on the hgemm workload's inputs: A row-major,
+    B column-major (a transposed view of its k-contiguous storage)."""
+    out = []
+    for dt, name in ((sk.F16, "f16"), (sk.BF16, "bf16")):
+        h = make_hgemm_inputs(torch, sk, S, dt)
+        n = h["n"]
+        a = h["A"].view(n, n)
+        b = h["B"].view(n, n).t()
+        for _ in range(warmup):
+            torch.mm(a, b)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            torch.mm(a, b)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out.append({"library_gemm": "torch.mm", "dtype": name, "shape": [n, n, n], "ms": round(ms, 4),
+                    "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)})
+        del h, a, b
     return out
 
 
@@ -406,6 +435,10 @@ def main():
         return
     if args.sweep:
         print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out)), flush=True)
+        return
+    if args.library_gemm:
+        for r in library_gemm(torch, sk, S, args.steps, args.warmup):
+            print(json.dumps(r), flush=True)
         return
     if args.compare_schedules:
         for r in compare_schedules(torch, sk, S, args.steps):
