@@ -84,6 +84,11 @@ def parse():
                    help="time only the vendor GEMM behind torch.mm on the 8192^3 fp16 and bf16 "
                         "inputs of the hgemm workload (context for the kernel's counters; not "
                         "this library's path)")
+    p.add_argument("--calibrate-model", type=int, default=0, metavar="SHAPES",
+                   help="measure the runtime model's constants a, b, c, d (single-tile and split-tile "
+                        "timings) for fp16 and fp32, then compare basic Stream-K at the model's grid "
+                        "(default and measured constants) with the best grid of an exhaustive search "
+                        "on SHAPES seeded fp16 sweep shapes below one wave")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
@@ -149,6 +154,111 @@ def library_gemm(torch, sk, S, steps, warmup):
         out.append({"library_gemm": "torch.mm", "dtype": name, "shape": [n, n, n], "ms": round(ms, 4),
                     "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)})
         del h, a, b
+    return out
+
+
+def _gpu_time_us(torch, sk, d, opts, spin, reps=7):
+    """Median of `reps` launches, each between its own HIP events, queued
+    behind a spin kernel (so the host's launch cost is not timed)."""
+    import statistics
+    sk.gemm_ex(d, opts)
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    torch.cuda._sleep(spin)
+    for e0, e1 in ev:
+        e0.record()
+        sk.gemm_ex(d, opts)
+        e1.record()
+    torch.cuda.synchronize()
+    return statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3
+
+
+def calibrate_model(torch, sk, S, n_shapes):
+    """The runtime model T(g) = a + b [split] + c ipc(g) + d (peers) of the
+    page's grid-size section, measured on this GPU.  Per element type, one
+    tile on one workgroup: T(ipt) = a + c ipt (least squares over ipt = 1 ..
+    256) gives a and c; one tile of 32 iterations split over g = 2 .. 32
+    workgroups by basic Stream-K (the owner adds g - 1 partials in a row)
+    gives b (one partial stored) and d (one partial added).  Constants are
+    reported in microseconds and in units of c.  Then, on fp16 sweep shapes
+    with fewer tiles than slots, basic Stream-K at the model's grid (library
+    defaults, and the measured constants) against the best of an exhaustive
+    set of grids."""
+    import numpy as np
+    spin = _spin_cycles(torch, 400e-6)
+    out = {"calibration": "runtime model"}
+    consts = {}
+    for dt, name in ((sk.F16, "f16"), (sk.F32, "f32")):
+        probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, dt, sk.A_ROW_B_COL))
+        bm, bk = probe.tile_m, probe.tile_k
+        tdt = torch.float16 if dt == sk.F16 else torch.float32
+        kmax = 256 * bk
+        A = torch.randn(bm * kmax, device="cuda").to(tdt)
+        B = torch.randn(bm * kmax, device="cuda").to(tdt)
+        C = torch.zeros(bm * bm, device="cuda", dtype=tdt)
+        ipts = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+        ts = []
+        for ipt in ipts:
+            d = sk.make_desc(bm, bm, ipt * bk, 1.0, A, ipt * bk, B, ipt * bk, 0.0, C, bm, dt, sk.A_ROW_B_COL)
+            ts.append(_gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_DP), spin))
+        c_us, a_us = np.polyfit(np.array(ipts, float), np.array(ts), 1)
+        gs = [2, 3, 4, 8, 16, 32]
+        d = sk.make_desc(bm, bm, 32 * bk, 1.0, A, 32 * bk, B, 32 * bk, 0.0, C, bm, dt, sk.A_ROW_B_COL)
+        rows, rhs = [], []
+        split_t = {}
+        for g in gs:
+            t = _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g), spin)
+            split_t[g] = round(t, 2)
+            rows.append([1.0, g - 1.0])
+            rhs.append(t - a_us - c_us * -(-32 // g))
+        (b_us, d_us), *_ = np.linalg.lstsq(np.array(rows), np.array(rhs), rcond=None)
+        consts[name] = (a_us / c_us, b_us / c_us, 1.0, d_us / c_us)
+        out[name] = {"tile": bm, "bk": bk, "single_tile_us": dict(zip(ipts, [round(x, 2) for x in ts])),
+                     "split_32_iterations_us": split_t,
+                     "us": {"a": round(a_us, 2), "b": round(b_us, 2), "c": round(c_us, 3), "d": round(d_us, 2)},
+                     "units_of_c": {k: round(v, 2) for k, v in zip("abcd", consts[name])}}
+        del A, B, C
+    # exhaustive grid search on fp16 shapes below one wave
+    probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, sk.F16, sk.A_ROW_B_COL))
+    shapes = [sh for sh in S.sweep_shapes(2000, S.SEED_SWEEP, probe.tile_m, probe.tile_n, probe.slots)
+              if sh[0] == "random"]
+    chosen = []
+    for kind, m, n, k in shapes:
+        t = -(-m // probe.tile_m) * -(-n // probe.tile_n)
+        if t < probe.slots and -(-k // 64) >= 16 and 2 * m * n * k >= 2e10:
+            chosen.append((m, n, k))
+        if len(chosen) == n_shapes:
+            break
+    mx = max(max(m * k, k * n, m * n) for m, n, k in chosen)
+    A = torch.randn(mx, device="cuda").to(torch.float16)
+    B = torch.randn(mx, device="cuda").to(torch.float16)
+    C = torch.zeros(mx, device="cuda", dtype=torch.float16)
+    regrets = {"default": [], "measured": [], "auto": []}
+    per_shape = []
+    for m, n, k in chosen:
+        d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+        p = sk.plan_query(d)
+        t, slots = p.tiles, p.slots
+        grid_default = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC)).grid
+        grid_measured = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC,
+                                                         model=consts["f16"])).grid
+        cands = sorted({g for g in [t * s for s in range(1, 9)] + [slots, grid_default, grid_measured]
+                        if t <= g <= slots})
+        times = {g: _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g), spin)
+                 for g in cands}
+        best = min(times.values())
+        t_auto = _gpu_time_us(torch, sk, d, sk.make_options(), spin)
+        regrets["default"].append(times[grid_default] / best)
+        regrets["measured"].append(times[grid_measured] / best)
+        regrets["auto"].append(t_auto / best)
+        per_shape.append({"shape": [m, n, k], "tiles": t, "best_g": min(times, key=times.get),
+                          "best_us": round(best, 1), "g_default": grid_default, "g_measured": grid_measured,
+                          "auto_us": round(t_auto, 1)})
+    out["grid_search"] = {
+        "shapes": len(chosen),
+        "basic_sk_time_over_best": {k: {"geomean": round(float(np.exp(np.mean(np.log(v)))), 4),
+                                        "max": round(float(max(v)), 3)} for k, v in regrets.items() if v},
+        "per_shape": per_shape}
     return out
 
 
@@ -435,6 +545,9 @@ def main():
         return
     if args.sweep:
         print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out)), flush=True)
+        return
+    if args.calibrate_model:
+        print(json.dumps(calibrate_model(torch, sk, S, args.calibrate_model)), flush=True)
         return
     if args.library_gemm:
         for r in library_gemm(torch, sk, S, args.steps, args.warmup):
