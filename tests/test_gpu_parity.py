@@ -51,8 +51,11 @@ def test_sgemm_384_uniform_auto_and_forced_grid4(forced):
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("layout", LAYOUTS)
 def test_ragged_shapes_all_layouts(dtype, layout):
+    # (520, 264, 320): interior tiles with vector-aligned rows and alpha, beta
+    # not 1, 0 (the epilogue's straight-line path) next to edge tiles
     for (m, n, k, pad, alpha, beta) in [(300, 520, 200, 0, 1.0, 0.0), (513, 257, 1000, 8, 0.5, -1.5),
-                                        (17, 33, 48, 0, 1.0, 1.0), (1, 1, 8, 0, 2.0, 0.0)]:
+                                        (17, 33, 48, 0, 1.0, 1.0), (1, 1, 8, 0, 2.0, 0.0),
+                                        (520, 264, 320, 0, 0.75, 1.25)]:
         _say("case ragged", dtype, layout, m, n, k, pad)
         c = Case(m, n, k, dtype, layout, 7 + m + layout, pad=pad)
         got = c.run(alpha, beta)

@@ -634,12 +634,75 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
   __syncthreads();
 }
 
+// Epilogue of one tile.  A tile that lies wholly inside C is written with
+// beta == 0 through LDS in whole cache lines (C 16-byte aligned, ldc a
+// multiple of 8), else, with rows that allow 4-element vector accesses, by
+// straight-line accesses; edge tiles take the per-element bounds checks of
+// store4.
 template <int DT>
 __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
                                            const typename HPolicy<DT>::Acc &acc) {
   using P = HPolicy<DT>;
+  using T = typename Elem<DT>::T;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int r0 = m0 + (w / P::WAVES_N) * P::WTM, c0 = n0 + (w % P::WAVES_N) * P::WTN;
+  const bool full = m0 + P::BM <= a.m && n0 + P::BN <= a.n;
+  if (full && a.beta == 0.f && reinterpret_cast<uintptr_t>(a.C) % 16 == 0 && a.ldc % 8 == 0) {
+    // Through LDS, half of the wave's block at a time: each lane holds 4
+    // consecutive columns of one row, so direct stores would touch 32 rows
+    // per instruction; read back as 8 rows x 128 contiguous bytes per
+    // instruction they cover whole cache lines.  Rows of RS = 136 bytes (34
+    // banks apart) put the 32 rows of one 8-byte LDS write on distinct banks.
+    // Each wave uses only its own region (64 rows: 8.5 KiB) and a wave's LDS
+    // accesses complete in order, so the passes need no barrier; the caller
+    // has passed a workgroup barrier since the last MAC-loop LDS read, and
+    // one at the end keeps the next tile's loads (which land in every
+    // wave's region) from overwriting rows another wave has not read yet.
+    constexpr int RS = P::WTN * 2 + 8, HALF = P::MB / 2;
+    // per-lane bases; every other offset is a compile-time constant
+    char *const wr = smem + w * (HALF * 32 * RS) + (lane & 31) * RS + 8 * (lane >> 5);
+    const char *const rd = smem + w * (HALF * 32 * RS) + (lane >> 3) * RS + (lane & 7) * 16;
+    char *cp = static_cast<char *>(a.C) + ((int64_t)(r0 + (lane >> 3)) * a.ldc + c0 + (lane & 7) * 8) * sizeof(T);
+    const int64_t step = (int64_t)8 * a.ldc * sizeof(T);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+      for (int mb = 0; mb < HALF; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            Elem<DT>::st4(wr + mb * 32 * RS + (nb * 32 + 8 * g) * 2, 0,
+                          a.alpha * P::get4(acc, ((h * HALF + mb) * P::NB + nb) * 4 + g));
+#pragma unroll
+      for (int it = 0; it < HALF * 32 / 8; ++it) {
+        *reinterpret_cast<u4_t *>(cp) = *reinterpret_cast<const u4_t *>(rd + it * 8 * RS);
+        cp += step;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads returned
+    __syncthreads();
+    return;
+  }
+  if (vec_ok && full) {
+    // beta != 0 (or C rows not 16-byte aligned): straight-line 4-element
+    // accesses at fixed offsets from one row pointer per 32-row block
+    T *cb = static_cast<T *>(a.C) + (int64_t)(r0 + (lane & 31)) * a.ldc + c0 + 4 * (lane >> 5);
+    const int64_t rstep = (int64_t)32 * a.ldc;
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          T *q = cb + mb * rstep;
+          const int o = nb * 32 + 8 * g;
+          f4_t v = a.alpha * P::get4(acc, (mb * P::NB + nb) * 4 + g);
+          if (a.beta != 0.f) v += a.beta * Elem<DT>::ld4(q, o);
+          Elem<DT>::st4(q, o, v);
+        }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < P::MB; ++mb)
 #pragma unroll
@@ -1180,6 +1243,27 @@ __device__ __forceinline__ void s_epilogue(const KernelArgs &a, bool vec_ok, int
   const int w = wave_id(), lane = threadIdx.x & 63;
   constexpr int WN = SCfg::BN / SCfg::WTN;
   const int r0 = m0 + (w / WN) * SCfg::WTM, c0 = n0 + (w % WN) * SCfg::WTN;
+  // a tile wholly inside C: straight-line stores (as in the HGEMM epilogue)
+  if (vec_ok && m0 + SCfg::BM <= a.m && n0 + SCfg::BN <= a.n) {
+    float *cb = static_cast<float *>(a.C) + (int64_t)(r0 + (lane & 15)) * a.ldc + c0 + 4 * (lane >> 4);
+    const int64_t rstep = (int64_t)16 * a.ldc;
+    if (a.beta == 0.f) {
+#pragma unroll
+      for (int mb = 0; mb < SCfg::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < SCfg::NB; ++nb)
+          Elem<SK_F32>::st4(cb + mb * rstep, nb * 16, a.alpha * acc.v[mb * SCfg::NB + nb]);
+    } else {
+#pragma unroll
+      for (int mb = 0; mb < SCfg::MB; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < SCfg::NB; ++nb) {
+          float *q = cb + mb * rstep;
+          Elem<SK_F32>::st4(q, nb * 16, a.alpha * acc.v[mb * SCfg::NB + nb] + a.beta * Elem<SK_F32>::ld4(q, nb * 16));
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int mb = 0; mb < SCfg::MB; ++mb)
 #pragma unroll
