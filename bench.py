@@ -77,6 +77,8 @@ def parse():
                    help="run the Stream-K shape sweep (first COUNT of the 2000 seeded fp16 "
                         "shapes), Stream-K (AUTO) vs data-parallel, and print its summary")
     p.add_argument("--sweep-out", default="", help="CSV file for the per-shape sweep results")
+    p.add_argument("--sweep-tiles", action="store_true",
+                   help="also time each sweep shape with each fp16 tile instance (AUTO schedule)")
     p.add_argument("--compare-schedules", action="store_true",
                    help="time AUTO, the page's schedules and data-parallel on a few fp16 shapes "
                         "(one launch each with --steps 1, e.g. under rocprofv3 --pmc)")
@@ -188,8 +190,11 @@ def calibrate_model(torch, sk, S, n_shapes):
     spin = _spin_cycles(torch, 400e-6)
     out = {"calibration": "runtime model"}
     consts = {}
-    for dt, name in ((sk.F16, "f16"), (sk.F32, "f32")):
-        probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, dt, sk.A_ROW_B_COL))
+    for dt, tile, name in ((sk.F16, sk.TILE_LARGE, "f16"), (sk.F16, sk.TILE_SMALL, "f16_small"),
+                           (sk.F32, sk.TILE_AUTO, "f32")):
+        topt = sk.make_options(tile=tile)
+        probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, dt, sk.A_ROW_B_COL),
+                              topt)
         bm, bk = probe.tile_m, probe.tile_k
         tdt = torch.float16 if dt == sk.F16 else torch.float32
         kmax = 256 * bk
@@ -200,14 +205,15 @@ def calibrate_model(torch, sk, S, n_shapes):
         ts = []
         for ipt in ipts:
             d = sk.make_desc(bm, bm, ipt * bk, 1.0, A, ipt * bk, B, ipt * bk, 0.0, C, bm, dt, sk.A_ROW_B_COL)
-            ts.append(_gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_DP), spin))
+            ts.append(_gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_DP, tile=tile), spin))
         c_us, a_us = np.polyfit(np.array(ipts, float), np.array(ts), 1)
         gs = [2, 3, 4, 8, 16, 32]
         d = sk.make_desc(bm, bm, 32 * bk, 1.0, A, 32 * bk, B, 32 * bk, 0.0, C, bm, dt, sk.A_ROW_B_COL)
         rows, rhs = [], []
         split_t = {}
         for g in gs:
-            t = _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g), spin)
+            t = _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g, tile=tile),
+                             spin)
             split_t[g] = round(t, 2)
             rows.append([1.0, g - 1.0])
             rhs.append(t - a_us - c_us * -(-32 // g))
@@ -237,17 +243,19 @@ def calibrate_model(torch, sk, S, n_shapes):
     per_shape = []
     for m, n, k in chosen:
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
-        p = sk.plan_query(d)
+        p = sk.plan_query(d, sk.make_options(tile=sk.TILE_LARGE))
         t, slots = p.tiles, p.slots
-        grid_default = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC)).grid
-        grid_measured = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC,
+        large = sk.TILE_LARGE
+        grid_default = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC, tile=large)).grid
+        grid_measured = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_BASIC, tile=large,
                                                          model=consts["f16"])).grid
         cands = sorted({g for g in [t * s for s in range(1, 9)] + [slots, grid_default, grid_measured]
                         if t <= g <= slots})
-        times = {g: _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g), spin)
+        times = {g: _gpu_time_us(torch, sk, d, sk.make_options(schedule=sk.SCHED_SK_BASIC, forced_grid=g,
+                                                                 tile=large), spin)
                  for g in cands}
         best = min(times.values())
-        t_auto = _gpu_time_us(torch, sk, d, sk.make_options(), spin)
+        t_auto = _gpu_time_us(torch, sk, d, sk.make_options(tile=large), spin)
         regrets["default"].append(times[grid_default] / best)
         regrets["measured"].append(times[grid_measured] / best)
         regrets["auto"].append(t_auto / best)
@@ -384,7 +392,7 @@ def _spin_cycles(torch, seconds):
     return max(1000, int(seconds / per_cycle))
 
 
-def shape_sweep(torch, sk, S, count, out_path, reps=5):
+def shape_sweep(torch, sk, S, count, out_path, reps=5, tile_legs=False):
     """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
     contiguous along k; alpha=1, beta=0) on the seeded shape list; each shape
     runs three schedules of the same kernel: AUTO (the XCD-aware split), the
@@ -419,14 +427,18 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
     for idx, (kind, m, n, k) in enumerate(shapes):
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
         p = sk.plan_query(d)
-        t, slots = p.tiles, p.slots
+        large = sk.TILE_LARGE
+        pl = sk.plan_query(d, sk.make_options(tile=large))
+        t, slots = pl.tiles, pl.slots
         w, r = divmod(t, slots)
         page = sk.SCHED_DP if r == 0 else sk.SCHED_SK_HYBRID2 if w >= 1 else sk.SCHED_SK_BASIC
         res = {}
-        legs = [("auto", sk.make_options()), ("page", sk.make_options(schedule=page)),
-                ("dp", sk.make_options(schedule=sk.SCHED_DP))]
+        legs = [("auto", sk.make_options()), ("page", sk.make_options(schedule=page, tile=large)),
+                ("dp", sk.make_options(schedule=sk.SCHED_DP, tile=large))]
+        if tile_legs:
+            legs += [("large", sk.make_options(tile=large)), ("small", sk.make_options(tile=sk.TILE_SMALL))]
         # rotate the order per shape so that clock ramps do not favour one leg
-        legs = legs[idx % 3:] + legs[:idx % 3]
+        legs = legs[idx % len(legs):] + legs[:idx % len(legs)]
         for sched_name, opts in legs:
             sk.gemm_ex(d, opts)
             torch.cuda._sleep(spin)
@@ -452,7 +464,9 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5):
                          util_auto=tmin / res["auto"], util_page=tmin / res["page"],
                          util_dp=tmin / res["dp"],
                          dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak),
-                         host_auto_us=res["host_auto"] * 1e6, host_dp_us=res["host_dp"] * 1e6))
+                         host_auto_us=res["host_auto"] * 1e6, host_dp_us=res["host_dp"] * 1e6,
+                         tile_auto=p.tile_m,
+                         **({"t_large_us": res["large"] * 1e6, "t_small_us": res["small"] * 1e6} if tile_legs else {})))
         if idx % 100 == 0:
             print(f"sweep {idx}/{len(shapes)}", file=sys.stderr, flush=True)
     if out_path:
@@ -544,7 +558,8 @@ def main():
         calibrate_copy(torch)
         return
     if args.sweep:
-        print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out)), flush=True)
+        print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out, tile_legs=args.sweep_tiles)),
+              flush=True)
         return
     if args.calibrate_model:
         print(json.dumps(calibrate_model(torch, sk, S, args.calibrate_model)), flush=True)

@@ -138,8 +138,15 @@ typedef struct {
   sk_abft_record records[SK_ABFT_MAX_RECORDS];
 } sk_abft_report;
 
+/* fp16/bf16 tile instances.  LARGE: 256 x 256 x 64 tiles, one 512-thread
+ * workgroup per CU.  SMALL: 128 x 128 x 64 tiles, two 256-thread workgroups
+ * per CU, for GEMMs with few large tiles (the page's observation that a
+ * large tile loses on small, bandwidth-bound shapes, evaluation section).
+ * AUTO picks the one the runtime model predicts faster. */
+typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2 } sk_tile;
+
 /* Options for sk_gemm_ex.  Zero-initialised options mean: AUTO schedule, no
- * forced grid, ABFT off, default model constants. */
+ * forced grid, ABFT off, default model constants, AUTO tile instance. */
 typedef struct {
   int32_t schedule;         /* sk_schedule */
   int32_t forced_grid;      /* > 0: basic Stream-K with exactly this many workgroups */
@@ -152,7 +159,7 @@ typedef struct {
    * fixed cost a, partial-output cost b, per-iteration cost c, per-peer cost d */
   float model_a, model_b, model_c, model_d;
   int32_t spin_limit_us;    /* fixup wait time-out in microseconds (0 = 2 s) */
-  int32_t reserved;
+  int32_t tile;             /* sk_tile: fp16/bf16 tile instance (ignored for SK_F32) */
 } sk_options;
 
 /* Plan of one call, for inspection (host only, needs no GPU when
@@ -214,7 +221,10 @@ int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report 
                hipStream_t stream);
 
 /* Plan the call would use.  slots > 0 plans for that many resident
- * workgroups without touching the GPU; slots == 0 asks the current device. */
+ * workgroups of the fp32 or large-tile fp16/bf16 kernel (the small-tile
+ * instance runs two workgroups where the large one runs one, so it is
+ * planned for 2 * slots) without touching the GPU; slots == 0 asks the
+ * current device. */
 int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slots, sk_plan *out);
 
 /* Segments of workgroup `wg` under `plan`, in execution order.  Writes at

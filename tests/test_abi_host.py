@@ -73,17 +73,25 @@ def _check_schedule(p):
             assert peers == list(range(owner[2] + 1, owner[5] + 1)), (tile, segs)
 
 
+TILES = [sk.TILE_LARGE, sk.TILE_SMALL]
+
+
 @pytest.mark.parametrize("shape", SHAPES)
 @pytest.mark.parametrize("dtype", [sk.F16, sk.F32])
 @pytest.mark.parametrize("slots", [256, 512, 8])
-def test_page_schedules_match_oracle_decomposition(shape, dtype, slots):
+@pytest.mark.parametrize("tile", TILES)
+def test_page_schedules_match_oracle_decomposition(shape, dtype, slots, tile):
     """The page's decompositions, chosen explicitly, against the oracle's own
-    construction of Algorithms 2 and 5 and section 5.2's hybrids."""
+    construction of Algorithms 2 and 5 and section 5.2's hybrids (both fp16
+    tile instances; the small one runs two workgroups per slot)."""
     m, n, k = shape
     d = _desc(m, n, k, dtype)
     for sched, mode in [(sk.SCHED_DP, oracle.DP_PERSISTENT), (sk.SCHED_SK_BASIC, oracle.SK),
                         (sk.SCHED_SK_HYBRID2, oracle.HYBRID2), (sk.SCHED_SK_HYBRID1, oracle.HYBRID1)]:
-        p = sk.plan_query(d, sk.make_options(schedule=sched), slots)
+        p = sk.plan_query(d, sk.make_options(schedule=sched, tile=tile), slots)
+        assert p.slots == (2 * slots if dtype != sk.F32 and tile == sk.TILE_SMALL else slots)
+        assert p.tile_m == (128 if dtype == sk.F32 or tile == sk.TILE_SMALL else 256)
+        slots = p.slots
         t, ipt = p.tiles, p.iters_per_tile
         assert t == -(-m // p.tile_m) * -(-n // p.tile_n) and ipt == -(-k // p.tile_k)
         w, r = t // slots, t % slots
@@ -108,10 +116,12 @@ def test_page_schedules_match_oracle_decomposition(shape, dtype, slots):
                                             (2048, 2048, 8192), (512, 512, 30000), (256 * 17, 256 * 16, 256)])
 @pytest.mark.parametrize("dtype", [sk.F16, sk.F32])
 @pytest.mark.parametrize("slots", [256, 512, 8])
-def test_auto_xcd_aligned_schedule_invariants(shape, dtype, slots):
+@pytest.mark.parametrize("tile", TILES)
+def test_auto_xcd_aligned_schedule_invariants(shape, dtype, slots, tile):
     m, n, k = shape
     d = _desc(m, n, k, dtype)
-    p = sk.plan_query(d, None, slots)
+    p = sk.plan_query(d, sk.make_options(tile=tile), slots)
+    slots = p.slots
     assert p.schedule == sk.SCHED_XCD_ALIGNED and p.group_rows == 8
     t, w, r = p.tiles, p.tiles // slots, p.tiles % slots
     if w >= 1 and r == 0:
@@ -330,12 +340,31 @@ def test_auto_below_a_wave_needs_a_clear_iteration_gain():
     11 % of the iterations, less than the single data-parallel wave gains
     from its 28 idle CUs (higher clock), so AUTO keeps the wave; 64 tiles
     split four ways save 75 % and keep the split."""
-    near = sk.plan_query(_desc(2896, 4816, 14608), None, 256)
+    large = sk.make_options(tile=sk.TILE_LARGE)
+    near = sk.plan_query(_desc(2896, 4816, 14608), large, 256)
     assert near.tiles == 228 and near.sk_tiles == 0 and near.grid == 228
-    forced = sk.plan_query(_desc(2896, 4816, 14608), sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256)
+    forced = sk.plan_query(_desc(2896, 4816, 14608),
+                           sk.make_options(schedule=sk.SCHED_XCD_ALIGNED, tile=sk.TILE_LARGE), 256)
     assert forced.sk_tiles == 228
-    far = sk.plan_query(_desc(2048, 2048, 8192), None, 256)
+    far = sk.plan_query(_desc(2048, 2048, 8192), large, 256)
     assert far.sk_tiles == 64 and far.grid == 256
+
+
+def test_auto_tile_instance():
+    """fp16 AUTO keeps the large tile once its tiles fill the grid and takes
+    the small one where the runtime model predicts it faster (few large
+    tiles of few iterations); an explicit instance is always honoured, and
+    fp32 has one instance."""
+    big = sk.plan_query(_desc(8192, 8192, 8192), None, 256)
+    assert (big.tile_m, big.slots) == (256, 256)
+    small = sk.plan_query(_desc(512, 512, 512), None, 256)
+    assert (small.tile_m, small.slots) == (128, 512)
+    for shape in [(512, 512, 512), (8192, 8192, 8192), (300, 5000, 700)]:
+        for tile, bm in [(sk.TILE_LARGE, 256), (sk.TILE_SMALL, 128)]:
+            assert sk.plan_query(_desc(*shape), sk.make_options(tile=tile), 256).tile_m == bm
+        assert sk.plan_query(_desc(*shape, sk.F32), sk.make_options(tile=sk.TILE_SMALL), 512).tile_m == 128
+    with pytest.raises(sk.SkError):
+        sk.plan_query(_desc(512, 512, 512), sk.make_options(tile=3), 256)
 
 
 def test_two_tile_hybrid_owner_has_one_peer():
@@ -355,22 +384,22 @@ def test_grid_model_regimes():
     basic = sk.SCHED_SK_BASIC
     # T(g) ~ c*I/g + d*g/t is minimised near sqrt(c*I*t/d); with t = 16 tiles
     # and I = 16 * 1024 iterations that lies beyond the 256 slots
-    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model, schedule=basic), 256)
+    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model, schedule=basic, tile=sk.TILE_LARGE), 256)
     assert p.grid == 256
     # 64 tiles of 4 iterations: splitting saves at most 2 iterations per
     # workgroup but costs b + d = 4
-    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model, schedule=basic), 256)
+    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model, schedule=basic, tile=sk.TILE_LARGE), 256)
     assert p.grid == 64
-    p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model, schedule=basic), 256)
+    p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model, schedule=basic, tile=sk.TILE_LARGE), 256)
     assert 1 < p.grid <= 16
     # the same regimes under the XCD-aware split (grid = D * ceil(t / s))
-    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model), 256)
+    p = sk.plan_query(_desc(256, 256 * 16, 65536), sk.make_options(model=model, tile=sk.TILE_LARGE), 256)
     assert p.sk_tiles == 16 and p.grid == 256
-    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model), 256)
+    p = sk.plan_query(_desc(256 * 8, 256 * 8, 256), sk.make_options(model=model, tile=sk.TILE_LARGE), 256)
     assert p.sk_tiles == 0 and p.grid == 64
     # one tile: its partials meet in a binary tree, so the owner waits for
     # only log2(pieces) of them and a deeper split than the page's pays
-    p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model), 256)
+    p = sk.plan_query(_desc(256, 256, 64 * 128), sk.make_options(model=model, tile=sk.TILE_LARGE), 256)
     assert 16 <= p.grid <= 64 and p.fixup_tree == 1
 
 

@@ -48,17 +48,23 @@ def test_sgemm_384_uniform_auto_and_forced_grid4(forced):
 
 # ------------------------------------- ragged shapes, all types and layouts
 
+TILES = [sk.TILE_AUTO, sk.TILE_LARGE, sk.TILE_SMALL]
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("layout", LAYOUTS)
-def test_ragged_shapes_all_layouts(dtype, layout):
+@pytest.mark.parametrize("tile", TILES)
+def test_ragged_shapes_all_layouts(dtype, layout, tile):
+    if dtype == sk.F32 and tile != sk.TILE_AUTO:
+        pytest.skip("fp32 has one tile instance")
     # (520, 264, 320): interior tiles with vector-aligned rows and alpha, beta
     # not 1, 0 (the epilogue's straight-line path) next to edge tiles
     for (m, n, k, pad, alpha, beta) in [(300, 520, 200, 0, 1.0, 0.0), (513, 257, 1000, 8, 0.5, -1.5),
                                         (17, 33, 48, 0, 1.0, 1.0), (1, 1, 8, 0, 2.0, 0.0),
                                         (520, 264, 320, 0, 0.75, 1.25)]:
-        _say("case ragged", dtype, layout, m, n, k, pad)
+        _say("case ragged", dtype, layout, tile, m, n, k, pad)
         c = Case(m, n, k, dtype, layout, 7 + m + layout, pad=pad)
-        got = c.run(alpha, beta)
+        got = c.run(alpha, beta, sk.make_options(tile=tile))
         ref, bound = c.reference(alpha, beta)
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
 
@@ -105,35 +111,38 @@ def test_beta_zero_does_not_read_c(dtype):
 
 # ------------------------------------------------- schedule equivalences
 
-@pytest.mark.parametrize("dtype", [sk.F32, sk.F16])
-def test_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype):
+@pytest.mark.parametrize("dtype,tile", [(sk.F32, sk.TILE_AUTO), (sk.F16, sk.TILE_LARGE),
+                                        (sk.F16, sk.TILE_SMALL)])
+def test_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype, tile):
     m, n, k = (1024, 768, 2048) if dtype != sk.F32 else (640, 512, 1024)
     c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 11)
     p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
-                                   sk.A_ROW_B_COL))
+                                   sk.A_ROW_B_COL), sk.make_options(tile=tile))
     t = p.tiles
-    dp = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP))
+    dp = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP, tile=tile))
     c.reset_c()
-    skg = c.run(1.0, 0.0, sk.make_options(forced_grid=t))
+    skg = c.run(1.0, 0.0, sk.make_options(forced_grid=t, tile=tile))
     assert np.array_equal(dp.view(np.uint8), skg.view(np.uint8))
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_grid_size_exact_on_integer_inputs(dtype):
     """Small integers make every partial sum exact in fp32, so every
-    decomposition gives the same bits."""
+    decomposition, and both fp16/bf16 tile instances, give the same bits."""
     m, n, k = (700, 600, 1024) if dtype == sk.F32 else (600, 520, 2048)
     c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 12, dist="int")
     ref = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP))
-    for g in [1, 2, 3, 5, 7, 13, 31, 100, 255, 256, 300]:
-        c.reset_c()
-        got = c.run(1.0, 0.0, sk.make_options(forced_grid=g))
-        assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), g
-    for sched in (sk.SCHED_SK_HYBRID1, sk.SCHED_SK_HYBRID2, sk.SCHED_SK_BASIC, sk.SCHED_XCD_ALIGNED,
-                  sk.SCHED_AUTO):
-        c.reset_c()
-        got = c.run(1.0, 0.0, sk.make_options(schedule=sched))
-        assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), sched
+    tiles = [sk.TILE_AUTO] if dtype == sk.F32 else [sk.TILE_LARGE, sk.TILE_SMALL]
+    for tile in tiles:
+        for g in [1, 2, 3, 5, 7, 13, 31, 100, 255, 256, 300]:
+            c.reset_c()
+            got = c.run(1.0, 0.0, sk.make_options(forced_grid=g, tile=tile))
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), (tile, g)
+        for sched in (sk.SCHED_DP, sk.SCHED_SK_HYBRID1, sk.SCHED_SK_HYBRID2, sk.SCHED_SK_BASIC,
+                      sk.SCHED_XCD_ALIGNED, sk.SCHED_AUTO):
+            c.reset_c()
+            got = c.run(1.0, 0.0, sk.make_options(schedule=sched, tile=tile))
+            assert np.array_equal(got.view(np.uint8), ref.view(np.uint8)), (tile, sched)
     # the fp32 sums are exact, so the one rounding to the output type must
     # give the oracle's rounded value bit for bit
     import oracle
@@ -200,11 +209,14 @@ XCD_CASES = [
 
 
 @pytest.mark.parametrize("case", XCD_CASES)
-def test_xcd_aligned_schedule_against_oracle(case):
+@pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
+def test_xcd_aligned_schedule_against_oracle(case, tile):
     m, n, k, dtype, layout = case
-    _say("case xcd aligned", case)
+    if dtype == sk.F32 and tile == sk.TILE_SMALL:
+        pytest.skip("fp32 has one tile instance")
+    _say("case xcd aligned", case, tile)
     c = Case(m, n, k, dtype, layout, 21, dist="normal", scale=1 / np.sqrt(k))
-    opts = sk.make_options(schedule=sk.SCHED_XCD_ALIGNED)
+    opts = sk.make_options(schedule=sk.SCHED_XCD_ALIGNED, tile=tile)
     p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
                                    layout), opts)
     assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles > 0
@@ -283,7 +295,8 @@ def test_sweep_shapes_auto_and_dp_against_oracle():
                  scale=1 / np.sqrt(k), with_c=False)
         rows, cols = sample_indices(m, n, 400, m * 7 + n)
         ref, bound = c.reference_entries(rows, cols)
-        for opts in (None, sk.make_options(schedule=sk.SCHED_DP)):
+        for opts in (None, sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE),
+                     sk.make_options(tile=sk.TILE_SMALL)):
             got = c.run(1.0, 0.0, opts)
             g = decode(got[rows, cols], sk.F16)
             assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F16], (kind, m, n, k)

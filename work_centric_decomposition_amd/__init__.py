@@ -25,6 +25,7 @@ F32, F16, BF16 = 0, 1, 2
 A_ROW_B_ROW, A_ROW_B_COL, A_COL_B_ROW, A_COL_B_COL = 0, 1, 2, 3
 SCHED_AUTO, SCHED_DP, SCHED_SK_BASIC, SCHED_SK_HYBRID2, SCHED_SK_HYBRID1 = 0, 1, 2, 3, 4
 SCHED_XCD_ALIGNED = 5
+TILE_AUTO, TILE_LARGE, TILE_SMALL = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT, ERR_NO_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 ABFT_MAX_RECORDS = 64
@@ -70,7 +71,7 @@ class Options(ctypes.Structure):
     _fields_ = [("schedule", i32), ("forced_grid", i32), ("abft", i32), ("hybrid_min_waves", i32),
                 ("faults", vp), ("n_faults", i32), ("abft_tau", f32), ("model_a", f32),
                 ("model_b", f32), ("model_c", f32), ("model_d", f32), ("spin_limit_us", i32),
-                ("reserved", i32)]
+                ("tile", i32)]
 
 
 class Plan(ctypes.Structure):
@@ -174,13 +175,14 @@ def gemm(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, dtype, layout, stream=Non
 
 def make_options(schedule=SCHED_AUTO, forced_grid=0, abft=False, hybrid_min_waves=0,
                  faults=None, n_faults=0, abft_tau=0.0, model=(0.0, 0.0, 0.0, 0.0),
-                 spin_limit_us=0) -> Options:
+                 spin_limit_us=0, tile=0) -> Options:
     o = Options()
     o.schedule, o.forced_grid, o.abft, o.hybrid_min_waves = schedule, forced_grid, int(abft), \
         hybrid_min_waves
     o.faults, o.n_faults, o.abft_tau = _ptr(faults), n_faults, abft_tau
     o.model_a, o.model_b, o.model_c, o.model_d = model
     o.spin_limit_us = spin_limit_us
+    o.tile = tile
     return o
 
 

@@ -32,8 +32,9 @@ int hip_fail(hipError_t e, const char *what) {
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
-  int slots[3] = {0, 0, 0};  // per dtype
-  int slots_abft = 0;        // fp32 with ABFT
+  int slots[3] = {0, 0, 0};        // per dtype (fp16/bf16: large tiles)
+  int slots_small[3] = {0, 0, 0};  // fp16/bf16 small-tile instance
+  int slots_abft = 0;              // fp32 with ABFT
   int64_t wall_khz = 100000;
 };
 
@@ -74,17 +75,19 @@ int device_info(int dev, DeviceInfo **out) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     d.wall_khz = khz;
-  for (int dt = 0; dt < 4; ++dt) {  // 3: fp32 with ABFT
+  // 0-2: per dtype; 3: fp32 with ABFT; 4, 5: fp16, bf16 small tiles
+  for (int dt = 0; dt < 6; ++dt) {
     int occ = 0;
-    const int dtype = dt == 3 ? SK_F32 : dt;
-    e = (hipError_t)kernel_occupancy(dtype, dt == 3, &occ);
+    const int dtype = dt == 3 ? SK_F32 : dt > 3 ? dt - 3 : dt;
+    const int inst = dt > 3 ? 1 : 0;
+    e = (hipError_t)kernel_occupancy(dtype, dt == 3, inst, &occ);
     if (e != hipSuccess) return hip_fail(e, "occupancy query");
-    const int want = tile_cfg(dtype).occupancy;
+    const int want = tile_cfg(dtype, inst).occupancy;
     if (occ < 1) {
       g_last_hip_error = "kernel does not fit on a CU";
       return SK_ERR_HIP;
     }
-    (dt == 3 ? d.slots_abft : d.slots[dt]) = d.cus * (occ < want ? occ : want);
+    (dt == 3 ? d.slots_abft : dt > 3 ? d.slots_small[dtype] : d.slots[dt]) = d.cus * (occ < want ? occ : want);
   }
   d.ok = true;
   forget.armed = false;
@@ -179,7 +182,9 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "scale kernel");
   }
   Plan P;
-  rc = make_plan(d, o, o.abft ? info->slots_abft : info->slots[d.dtype], P);
+  const int slots[2] = {o.abft && d.dtype == SK_F32 ? info->slots_abft : info->slots[d.dtype],
+                        d.dtype == SK_F32 ? 1 : info->slots_small[d.dtype]};
+  rc = make_plan(d, o, slots, P);
   if (rc != SK_OK) return rc;
   const int es = d.dtype == SK_F32 ? 4 : 2;
   const bool ak = a_kmajor_of(d.layout), bk = b_kmajor_of(d.layout);
@@ -284,6 +289,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
   if (!desc || !out || slots < 0) return SK_ERR_INVALID_ARG;
   const sk_options &o = opts ? *opts : kDefaultOpts;
   try {
+    int slots2 = 0;  // small-tile instance
     if (slots == 0) {
       int dev = 0;
       hipError_t e = hipGetDevice(&dev);
@@ -294,9 +300,12 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       if (rc != SK_OK) return rc;
       if (desc->dtype < 0 || desc->dtype > 2) return SK_ERR_INVALID_ARG;
       slots = o.abft && desc->dtype == SK_F32 ? info->slots_abft : info->slots[desc->dtype];
+      slots2 = desc->dtype == SK_F32 ? 1 : info->slots_small[desc->dtype];
     }
+    if (slots2 == 0) slots2 = 2 * slots;
+    const int both[2] = {slots, slots2};
     Plan P;
-    int rc = make_plan(*desc, o, slots, P);
+    int rc = make_plan(*desc, o, both, P);
     if (rc != SK_OK) return rc;
     std::memset(out, 0, sizeof(*out));
     out->tile_m = P.cfg.bm; out->tile_n = P.cfg.bn; out->tile_k = P.cfg.bk;

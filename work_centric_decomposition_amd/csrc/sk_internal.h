@@ -23,32 +23,29 @@ struct TileCfg {
   int lds_bytes;     // dynamic LDS per workgroup
   // default grid-size model constants, in units of one MAC iteration
   float a, b, c, d;
+  int inst;          // HGEMM tile instance (0: 256 x 256, 1: 128 x 128)
+  // the tile-instance choice, microseconds: fixed cost of a launch (start,
+  // first loads, epilogue), one iteration of the busiest workgroup, one
+  // level of partial exchange (least-squares fit to the fp16 shape sweep
+  // below one wave of large tiles, every workgroup busy)
+  float fixed_us, iter_us, level_us;
 };
 
-// k-depth of an HGEMM tile iteration and number of LDS stages (a build-time
-// choice; the default is two stages of 64).
-#ifndef SK_HGEMM_BK
-#define SK_HGEMM_BK 64
-#endif
-#ifndef SK_HGEMM_STAGES
-#define SK_HGEMM_STAGES 2
-#endif
-// waves per HGEMM workgroup: 8 (two per SIMD, 128 x 64 wave tiles) or 4 (one
-// per SIMD, 128 x 128 wave tiles)
-#ifndef SK_HGEMM_WAVES
-#define SK_HGEMM_WAVES 8
-#endif
-
-inline TileCfg tile_cfg(int dtype) {
+// Tile instances.  fp32: 128 x 128 x 32, 4 waves, two workgroups per CU.
+// fp16/bf16: instance 0, 256 x 256 x 64 with 8 waves and one workgroup per
+// CU; instance 1, 128 x 128 x 64 with 4 waves and two per CU, for shapes
+// with few large tiles.  Model constants in units of one MAC iteration of
+// the instance.
+inline TileCfg tile_cfg(int dtype, int inst = 0) {
   // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
-  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f};
-  // model constants in units of one iteration, fitted to the fp16 shape
-  // sweep on MI355X: a 256 x 256 fp32 partial (256 KiB) costs about five
-  // 64-deep iterations to write and four to read and add when every
-  // workgroup exchanges one at the same time
-  const float it = SK_HGEMM_BK / 64.f;
-  return TileCfg{256, 256, SK_HGEMM_BK, 64 * SK_HGEMM_WAVES, 1, SK_HGEMM_STAGES * 2 * 256 * SK_HGEMM_BK * 2,
-                 4.f / it, 5.f / it, 1.f, 4.f / it};
+  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f, 0, 8.3f, 2.f, 3.3f};
+  // 128 x 128 fp16: a 64 KiB partial against a quarter of the large tile's
+  // iteration work
+  if (inst == 1) return TileCfg{128, 128, 64, 256, 2, 2 * 2 * 128 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 1, 3.55f, 1.27f, 2.95f};
+  // model constants fitted to the fp16 shape sweep on MI355X: a 256 x 256
+  // fp32 partial (256 KiB) costs about five 64-deep iterations to write and
+  // four to read and add when every workgroup exchanges one at the same time
+  return TileCfg{256, 256, 64, 512, 1, 2 * 2 * 256 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 0, 6.7f, 1.83f, 8.3f};
 }
 
 // How the kernels walk the work (shared by the kernels and the host's
@@ -265,8 +262,11 @@ struct Plan {
   }
 };
 
-// Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots > 0.
-int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &plan);
+// Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots:
+// resident workgroups of the large (or fp32) and of the small-tile instance.
+int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &plan);
+// The runtime model's predicted time of a plan, in microseconds.
+double plan_cost_us(const Plan &plan);
 // Most partials any owner adds under `plan` (O(tiles); for inspection).
 int plan_max_peers(const Plan &plan);
 
@@ -313,6 +313,6 @@ int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_
                 int64_t k, void *dst, int64_t ldd, hipStream_t stream);
 int launch_zero_report(sk_abft_report *report, hipStream_t stream);
 // Occupancy query for the GEMM kernel of `dtype` (fp32: with or without ABFT).
-int kernel_occupancy(int dtype, bool abft, int *blocks_per_cu);
+int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu);
 
 }  // namespace sk

@@ -243,14 +243,17 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // 32x32 block layout, with the product formed as C^T = B^T A^T: register r
 // of lane l holds row (l & 31) and column 8*(r/4) + 4*(l >> 5) + (r & 3) of
 // the block, i.e. four consecutive columns per register quad.
-template <int DT>
+// HGEMM instances: 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each;
+// one workgroup per CU) and 128 x 128 tiles with 4 waves (2 x 2, 64 x 64
+// each; two workgroups per CU) for shapes with few large tiles.
+template <int DT, int TILE>
 struct HPolicy {
-  static constexpr int BM = 256, BN = 256, BK = SK_HGEMM_BK, NSTAGE = SK_HGEMM_STAGES;
-  static constexpr int WAVES = SK_HGEMM_WAVES, NT = 64 * WAVES;
+  static constexpr int ET = DT;
+  static constexpr int BM = TILE, BN = TILE, BK = 64, NSTAGE = 2;
+  static constexpr int WAVES = TILE == 256 ? 8 : 4, NT = 64 * WAVES;
   static constexpr int SUBS = BK / 16;  // k-substeps of one iteration
-  static_assert(SUBS % 2 == 0 && NSTAGE >= 2 && NSTAGE <= 5, "pipeline shape");
-  static_assert(WAVES == 4 || WAVES == 8, "2 x 2 or 2 x 4 waves");
-  static constexpr int WTM = 128, WTN = BN / (WAVES / 2), MB = WTM / 32, NB = WTN / 32;
+  static_assert(TILE == 256 || TILE == 128, "tile");
+  static constexpr int WTM = BM / 2, WTN = BN / (WAVES / 2), MB = WTM / 32, NB = WTN / 32;
   static constexpr int WAVES_N = BN / WTN;
   static constexpr int NACC4 = MB * NB * 4;
   static constexpr int ROW = BK * 2;  // bytes of one LDS row (k-contiguous)
@@ -288,9 +291,8 @@ struct HPolicy {
 // past the matrix) are computed once per tile; each k-iteration only adds
 // the scalar offset k0 * 2.  In the iteration that holds the end of k,
 // chunks at or past k are fetched out of range (zeros).
-template <int DT>
+template <class P>
 struct HLoader {
-  using P = HPolicy<DT>;
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[P::LOADS], vb[P::LOADS];
   int chunk[P::LOADS];  // 16-byte k-chunk each load fetches (same for A and B)
@@ -354,29 +356,6 @@ struct HLoader {
   }
 };
 
-// Fragments of k-substep `sub` (16 values of k) of an LDS stage: lane l
-// holds row (l & 31) of each 32-row block and k chunk 2*sub + (l >> 5).
-template <int DT>
-__device__ __forceinline__ void h_frags(int stage, int sub, int wm, int wn,
-                                        typename Elem<DT>::V8 (&af)[HPolicy<DT>::MB],
-                                        typename Elem<DT>::V8 (&bf)[HPolicy<DT>::NB]) {
-  using P = HPolicy<DT>;
-  using V8 = typename Elem<DT>::V8;
-  const int lane = threadIdx.x & 63;
-  const int As = stage * P::STAGE, Bs = As + P::A_BYTES;
-  const int c = sub * 2 + (lane >> 5);
-#pragma unroll
-  for (int nb = 0; nb < P::NB; ++nb) {
-    const int row = wn * P::WTN + nb * 32 + (lane & 31);
-    bf[nb] = *reinterpret_cast<const V8 *>(smem + Bs + row * P::ROW + ((c ^ P::swz(row)) << 4));
-  }
-#pragma unroll
-  for (int mb = 0; mb < P::MB; ++mb) {
-    const int row = wm * P::WTM + mb * 32 + (lane & 31);
-    af[mb] = *reinterpret_cast<const V8 *>(smem + As + row * P::ROW + ((c ^ P::swz(row)) << 4));
-  }
-}
-
 template <int DT>
 __device__ __forceinline__ f16v_t h_mfma(typename Elem<DT>::V8 a, typename Elem<DT>::V8 b, f16v_t c);
 template <>
@@ -388,132 +367,9 @@ __device__ __forceinline__ f16v_t h_mfma<SK_BF16>(b8_t a, b8_t b, f16v_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int DT>
-__device__ __forceinline__ void h_mfmas(const typename Elem<DT>::V8 (&af)[HPolicy<DT>::MB],
-                                        const typename Elem<DT>::V8 (&bf)[HPolicy<DT>::NB],
-                                        typename HPolicy<DT>::Acc &acc) {
-  using P = HPolicy<DT>;
-#pragma unroll
-  for (int mb = 0; mb < P::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < P::NB; ++nb)
-      acc.v[mb * P::NB + nb] = h_mfma<DT>(bf[nb], af[mb], acc.v[mb * P::NB + nb]);
-}
-
 // s_waitcnt immediate: at most n vector-memory operations of this wave
 // outstanding and no LDS read outstanding.
 constexpr int vmcnt_le_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
-
-// Waits until at most `stages` stages of this wave's loads are outstanding
-// (and all of its LDS reads have completed).  A wave's vector-memory
-// operations complete in issue order.
-template <int LPS>
-__device__ __forceinline__ void wait_stages(int stages) {
-  if (stages >= 3) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(3 * LPS));
-  else if (stages == 2) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(2 * LPS));
-  else if (stages == 1) __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(LPS));
-  else __builtin_amdgcn_s_waitcnt(0);
-}
-
-// Instruction-scheduling knobs of the HGEMM main loop (build-time):
-//  SK_HGEMM_INTERLEAVE: let the scheduler interleave the LDS reads of
-//    substep s+1 one by one with the MFMAs of substep s (instead of issuing
-//    all reads first);
-//  SK_HGEMM_SETPRIO: raise the wave's issue priority while it issues MFMAs,
-//    so that of the two waves sharing a SIMD the one with MFMAs ready wins.
-#ifndef SK_HGEMM_INTERLEAVE
-#define SK_HGEMM_INTERLEAVE 1
-#endif
-#ifndef SK_HGEMM_SETPRIO
-#define SK_HGEMM_SETPRIO 0
-#endif
-#if SK_HGEMM_INTERLEAVE
-#define H_PHASE_SPLIT() ((void)0)
-#define H_INTERLEAVE()                                                  \
-  do {                                                                  \
-    _Pragma("unroll") for (int q = 0; q < P::MB + P::NB; ++q) {         \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                \
-    }                                                                   \
-    __builtin_amdgcn_sched_group_barrier(0x008, P::MB * P::NB, 0);      \
-  } while (0)
-#else
-#define H_PHASE_SPLIT() __builtin_amdgcn_sched_barrier(0)
-#define H_INTERLEAVE() ((void)0)
-#endif
-#if SK_HGEMM_SETPRIO
-#define H_PRIO_UP() __builtin_amdgcn_s_setprio(1)
-#define H_PRIO_DOWN() __builtin_amdgcn_s_setprio(0)
-#else
-#define H_PRIO_UP() ((void)0)
-#define H_PRIO_DOWN() ((void)0)
-#endif
-
-// MacLoop over iterations [lb, le) of the tile at (m0, n0).
-//
-// Software pipeline: NSTAGE LDS stages and two register sets of fragments.
-// While the MFMAs of substep s run, the fragments of substep s+1 are read.
-// Before the last substep: wait until this wave's loads of stage i+1 have
-// landed, barrier (every wave has also finished reading stage i), issue the
-// loads of iteration i+NSTAGE into stage i's buffer, and read substep 0 of
-// stage i+1 while the MFMAs of the last substep run.  A load thus has
-// NSTAGE-1 iterations to land, and LDS latency is covered by MFMAs.
-template <int DT>
-__device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
-                                          typename HPolicy<DT>::Acc &acc) {
-  using P = HPolicy<DT>;
-  using V8 = typename Elem<DT>::V8;
-  constexpr int NS = P::NSTAGE, LPS = 2 * P::LOADS;
-  const int w = wave_id();
-  const int wm = w / P::WAVES_N, wn = w % P::WAVES_N;
-  P::zero(acc);
-  const int n = le - lb;
-  if (n <= 0) return;
-  HLoader<DT> ld;
-  ld.init(a, m0, n0);
-  const int pre = n < NS ? n : NS;
-  for (int s = 0; s < pre; ++s) ld.load(a, s, lb + s);
-  wait_stages<LPS>(pre - 1);
-  __syncthreads();
-  V8 fa0[P::MB], fb0[P::NB], fa1[P::MB], fb1[P::NB];
-  h_frags<DT>(0, 0, wm, wn, fa0, fb0);
-  int buf = 0;
-  for (int i = 0; i < n; ++i) {
-#pragma unroll
-    for (int sub = 0; sub + 1 < P::SUBS; ++sub) {
-      if (sub % 2 == 0) {
-        h_frags<DT>(buf, sub + 1, wm, wn, fa1, fb1);
-        H_PHASE_SPLIT();
-        H_PRIO_UP();
-        h_mfmas<DT>(fa0, fb0, acc);
-      } else {
-        h_frags<DT>(buf, sub + 1, wm, wn, fa0, fb0);
-        H_PHASE_SPLIT();
-        H_PRIO_UP();
-        h_mfmas<DT>(fa1, fb1, acc);
-      }
-      H_INTERLEAVE();
-      H_PRIO_DOWN();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // last substep: switch stages.  Stages issued beyond i+1:
-    // min(i+NS-1, n-1) - (i+1).
-    const int last = i + NS - 1 < n - 1 ? i + NS - 1 : n - 1;
-    wait_stages<LPS>(last - (i + 1));
-    __syncthreads();
-    if (i + NS < n) ld.load(a, buf, lb + i + NS);
-    const int nbuf = buf + 1 == NS ? 0 : buf + 1;
-    if (i + 1 < n) h_frags<DT>(nbuf, 0, wm, wn, fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
-    h_mfmas<DT>(fa1, fb1, acc);
-    __builtin_amdgcn_sched_barrier(0);
-    buf = nbuf;
-  }
-}
-
-#ifndef SK_HGEMM_LOOKAHEAD
-#define SK_HGEMM_LOOKAHEAD 2
-#endif
 
 // MacLoop with fragments read two substeps ahead (three fragment sets in
 // rotation) for the two-stage, four-substep configuration.  The stage
@@ -522,18 +378,17 @@ __device__ __forceinline__ void h_macloop(const KernelArgs &a, int m0, int n0, i
 // i+1 have landed and its LDS reads have returned, one workgroup barrier
 // both publishes stage i+1 and frees stage i for the loads of iteration
 // i+2.
-template <int DT>
+template <class P>
 struct HFrag {
-  typename Elem<DT>::V8 a[HPolicy<DT>::MB], b[HPolicy<DT>::NB];
+  typename Elem<P::ET>::V8 a[P::MB], b[P::NB];
 };
 
 // One fragment read (q < NB: B block q, else A block q - NB) and one MFMA
 // (block row q / NB, column q % NB) of a substep, for the pinned
 // interleaving below.
-template <int DT>
-__device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, int q, HFrag<DT> &F) {
-  using P = HPolicy<DT>;
-  using V8 = typename Elem<DT>::V8;
+template <class P>
+__device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, int q, HFrag<P> &F) {
+  using V8 = typename Elem<P::ET>::V8;
   const int lane = threadIdx.x & 63;
   const int As = stage * P::STAGE, Bs = As + P::A_BYTES;
   const int c = sub * 2 + (lane >> 5);
@@ -546,45 +401,47 @@ __device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, i
   }
 }
 
-template <int DT>
-__device__ __forceinline__ void h_mfma_one(const HFrag<DT> &F, typename HPolicy<DT>::Acc &acc, int q) {
-  using P = HPolicy<DT>;
+template <class P>
+__device__ __forceinline__ void h_mfma_one(const HFrag<P> &F, typename P::Acc &acc, int q) {
   const int mb = q / P::NB, nb = q % P::NB;
-  acc.v[q] = h_mfma<DT>(F.b[nb], F.a[mb], acc.v[q]);
+  acc.v[q] = h_mfma<P::ET>(F.b[nb], F.a[mb], acc.v[q]);
 }
 
 // One substep: the MFMAs of fragment set M, each followed (in this exact
 // order: the scheduler may not regroup them) by one fragment read of
-// substep `sub` of stage `stage` into set R and, while q < nl, by load q of
-// this wave's share of iteration `kit` into stage `lstage`.  Spreading the
+// substep `sub` of stage `stage` into set R and by the next of the first nl
+// loads of this wave's share of iteration `kit` into stage `lstage` (two
+// per MFMA where a wave has more loads than MFMAs in a substep).  Spreading the
 // reads and loads this way keeps a single wave issuing MFMAs back to back:
 // grouped loads stall its issue for longer than an MFMA takes.
-template <int DT>
-__device__ __forceinline__ void h_substep(const KernelArgs &a, const HLoader<DT> &ld, const HFrag<DT> &M,
-                                          HFrag<DT> &R, int stage, int sub, int wm, int wn,
-                                          typename HPolicy<DT>::Acc &acc, int nl, int lstage, int kit, bool live) {
-  using P = HPolicy<DT>;
+template <class P>
+__device__ __forceinline__ void h_substep(const KernelArgs &a, const HLoader<P> &ld, const HFrag<P> &M,
+                                          HFrag<P> &R, int stage, int sub, int wm, int wn,
+                                          typename P::Acc &acc, int nl, int lstage, int kit, bool live) {
   constexpr int NM = P::MB * P::NB, NR = P::MB + P::NB;
-  static_assert(NR <= NM && 2 * P::LOADS <= NM, "one read and one load per MFMA at most");
+  constexpr int LPM = (2 * P::LOADS + NM - 1) / NM;  // loads after each MFMA
+  static_assert(NR <= NM, "one fragment read per MFMA at most");
 #pragma unroll
   for (int q = 0; q < NM; ++q) {
-    h_mfma_one<DT>(M, acc, q);
+    h_mfma_one<P>(M, acc, q);
     __builtin_amdgcn_sched_barrier(0);
-    if (q < nl) ld.load_one(a, lstage, kit, live, q);
-    if (q < NR) h_frag_one<DT>(stage, sub, wm, wn, q, R);
+#pragma unroll
+    for (int l = q * LPM; l < (q + 1) * LPM; ++l)
+      if (l < nl) ld.load_one(a, lstage, kit, live, l);
+    if (q < NR) h_frag_one<P>(stage, sub, wm, wn, q, R);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
 // Iteration i of the lookahead-2 loop.  Global substep g = 4 i + s uses
 // fragment set F[g % 3]; with i = PH (mod 3), 4 i = PH (mod 3).
-template <int DT, int PH>
-__device__ __forceinline__ void h_iter_la2(const KernelArgs &a, const HLoader<DT> &ld, int i, int n, int lb,
-                                           int wm, int wn, HFrag<DT> (&F)[3], typename HPolicy<DT>::Acc &acc) {
+template <class P, int PH>
+__device__ __forceinline__ void h_iter_la2(const KernelArgs &a, const HLoader<P> &ld, int i, int n, int lb,
+                                           int wm, int wn, HFrag<P> (&F)[3], typename P::Acc &acc) {
   constexpr int f0 = (PH + 0) % 3, f1 = (PH + 1) % 3, f2 = (PH + 2) % 3;
   const int buf = i & 1;
-  h_substep<DT>(a, ld, F[f0], F[f2], buf, 2, wm, wn, acc, 0, 0, 0, false);
-  h_substep<DT>(a, ld, F[f1], F[f0], buf, 3, wm, wn, acc, 0, 0, 0, false);
+  h_substep<P>(a, ld, F[f0], F[f2], buf, 2, wm, wn, acc, 0, 0, 0, false);
+  h_substep<P>(a, ld, F[f1], F[f0], buf, 3, wm, wn, acc, 0, 0, 0, false);
   // stage switch: stage i+1 complete (its loads were the only ones in
   // flight) and every read of stage i returned
   __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(0));
@@ -592,14 +449,13 @@ __device__ __forceinline__ void h_iter_la2(const KernelArgs &a, const HLoader<DT
   // no branches from here to the next stage switch: in the last two
   // iterations the loads fetch nothing (zeros into the stage just freed)
   // and the last iteration's reads of stage i+1 go unused
-  h_substep<DT>(a, ld, F[f2], F[f1], buf ^ 1, 0, wm, wn, acc, 2 * HPolicy<DT>::LOADS, buf, lb + i + 2, i + 2 < n);
-  h_substep<DT>(a, ld, F[f0], F[f2], buf ^ 1, 1, wm, wn, acc, 0, 0, 0, false);
+  h_substep<P>(a, ld, F[f2], F[f1], buf ^ 1, 0, wm, wn, acc, 2 * P::LOADS, buf, lb + i + 2, i + 2 < n);
+  h_substep<P>(a, ld, F[f0], F[f2], buf ^ 1, 1, wm, wn, acc, 0, 0, 0, false);
 }
 
-template <int DT>
+template <class P>
 __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n0, int lb, int le,
-                                              typename HPolicy<DT>::Acc &acc) {
-  using P = HPolicy<DT>;
+                                              typename P::Acc &acc) {
   static_assert(P::NSTAGE == 2 && P::SUBS == 4, "lookahead-2 loop: two stages of four substeps");
   constexpr int LPS = 2 * P::LOADS;
   const int w = wave_id();
@@ -607,7 +463,7 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
   P::zero(acc);
   const int n = le - lb;
   if (n <= 0) return;
-  HLoader<DT> ld;
+  HLoader<P> ld;
   ld.init(a, m0, n0);
   ld.load(a, 0, lb);
   if (n > 1) {
@@ -617,17 +473,20 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
     __builtin_amdgcn_s_waitcnt(vmcnt_le_lgkm0(0));
   }
   __syncthreads();
-  HFrag<DT> F[3];
-  h_frags<DT>(0, 0, wm, wn, F[0].a, F[0].b);
-  h_frags<DT>(0, 1, wm, wn, F[1].a, F[1].b);
+  HFrag<P> F[3];
+#pragma unroll
+  for (int q = 0; q < P::MB + P::NB; ++q) {
+    h_frag_one<P>(0, 0, wm, wn, q, F[0]);
+    h_frag_one<P>(0, 1, wm, wn, q, F[1]);
+  }
   int i = 0;
   for (; i + 3 <= n; i += 3) {
-    h_iter_la2<DT, 0>(a, ld, i, n, lb, wm, wn, F, acc);
-    h_iter_la2<DT, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
-    h_iter_la2<DT, 2>(a, ld, i + 2, n, lb, wm, wn, F, acc);
+    h_iter_la2<P, 0>(a, ld, i, n, lb, wm, wn, F, acc);
+    h_iter_la2<P, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
+    h_iter_la2<P, 2>(a, ld, i + 2, n, lb, wm, wn, F, acc);
   }
-  if (i < n) h_iter_la2<DT, 0>(a, ld, i, n, lb, wm, wn, F, acc);
-  if (i + 1 < n) h_iter_la2<DT, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
+  if (i < n) h_iter_la2<P, 0>(a, ld, i, n, lb, wm, wn, F, acc);
+  if (i + 1 < n) h_iter_la2<P, 1>(a, ld, i + 1, n, lb, wm, wn, F, acc);
   // the last iterations' (empty) loads and reads have landed in every wave
   // before the caller reuses LDS
   __builtin_amdgcn_s_waitcnt(0);
@@ -639,11 +498,10 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
 // multiple of 8), else, with rows that allow 4-element vector accesses, by
 // straight-line accesses; edge tiles take the per-element bounds checks of
 // store4.
-template <int DT>
+template <class P>
 __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
-                                           const typename HPolicy<DT>::Acc &acc) {
-  using P = HPolicy<DT>;
-  using T = typename Elem<DT>::T;
+                                           const typename P::Acc &acc) {
+  using T = typename Elem<P::ET>::T;
   const int w = wave_id(), lane = threadIdx.x & 63;
   const int r0 = m0 + (w / P::WAVES_N) * P::WTM, c0 = n0 + (w % P::WAVES_N) * P::WTN;
   const bool full = m0 + P::BM <= a.m && n0 + P::BN <= a.n;
@@ -672,7 +530,7 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
         for (int nb = 0; nb < P::NB; ++nb)
 #pragma unroll
           for (int g = 0; g < 4; ++g)
-            Elem<DT>::st4(wr + mb * 32 * RS + (nb * 32 + 8 * g) * 2, 0,
+            Elem<P::ET>::st4(wr + mb * 32 * RS + (nb * 32 + 8 * g) * 2, 0,
                           a.alpha * P::get4(acc, ((h * HALF + mb) * P::NB + nb) * 4 + g));
 #pragma unroll
       for (int it = 0; it < HALF * 32 / 8; ++it) {
@@ -698,8 +556,8 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
           T *q = cb + mb * rstep;
           const int o = nb * 32 + 8 * g;
           f4_t v = a.alpha * P::get4(acc, (mb * P::NB + nb) * 4 + g);
-          if (a.beta != 0.f) v += a.beta * Elem<DT>::ld4(q, o);
-          Elem<DT>::st4(q, o, v);
+          if (a.beta != 0.f) v += a.beta * Elem<P::ET>::ld4(q, o);
+          Elem<P::ET>::st4(q, o, v);
         }
     return;
   }
@@ -709,7 +567,7 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
     for (int nb = 0; nb < P::NB; ++nb)
 #pragma unroll
       for (int g = 0; g < 4; ++g)
-        store4<DT>(a, vec_ok, r0 + mb * 32 + (lane & 31), c0 + nb * 32 + 8 * g + 4 * (lane >> 5),
+        store4<P::ET>(a, vec_ok, r0 + mb * 32 + (lane & 31), c0 + nb * 32 + 8 * g + 4 * (lane >> 5),
                    P::get4(acc, (mb * P::NB + nb) * 4 + g));
 }
 
@@ -1327,19 +1185,11 @@ __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop maclo
   while (sched_next(a.sched, I, g)) run_segment<P>(a, x, g, macloop, epilogue);
 }
 
-template <int DT>
-__global__ __launch_bounds__(HPolicy<DT>::NT) void hgemm_kernel(KernelArgs a, int vec_ok) {
-  using P = HPolicy<DT>;
+template <class P>
+__global__ __launch_bounds__(P::NT, 2) void hgemm_kernel(KernelArgs a, int vec_ok) {
   run_workgroup<P>(
-      a,
-      [&](int m0, int n0, int lb, int le, typename P::Acc &acc) {
-#if SK_HGEMM_LOOKAHEAD == 2
-        h_macloop_la2<DT>(a, m0, n0, lb, le, acc);
-#else
-        h_macloop<DT>(a, m0, n0, lb, le, acc);
-#endif
-      },
-      [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<DT>(a, vec_ok != 0, m0, n0, acc); });
+      a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { h_macloop_la2<P>(a, m0, n0, lb, le, acc); },
+      [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
 }
 
 template <bool AK, bool BKM, bool ABFT>
@@ -1423,20 +1273,24 @@ static const void *sgemm_entry(bool ak, bool bk, bool abft) {
   return reinterpret_cast<const void *>(&sgemm_kernel<false, false, false>);
 }
 
+// Entry point of an fp16/bf16 tile instance.
+static const void *hgemm_entry(int dtype, int inst) {
+  using namespace dev;
+  if (inst == 1)
+    return dtype == SK_F16 ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_F16, 128>>)
+                           : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_BF16, 128>>);
+  return dtype == SK_F16 ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_F16, 256>>)
+                         : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_BF16, 256>>);
+}
+
 int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   dim3 grid(p.grid), block(p.cfg.threads);
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
   const size_t lds = p.cfg.lds_bytes;
-  if (p.dtype == SK_F16) {
-    hipLaunchKernelGGL(dev::hgemm_kernel<SK_F16>, grid, block, lds, stream, a, vec_ok);
-  } else if (p.dtype == SK_BF16) {
-    hipLaunchKernelGGL(dev::hgemm_kernel<SK_BF16>, grid, block, lds, stream, a, vec_ok);
-  } else {
-    const void *f = sgemm_entry(a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
-    void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
-    return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
-  }
-  return (int)hipGetLastError();
+  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst)
+                                    : sgemm_entry(a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
+  void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
+  return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
 }
 
 int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t ldc,
@@ -1475,8 +1329,8 @@ int launch_zero_report(sk_abft_report *report, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
-int kernel_occupancy(int dtype, bool abft, int *blocks_per_cu) {
-  const TileCfg c = tile_cfg(dtype);
+int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu) {
+  const TileCfg c = tile_cfg(dtype, inst);
   hipError_t e = hipSuccess;
   int nb = 0;
   if (dtype == SK_F32) {
@@ -1491,14 +1345,9 @@ int kernel_occupancy(int dtype, bool abft, int *blocks_per_cu) {
       if (o < nb) nb = o;
     }
   } else {
-    const void *f16 = reinterpret_cast<const void *>(&dev::hgemm_kernel<SK_F16>);
-    const void *bf16 = reinterpret_cast<const void *>(&dev::hgemm_kernel<SK_BF16>);
-    e = hipFuncSetAttribute(f16, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
-    if (e == hipSuccess) e = hipFuncSetAttribute(bf16, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
-    if (e == hipSuccess)
-      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &nb, dtype == SK_F16 ? dev::hgemm_kernel<SK_F16> : dev::hgemm_kernel<SK_BF16>, c.threads,
-          c.lds_bytes);
+    const void *f = hgemm_entry(dtype, inst);
+    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
+    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, c.threads, c.lds_bytes);
   }
   *blocks_per_cu = nb;
   return (int)e;

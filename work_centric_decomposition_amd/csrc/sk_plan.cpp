@@ -169,12 +169,12 @@ static double aligned_small(int64_t t, int64_t ipt, int slots, float a, float b,
 }
 
 struct DecisionKey {
-  int dtype;
+  int dtype, inst;
   int64_t tiles_m, tiles_n, ipt;
   int slots, schedule, forced_grid, min_waves;
   float ma, mb, mc, md;
   bool operator==(const DecisionKey &o) const {
-    return dtype == o.dtype && tiles_m == o.tiles_m && tiles_n == o.tiles_n && ipt == o.ipt && slots == o.slots &&
+    return dtype == o.dtype && inst == o.inst && tiles_m == o.tiles_m && tiles_n == o.tiles_n && ipt == o.ipt && slots == o.slots &&
            schedule == o.schedule && forced_grid == o.forced_grid && min_waves == o.min_waves && ma == o.ma &&
            mb == o.mb && mc == o.mc && md == o.md;
   }
@@ -207,18 +207,12 @@ static void store_decision(const DecisionKey &k, const Plan &P) {
   e = Decision{k, P.schedule, P.grid, P.phase_div, P.blocks, P.group_rows, P.sk_tiles, P.sk_q, P.sk_r, true};
 }
 
-int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
+// The plan of one tile instance (arguments already validated).
+static int plan_inst(const sk_gemm_desc &d, const sk_options &o, int inst, int slots, Plan &P) {
   std::memset(&P, 0, sizeof(P));
-  if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
-  if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
-  if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
-  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
-  if (o.forced_grid < 0 || slots <= 0) return SK_ERR_INVALID_ARG;
-  // 32-bit indices inside the kernels
-  if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
   P.m = d.m; P.n = d.n; P.k = d.k;
   P.dtype = d.dtype; P.layout = d.layout;
-  P.cfg = tile_cfg(d.dtype);
+  P.cfg = tile_cfg(d.dtype, inst);
   P.slots = slots;
   const TileCfg &c = P.cfg;
   P.tiles_m = cdiv(d.m, c.bm);
@@ -245,7 +239,7 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
   // The schedule depends only on these integers and the options; a small
   // cache keeps its search (a few microseconds below a wave) off the launch
   // path of repeated shapes.
-  const DecisionKey key{d.dtype, P.tiles_m, P.tiles_n, P.ipt, slots, o.schedule, o.forced_grid, min_waves,
+  const DecisionKey key{d.dtype, inst, P.tiles_m, P.tiles_n, P.ipt, slots, o.schedule, o.forced_grid, min_waves,
                         ma, mb, mc, md};
   if (lookup_decision(key, P)) return SK_OK;
 
@@ -330,14 +324,103 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, int slots, Plan &P) {
     if (o.schedule != SK_SCHED_AUTO) return SK_ERR_UNSUPPORTED;
     sk_options o2 = o;
     o2.schedule = SK_SCHED_SK_HYBRID2;
-    int rc = make_plan(d, o2, slots, P);
+    int rc = plan_inst(d, o2, inst, slots, P);
     if (rc == SK_ERR_UNSUPPORTED) {
       o2.schedule = SK_SCHED_DP;
-      rc = make_plan(d, o2, slots, P);
+      rc = plan_inst(d, o2, inst, slots, P);
     }
     if (rc != SK_OK) return rc;
   }
   store_decision(key, P);
+  return SK_OK;
+}
+
+// Predicted time of a plan in microseconds, by the runtime model: the fixed
+// cost, the workgroup with the most iterations (its Stream-K range plus its
+// data-parallel tiles), and the exchanges on the critical path of the most
+// divided tile (s - 1 partials added in a row by the page's owner, or
+// ceil(log2 s) store/add levels in the tree); constants per tile instance.
+double plan_cost_us(const Plan &P) {
+  const TileCfg &c = P.cfg;
+  if (P.tiles == 0 || P.ipt == 0) return 0.0;
+  double work = (double)cdiv(P.dp_tiles, std::max(P.grid, 1)) * (double)P.ipt;
+  int64_t pieces = 1;
+  if (P.sk_tiles > 0) {
+    work += P.phase_div > 0 ? (double)cdiv((int64_t)P.blocks * P.ipt, P.phase_div)
+                            : (double)(P.sk_q + (P.sk_r > 0 ? 1 : 0));
+    const Sched S = P.sched();
+    for (int32_t L = 0; L < S.sk_tiles; ++L) {
+      const int32_t ts = L * S.ipt;
+      pieces = std::max<int64_t>(pieces, sched_owner_of(S, ts + S.ipt - 1) - sched_owner_of(S, ts) + 1);
+    }
+  }
+  double levels = 0.0;
+  if (pieces > 1) {
+    if (P.phase_div > 0) {
+      int l = 0;
+      while (((int64_t)1 << l) < pieces) ++l;
+      levels = l;
+    } else {
+      levels = (double)(pieces - 1);
+    }
+  }
+  return c.fixed_us + c.iter_us * work + c.level_us * levels;
+}
+
+struct InstKey {
+  int dtype;
+  int64_t tm, tn, ipt;  // 128-row and 128-column tile counts, k-iterations
+  int slots0, slots1, schedule, forced_grid, min_waves;
+  float ma, mb, mc, md;
+  bool operator==(const InstKey &o) const {
+    return dtype == o.dtype && tm == o.tm && tn == o.tn && ipt == o.ipt && slots0 == o.slots0 &&
+           slots1 == o.slots1 && schedule == o.schedule && forced_grid == o.forced_grid &&
+           min_waves == o.min_waves && ma == o.ma && mb == o.mb && mc == o.mc && md == o.md;
+  }
+};
+static std::mutex g_inst_mu;
+static std::pair<InstKey, int> g_inst[64];
+static bool g_inst_valid[64];
+static unsigned g_inst_next = 0;
+
+int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &P) {
+  std::memset(&P, 0, sizeof(P));
+  if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
+  if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
+  if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
+  if (o.tile < SK_TILE_AUTO || o.tile > SK_TILE_SMALL) return SK_ERR_INVALID_ARG;
+  if (o.forced_grid < 0 || slots[0] <= 0 || slots[1] <= 0) return SK_ERR_INVALID_ARG;
+  // 32-bit indices inside the kernels
+  if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
+  if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE) return plan_inst(d, o, 0, slots[0], P);
+  if (o.tile == SK_TILE_SMALL) return plan_inst(d, o, 1, slots[1], P);
+  // AUTO: whichever instance the model predicts faster (cached per shape
+  // class); measured on the fp16 shape sweep, the small tile wins on most
+  // shapes below one wave of large tiles and on short-k shapes up to about
+  // two waves, the large one on long-k and large shapes
+  int rc = plan_inst(d, o, 0, slots[0], P);
+  if (rc != SK_OK || P.tiles == 0 || P.ipt == 0) return rc;
+  const InstKey key{d.dtype, cdiv(d.m, 128), cdiv(d.n, 128), P.ipt, slots[0], slots[1], o.schedule,
+                    o.forced_grid, o.hybrid_min_waves, o.model_a, o.model_b, o.model_c, o.model_d};
+  int inst = -1;
+  {
+    std::lock_guard<std::mutex> lock(g_inst_mu);
+    for (int i = 0; i < 64; ++i)
+      if (g_inst_valid[i] && g_inst[i].first == key) inst = g_inst[i].second;
+  }
+  if (inst == 0) return SK_OK;
+  Plan Q;
+  rc = plan_inst(d, o, 1, slots[1], Q);
+  if (rc != SK_OK) return SK_OK;  // the large-tile plan stands
+  if (inst < 0) {
+    inst = plan_cost_us(Q) < plan_cost_us(P) ? 1 : 0;
+    std::lock_guard<std::mutex> lock(g_inst_mu);
+    const unsigned i = g_inst_next++ % 64;
+    g_inst[i] = {key, inst};
+    g_inst_valid[i] = true;
+  }
+  if (inst == 1) P = Q;
   return SK_OK;
 }
 
