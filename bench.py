@@ -45,11 +45,11 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "d53683e247cde8b9",
+TRAFFIC = {"kernel_hash": "05d867e4ab7a9fee",
            # mean over the six launches of one step (1024^3 ... 6144^3)
-           "sgemm-sweep": 1166177879,
+           "sgemm-sweep": 966024056,
            # fp16 8192^3 launch
-           "hgemm-8192": 1823461662}
+           "hgemm-8192": 1769573938}
 
 
 def kernel_hash():
@@ -101,11 +101,12 @@ COMPARE_SHAPES = [(9392, 2976, 14144), (4352, 4096, 4096), (3808, 4624, 720), (2
 
 
 def compare_schedules(torch, sk, S, steps):
-    """Each shape of COMPARE_SHAPES (fp16, A row-major, B column-major) under
-    the data-parallel schedule, the page's two-tile hybrid (basic Stream-K
-    below one wave) and AUTO, in that order; `steps` timed launches each after
-    one warm-up (with steps == 1 the launches are easy to pick out of a
-    counter trace: dispatches come in pairs per schedule)."""
+    """Each shape of COMPARE_SHAPES (fp16, A row-major, B column-major) on the
+    256x256 tile under the data-parallel schedule, the page's two-tile hybrid
+    (basic Stream-K below one wave) and the XCD-aware split, then AUTO with
+    its own tile choice, in that order; `steps` timed launches each after one
+    warm-up (with steps == 1 the launches are easy to pick out of a counter
+    trace: dispatches come in pairs per leg)."""
     out = []
     g = torch.Generator(device="cuda")
     g.manual_seed(S.SEED_SWEEP)
@@ -114,10 +115,12 @@ def compare_schedules(torch, sk, S, steps):
         B = torch.randn(k * n, generator=g, device="cuda").to(torch.float16)
         C = torch.empty(m * n, device="cuda", dtype=torch.float16)
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
-        t = sk.plan_query(d).tiles
-        page = sk.SCHED_SK_HYBRID2 if t >= sk.plan_query(d).slots else sk.SCHED_SK_BASIC
-        for name, opts in (("dp", sk.make_options(schedule=sk.SCHED_DP)),
-                           ("page", sk.make_options(schedule=page)), ("auto", sk.make_options())):
+        large = sk.TILE_LARGE
+        pl = sk.plan_query(d, sk.make_options(tile=large))
+        page = sk.SCHED_SK_HYBRID2 if pl.tiles >= pl.slots else sk.SCHED_SK_BASIC
+        for name, opts in (("dp", sk.make_options(schedule=sk.SCHED_DP, tile=large)),
+                           ("page", sk.make_options(schedule=page, tile=large)),
+                           ("auto", sk.make_options(tile=large)), ("auto_tile", sk.make_options())):
             sk.gemm_ex(d, opts)
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
@@ -127,7 +130,7 @@ def compare_schedules(torch, sk, S, steps):
             torch.cuda.synchronize()
             us = e0.elapsed_time(e1) / steps * 1e3
             p = sk.plan_query(d, opts)
-            out.append({"shape": [m, n, k], "schedule": name, "resolved": p.schedule, "grid": p.grid,
+            out.append({"shape": [m, n, k], "schedule": name, "resolved": p.schedule, "tile": p.tile_m, "grid": p.grid,
                         "sk_tiles": p.sk_tiles, "phase_div": p.phase_div, "us": round(us, 1),
                         "tflops": round(2.0 * m * n * k / us / 1e6, 1)})
         del A, B, C

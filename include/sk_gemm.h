@@ -149,7 +149,8 @@ typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2 } sk_tile;
  * forced grid, ABFT off, default model constants, AUTO tile instance. */
 typedef struct {
   int32_t schedule;         /* sk_schedule */
-  int32_t forced_grid;      /* > 0: basic Stream-K with exactly this many workgroups */
+  int32_t forced_grid;      /* > 0: basic Stream-K with exactly this many workgroups (on the
+                             * large fp16/bf16 tile unless `tile` names one) */
   int32_t abft;             /* nonzero: ABFT mode (checksums, verify, correct); SK_F32 only */
   int32_t hybrid_min_waves; /* full waves needed before the two-tile hybrid is used (default 1) */
   const sk_fault *faults;   /* device array of injected faults (testing), or NULL */

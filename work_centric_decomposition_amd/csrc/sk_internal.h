@@ -24,11 +24,14 @@ struct TileCfg {
   // default grid-size model constants, in units of one MAC iteration
   float a, b, c, d;
   int inst;          // HGEMM tile instance (0: 256 x 256, 1: 128 x 128)
-  // the tile-instance choice, microseconds: fixed cost of a launch (start,
-  // first loads, epilogue), one iteration of the busiest workgroup, one
-  // level of partial exchange (least-squares fit to the fp16 shape sweep
-  // below one wave of large tiles, every workgroup busy)
-  float fixed_us, iter_us, level_us;
+  // the tile-instance choice, microseconds (least-squares fit, relative
+  // error, to the fp16 shape sweep timed on each instance): fixed cost of a
+  // launch (start, first loads, epilogue), one level of partial exchange,
+  // and one iteration of the busiest workgroup, which depends on how busy
+  // the chip is: with one workgroup per CU, iter_a + iter_b * grid / slots
+  // (a partly idle chip runs at a higher clock); with two, iter_a while
+  // every workgroup has a CU to itself and iter_b once two share one
+  float fixed_us, level_us, iter_a_us, iter_b_us;
 };
 
 // Tile instances.  fp32: 128 x 128 x 32, 4 waves, two workgroups per CU.
@@ -38,14 +41,14 @@ struct TileCfg {
 // the instance.
 inline TileCfg tile_cfg(int dtype, int inst = 0) {
   // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
-  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f, 0, 8.3f, 2.f, 3.3f};
+  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f, 0, 8.3f, 3.3f, 2.f, 2.f};
   // 128 x 128 fp16: a 64 KiB partial against a quarter of the large tile's
   // iteration work
-  if (inst == 1) return TileCfg{128, 128, 64, 256, 2, 2 * 2 * 128 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 1, 3.55f, 1.27f, 2.95f};
+  if (inst == 1) return TileCfg{128, 128, 64, 256, 2, 2 * 2 * 128 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 1, 9.16f, 3.39f, 0.413f, 1.2f};
   // model constants fitted to the fp16 shape sweep on MI355X: a 256 x 256
   // fp32 partial (256 KiB) costs about five 64-deep iterations to write and
   // four to read and add when every workgroup exchanges one at the same time
-  return TileCfg{256, 256, 64, 512, 1, 2 * 2 * 256 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 0, 6.7f, 1.83f, 8.3f};
+  return TileCfg{256, 256, 64, 512, 1, 2 * 2 * 256 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 0, 13.8f, 8.45f, 0.745f, 1.153f};
 }
 
 // How the kernels walk the work (shared by the kernels and the host's

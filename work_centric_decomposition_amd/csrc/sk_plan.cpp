@@ -364,7 +364,9 @@ double plan_cost_us(const Plan &P) {
       levels = (double)(pieces - 1);
     }
   }
-  return c.fixed_us + c.iter_us * work + c.level_us * levels;
+  const double iter = c.occupancy == 1 ? c.iter_a_us + c.iter_b_us * (double)P.grid / P.slots
+                                       : (P.grid * c.occupancy <= P.slots ? c.iter_a_us : c.iter_b_us);
+  return c.fixed_us + iter * work + c.level_us * levels;
 }
 
 struct InstKey {
@@ -393,7 +395,9 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Pl
   if (o.forced_grid < 0 || slots[0] <= 0 || slots[1] <= 0) return SK_ERR_INVALID_ARG;
   // 32-bit indices inside the kernels
   if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
-  if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE) return plan_inst(d, o, 0, slots[0], P);
+  // a forced grid is a count of large-tile workgroups unless a tile is given
+  if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE || (o.tile == SK_TILE_AUTO && o.forced_grid > 0))
+    return plan_inst(d, o, 0, slots[0], P);
   if (o.tile == SK_TILE_SMALL) return plan_inst(d, o, 1, slots[1], P);
   // AUTO: whichever instance the model predicts faster (cached per shape
   // class); measured on the fp16 shape sweep, the small tile wins on most
