@@ -467,6 +467,7 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5, tile_legs=False):
                          util_auto=tmin / res["auto"], util_page=tmin / res["page"],
                          util_dp=tmin / res["dp"],
                          dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak),
+                         tmin_us=tmin * 1e6,
                          host_auto_us=res["host_auto"] * 1e6, host_dp_us=res["host_dp"] * 1e6,
                          tile_auto=p.tile_m,
                          **({"t_large_us": res["large"] * 1e6, "t_small_us": res["small"] * 1e6} if tile_legs else {})))
@@ -501,6 +502,8 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5, tile_legs=False):
                                    "cv": round(cv([r[f"util_{name}"] for r in sel]), 4)}
             out[f"tflops_{name}_mean"] = round(statistics.fmean(r[f"tflops_{name}"] for r in sel), 2)
         out["dp_quant_eff_mean"] = round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)
+        u = sorted(r["util_auto"] for r in sel)
+        out["util_auto_p5_p95"] = [round(u[int(0.05 * (len(u) - 1))], 4), round(u[int(0.95 * (len(u) - 1))], 4)]
         # host time of one sk_gemm call from Python (plan + launch)
         out["host_launch_us_median"] = {name: round(statistics.median(r[f"host_{name}_us"] for r in sel), 2)
                                         for name in ("auto", "dp")}
@@ -509,6 +512,10 @@ def shape_sweep(torch, sk, S, count, out_path, reps=5, tile_legs=False):
     return {"sweep": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0",
             "all": summary(rows),
             "compute_bound": summary([r for r in rows if not r["mem_bound"]]),
+            # shapes whose roofline time is at least 100 us: the fixed cost of
+            # a launch (8-12 us) no longer dominates them
+            "compute_bound_tmin_100us": summary([r for r in rows if not r["mem_bound"]
+                                                 and r["tmin_us"] >= 100.0]),
             "memory_bound": summary([r for r in rows if r["mem_bound"]]),
             "random": summary([r for r in rows if r["kind"] == "random"]),
             "skinny": summary([r for r in rows if r["kind"] == "skinny"]),
