@@ -33,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_TFLOPS = {"f32": 157.3, "f16": 2516.6, "bf16": 2516.6}
+PEAK_HBM_GBS = 8000.0
 METRIC = "GEMM TFLOPS + % of MI355X MFMA peak (fp32, fp16) over shape sweep"
 SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # HBM bytes per dispatch measured with rocprofv3 counters (FETCH_SIZE and
@@ -79,6 +80,8 @@ def parse():
     p.add_argument("--sweep-out", default="", help="CSV file for the per-shape sweep results")
     p.add_argument("--sweep-tiles", action="store_true",
                    help="also time each sweep shape with each fp16 tile instance (AUTO schedule)")
+    p.add_argument("--gemv", action="store_true",
+                   help="time the matrix-vector products only (m == 1 or n == 1 shapes)")
     p.add_argument("--compare-schedules", action="store_true",
                    help="time AUTO, the page's schedules and data-parallel on a few fp16 shapes "
                         "(one launch each with --steps 1, e.g. under rocprofv3 --pmc)")
@@ -159,6 +162,48 @@ def library_gemm(torch, sk, S, steps, warmup):
         out.append({"library_gemm": "torch.mm", "dtype": name, "shape": [n, n, n], "ms": round(ms, 4),
                     "tflops": round(2.0 * n ** 3 / (ms * 1e-3) / 1e12, 1)})
         del h, a, b
+    return out
+
+
+GEMV_SHAPES = [(1, 16384, 16384, "f16"), (16384, 1, 16384, "f16"), (1, 16384, 16384, "f32"),
+               (1, 1, 1 << 24, "f32")]
+
+
+def gemv_leg(torch, sk, S, reps=20):
+    """Matrix-vector products through the even split of dot products (AUTO
+    picks it for m == 1 or n == 1): per-launch time queued behind a spin
+    kernel, bytes = the matrix, the vector and the output once each, against
+    the 8 TB/s HBM peak; torch.matmul on the same operands for context."""
+    import statistics
+    dts = {"f16": (sk.F16, torch.float16, 2), "f32": (sk.F32, torch.float32, 4)}
+    spin = _spin_cycles(torch, 300e-6)
+    out = []
+    for (m, n, k, name) in GEMV_SHAPES:
+        dt, tdt, es = dts[name]
+        g = torch.Generator(device="cuda").manual_seed(m + n + k)
+        A = (torch.rand(m * k, device="cuda", generator=g) * 2 - 1).to(tdt)
+        B = (torch.rand(k * n, device="cuda", generator=g) * 2 - 1).to(tdt)
+        C = torch.zeros(m * n, device="cuda", dtype=tdt)
+        d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, dt, sk.A_ROW_B_COL)
+        p = sk.plan_query(d)
+        opts = sk.make_options()
+        us = min(_gpu_time_us(torch, sk, d, opts, spin, reps) for _ in range(3))
+        Am, Bm = A.view(m, k), B.view(n, k)
+        torch.matmul(Am, Bm.t())
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+        torch.cuda._sleep(spin)
+        for e0, e1 in ev:
+            e0.record()
+            torch.matmul(Am, Bm.t())
+            e1.record()
+        torch.cuda.synchronize()
+        lib_us = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3
+        by = es * (m * k + k * n + m * n)
+        out.append({"shape": [m, n, k], "dtype": name, "schedule": int(p.schedule), "chunks": int(p.sk_blocks),
+                    "grid": int(p.grid), "us": round(us, 2), "GB_s": round(by / us / 1e3, 1),
+                    "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4), "torch_matmul_us": round(lib_us, 2)})
+        del A, B, C
     return out
 
 
@@ -578,6 +623,9 @@ def main():
         for r in library_gemm(torch, sk, S, args.steps, args.warmup):
             print(json.dumps(r), flush=True)
         return
+    if args.gemv:
+        print(json.dumps(gemv_leg(torch, sk, S)), flush=True)
+        return
     if args.compare_schedules:
         for r in compare_schedules(torch, sk, S, args.steps):
             print(json.dumps(r), flush=True)
@@ -651,6 +699,7 @@ def main():
         line["cpu_baseline"] = cpu_baseline(S)
     if not args.no_extra:
         line["abft"] = abft_overhead(torch, sk, S)
+        line["gemv"] = gemv_leg(torch, sk, S)
     for wl, r in results.items():
         if wl == args.workload:
             continue

@@ -77,16 +77,29 @@ typedef enum {
  * the A and B slices they read in that XCD's L2), and data-parallel tiles are
  * dealt in compact per-XCD blocks.  With no leftover tiles it is
  * data-parallel in that XCD-aware order.
- *  SK_SCHED_AUTO      SK_SCHED_XCD_ALIGNED with the quantum and grid chosen by
- *                     the runtime model, or its data-parallel form when the
- *                     model predicts the split does not pay. */
+ *  SK_SCHED_GEMV_SPLIT matrix-vector products (m == 1 or n == 1, the matrix
+ *                     operand k-contiguous with 16-byte aligned rows, the vector
+ *                     contiguous): every output is a dot product of length k,
+ *                     and the rows x k work is split evenly over the workgroups
+ *                     in equal k-chunks (the KBLAS page's even split of GEMV;
+ *                     Stream-K's work-centric idea at the level of dot
+ *                     products); chunk sums are added in a fixed order by a
+ *                     second kernel, so results are reproducible.  Chosen
+ *                     explicitly, it returns SK_ERR_UNSUPPORTED for other
+ *                     shapes or operand layouts.
+ *  SK_SCHED_AUTO      SK_SCHED_GEMV_SPLIT for eligible matrix-vector shapes
+ *                     (with default tile, grid and ABFT options); otherwise
+ *                     SK_SCHED_XCD_ALIGNED with the tile instance, quantum and
+ *                     grid chosen by the runtime model, or its data-parallel
+ *                     form when the model predicts the split does not pay. */
 typedef enum {
   SK_SCHED_AUTO = 0,
   SK_SCHED_DP = 1,
   SK_SCHED_SK_BASIC = 2,
   SK_SCHED_SK_HYBRID2 = 3,
   SK_SCHED_SK_HYBRID1 = 4,
-  SK_SCHED_XCD_ALIGNED = 5
+  SK_SCHED_XCD_ALIGNED = 5,
+  SK_SCHED_GEMV_SPLIT = 6
 } sk_schedule;
 
 /* One GEMM. */
@@ -164,7 +177,11 @@ typedef struct {
 } sk_options;
 
 /* Plan of one call, for inspection (host only, needs no GPU when
- * sk_plan_query is given an explicit slot count). */
+ * sk_plan_query is given an explicit slot count).  For SK_SCHED_GEMV_SPLIT:
+ * tiles = the number of dot products (m or n), tile_k = the k-chunk length
+ * in elements, sk_blocks = chunks per dot product, iters_per_tile = 1,
+ * grid = workgroups of 256 threads; the tile fields that describe GEMM tiles
+ * are 0, and sk_plan_segments lists no segments. */
 typedef struct {
   int32_t tile_m, tile_n, tile_k; /* BLK_M, BLK_N, BLK_K of the kernel */
   int32_t slots;                  /* p: workgroups resident at once */

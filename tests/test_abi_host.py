@@ -367,6 +367,56 @@ def test_auto_tile_instance():
         sk.plan_query(_desc(512, 512, 512), sk.make_options(tile=3), 256)
 
 
+@pytest.mark.parametrize("dtype", [sk.F32, sk.F16, sk.BF16])
+@pytest.mark.parametrize("m,n,k", [(1, 16384, 16384), (16384, 1, 16384), (1, 1, 1 << 24),
+                                   (3, 1, 100003), (1, 5000, 7), (1, 300, 4097)])
+def test_matrix_vector_split(dtype, m, n, k):
+    """AUTO sends m == 1 or n == 1 to the even split of dot products: the
+    chunks are whole 16-byte pieces, S chunks cover k exactly (the last one
+    not empty), and there are enough (row, chunk) tasks for every CU."""
+    vec = 4 if dtype == sk.F32 else 8
+    slots = 512 if dtype == sk.F32 else 256
+    for layout in ([sk.A_ROW_B_COL, sk.A_COL_B_COL] if m == 1 else [sk.A_ROW_B_COL, sk.A_ROW_B_ROW]):
+        kp = -(-k // vec) * vec  # rows padded to 16 bytes
+        lda = kp if layout in (0, 1) else 1
+        ldb = kp if layout in (1, 3) else 1
+        d = sk.make_desc(m, n, k, 1.0, 1 << 20, lda, 1 << 21, ldb, 0.0, 1 << 22, n, dtype, layout)
+        p = sk.plan_query(d, None, slots)
+        assert p.schedule == sk.SCHED_GEMV_SPLIT
+        rows, S, chunk = p.tiles, p.sk_blocks, p.tile_k
+        assert rows == (n if m == 1 else m) and p.total_iters == rows * S
+        assert chunk % vec == 0 and S * chunk >= k > (S - 1) * chunk
+        assert chunk >= min(k, 4 * 64 * vec) - (vec - 1) or S == 1
+        assert rows * S >= min(32 * 256, rows * max(1, k // (4 * 64 * vec)))
+        assert 1 <= p.grid <= 8 * 256
+        assert sk.plan_segments(p, 0) == []
+        assert sk.plan_query(d, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT), slots).schedule == \
+            sk.SCHED_GEMV_SPLIT
+
+
+def test_matrix_vector_fallbacks():
+    """Shapes or options the matrix-vector path does not take go to the
+    tiled schedules under AUTO, and are refused under an explicit request."""
+    gemv = sk.make_options(schedule=sk.SCHED_GEMV_SPLIT)
+    cases = [
+        sk.make_desc(2, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),  # m = 2
+        sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 0),  # B n-contiguous
+        sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 65, 0.0, 1 << 22, 64, sk.F16, 1),  # rows unaligned
+        sk.make_desc(1, 64, 64, 1.0, (1 << 20) + 2, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),
+        sk.make_desc(64, 1, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 0),  # ldb 64
+        sk.make_desc(64, 1, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 2),  # A m-contiguous
+    ]
+    for d in cases:
+        assert sk.plan_query(d, None, 256).schedule != sk.SCHED_GEMV_SPLIT
+        with pytest.raises(sk.SkError):
+            sk.plan_query(d, gemv, 256)
+    d = sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F32, 1)
+    assert sk.plan_query(d, None, 512).schedule == sk.SCHED_GEMV_SPLIT
+    for o in [sk.make_options(tile=sk.TILE_LARGE), sk.make_options(forced_grid=4),
+              sk.make_options(schedule=sk.SCHED_DP)]:
+        assert sk.plan_query(d, o, 512).schedule != sk.SCHED_GEMV_SPLIT
+
+
 def test_two_tile_hybrid_owner_has_one_peer():
     for t_m, t_n in [(17, 17), (23, 12), (16, 17)]:
         d = _desc(256 * t_m, 256 * t_n, 4096, sk.F16)
@@ -430,7 +480,7 @@ def test_invalid_arguments_are_rejected_before_any_gpu_call():
                       check=False) == sk.ERR_INVALID_ARG
     assert sk.gemm(8, 8, 8, 1.0, 16, 7, 16, 8, 0.0, 16, 8, sk.F32, 0, stream=0,
                    check=False) == sk.ERR_INVALID_ARG  # lda < k
-    assert sk.gemm_ex(d, sk.make_options(schedule=sk.SCHED_XCD_ALIGNED + 1), stream=0,
+    assert sk.gemm_ex(d, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT + 1), stream=0,
                       check=False) == sk.ERR_INVALID_ARG
     assert sk.plan_query(d, sk.make_options(schedule=sk.SCHED_XCD_ALIGNED), 256).schedule == \
         sk.SCHED_XCD_ALIGNED

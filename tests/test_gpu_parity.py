@@ -301,3 +301,72 @@ def test_sweep_shapes_auto_and_dp_against_oracle():
             g = decode(got[rows, cols], sk.F16)
             assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F16], (kind, m, n, k)
             assert c.freivalds(got) <= TOL[sk.F16]
+
+
+# ------------------------------------------------ matrix-vector products
+
+def _gemv_cases(dtype):
+    """(m, n, k, layout, pad, alpha, beta): pad makes the matrix rows 16-byte
+    aligned for a ragged k (and strides C for n == 1)."""
+    vec = 4 if dtype == sk.F32 else 8
+    out = []
+    for k in (1, 5, 8, 64, 1000, 4097, 65539):
+        pad = (-k) % vec
+        for r in ((1, 7, 300, 4099) if k <= 4097 else (1, 7, 300)):
+            out.append((1, r, k, sk.A_ROW_B_COL, pad, 1.0, 0.0))
+            out.append((r, 1, k, sk.A_ROW_B_COL, pad + vec, 0.5, -1.5))
+    for k in (8, 2048, 30000 - 30000 % vec):
+        out.append((1, 513, k, sk.A_COL_B_COL, 0, 1.0, 1.0))
+        out.append((513, 1, k, sk.A_ROW_B_ROW, 0, -2.0, 0.25))
+    return out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_matrix_vector_split_against_oracle(dtype):
+    """m == 1 and n == 1 products go to the even split of dot products (one
+    chunk or many, k tails, strided C, alpha/beta, all operand orders the
+    path takes) and match the oracle; repeated calls are bitwise equal."""
+    for (m, n, k, layout, pad, alpha, beta) in _gemv_cases(dtype):
+        _say("case gemv", dtype, m, n, k, layout, pad)
+        c = Case(m, n, k, dtype, layout, 11 + m + 3 * n + k, pad=pad)
+        d = sk.make_desc(m, n, k, alpha, c.dA, c.lda, c.dB, c.ldb, beta, c.dC, c.ldc, dtype, layout)
+        assert sk.plan_query(d).schedule == sk.SCHED_GEMV_SPLIT, (m, n, k, layout)
+        got = c.run(alpha, beta)
+        ref, bound = c.reference(alpha, beta)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
+        c.reset_c()
+        again = c.run(alpha, beta, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT))
+        assert np.array_equal(got.view(np.uint8), again.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_matrix_vector_fallback_and_beta_zero(dtype):
+    """Unaligned rows fall back to the tiled kernels (AUTO) or are refused
+    (explicit split); beta == 0 never reads C."""
+    c = Case(1, 300, 1001, dtype, sk.A_ROW_B_COL, 3, pad=2 if dtype == sk.F32 else 1)
+    d = sk.make_desc(1, 300, 1001, 1.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc, dtype,
+                     sk.A_ROW_B_COL)
+    assert sk.plan_query(d).schedule != sk.SCHED_GEMV_SPLIT
+    assert sk.gemm_ex(d, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT), check=False) == \
+        sk.ERR_UNSUPPORTED
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+    c = Case(5000, 1, 4096, dtype, sk.A_ROW_B_COL, 4)
+    c.dC.fill_(float("nan"))
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+
+
+@pytest.mark.parametrize("dtype,m,n,k", [(sk.F32, 1, 16384, 4096), (sk.F16, 16384, 1, 4096),
+                                         (sk.BF16, 1, 4096, 16384)])
+def test_matrix_vector_large(dtype, m, n, k):
+    """A 16384 x 4096 matrix against a vector (one chunk per dot product, or
+    two when the rows are fewer and longer), against the oracle on every
+    output."""
+    _say("case gemv large", dtype, m, n, k)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 21 + m, with_c=False)
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]

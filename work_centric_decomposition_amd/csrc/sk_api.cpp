@@ -145,7 +145,7 @@ int validate(const sk_gemm_desc &d, const sk_options &o, const sk_abft_report *r
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
   if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
   if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
-  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_GEMV_SPLIT) return SK_ERR_INVALID_ARG;
   if (o.forced_grid < 0 || o.hybrid_min_waves < 0 || o.n_faults < 0 || o.spin_limit_us < 0)
     return SK_ERR_INVALID_ARG;
   if (o.n_faults > 0 && o.faults == nullptr) return SK_ERR_INVALID_ARG;
@@ -180,6 +180,24 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   if (d.k == 0 || d.alpha == 0.f) {  // C = beta * C
     rc = launch_scale(d.dtype, d.m, d.n, d.beta, d.C, d.ldc, stream);
     return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "scale kernel");
+  }
+  // matrix-vector products: the even split of dot products
+  if (o.schedule == SK_SCHED_GEMV_SPLIT ||
+      (o.schedule == SK_SCHED_AUTO && !o.abft && o.forced_grid == 0 && o.tile == SK_TILE_AUTO)) {
+    GemvPlan g;
+    if (!o.abft && gemv_plan(d, info->cus, g)) {
+      float *part = nullptr;
+      if (g.S > 1) {
+        Workspace *ws = nullptr;
+        rc = get_workspace(dev, stream, 1, (size_t)(g.S * g.R) * sizeof(float), &ws);
+        if (rc != SK_OK) return rc;
+        part = ws->partials;
+      }
+      rc = launch_gemv(d.dtype, g.M, g.ldm, g.v, g.R, g.K, g.chunk, g.S, g.grid, part, g.out, g.ldo, d.alpha,
+                       d.beta, stream);
+      return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "matrix-vector kernel launch");
+    }
+    if (o.schedule == SK_SCHED_GEMV_SPLIT) return SK_ERR_UNSUPPORTED;
   }
   Plan P;
   const int slots[2] = {o.abft && d.dtype == SK_F32 ? info->slots_abft : info->slots[d.dtype],
@@ -303,6 +321,22 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       slots2 = desc->dtype == SK_F32 ? 1 : info->slots_small[desc->dtype];
     }
     if (slots2 == 0) slots2 = 2 * slots;
+    GemvPlan g;
+    if ((o.schedule == SK_SCHED_GEMV_SPLIT ||
+         (o.schedule == SK_SCHED_AUTO && !o.abft && o.forced_grid == 0 && o.tile == SK_TILE_AUTO)) &&
+        desc->dtype >= 0 && desc->dtype <= 2 && desc->layout >= 0 && desc->layout <= 3 && !o.abft &&
+        desc->m >= 0 && desc->n >= 0 && gemv_plan(*desc, desc->dtype == SK_F32 ? slots / 2 : slots, g)) {
+      std::memset(out, 0, sizeof(*out));
+      out->schedule = SK_SCHED_GEMV_SPLIT;
+      out->slots = slots;
+      out->grid = g.grid;
+      out->tile_k = (int32_t)g.chunk;
+      out->tiles = g.R;
+      out->iters_per_tile = 1;
+      out->total_iters = g.R * g.S;
+      out->sk_blocks = (int32_t)g.S;
+      return SK_OK;
+    }
     const int both[2] = {slots, slots2};
     Plan P;
     int rc = make_plan(*desc, o, both, P);

@@ -265,6 +265,24 @@ struct Plan {
   }
 };
 
+// Matrix-vector path (SK_SCHED_GEMV_SPLIT): out[r] = alpha * (M row r) . v +
+// beta * out[r * ldo] for r < R, each row split in S chunks of `chunk`
+// elements, `grid` workgroups of 256 threads.
+struct GemvPlan {
+  const void *M, *v;
+  void *out;
+  int64_t ldm, ldo, R, K, chunk, S;
+  int grid;
+};
+// Fills `g` and returns true if the call is a matrix-vector product the
+// path takes (m == 1 or n == 1, the matrix operand k-contiguous with
+// 16-byte aligned rows, the vector contiguous and 16-byte aligned); cus:
+// compute units.
+bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g);
+int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
+                int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
+                hipStream_t stream);
+
 // Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots:
 // resident workgroups of the large (or fp32) and of the small-tile instance.
 int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &plan);

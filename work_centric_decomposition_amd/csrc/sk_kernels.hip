@@ -245,12 +245,18 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // the block, i.e. four consecutive columns per register quad.
 // HGEMM instances: 256 x 256 tiles with 8 waves (2 x 4, 128 x 64 each;
 // one workgroup per CU) and 128 x 128 tiles with 4 waves (2 x 2, 64 x 64
-// each; two workgroups per CU) for shapes with few large tiles.
-template <int DT, int TILE>
+// each; two workgroups per CU) for shapes with few large tiles.  W = 4 with
+// 256 x 256 tiles (128 x 128 per wave, one wave per SIMD, a third fewer LDS
+// fragment reads per MFMA) also builds and gives the same bits, but one wave
+// per SIMD cannot hide its own LDS and barrier waits: about 6 % slower on
+// large squares, so it is not instantiated.
+template <int DT, int TILE, int W = (TILE == 256 ? 8 : 4)>
 struct HPolicy {
   static constexpr int ET = DT;
   static constexpr int BM = TILE, BN = TILE, BK = 64, NSTAGE = 2;
-  static constexpr int WAVES = TILE == 256 ? 8 : 4, NT = 64 * WAVES;
+  static constexpr int WAVES = W, NT = 64 * WAVES;
+  // waves per SIMD the register budget is sized for
+  static constexpr int WPE = TILE == 256 && W == 4 ? 1 : 2;
   static constexpr int SUBS = BK / 16;  // k-substeps of one iteration
   static_assert(TILE == 256 || TILE == 128, "tile");
   static constexpr int WTM = BM / 2, WTN = BN / (WAVES / 2), MB = WTM / 32, NB = WTN / 32;
@@ -508,20 +514,23 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
   if (full && a.beta == 0.f && reinterpret_cast<uintptr_t>(a.C) % 16 == 0 && a.ldc % 8 == 0) {
     // Through LDS, half of the wave's block at a time: each lane holds 4
     // consecutive columns of one row, so direct stores would touch 32 rows
-    // per instruction; read back as 8 rows x 128 contiguous bytes per
-    // instruction they cover whole cache lines.  Rows of RS = 136 bytes (34
-    // banks apart) put the 32 rows of one 8-byte LDS write on distinct banks.
-    // Each wave uses only its own region (64 rows: 8.5 KiB) and a wave's LDS
-    // accesses complete in order, so the passes need no barrier; the caller
-    // has passed a workgroup barrier since the last MAC-loop LDS read, and
-    // one at the end keeps the next tile's loads (which land in every
-    // wave's region) from overwriting rows another wave has not read yet.
+    // per instruction; read back as whole rows of the wave's block (2 WTN
+    // contiguous bytes, 64 / (WTN / 8) rows per instruction) they cover whole
+    // cache lines.  Rows of RS = 2 WTN + 8 bytes (an odd number of 8-byte
+    // bank pairs apart) put the 32 rows of one 8-byte LDS write on distinct
+    // banks.  Each wave uses only its own region (MB / 2 x 32 rows) and a
+    // wave's LDS accesses complete in order, so the passes need no barrier;
+    // the caller has passed a workgroup barrier since the last MAC-loop LDS
+    // read, and one at the end keeps the next tile's loads (which land in
+    // every wave's region) from overwriting rows another wave has not read
+    // yet.
     constexpr int RS = P::WTN * 2 + 8, HALF = P::MB / 2;
+    constexpr int LPR = P::WTN * 2 / 16, RPI = 64 / LPR;  // lanes per row, rows per read
     // per-lane bases; every other offset is a compile-time constant
     char *const wr = smem + w * (HALF * 32 * RS) + (lane & 31) * RS + 8 * (lane >> 5);
-    const char *const rd = smem + w * (HALF * 32 * RS) + (lane >> 3) * RS + (lane & 7) * 16;
-    char *cp = static_cast<char *>(a.C) + ((int64_t)(r0 + (lane >> 3)) * a.ldc + c0 + (lane & 7) * 8) * sizeof(T);
-    const int64_t step = (int64_t)8 * a.ldc * sizeof(T);
+    const char *const rd = smem + w * (HALF * 32 * RS) + (lane / LPR) * RS + (lane % LPR) * 16;
+    char *cp = static_cast<char *>(a.C) + ((int64_t)(r0 + lane / LPR) * a.ldc + c0 + (lane % LPR) * 8) * sizeof(T);
+    const int64_t step = (int64_t)RPI * a.ldc * sizeof(T);
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
@@ -533,8 +542,8 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
             Elem<P::ET>::st4(wr + mb * 32 * RS + (nb * 32 + 8 * g) * 2, 0,
                           a.alpha * P::get4(acc, ((h * HALF + mb) * P::NB + nb) * 4 + g));
 #pragma unroll
-      for (int it = 0; it < HALF * 32 / 8; ++it) {
-        *reinterpret_cast<u4_t *>(cp) = *reinterpret_cast<const u4_t *>(rd + it * 8 * RS);
+      for (int it = 0; it < HALF * 32 / RPI; ++it) {
+        *reinterpret_cast<u4_t *>(cp) = *reinterpret_cast<const u4_t *>(rd + it * RPI * RS);
         cp += step;
       }
     }
@@ -1186,7 +1195,7 @@ __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop maclo
 }
 
 template <class P>
-__global__ __launch_bounds__(P::NT, 2) void hgemm_kernel(KernelArgs a, int vec_ok) {
+__global__ __launch_bounds__(P::NT, P::WPE) void hgemm_kernel(KernelArgs a, int vec_ok) {
   run_workgroup<P>(
       a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { h_macloop_la2<P>(a, m0, n0, lb, le, acc); },
       [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
@@ -1291,6 +1300,124 @@ int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
                                     : sgemm_entry(a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
   void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
   return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
+}
+
+namespace dev {
+
+// ------------------------------------------------ matrix-vector products
+//
+// out[r] = alpha * (M row r) . v + beta * out[r] for r < R, M rows of K
+// elements at M + r * ldm (k-contiguous, 16-byte aligned rows), v
+// contiguous.  Task t = (r, s) is chunk s of row r: elements
+// [s * chunk, min((s + 1) * chunk, K)).  Each wave takes tasks t = wave,
+// wave + waves, ...; lane l multiplies 16-byte pieces l, l + 64, ... of the
+// chunk (fp32 products and sums), four pieces in flight per lane, the
+// partial sums are reduced across the wave, and the wave's lane 0 writes
+// the chunk sum to part[r * S + s] = part[t] (S > 1) or the result itself
+// (S == 1).
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_kernel(const void *M, int64_t ldm, const void *v, int64_t R,
+                                                   int64_t K, int64_t chunk, int64_t S, float *part, void *out,
+                                                   int64_t ldo, float alpha, float beta) {
+  using E = Elem<DT>;
+  using T = typename E::T;
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t tasks = R * S;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < tasks; t += waves) {
+    const int64_t r = t / S, s = t - r * S;
+    const int64_t k0 = s * chunk, k1 = k0 + chunk < K ? k0 + chunk : K;
+    const T *row = static_cast<const T *>(M) + r * ldm;
+    const T *vec = static_cast<const T *>(v);
+    float acc = 0.f;
+    // whole 16-byte pieces of this chunk (chunks start on piece boundaries)
+    const int64_t pieces = (k1 - k0) / VEC;
+    int64_t p = lane;
+    for (; p + 3 * 64 < pieces; p += 4 * 64) {
+      u4_t mv[4], vv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mv[u] = *reinterpret_cast<const u4_t *>(row + k0 + (p + u * 64) * VEC);
+        vv[u] = *reinterpret_cast<const u4_t *>(vec + k0 + (p + u * 64) * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const T *mx = reinterpret_cast<const T *>(&mv[u]);
+        const T *vx = reinterpret_cast<const T *>(&vv[u]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += (float)mx[e] * (float)vx[e];
+      }
+    }
+    for (; p < pieces; p += 64) {
+      const u4_t mv = *reinterpret_cast<const u4_t *>(row + k0 + p * VEC);
+      const u4_t vv = *reinterpret_cast<const u4_t *>(vec + k0 + p * VEC);
+      const T *mx = reinterpret_cast<const T *>(&mv);
+      const T *vx = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += (float)mx[e] * (float)vx[e];
+    }
+    // the last (K mod VEC) elements of the row, in the chunk that ends at K
+    for (int64_t kk = k0 + pieces * VEC + lane; kk < k1; kk += 64) acc += (float)row[kk] * (float)vec[kk];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) {
+      if (S > 1) {
+        part[t] = acc;
+      } else {
+        float o = alpha * acc;
+        if (beta != 0.f) o += beta * E::ld(out, r * ldo);
+        E::st(out, r * ldo, o);
+      }
+    }
+  }
+}
+
+// out[r] = alpha * sum_s part[r * S + s] + beta * out[r], one wave per row:
+// lane l adds chunks l, l + 64, ... in increasing order, then the lanes'
+// sums are combined by a fixed butterfly, so repeated calls agree bitwise.
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *part, int64_t R, int64_t S, void *out,
+                                                          int64_t ldo, float alpha, float beta) {
+  using E = Elem<DT>;
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); r < R; r += waves) {
+    float acc = 0.f;
+    for (int64_t s = lane; s < S; s += 64) acc += part[r * S + s];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) {
+      float o = alpha * acc;
+      if (beta != 0.f) o += beta * E::ld(out, r * ldo);
+      E::st(out, r * ldo, o);
+    }
+  }
+}
+
+}  // namespace dev
+
+int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
+                int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
+                hipStream_t stream) {
+  const dim3 g(grid), b(256);
+  if (dtype == SK_F32)
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_F32>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  else if (dtype == SK_F16)
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_F16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  else
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_BF16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return (int)e;
+  int64_t rb = (R + 3) / 4;
+  const dim3 rg((unsigned)(rb < 4096 ? rb : 4096));
+  if (dtype == SK_F32)
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F32>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  else if (dtype == SK_F16)
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  else
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_BF16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  return (int)hipGetLastError();
 }
 
 int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t ldc,

@@ -390,7 +390,8 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Pl
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
   if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
   if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
-  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_XCD_ALIGNED) return SK_ERR_INVALID_ARG;
+  if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_GEMV_SPLIT) return SK_ERR_INVALID_ARG;
+  if (o.schedule == SK_SCHED_GEMV_SPLIT) return SK_ERR_UNSUPPORTED;  // not a matrix-vector call
   if (o.tile < SK_TILE_AUTO || o.tile > SK_TILE_SMALL) return SK_ERR_INVALID_ARG;
   if (o.forced_grid < 0 || slots[0] <= 0 || slots[1] <= 0) return SK_ERR_INVALID_ARG;
   // 32-bit indices inside the kernels
@@ -428,6 +429,32 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Pl
   return SK_OK;
 }
 
+bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
+  if (d.k <= 0 || (d.m != 1 && d.n != 1) || cus <= 0) return false;
+  const int64_t es = d.dtype == SK_F32 ? 4 : 2, vec = 16 / es;
+  const bool ak = d.layout == SK_A_ROW_B_ROW || d.layout == SK_A_ROW_B_COL;
+  const bool bk = d.layout == SK_A_ROW_B_COL || d.layout == SK_A_COL_B_COL;
+  if (d.n == 1 && ak && (bk || d.ldb == 1 || d.k == 1)) {  // rows of A against the column B
+    g.M = d.A; g.ldm = d.lda; g.v = d.B; g.R = d.m; g.out = d.C; g.ldo = d.ldc;
+  } else if (d.m == 1 && bk && (ak || d.lda == 1 || d.k == 1)) {  // the row A against columns of B
+    g.M = d.B; g.ldm = d.ldb; g.v = d.A; g.R = d.n; g.out = d.C; g.ldo = 1;
+  } else {
+    return false;
+  }
+  if (reinterpret_cast<uintptr_t>(g.M) % 16 || reinterpret_cast<uintptr_t>(g.v) % 16) return false;
+  if (g.R > 1 && (g.ldm * es) % 16) return false;
+  g.K = d.k;
+  // enough chunks to keep every CU busy (about 32 per CU), none shorter
+  // than four 1 KiB passes of a wave
+  const int64_t piece = 64 * vec;
+  const int64_t want = cdiv((int64_t)32 * cus, g.R);
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (4 * piece)));
+  g.chunk = cdiv(cdiv(g.K, S), vec) * vec;
+  g.S = cdiv(g.K, g.chunk);
+  g.grid = (int)std::min<int64_t>(cdiv(g.R * g.S, 4), (int64_t)8 * cus);
+  return true;
+}
+
 int plan_max_peers(const Plan &P) {
   if (P.sk_tiles <= 0) return 0;
   if (P.phase_div <= 0) return split_peers(P.sk_tiles, P.ipt, P.grid, nullptr);
@@ -446,6 +473,7 @@ using namespace sk;
 
 extern "C" int64_t sk_plan_segments(const sk_plan *plan, int64_t x, sk_segment *out, int64_t cap) {
   if (!plan || x < 0 || cap < 0 || (cap > 0 && !out)) return SK_ERR_INVALID_ARG;
+  if (plan->schedule == SK_SCHED_GEMV_SPLIT) return 0;
   if (x >= plan->grid) return 0;
   if (plan->iters_per_tile <= 0 || plan->tiles <= 0) return 0;
   if (plan->phase_div > 0 && plan->sk_blocks <= 0) return SK_ERR_INVALID_ARG;
