@@ -386,8 +386,8 @@ def test_matrix_vector_split(dtype, m, n, k):
         rows, S, chunk = p.tiles, p.sk_blocks, p.tile_k
         assert rows == (n if m == 1 else m) and p.total_iters == rows * S
         assert chunk % vec == 0 and S * chunk >= k > (S - 1) * chunk
-        assert chunk >= min(k, 4 * 64 * vec) - (vec - 1) or S == 1
-        assert rows * S >= min(32 * 256, rows * max(1, k // (4 * 64 * vec)))
+        assert chunk >= min(k, 8 * 64 * vec) - (vec - 1) or S == 1
+        assert rows * S >= min(32 * 256, rows * max(1, k // (8 * 64 * vec)))
         assert 1 <= p.grid <= 8 * 256
         assert sk.plan_segments(p, 0) == []
         assert sk.plan_query(d, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT), slots).schedule == \

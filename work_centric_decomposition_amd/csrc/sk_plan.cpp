@@ -445,10 +445,10 @@ bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
   if (g.R > 1 && (g.ldm * es) % 16) return false;
   g.K = d.k;
   // enough chunks to keep every CU busy (about 32 per CU), none shorter
-  // than four 1 KiB passes of a wave
+  // than eight 1 KiB passes of a wave (the kernel keeps eight in flight)
   const int64_t piece = 64 * vec;
   const int64_t want = cdiv((int64_t)32 * cus, g.R);
-  int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (4 * piece)));
+  int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (8 * piece)));
   g.chunk = cdiv(cdiv(g.K, S), vec) * vec;
   g.S = cdiv(g.K, g.chunk);
   g.grid = (int)std::min<int64_t>(cdiv(g.R * g.S, 4), (int64_t)8 * cus);
