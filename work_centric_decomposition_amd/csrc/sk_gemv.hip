@@ -1,0 +1,141 @@
+// sk_gemv.hip -- matrix-vector products (m == 1 or n == 1) for CDNA4
+// (gfx950): the even split of every dot product into chunks (the KBLAS
+// page's block-row split, section 6.2, which is Stream-K's work-centric
+// idea at the level of dot products), with the chunk sums combined in a
+// fixed order by a second kernel instead of the page's atomic additions, so
+// results are reproducible and beta is applied by the one writer of each
+// output (the page needs a separate scaling kernel first, section 6.4).
+// The path is bound by HBM bandwidth: the matrix is read once, with 16-byte
+// loads of 1 KiB per wave instruction.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sk_internal.h"
+
+namespace sk {
+namespace dev {
+
+typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+
+// Storage type of each sk_dtype; products and sums are fp32, outputs are
+// rounded once (to nearest even) by the conversion.
+template <int DT> struct GvElem;
+template <> struct GvElem<SK_F32> { using T = float; };
+template <> struct GvElem<SK_F16> { using T = _Float16; };
+template <> struct GvElem<SK_BF16> { using T = __bf16; };
+
+// out[r] = alpha * (M row r) . v + beta * out[r] for r < R, M rows of K
+// elements at M + r * ldm (k-contiguous, 16-byte aligned rows), v
+// contiguous.  Task t = (r, s) is chunk s of row r: elements
+// [s * chunk, min((s + 1) * chunk, K)).  Each wave takes tasks t = wave,
+// wave + waves, ...; lane l multiplies 16-byte pieces l, l + 64, ... of the
+// chunk (fp32 products and sums), eight pieces in flight per lane (four
+// gave 6 % less bandwidth on a 16384 x 16384 matrix), the
+// partial sums are reduced across the wave, and the wave's lane 0 writes
+// the chunk sum to part[r * S + s] = part[t] (S > 1) or the result itself
+// (S == 1).
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_kernel(const void *M, int64_t ldm, const void *v, int64_t R,
+                                                   int64_t K, int64_t chunk, int64_t S, float *part, void *out,
+                                                   int64_t ldo, float alpha, float beta) {
+  using T = typename GvElem<DT>::T;
+  constexpr int VEC = 16 / sizeof(T);
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t tasks = R * S;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < tasks; t += waves) {
+    const int64_t r = t / S, s = t - r * S;
+    const int64_t k0 = s * chunk, k1 = k0 + chunk < K ? k0 + chunk : K;
+    const T *row = static_cast<const T *>(M) + r * ldm;
+    const T *vec = static_cast<const T *>(v);
+    float acc = 0.f;
+    // whole 16-byte pieces of this chunk (chunks start on piece boundaries)
+    const int64_t pieces = (k1 - k0) / VEC;
+    int64_t p = lane;
+    for (; p + 7 * 64 < pieces; p += 8 * 64) {
+      u4_t mv[8], vv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        mv[u] = *reinterpret_cast<const u4_t *>(row + k0 + (p + u * 64) * VEC);
+        vv[u] = *reinterpret_cast<const u4_t *>(vec + k0 + (p + u * 64) * VEC);
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const T *mx = reinterpret_cast<const T *>(&mv[u]);
+        const T *vx = reinterpret_cast<const T *>(&vv[u]);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc += (float)mx[e] * (float)vx[e];
+      }
+    }
+    for (; p < pieces; p += 64) {
+      const u4_t mv = *reinterpret_cast<const u4_t *>(row + k0 + p * VEC);
+      const u4_t vv = *reinterpret_cast<const u4_t *>(vec + k0 + p * VEC);
+      const T *mx = reinterpret_cast<const T *>(&mv);
+      const T *vx = reinterpret_cast<const T *>(&vv);
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) acc += (float)mx[e] * (float)vx[e];
+    }
+    // the last (K mod VEC) elements of the row, in the chunk that ends at K
+    for (int64_t kk = k0 + pieces * VEC + lane; kk < k1; kk += 64) acc += (float)row[kk] * (float)vec[kk];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) {
+      if (S > 1) {
+        part[t] = acc;
+      } else {
+        float o = alpha * acc;
+        if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[r * ldo];
+        static_cast<T *>(out)[r * ldo] = (T)o;
+      }
+    }
+  }
+}
+
+// out[r] = alpha * sum_s part[r * S + s] + beta * out[r], one wave per row:
+// lane l adds chunks l, l + 64, ... in increasing order, then the lanes'
+// sums are combined by a fixed butterfly, so repeated calls agree bitwise.
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *part, int64_t R, int64_t S, void *out,
+                                                          int64_t ldo, float alpha, float beta) {
+  using T = typename GvElem<DT>::T;
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); r < R; r += waves) {
+    float acc = 0.f;
+    for (int64_t s = lane; s < S; s += 64) acc += part[r * S + s];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
+    if (lane == 0) {
+      float o = alpha * acc;
+      if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[r * ldo];
+      static_cast<T *>(out)[r * ldo] = (T)o;
+    }
+  }
+}
+
+}  // namespace dev
+
+int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
+                int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
+                hipStream_t stream) {
+  const dim3 g(grid), b(256);
+  if (dtype == SK_F32)
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_F32>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  else if (dtype == SK_F16)
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_F16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  else
+    hipLaunchKernelGGL(dev::gemv_kernel<SK_BF16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || S == 1) return (int)e;
+  int64_t rb = (R + 3) / 4;
+  const dim3 rg((unsigned)(rb < 4096 ? rb : 4096));
+  if (dtype == SK_F32)
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F32>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  else if (dtype == SK_F16)
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  else
+    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_BF16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+  return (int)hipGetLastError();
+}
+
+}  // namespace sk
