@@ -359,6 +359,22 @@ def test_matrix_vector_fallback_and_beta_zero(dtype):
     assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
 
 
+@pytest.mark.parametrize("dtype,m,n,k", [(sk.F32, 1, 1, 1 << 21), (sk.F32, 3, 1, 1 << 20),
+                                         (sk.BF16, 1, 2, 1 << 21)])
+def test_matrix_vector_long_dot_products(dtype, m, n, k):
+    """Few, long dot products: hundreds of chunks per output, added by a
+    workgroup per output; two calls agree bitwise."""
+    _say("case gemv long", dtype, m, n, k)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 31 + m + n, with_c=False)
+    d = sk.make_desc(m, n, k, 1.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
+    assert sk.plan_query(d).sk_blocks >= 512
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+    again = c.run(1.0, 0.0)
+    assert np.array_equal(got.view(np.uint8), again.view(np.uint8))
+
+
 @pytest.mark.parametrize("dtype,m,n,k", [(sk.F32, 1, 16384, 4096), (sk.F16, 16384, 1, 4096),
                                          (sk.BF16, 1, 4096, 16384)])
 def test_matrix_vector_large(dtype, m, n, k):

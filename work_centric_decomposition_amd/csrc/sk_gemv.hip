@@ -91,21 +91,42 @@ __global__ __launch_bounds__(256) void gemv_kernel(const void *M, int64_t ldm, c
   }
 }
 
-// out[r] = alpha * sum_s part[r * S + s] + beta * out[r], one wave per row:
-// lane l adds chunks l, l + 64, ... in increasing order, then the lanes'
-// sums are combined by a fixed butterfly, so repeated calls agree bitwise.
-template <int DT>
+// out[r] = alpha * sum_s part[r * S + s] + beta * out[r], RT threads per row
+// (one wave, or the whole workgroup when there are many chunks): thread j
+// adds chunks j, j + RT, ... in increasing order (loads issued eight at a
+// time, the sums still taken one after another), the wave's lanes are
+// combined by a fixed butterfly and, with RT = 256, the four wave sums in
+// wave order, so repeated calls agree bitwise.
+template <int DT, int RT>
 __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *part, int64_t R, int64_t S, void *out,
                                                           int64_t ldo, float alpha, float beta) {
   using T = typename GvElem<DT>::T;
-  const int lane = threadIdx.x & 63;
-  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
-  for (int64_t r = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); r < R; r += waves) {
+  static_assert(RT == 64 || RT == 256, "threads per row");
+  __shared__ float wsum[4];
+  const int j = threadIdx.x % RT, lane = threadIdx.x & 63;
+  const int64_t rows_per_block = 256 / RT;
+  for (int64_t r = (int64_t)blockIdx.x * rows_per_block + threadIdx.x / RT; r < R;
+       r += (int64_t)gridDim.x * rows_per_block) {
+    const float *pr = part + r * S;
     float acc = 0.f;
-    for (int64_t s = lane; s < S; s += 64) acc += part[r * S + s];
+    int64_t s = j;
+    for (; s + 7 * RT < S; s += 8 * RT) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = pr[s + u * RT];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; s < S; s += RT) acc += pr[s];
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off, 64);
-    if (lane == 0) {
+    if (RT == 256) {
+      if (lane == 0) wsum[threadIdx.x >> 6] = acc;
+      __syncthreads();
+      acc = ((wsum[0] + wsum[1]) + wsum[2]) + wsum[3];
+      __syncthreads();  // wsum is reused by the next row
+    }
+    if (j == 0) {
       float o = alpha * acc;
       if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[r * ldo];
       static_cast<T *>(out)[r * ldo] = (T)o;
@@ -114,6 +135,17 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *part, int
 }
 
 }  // namespace dev
+
+namespace {
+template <int DT>
+void launch_reduce(bool wide, dim3 rg, float *part, int64_t R, int64_t S, void *out, int64_t ldo, float alpha,
+                   float beta, hipStream_t stream) {
+  if (wide)
+    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 256>), rg, dim3(256), 0, stream, part, R, S, out, ldo, alpha, beta);
+  else
+    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 64>), rg, dim3(256), 0, stream, part, R, S, out, ldo, alpha, beta);
+}
+}  // namespace
 
 int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
                 int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
@@ -127,14 +159,16 @@ int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R,
     hipLaunchKernelGGL(dev::gemv_kernel<SK_BF16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || S == 1) return (int)e;
-  int64_t rb = (R + 3) / 4;
+  // many chunks per row (few, long rows): a workgroup per row
+  const bool wide = S >= 512;
+  const int64_t rb = wide ? R : (R + 3) / 4;
   const dim3 rg((unsigned)(rb < 4096 ? rb : 4096));
   if (dtype == SK_F32)
-    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F32>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+    launch_reduce<SK_F32>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
   else if (dtype == SK_F16)
-    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_F16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+    launch_reduce<SK_F16>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
   else
-    hipLaunchKernelGGL(dev::gemv_reduce_kernel<SK_BF16>, rg, b, 0, stream, part, R, S, out, ldo, alpha, beta);
+    launch_reduce<SK_BF16>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
   return (int)hipGetLastError();
 }
 
