@@ -218,7 +218,10 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     e = hipMallocAsync(&pa, (size_t)d.m * kp * es, stream);
     if (e != hipSuccess) { (void)hipGetLastError(); return SK_ERR_NO_MEMORY; }
     rc = launch_pack(d.dtype, d.A, d.lda, ak, d.m, d.k, pa, kp, stream);
-    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack A");
+    if (rc != hipSuccess) {
+      (void)hipFreeAsync(pa, stream);
+      return hip_fail((hipError_t)rc, "pack A");
+    }
     a.A = pa; a.lda = kp; a.a_kmajor = 1; a.a_kext = (int32_t)kp;
   }
   if (P.pack_b) {
@@ -229,7 +232,11 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
       return SK_ERR_NO_MEMORY;
     }
     rc = launch_pack(d.dtype, d.B, d.ldb, bk, d.n, d.k, pb, kp, stream);
-    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack B");
+    if (rc != hipSuccess) {
+      if (pa) (void)hipFreeAsync(pa, stream);
+      (void)hipFreeAsync(pb, stream);
+      return hip_fail((hipError_t)rc, "pack B");
+    }
     a.B = pb; a.ldb = kp; a.b_kmajor = 1; a.b_kext = (int32_t)kp;
   }
   // 32-bit buffer offsets inside a k-major tile: rows * ld * es must fit
