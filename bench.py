@@ -83,6 +83,8 @@ def parse():
     p.add_argument("--skinny", action="store_true",
                    help="time eight memory-bound skinny fp16 shapes of the sweep (AUTO and DP), "
                         "--steps launches each")
+    p.add_argument("--peaks", action="store_true",
+                   help="measure the sustained MFMA rates and the HBM read rate only")
     p.add_argument("--gemv", action="store_true",
                    help="time the matrix-vector products only (m == 1 or n == 1 shapes)")
     p.add_argument("--compare-schedules", action="store_true",
@@ -254,6 +256,53 @@ def skinny_leg(torch, sk, S, reps=7):
         out.append(row)
         del A, B, C
     return out
+
+
+def measured_peaks(torch, sk, reps=5):
+    """The machine's own sustained rates (libskmb.so, include/sk_microbench.h):
+    MFMA issue rate per type with two waves on every SIMD (8 independent MFMAs
+    per round, 20000 rounds per launch) and the HBM read rate of a 4 GiB
+    buffer; each the best of `reps` launches after two warm-up launches, HIP
+    events on the launch stream."""
+    import ctypes
+    mb = ctypes.CDLL(os.path.join(os.path.dirname(sk.LIB_PATH), "libskmb.so"))
+    mb.skmb_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    mb.skmb_mfma.restype = ctypes.c_int
+    mb.skmb_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    mb.skmb_read.restype = ctypes.c_int
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+    sp = ctypes.c_void_p(stream.cuda_stream)
+
+    def best_ms(launch):
+        for _ in range(2):
+            assert launch() == 0
+        out = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            assert launch() == 0
+            e1.record(stream)
+            torch.cuda.synchronize()
+            out.append(e0.elapsed_time(e1))
+        return min(out)
+
+    res = {}
+    grid, rounds = 2 * cus, 20000
+    sink = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
+    for dt, name, fl in ((0, "f32", 2048), (1, "f16", 32768), (2, "bf16", 32768)):
+        ms = best_ms(lambda: mb.skmb_mfma(dt, rounds, grid, ctypes.c_void_p(sink.data_ptr()), sp))
+        res[f"mfma_{name}_tflops"] = round(grid * 4 * rounds * 8 * fl / (ms * 1e-3) / 1e12, 1)
+    nbytes = 4 << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    rgrid = 16 * cus
+    rsink = torch.empty(rgrid * 256, dtype=torch.int32, device="cuda")
+    ms = best_ms(lambda: mb.skmb_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rgrid,
+                                      ctypes.c_void_p(rsink.data_ptr()), sp))
+    res["hbm_read_GB_s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    del buf
+    torch.cuda.empty_cache()
+    return res
 
 
 def _gpu_time_us(torch, sk, d, opts, spin, reps=7):
@@ -681,6 +730,9 @@ def main():
     if args.gemv:
         print(json.dumps(gemv_leg(torch, sk, S)), flush=True)
         return
+    if args.peaks:
+        print(json.dumps(measured_peaks(torch, sk)), flush=True)
+        return
     if args.skinny:
         for r in skinny_leg(torch, sk, S, reps=args.steps):
             print(json.dumps(r), flush=True)
@@ -759,6 +811,7 @@ def main():
     if not args.no_extra:
         line["abft"] = abft_overhead(torch, sk, S)
         line["gemv"] = gemv_leg(torch, sk, S)
+        line["measured_peaks"] = measured_peaks(torch, sk)
     for wl, r in results.items():
         if wl == args.workload:
             continue
@@ -769,6 +822,17 @@ def main():
         if "per_shape" in r:
             extra["per_shape_tflops"] = r["per_shape"]
         line["hgemm" if wl == "hgemm-8192" else "sgemm"] = extra
+    if "measured_peaks" in line:
+        # the same kernels' rates against what this chip sustains
+        peaks = line["measured_peaks"]
+        key = {"f32": "mfma_f32_tflops", "f16": "mfma_f16_tflops", "bf16": "mfma_bf16_tflops"}
+        for obj in (line, line.get("sgemm"), line.get("hgemm"), (line.get("hgemm") or {}).get("bf16")):
+            if obj and "roofline" in obj:
+                rf = obj["roofline"]
+                dt = "f32" if rf["peak"] == PEAK_TFLOPS["f32"] else ("bf16" if "bf16" in rf["kernel"] else "f16")
+                rf["frac_of_measured"] = round(rf["achieved"] / peaks[key[dt]], 4)
+        for g in line.get("gemv", []):
+            g["frac_of_measured_hbm"] = round(g["GB_s"] / peaks["hbm_read_GB_s"], 4)
     print(json.dumps(line), flush=True)
 
 

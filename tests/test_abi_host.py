@@ -19,6 +19,25 @@ def test_every_declared_function_is_exported():
         assert hasattr(lib, name), name
 
 
+def test_measurement_library_exports_what_its_header_declares():
+    """libskmb.so (the machine-peak kernels bench.py reports against) loads
+    without a GPU and exports every function include/sk_microbench.h
+    declares; invalid sizes are refused before any launch."""
+    import os
+    import re
+    hdr = open(os.path.join(os.path.dirname(sk.HEADER_PATH), "sk_microbench.h")).read()
+    names = re.findall(r"^int (skmb_\w+)\(", hdr, re.M)
+    assert set(names) == {"skmb_mfma", "skmb_read"}
+    mb = ctypes.CDLL(os.path.join(os.path.dirname(sk.LIB_PATH), "libskmb.so"))
+    for name in names:
+        assert hasattr(mb, name), name
+    mb.skmb_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    mb.skmb_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert mb.skmb_mfma(3, 10, 1, 16, None) != 0  # unknown type
+    assert mb.skmb_mfma(1, 0, 1, 16, None) != 0   # no rounds
+    assert mb.skmb_read(16, 24, 1, 16, None) != 0  # not a multiple of 16 bytes
+
+
 def _desc(m, n, k, dtype=sk.F16, layout=sk.A_ROW_B_COL):
     # aligned fake pointers: the planner only inspects their alignment
     return sk.make_desc(m, n, k, 1.0, 1 << 20, k if layout in (0, 1) else m, 1 << 21,
