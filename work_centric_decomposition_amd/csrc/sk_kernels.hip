@@ -1145,11 +1145,11 @@ __device__ __forceinline__ void s_epilogue(const KernelArgs &a, bool vec_ok, int
 
 // Runs one segment: MacLoop, then partial store, or fixup + epilogue.
 template <class P, class MacLoop, class Epilogue>
-__device__ __forceinline__ void run_segment(const KernelArgs &a, int x, const Segment &g, MacLoop macloop,
-                                            Epilogue epilogue) {
+__device__ __forceinline__ void run_segment(const KernelArgs &a, const Sched &S, int x, const Segment &g,
+                                            MacLoop macloop, Epilogue epilogue) {
   typename P::Acc acc;
   const int tile = (int)g.tile;
-  const int tm = tile / a.tiles_n, tn = tile % a.tiles_n;
+  const int tm = sched_div(tile, S.tiles_n), tn = tile - tm * S.tiles_n;
   const int m0 = tm * P::BM, n0 = tn * P::BN;
   macloop(m0, n0, (int)g.lb, (int)g.le, acc);
   // One call site each for the partial store, the partial add and the
@@ -1157,7 +1157,7 @@ __device__ __forceinline__ void run_segment(const KernelArgs &a, int x, const Se
   //  page order: a non-owner stores; the owner adds x+1 .. last_peer;
   //  tree (sk_gemm.h, fixup_tree): with r = x - first, at level l a
   //  workgroup with bit l of r set stores, else adds the subtree of r + 2^l.
-  const bool tree = a.sched.tree != 0;
+  const bool tree = S.tree != 0;
   const int first = g.first < 0 ? x : (int)g.first, last = g.last < 0 ? x : (int)g.last;
   const int pieces = last - first + 1, r = x - first;
   bool publish = false;
@@ -1186,14 +1186,34 @@ __device__ __forceinline__ void run_segment(const KernelArgs &a, int x, const Se
     epilogue(m0, n0, acc);
 }
 
+// The schedule, read from the kernel arguments once and held in scalar
+// registers: an empty asm statement that may change each field makes it a
+// computed value, which the compiler keeps, instead of a load it re-issues
+// after every branch of the walk (each such reload waited a full memory
+// round trip at kernel start, about a microsecond in all before the first
+// tile).
+__device__ __forceinline__ int32_t sgpr(int32_t v) {
+  asm volatile("" : "+s"(v));
+  return v;
+}
+__device__ __forceinline__ Sched sched_in_sgprs(const Sched &s) {
+  Sched r;
+  r.ipt = sgpr(s.ipt); r.tiles = sgpr(s.tiles); r.tiles_m = sgpr(s.tiles_m); r.tiles_n = sgpr(s.tiles_n);
+  r.sk_tiles = sgpr(s.sk_tiles); r.sk_q = sgpr(s.sk_q); r.sk_r = sgpr(s.sk_r); r.grid = sgpr(s.grid);
+  r.phase_div = sgpr(s.phase_div); r.blocks = sgpr(s.blocks); r.block_len = sgpr(s.block_len);
+  r.block_cut = sgpr(s.block_cut); r.group_rows = sgpr(s.group_rows); r.tree = sgpr(s.tree);
+  return r;
+}
+
 // All segments of workgroup blockIdx.x, in the order the schedule gives
 // them: its Stream-K range, then its data-parallel tiles.
 template <class P, class MacLoop, class Epilogue>
 __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop macloop, Epilogue epilogue) {
   const int x = blockIdx.x;
-  SegIter I = sched_begin(a.sched, x);
+  const Sched S = sched_in_sgprs(a.sched);
+  SegIter I = sched_begin(S, x);
   Segment g;
-  while (sched_next(a.sched, I, g)) run_segment<P>(a, x, g, macloop, epilogue);
+  while (sched_next(S, I, g)) run_segment<P>(a, S, x, g, macloop, epilogue);
 }
 
 template <class P>
