@@ -170,8 +170,11 @@ def library_gemm(torch, sk, S, steps, warmup):
     return out
 
 
-GEMV_SHAPES = [(1, 16384, 16384, "f16"), (16384, 1, 16384, "f16"), (1, 16384, 16384, "f32"),
-               (1, 1, 1 << 24, "f32")]
+# (m, n, k, dtype, layout): k-contiguous matrix operand (dot-product form),
+# then the matrix contiguous along the output (axpy form)
+GEMV_SHAPES = [(1, 16384, 16384, "f16", 1), (16384, 1, 16384, "f16", 1), (1, 16384, 16384, "f32", 1),
+               (1, 1, 1 << 24, "f32", 1), (1, 16384, 16384, "f16", 0), (16384, 1, 16384, "f16", 3),
+               (1, 16384, 16384, "f32", 0)]
 
 
 def gemv_leg(torch, sk, S, reps=20):
@@ -183,31 +186,37 @@ def gemv_leg(torch, sk, S, reps=20):
     dts = {"f16": (sk.F16, torch.float16, 2), "f32": (sk.F32, torch.float32, 4)}
     spin = _spin_cycles(torch, 300e-6)
     out = []
-    for (m, n, k, name) in GEMV_SHAPES:
+    for (m, n, k, name, layout) in GEMV_SHAPES:
         dt, tdt, es = dts[name]
         g = torch.Generator(device="cuda").manual_seed(m + n + k)
         A = (torch.rand(m * k, device="cuda", generator=g) * 2 - 1).to(tdt)
         B = (torch.rand(k * n, device="cuda", generator=g) * 2 - 1).to(tdt)
         C = torch.zeros(m * n, device="cuda", dtype=tdt)
-        d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, dt, sk.A_ROW_B_COL)
+        a_row, b_row = layout in (0, 1), layout in (0, 2)
+        d = sk.make_desc(m, n, k, 1.0, A, k if a_row else m, B, n if b_row else k, 0.0, C, n, dt, layout)
         p = sk.plan_query(d)
         opts = sk.make_options()
         us = min(_gpu_time_us(torch, sk, d, opts, spin, reps) for _ in range(3))
-        Am, Bm = A.view(m, k), B.view(n, k)
-        torch.matmul(Am, Bm.t())
+        # the same operands as torch tensors (row-major views or transposed ones)
+        Am = A.view(m, k) if a_row else A.view(k, m).t()
+        Bm = B.view(k, n) if b_row else B.view(n, k).t()
+        torch.matmul(Am, Bm)
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
         torch.cuda._sleep(spin)
         for e0, e1 in ev:
             e0.record()
-            torch.matmul(Am, Bm.t())
+            torch.matmul(Am, Bm)
             e1.record()
         torch.cuda.synchronize()
         lib_us = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e3
         by = es * (m * k + k * n + m * n)
-        out.append({"shape": [m, n, k], "dtype": name, "schedule": int(p.schedule), "chunks": int(p.sk_blocks),
-                    "grid": int(p.grid), "us": round(us, 2), "GB_s": round(by / us / 1e3, 1),
-                    "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4), "torch_matmul_us": round(lib_us, 2)})
+        out.append({"shape": [m, n, k], "dtype": name, "layout": ["A row, B row", "A row, B col", "A col, B row",
+                                                                  "A col, B col"][layout],
+                    "form": "axpy" if p.tile_n > 0 else "dot", "schedule": int(p.schedule),
+                    "chunks": int(p.sk_blocks), "grid": int(p.grid), "us": round(us, 2),
+                    "GB_s": round(by / us / 1e3, 1), "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
+                    "torch_matmul_us": round(lib_us, 2)})
         del A, B, C
     return out
 

@@ -77,17 +77,20 @@ typedef enum {
  * the A and B slices they read in that XCD's L2), and data-parallel tiles are
  * dealt in compact per-XCD blocks.  With no leftover tiles it is
  * data-parallel in that XCD-aware order.
- *  SK_SCHED_GEMV_SPLIT matrix-vector products (m == 1 or n == 1, the matrix
- *                     operand k-contiguous with 16-byte aligned base and rows,
- *                     the vector contiguous with a 16-byte aligned base): every
- *                     output is a dot product of length k, and the rows x k
- *                     work is split evenly over the workgroups in equal
- *                     k-chunks (the KBLAS page's block-row split, section 6.2;
- *                     Stream-K's work-centric idea at the level of dot
- *                     products); chunk sums are added in a fixed order by a
- *                     second kernel, so results are reproducible.  Chosen
- *                     explicitly, it returns SK_ERR_UNSUPPORTED for other
- *                     shapes, operand layouts or alignments, and with ABFT.
+ *  SK_SCHED_GEMV_SPLIT matrix-vector products (m == 1 or n == 1), the work
+ *                     split evenly over the workgroups (the KBLAS page's
+ *                     block-row split, section 6.2; Stream-K's work-centric
+ *                     idea at the level of dot products).  With the matrix
+ *                     operand k-contiguous (16-byte aligned base and rows)
+ *                     and the vector contiguous and 16-byte aligned, every
+ *                     output is a dot product split in equal k-chunks; with
+ *                     the matrix operand contiguous along the output instead
+ *                     (16-byte aligned base and rows, any vector stride),
+ *                     each workgroup wave accumulates a block of outputs over
+ *                     a chunk of the k rows.  Chunk sums are added in a fixed
+ *                     order by a second kernel, so results are reproducible.
+ *                     Chosen explicitly, it returns SK_ERR_UNSUPPORTED for
+ *                     other shapes or alignments, and with ABFT.
  *  SK_SCHED_AUTO      SK_SCHED_GEMV_SPLIT for eligible matrix-vector shapes
  *                     (with default tile, grid and ABFT options); otherwise
  *                     SK_SCHED_XCD_ALIGNED with the tile instance, quantum and
@@ -179,11 +182,12 @@ typedef struct {
 
 /* Plan of one call, for inspection (host only, needs no GPU when
  * sk_plan_query is given an explicit slot count).  For SK_SCHED_GEMV_SPLIT:
- * tiles = the number of dot products (m or n), tile_k = the k-chunk length
- * in elements, sk_blocks = chunks per dot product, iters_per_tile = 1,
- * total_iters = tiles * sk_blocks (the (dot product, chunk) tasks), grid =
- * workgroups of 256 threads; the fields that describe GEMM tiles are 0, and
- * sk_plan_segments lists no segments. */
+ * tiles = the number of outputs (m or n), tile_k = the k-chunk length
+ * in elements, sk_blocks = chunks per output, iters_per_tile = 1, tile_n =
+ * 0 for the dot-product form, else the outputs one task covers (64 x the
+ * elements in 16 bytes), total_iters = the tasks (outputs or output blocks
+ * times chunks), grid = workgroups of 256 threads; the other fields that
+ * describe GEMM tiles are 0, and sk_plan_segments lists no segments. */
 typedef struct {
   int32_t tile_m, tile_n, tile_k; /* BLK_M, BLK_N, BLK_K of the kernel */
   int32_t slots;                  /* p: workgroups resident at once */

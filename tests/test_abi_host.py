@@ -413,17 +413,48 @@ def test_matrix_vector_split(dtype, m, n, k):
             sk.SCHED_GEMV_SPLIT
 
 
+@pytest.mark.parametrize("dtype", [sk.F32, sk.F16, sk.BF16])
+@pytest.mark.parametrize("m,n,k", [(1, 16384, 16384), (16384, 1, 16384), (1, 300, 4097), (5000, 1, 7),
+                                   (1, 1, 1 << 20), (1, 100003, 64)])
+def test_matrix_vector_output_contiguous_form(dtype, m, n, k):
+    """With the matrix operand contiguous along the output (m == 1 with B
+    row-major, n == 1 with A column-major) AUTO takes the axpy form of the
+    split: tasks are (block of one wave's width of outputs, chunk of k rows),
+    the chunks cover k exactly, at least 64 rows each unless there is only
+    one, and there are enough tasks for every CU; any vector stride."""
+    vec = 4 if dtype == sk.F32 else 8
+    slots = 512 if dtype == sk.F32 else 256
+    layouts = [sk.A_ROW_B_ROW, sk.A_COL_B_ROW] if m == 1 else [sk.A_COL_B_COL, sk.A_COL_B_ROW]
+    for layout in layouts:
+        R = n if m == 1 else m
+        ldm = -(-R // vec) * vec  # rows padded to 16 bytes
+        if m == 1:
+            lda = k if layout in (0, 1) else 7
+            d = sk.make_desc(m, n, k, 1.0, 1 << 20, lda, 1 << 21, ldm, 0.0, 1 << 22, n, dtype, layout)
+        else:
+            ldb = 3 if layout in (0, 2) else k
+            d = sk.make_desc(m, n, k, 1.0, 1 << 20, ldm, 1 << 21, ldb, 0.0, 1 << 22, 5, dtype, layout)
+        p = sk.plan_query(d, None, slots)
+        assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_n == 64 * vec, (layout, p.schedule, p.tile_n)
+        S, chunk, blocks = p.sk_blocks, p.tile_k, -(-R // (64 * vec))
+        assert p.tiles == R and p.total_iters == blocks * S
+        assert S * chunk >= k > (S - 1) * chunk and (chunk >= 64 or S == 1)
+        assert blocks * S >= min(8 * 256, blocks * max(1, k // 64))
+        assert sk.plan_segments(p, 0) == []
+
+
 def test_matrix_vector_fallbacks():
     """Shapes or options the matrix-vector path does not take go to the
     tiled schedules under AUTO, and are refused under an explicit request."""
     gemv = sk.make_options(schedule=sk.SCHED_GEMV_SPLIT)
     cases = [
         sk.make_desc(2, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),  # m = 2
-        sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 0),  # B n-contiguous
         sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 65, 0.0, 1 << 22, 64, sk.F16, 1),  # rows unaligned
         sk.make_desc(1, 64, 64, 1.0, (1 << 20) + 2, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),
         sk.make_desc(64, 1, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 0),  # ldb 64
-        sk.make_desc(64, 1, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 2),  # A m-contiguous
+        sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 65, 0.0, 1 << 22, 64, sk.F16, 0),  # B rows unaligned
+        sk.make_desc(64, 1, 64, 1.0, 1 << 20, 66, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 2),  # A columns unaligned
+        sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, (1 << 21) + 4, 64, 0.0, 1 << 22, 64, sk.F16, 0),
     ]
     for d in cases:
         assert sk.plan_query(d, None, 256).schedule != sk.SCHED_GEMV_SPLIT

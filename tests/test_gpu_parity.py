@@ -386,3 +386,54 @@ def test_matrix_vector_large(dtype, m, n, k):
     got = c.run(1.0, 0.0)
     ref, bound = c.reference(1.0, 0.0)
     assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+
+
+def _axpy_cases(dtype):
+    """(m, n, k, layout, pad, alpha, beta) with the matrix operand contiguous
+    along the output: pad aligns its rows to 16 bytes and also strides the
+    vector (column-major A for m == 1, row-major B for n == 1) and C."""
+    vec = 4 if dtype == sk.F32 else 8
+    out = []
+    for k in (1, 5, 64, 1000, 4097):
+        for r in ((1, 7, 300, 4099, 20000) if k <= 1000 else (1, 7, 300, 4099)):
+            pad = (-r) % vec
+            out.append((1, r, k, sk.A_ROW_B_ROW, pad, 1.0, 0.0))
+            out.append((r, 1, k, sk.A_COL_B_COL, pad + vec, 0.5, -1.5))
+    for k in (8, 2048):
+        out.append((1, 513, k, sk.A_COL_B_ROW, (-513) % vec, 1.0, 1.0))
+        out.append((513, 1, k, sk.A_COL_B_ROW, (-513) % vec, -2.0, 0.25))
+    return out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_matrix_vector_output_contiguous_against_oracle(dtype):
+    """m == 1 with B row-major and n == 1 with A column-major take the axpy
+    form (blocks of outputs over chunks of k rows; strided vectors and C,
+    alpha/beta, ragged output lengths) and match the oracle; repeated calls
+    are bitwise equal."""
+    for (m, n, k, layout, pad, alpha, beta) in _axpy_cases(dtype):
+        _say("case gemv axpy", dtype, m, n, k, layout, pad)
+        c = Case(m, n, k, dtype, layout, 13 + m + 5 * n + k, pad=pad)
+        d = sk.make_desc(m, n, k, alpha, c.dA, c.lda, c.dB, c.ldb, beta, c.dC, c.ldc, dtype, layout)
+        p = sk.plan_query(d)
+        # a single output may take either form
+        assert p.schedule == sk.SCHED_GEMV_SPLIT and (p.tile_n > 0 or m == n == 1), (m, n, k, layout)
+        got = c.run(alpha, beta)
+        ref, bound = c.reference(alpha, beta)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
+        c.reset_c()
+        again = c.run(alpha, beta, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT))
+        assert np.array_equal(got.view(np.uint8), again.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,m,n,k,layout", [(sk.F16, 1, 16384, 4096, sk.A_ROW_B_ROW),
+                                                (sk.F32, 8192, 1, 8192, sk.A_COL_B_COL),
+                                                (sk.BF16, 1, 1, 1 << 20, sk.A_ROW_B_ROW)])
+def test_matrix_vector_output_contiguous_large(dtype, m, n, k, layout):
+    """Large axpy-form products (one output block over many row chunks, or
+    many blocks) against the oracle on every output."""
+    _say("case gemv axpy large", dtype, m, n, k, layout)
+    c = Case(m, n, k, dtype, layout, 41 + m, with_c=False)
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]

@@ -193,8 +193,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
         if (rc != SK_OK) return rc;
         part = ws->partials;
       }
-      rc = launch_gemv(d.dtype, g.M, g.ldm, g.v, g.R, g.K, g.chunk, g.S, g.grid, part, g.out, g.ldo, d.alpha,
-                       d.beta, stream);
+      rc = launch_gemv(d.dtype, g, part, d.alpha, d.beta, stream);
       return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "matrix-vector kernel launch");
     }
     if (o.schedule == SK_SCHED_GEMV_SPLIT) return SK_ERR_UNSUPPORTED;
@@ -340,8 +339,13 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       out->tile_k = (int32_t)g.chunk;
       out->tiles = g.R;
       out->iters_per_tile = 1;
-      out->total_iters = g.R * g.S;
       out->sk_blocks = (int32_t)g.S;
+      if (g.axpy) {  // outputs per task: one wave's width
+        out->tile_n = (desc->dtype == SK_F32 ? 4 : 8) * 64;
+        out->total_iters = (g.R + out->tile_n - 1) / out->tile_n * g.S;
+      } else {
+        out->total_iters = g.R * g.S;
+      }
       return SK_OK;
     }
     const int both[2] = {slots, slots2};

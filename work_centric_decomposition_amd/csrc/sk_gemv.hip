@@ -1,12 +1,16 @@
 // sk_gemv.hip -- matrix-vector products (m == 1 or n == 1) for CDNA4
-// (gfx950): the even split of every dot product into chunks (the KBLAS
-// page's block-row split, section 6.2, which is Stream-K's work-centric
-// idea at the level of dot products), with the chunk sums combined in a
-// fixed order by a second kernel instead of the page's atomic additions, so
-// results are reproducible and beta is applied by the one writer of each
-// output (the page needs a separate scaling kernel first, section 6.4).
-// The path is bound by HBM bandwidth: the matrix is read once, with 16-byte
-// loads of 1 KiB per wave instruction.
+// (gfx950): the even split of the work (the KBLAS page's block-row split,
+// section 6.2, which is Stream-K's work-centric idea at the level of dot
+// products), with the chunk sums combined in a fixed order by a second
+// kernel instead of the page's atomic additions, so results are reproducible
+// and beta is applied by the one writer of each output (the page needs a
+// separate scaling kernel first, section 6.4).  Two forms, by the matrix
+// operand's storage: rows contiguous along k (one dot product per output,
+// split in k-chunks), or contiguous along the output (the page's transposed
+// case: a wave owns a block of outputs and accumulates rows scaled by the
+// vector's entries, the rows split in chunks).  The path is bound by HBM
+// bandwidth: the matrix is read once, with 16-byte loads of 1 KiB per wave
+// instruction.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -134,41 +138,156 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(const float *part, int
   }
 }
 
+// The axpy form: out[j * ldo] = alpha * sum_r v[r * incv] M[r * ldm + j] +
+// beta * out[j * ldo] for j < R, r < K, the rows of M contiguous along the
+// output (16-byte aligned base and rows).  Task t = s * blocks + b takes
+// output block b (W = 64 VEC elements: lane l holds elements b W + l VEC
+// .. + VEC - 1) over rows [s * chunk, min((s + 1) * chunk, K)) in order,
+// eight rows' 16-byte pieces in flight (a wave reads 1 KiB of each row);
+// fp32 products and sums.  The block's partial goes to part[s * R + j]
+// (S > 1) or, with alpha and beta, to the output (S == 1).  The piece that
+// holds the output's end, if partial, is read element by element.
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_axpy_kernel(const void *M, int64_t ldm, const void *v, int64_t incv,
+                                                        int64_t R, int64_t K, int64_t chunk, int64_t S, float *part,
+                                                        void *out, int64_t ldo, float alpha, float beta) {
+  using T = typename GvElem<DT>::T;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int64_t W = 64 * VEC;
+  const int lane = threadIdx.x & 63;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t blocks = (R + W - 1) / W, tasks = blocks * S;
+  const T *vp = static_cast<const T *>(v);
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < tasks; t += waves) {
+    const int64_t s = t / blocks, b = t - s * blocks;
+    const int64_t r0 = s * chunk, r1 = r0 + chunk < K ? r0 + chunk : K;
+    const int64_t j = b * W + (int64_t)lane * VEC;
+    const T *col = static_cast<const T *>(M) + j;
+    float acc[VEC];
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) acc[e] = 0.f;
+    int64_t r = r0;
+    if (j + VEC <= R) {
+      for (; r + 8 <= r1; r += 8) {
+        u4_t mv[8];
+        float xv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          mv[u] = *reinterpret_cast<const u4_t *>(col + (r + u) * ldm);
+          xv[u] = (float)vp[(r + u) * incv];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const T *mx = reinterpret_cast<const T *>(&mv[u]);
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) acc[e] += xv[u] * (float)mx[e];
+        }
+      }
+      for (; r < r1; ++r) {
+        const u4_t mv = *reinterpret_cast<const u4_t *>(col + r * ldm);
+        const float xr = (float)vp[r * incv];
+        const T *mx = reinterpret_cast<const T *>(&mv);
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) acc[e] += xr * (float)mx[e];
+      }
+    } else if (j < R) {
+      for (; r < r1; ++r) {
+        const float xr = (float)vp[r * incv];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e)
+          if (j + e < R) acc[e] += xr * (float)col[r * ldm + e];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (j + e >= R) break;
+      if (S > 1) {
+        part[s * R + j + e] = acc[e];
+      } else {
+        float o = alpha * acc[e];
+        if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[(j + e) * ldo];
+        static_cast<T *>(out)[(j + e) * ldo] = (T)o;
+      }
+    }
+  }
+}
+
+// out[j * ldo] = alpha * sum_s part[s * R + j] + beta * out[j * ldo]: a
+// workgroup per 64 outputs, its wave w adding chunks [w S / 4, (w + 1) S / 4)
+// of each in increasing order (eight loads in flight), then the four wave
+// sums added in wave order, so repeated calls agree bitwise.
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_axpy_reduce_kernel(const float *part, int64_t R, int64_t S, void *out,
+                                                               int64_t ldo, float alpha, float beta) {
+  using T = typename GvElem<DT>::T;
+  __shared__ float wsum[4][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t s0 = S * w / 4, s1 = S * (w + 1) / 4;
+  for (int64_t j0 = (int64_t)blockIdx.x * 64; j0 < R; j0 += (int64_t)gridDim.x * 64) {
+    const int64_t j = j0 + lane;
+    float acc = 0.f;
+    if (j < R) {
+      int64_t s = s0;
+      for (; s + 8 <= s1; s += 8) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = part[(s + u) * R + j];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+      }
+      for (; s < s1; ++s) acc += part[s * R + j];
+    }
+    wsum[w][lane] = acc;
+    __syncthreads();
+    if (w == 0 && j < R) {
+      float o = alpha * (((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]);
+      if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[j * ldo];
+      static_cast<T *>(out)[j * ldo] = (T)o;
+    }
+    __syncthreads();  // wsum is reused by the next block of outputs
+  }
+}
+
 }  // namespace dev
 
 namespace {
 template <int DT>
-void launch_reduce(bool wide, dim3 rg, float *part, int64_t R, int64_t S, void *out, int64_t ldo, float alpha,
-                   float beta, hipStream_t stream) {
-  if (wide)
-    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 256>), rg, dim3(256), 0, stream, part, R, S, out, ldo, alpha, beta);
-  else
-    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 64>), rg, dim3(256), 0, stream, part, R, S, out, ldo, alpha, beta);
+void launch_axpy(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::gemv_axpy_kernel<DT>, dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.incv, g.R,
+                     g.K, g.chunk, g.S, part, g.out, g.ldo, alpha, beta);
+  if (g.S > 1 && hipPeekAtLastError() == hipSuccess) {
+    const int64_t rb = (g.R + 63) / 64;
+    hipLaunchKernelGGL(dev::gemv_axpy_reduce_kernel<DT>, dim3((unsigned)(rb < 8192 ? rb : 8192)), dim3(256), 0,
+                       stream, part, g.R, g.S, g.out, g.ldo, alpha, beta);
+  }
 }
+
+template <int DT>
+void launch_dot(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::gemv_kernel<DT>, dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.R, g.K, g.chunk,
+                     g.S, part, g.out, g.ldo, alpha, beta);
+  if (g.S == 1 || hipPeekAtLastError() != hipSuccess) return;
+  // many chunks per row (few, long rows): a workgroup per row
+  const bool wide = g.S >= 512;
+  const int64_t rb = wide ? g.R : (g.R + 3) / 4;
+  const dim3 rg((unsigned)(rb < 4096 ? rb : 4096));
+  if (wide)
+    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 256>), rg, dim3(256), 0, stream, part, g.R, g.S, g.out, g.ldo,
+                       alpha, beta);
+  else
+    hipLaunchKernelGGL((dev::gemv_reduce_kernel<DT, 64>), rg, dim3(256), 0, stream, part, g.R, g.S, g.out, g.ldo,
+                       alpha, beta);
+}
+
 }  // namespace
 
-int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
-                int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
-                hipStream_t stream) {
-  const dim3 g(grid), b(256);
+int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
   if (dtype == SK_F32)
-    hipLaunchKernelGGL(dev::gemv_kernel<SK_F32>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+    g.axpy ? launch_axpy<SK_F32>(g, part, alpha, beta, stream) : launch_dot<SK_F32>(g, part, alpha, beta, stream);
   else if (dtype == SK_F16)
-    hipLaunchKernelGGL(dev::gemv_kernel<SK_F16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
+    g.axpy ? launch_axpy<SK_F16>(g, part, alpha, beta, stream) : launch_dot<SK_F16>(g, part, alpha, beta, stream);
   else
-    hipLaunchKernelGGL(dev::gemv_kernel<SK_BF16>, g, b, 0, stream, M, ldm, v, R, K, chunk, S, part, out, ldo, alpha, beta);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || S == 1) return (int)e;
-  // many chunks per row (few, long rows): a workgroup per row
-  const bool wide = S >= 512;
-  const int64_t rb = wide ? R : (R + 3) / 4;
-  const dim3 rg((unsigned)(rb < 4096 ? rb : 4096));
-  if (dtype == SK_F32)
-    launch_reduce<SK_F32>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
-  else if (dtype == SK_F16)
-    launch_reduce<SK_F16>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
-  else
-    launch_reduce<SK_BF16>(wide, rg, part, R, S, out, ldo, alpha, beta, stream);
+    g.axpy ? launch_axpy<SK_BF16>(g, part, alpha, beta, stream) : launch_dot<SK_BF16>(g, part, alpha, beta, stream);
   return (int)hipGetLastError();
 }
 

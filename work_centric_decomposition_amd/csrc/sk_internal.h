@@ -265,23 +265,30 @@ struct Plan {
   }
 };
 
-// Matrix-vector path (SK_SCHED_GEMV_SPLIT): out[r] = alpha * (M row r) . v +
-// beta * out[r * ldo] for r < R, each row split in S chunks of `chunk`
-// elements, `grid` workgroups of 256 threads.
+// Matrix-vector path (SK_SCHED_GEMV_SPLIT), in one of two forms:
+//  dot (axpy == 0): out[r * ldo] = alpha * (M row r) . v + beta * out[r * ldo]
+//    for r < R, M rows of K elements (k-contiguous, stride ldm), v
+//    contiguous; each row split in S chunks of `chunk` elements;
+//  axpy (axpy == 1): out[j * ldo] = alpha * sum_r v[r * incv] M[r, j] +
+//    beta * out[j * ldo] for j < R, M rows of R elements (contiguous along
+//    the output, stride ldm), r < K; the output is cut in blocks of one wave's
+//    width and the K rows in S chunks of `chunk` rows.
+// `grid` workgroups of 256 threads.
 struct GemvPlan {
   const void *M, *v;
   void *out;
-  int64_t ldm, ldo, R, K, chunk, S;
+  int64_t ldm, ldo, incv, R, K, chunk, S;
+  int axpy;
   int grid;
 };
 // Fills `g` and returns true if the call is a matrix-vector product the
-// path takes (m == 1 or n == 1, the matrix operand k-contiguous with
-// 16-byte aligned rows, the vector contiguous and 16-byte aligned); cus:
+// path takes (m == 1 or n == 1; dot form: the matrix operand k-contiguous
+// with 16-byte aligned base and rows, the vector contiguous and 16-byte
+// aligned; axpy form, when the matrix operand is contiguous along the
+// output instead: 16-byte aligned base and rows, any vector stride); cus:
 // compute units.
 bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g);
-int launch_gemv(int dtype, const void *M, int64_t ldm, const void *v, int64_t R, int64_t K, int64_t chunk,
-                int64_t S, int grid, float *part, void *out, int64_t ldo, float alpha, float beta,
-                hipStream_t stream);
+int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream);
 
 // Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots:
 // resident workgroups of the large (or fp32) and of the small-tile instance.

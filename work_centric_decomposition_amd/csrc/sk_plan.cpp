@@ -434,24 +434,47 @@ bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
   const int64_t es = d.dtype == SK_F32 ? 4 : 2, vec = 16 / es;
   const bool ak = d.layout == SK_A_ROW_B_ROW || d.layout == SK_A_ROW_B_COL;
   const bool bk = d.layout == SK_A_ROW_B_COL || d.layout == SK_A_COL_B_COL;
+  g.axpy = 0;
+  g.incv = 1;
   if (d.n == 1 && ak && (bk || d.ldb == 1 || d.k == 1)) {  // rows of A against the column B
     g.M = d.A; g.ldm = d.lda; g.v = d.B; g.R = d.m; g.out = d.C; g.ldo = d.ldc;
   } else if (d.m == 1 && bk && (ak || d.lda == 1 || d.k == 1)) {  // the row A against columns of B
     g.M = d.B; g.ldm = d.ldb; g.v = d.A; g.R = d.n; g.out = d.C; g.ldo = 1;
+  } else if (d.m == 1 && !bk) {  // C row = sum_k A[0, k] B[k, :], B rows contiguous along n
+    g.axpy = 1;
+    g.M = d.B; g.ldm = d.ldb; g.v = d.A; g.incv = ak ? 1 : d.lda; g.R = d.n; g.out = d.C; g.ldo = 1;
+  } else if (d.n == 1 && !ak) {  // C column = sum_k A[:, k] B[k, 0], A columns contiguous along m
+    g.axpy = 1;
+    g.M = d.A; g.ldm = d.lda; g.v = d.B; g.incv = bk ? 1 : d.ldb; g.R = d.m; g.out = d.C; g.ldo = d.ldc;
   } else {
     return false;
   }
-  if (reinterpret_cast<uintptr_t>(g.M) % 16 || reinterpret_cast<uintptr_t>(g.v) % 16) return false;
-  if (g.R > 1 && (g.ldm * es) % 16) return false;
   g.K = d.k;
-  // enough chunks to keep every CU busy (about 32 per CU), none shorter
-  // than eight 1 KiB passes of a wave (the kernel keeps eight in flight)
-  const int64_t piece = 64 * vec;
-  const int64_t want = cdiv((int64_t)32 * cus, g.R);
-  int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (8 * piece)));
-  g.chunk = cdiv(cdiv(g.K, S), vec) * vec;
+  if (reinterpret_cast<uintptr_t>(g.M) % 16) return false;
+  if (!g.axpy) {
+    if (reinterpret_cast<uintptr_t>(g.v) % 16) return false;
+    if (g.R > 1 && (g.ldm * es) % 16) return false;
+    // enough chunks to keep every CU busy (about 32 per CU), none shorter
+    // than eight 1 KiB passes of a wave (the kernel keeps eight in flight)
+    const int64_t piece = 64 * vec;
+    const int64_t want = cdiv((int64_t)32 * cus, g.R);
+    int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (8 * piece)));
+    g.chunk = cdiv(cdiv(g.K, S), vec) * vec;
+    g.S = cdiv(g.K, g.chunk);
+    g.grid = (int)std::min<int64_t>(cdiv(g.R * g.S, 4), (int64_t)8 * cus);
+    return true;
+  }
+  if (g.K > 1 && (g.ldm * es) % 16) return false;
+  // output blocks of one wave's width (64 lanes x 16 bytes); chunks of at
+  // least 64 rows, enough (block, chunk) tasks for about 8 per CU: each
+  // task streams a whole chunk, and more chunks only add partial sums to
+  // write and add up
+  const int64_t blocks = cdiv(g.R, 64 * vec);
+  const int64_t want = cdiv((int64_t)8 * cus, blocks);
+  const int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / 64));
+  g.chunk = cdiv(g.K, S);
   g.S = cdiv(g.K, g.chunk);
-  g.grid = (int)std::min<int64_t>(cdiv(g.R * g.S, 4), (int64_t)8 * cus);
+  g.grid = (int)std::min<int64_t>(cdiv(blocks * g.S, 4), (int64_t)8 * cus);
   return true;
 }
 
