@@ -3,7 +3,11 @@ call through the C ABI, and the comparison with the oracle.
 
 Error metric: max over elements of |C_gpu - C_ref| / D, where C_ref is the
 oracle's unrounded fp64 value and D = |alpha| |A||B| + |beta| |C_in| is the
-componentwise bound (elements with D == 0 must match exactly).
+componentwise bound (elements with D == 0 must match exactly).  The one
+rounding of the result to the output format is allowed its absolute floor:
+below the smallest normal number the format's spacing is fixed (fp16:
+2^-24), so a correctly rounded subnormal result may be off by half of it
+whatever its size; that much is taken off |C_gpu - C_ref| first.
 """
 from __future__ import annotations
 
@@ -109,9 +113,13 @@ class Case:
                                 self.dtype, self.layout, X)
 
 
+# half the spacing of each output format's subnormal numbers
+SUBNORMAL_HALF_ULP = {sk.F32: 2.0 ** -150, sk.F16: 2.0 ** -25, sk.BF16: 2.0 ** -134}
+
+
 def rel_err(got: np.ndarray, dtype: int, ref64: np.ndarray, bound: np.ndarray) -> float:
     g = decode(got, dtype)
-    diff = np.abs(g - ref64)
+    diff = np.maximum(np.abs(g - ref64) - SUBNORMAL_HALF_ULP[dtype], 0.0)
     zero = bound == 0
     if np.any(zero & (diff != 0)) or np.any(~np.isfinite(g)):
         return float("inf")

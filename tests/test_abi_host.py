@@ -443,12 +443,41 @@ def test_matrix_vector_output_contiguous_form(dtype, m, n, k):
         assert sk.plan_segments(p, 0) == []
 
 
+@pytest.mark.parametrize("dtype", [sk.F32, sk.F16, sk.BF16])
+@pytest.mark.parametrize("m,n,k", [(8, 16384, 16384), (16384, 2, 4096), (16, 16, 16), (3, 1000, 4097),
+                                   (2, 5, 100003)])
+def test_matrix_vector_few_vectors_form(dtype, m, n, k):
+    """2 .. 16 vectors against k-contiguous rows (both operands k-contiguous)
+    take the multi form: tasks are blocks of 16 rows times chunks of whole
+    64-byte slabs of k (the last chunk ends at k), at least eight slabs each
+    unless there is only one chunk, and enough of them for every CU."""
+    es = 4 if dtype == sk.F32 else 2
+    slab = 64 // es
+    slots = 512 if dtype == sk.F32 else 256
+    kp = -(-k // (16 // es)) * (16 // es)
+    d = sk.make_desc(m, n, k, 1.0, 1 << 20, kp, 1 << 21, kp, 0.0, 1 << 22, n, dtype, sk.A_ROW_B_COL)
+    p = sk.plan_query(d, None, slots)
+    V, R = (m, n) if m <= 16 else (n, m)
+    assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_m == V and p.tile_n == 16
+    S, chunk, blocks = p.sk_blocks, p.tile_k, -(-R // 16)
+    assert p.tiles == V * R and p.total_iters == blocks * S
+    assert chunk % slab == 0 and S * chunk >= k > (S - 1) * chunk
+    assert chunk >= 8 * slab or S == 1
+    assert 2 * blocks * S >= min(8 * 256, blocks * max(1, k // (8 * slab)))  # chunks round up to slabs
+    # any other operand order, or ABFT, keeps the tiled schedules
+    other = sk.make_desc(m, n, k, 1.0, 1 << 20, kp, 1 << 21, n, 0.0, 1 << 22, n, dtype, sk.A_ROW_B_ROW)
+    if min(m, n) > 1:
+        assert sk.plan_query(other, None, slots).schedule != sk.SCHED_GEMV_SPLIT
+
+
 def test_matrix_vector_fallbacks():
     """Shapes or options the matrix-vector path does not take go to the
     tiled schedules under AUTO, and are refused under an explicit request."""
     gemv = sk.make_options(schedule=sk.SCHED_GEMV_SPLIT)
     cases = [
-        sk.make_desc(2, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),  # m = 2
+        sk.make_desc(17, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),  # m = 17
+        sk.make_desc(2, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 0),  # m = 2, B n-major
+        sk.make_desc(4, 64, 64, 1.0, 1 << 20, 66, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),  # A rows unaligned
         sk.make_desc(1, 64, 64, 1.0, 1 << 20, 64, 1 << 21, 65, 0.0, 1 << 22, 64, sk.F16, 1),  # rows unaligned
         sk.make_desc(1, 64, 64, 1.0, (1 << 20) + 2, 64, 1 << 21, 64, 0.0, 1 << 22, 64, sk.F16, 1),
         sk.make_desc(64, 1, 64, 1.0, 1 << 20, 64, 1 << 21, 64, 0.0, 1 << 22, 1, sk.F16, 0),  # ldb 64

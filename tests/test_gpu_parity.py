@@ -437,3 +437,49 @@ def test_matrix_vector_output_contiguous_large(dtype, m, n, k, layout):
     got = c.run(1.0, 0.0)
     ref, bound = c.reference(1.0, 0.0)
     assert rel_err(got, dtype, ref, bound) <= TOL[dtype]
+
+
+def _multi_cases(dtype):
+    """(m, n, k, pad, alpha, beta): 2 .. 16 vectors (m, or n with m > 16)
+    against k-contiguous rows (A row-major, B column-major); pad aligns the
+    rows for a ragged k and strides C."""
+    vec = 4 if dtype == sk.F32 else 8
+    out = []
+    for k in (1, 5, 31, 64, 1000, 4097):
+        pad = (-k) % vec
+        for V in (2, 5, 16):
+            for R in ((7, 4099) if k <= 1000 else (300,)):
+                out.append((V, R, k, pad, 1.0, 0.0))
+                out.append((R + 16, V, k, pad + vec, 0.5, -1.5))
+    return out
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_matrix_vector_few_vectors_against_oracle(dtype):
+    """2 .. 16 vectors against k-contiguous rows take the multi form (MFMA
+    over 16-row blocks and k-chunks; k tails, rows and vectors past the end,
+    strided C, alpha/beta) and match the oracle; repeated calls are bitwise
+    equal."""
+    for (m, n, k, pad, alpha, beta) in _multi_cases(dtype):
+        _say("case gemv multi", dtype, m, n, k, pad)
+        c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 17 + m + 3 * n + k, pad=pad)
+        d = sk.make_desc(m, n, k, alpha, c.dA, c.lda, c.dB, c.ldb, beta, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
+        p = sk.plan_query(d)
+        assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_n == 16, (m, n, k)
+        got = c.run(alpha, beta)
+        ref, bound = c.reference(alpha, beta)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
+        c.reset_c()
+        again = c.run(alpha, beta, sk.make_options(schedule=sk.SCHED_GEMV_SPLIT))
+        assert np.array_equal(got.view(np.uint8), again.view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,m,n,k", [(sk.F16, 8, 16384, 4096), (sk.BF16, 16384, 4, 4096),
+                                         (sk.F32, 16, 8192, 4096), (sk.F32, 3, 5, 1 << 20)])
+def test_matrix_vector_few_vectors_large(dtype, m, n, k):
+    """Large multi-form products against the oracle on every output."""
+    _say("case gemv multi large", dtype, m, n, k)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 51 + m, with_c=False)
+    got = c.run(1.0, 0.0)
+    ref, bound = c.reference(1.0, 0.0)
+    assert rel_err(got, dtype, ref, bound) <= TOL[dtype]

@@ -189,7 +189,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
       float *part = nullptr;
       if (g.S > 1) {
         Workspace *ws = nullptr;
-        rc = get_workspace(dev, stream, 1, (size_t)(g.S * g.R) * sizeof(float), &ws);
+        rc = get_workspace(dev, stream, 1, (size_t)(g.S * g.R * g.V) * sizeof(float), &ws);
         if (rc != SK_OK) return rc;
         part = ws->partials;
       }
@@ -340,9 +340,14 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       out->tiles = g.R;
       out->iters_per_tile = 1;
       out->sk_blocks = (int32_t)g.S;
-      if (g.axpy) {  // outputs per task: one wave's width
+      if (g.form == kGemvAxpy) {  // outputs per task: one wave's width
         out->tile_n = (desc->dtype == SK_F32 ? 4 : 8) * 64;
         out->total_iters = (g.R + out->tile_n - 1) / out->tile_n * g.S;
+      } else if (g.form == kGemvMulti) {  // vectors x 16 rows per task
+        out->tile_m = g.V;
+        out->tile_n = 16;
+        out->tiles = (int64_t)g.V * g.R;
+        out->total_iters = (g.R + 15) / 16 * g.S;
       } else {
         out->total_iters = g.R * g.S;
       }

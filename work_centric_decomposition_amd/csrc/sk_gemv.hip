@@ -20,6 +20,9 @@ namespace sk {
 namespace dev {
 
 typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 
 // Storage type of each sk_dtype; products and sums are fp32, outputs are
 // rounded once (to nearest even) by the conversion.
@@ -212,54 +215,169 @@ __global__ __launch_bounds__(256) void gemv_axpy_kernel(const void *M, int64_t l
   }
 }
 
-// out[j * ldo] = alpha * sum_s part[s * R + j] + beta * out[j * ldo]: a
-// workgroup per 64 outputs, its wave w adding chunks [w S / 4, (w + 1) S / 4)
-// of each in increasing order (eight loads in flight), then the four wave
-// sums added in wave order, so repeated calls agree bitwise.
+// Output o < NO (o = i * R + j: vector i, output j) is
+// out[i * ld_i + j * ld_j] = alpha * sum_s part[s * NO + o] + beta * (the
+// same): a workgroup per 64 outputs, its wave w adding chunks
+// [w S / 4, (w + 1) S / 4) of each in increasing order (eight loads in
+// flight), then the four wave sums added in wave order, so repeated calls
+// agree bitwise.
 template <int DT>
-__global__ __launch_bounds__(256) void gemv_axpy_reduce_kernel(const float *part, int64_t R, int64_t S, void *out,
-                                                               int64_t ldo, float alpha, float beta) {
+__global__ __launch_bounds__(256) void gemv_part_reduce_kernel(const float *part, int64_t NO, int64_t R, int64_t S,
+                                                               void *out, int64_t ld_i, int64_t ld_j, float alpha,
+                                                               float beta) {
   using T = typename GvElem<DT>::T;
   __shared__ float wsum[4][64];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int64_t s0 = S * w / 4, s1 = S * (w + 1) / 4;
-  for (int64_t j0 = (int64_t)blockIdx.x * 64; j0 < R; j0 += (int64_t)gridDim.x * 64) {
-    const int64_t j = j0 + lane;
+  for (int64_t o0 = (int64_t)blockIdx.x * 64; o0 < NO; o0 += (int64_t)gridDim.x * 64) {
+    const int64_t o = o0 + lane;
     float acc = 0.f;
-    if (j < R) {
+    if (o < NO) {
       int64_t s = s0;
       for (; s + 8 <= s1; s += 8) {
         float v[8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = part[(s + u) * R + j];
+        for (int u = 0; u < 8; ++u) v[u] = part[(s + u) * NO + o];
 #pragma unroll
         for (int u = 0; u < 8; ++u) acc += v[u];
       }
-      for (; s < s1; ++s) acc += part[s * R + j];
+      for (; s < s1; ++s) acc += part[s * NO + o];
     }
     wsum[w][lane] = acc;
     __syncthreads();
-    if (w == 0 && j < R) {
-      float o = alpha * (((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]);
-      if (beta != 0.f) o += beta * (float)static_cast<const T *>(out)[j * ldo];
-      static_cast<T *>(out)[j * ldo] = (T)o;
+    if (w == 0 && o < NO) {
+      const int64_t i = o / R, j = o - i * R;
+      T *dst = static_cast<T *>(out) + i * ld_i + j * ld_j;
+      float r = alpha * (((wsum[0][lane] + wsum[1][lane]) + wsum[2][lane]) + wsum[3][lane]);
+      if (beta != 0.f) r += beta * (float)*dst;
+      *dst = (T)r;
     }
     __syncthreads();  // wsum is reused by the next block of outputs
+  }
+}
+
+// The multi form: D[i][r] = sum_k X[i][k] M[r][k] for vectors i < V (<= 16),
+// rows r < R, both k-contiguous (16-byte aligned base and rows).  Task
+// t = s * blocks + b takes rows [16 b, 16 b + 16) over k-chunk s in slabs of
+// one 16-byte load per lane: lane l loads row 16 b + (l & 15) of M and row
+// (l & 15) of X at k offset VEC (l >> 4) of the slab, rows or vectors past
+// the end as zeros, and the MFMA sums over the slab (fp16/bf16:
+// v_mfma_f32_16x16x32 with X as the first operand, one per 32-k slab;
+// fp32: four v_mfma_f32_16x16x4 steps per 16-k slab, step q taking the
+// q-th element of every lane's four, so that the lane groups cover
+// k = 4 (l >> 4) + q).  Lane l then holds D for vectors 4 (l >> 4) + e and
+// row 16 b + (l & 15).  A slab holding the end of k loads element by
+// element, zeros past k.  The 16 x 16 partial goes to part[s * V R + i R + r]
+// (S > 1) or, with alpha and beta, to out[i ld_v + r ld_r] (S == 1).
+template <int DT>
+__global__ __launch_bounds__(256) void gemv_multi_kernel(const void *M, int64_t ldm, const void *X, int64_t ldx,
+                                                         int V, int64_t R, int64_t K, int64_t chunk, int64_t S,
+                                                         float *part, void *out, int64_t ld_v, int64_t ld_r,
+                                                         float alpha, float beta) {
+  using T = typename GvElem<DT>::T;
+  constexpr int VEC = 16 / sizeof(T);
+  constexpr int64_t SLAB = 4 * VEC;
+  const int lane = threadIdx.x & 63, li = lane & 15, kg = lane >> 4;
+  const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
+  const int64_t blocks = (R + 15) / 16, tasks = blocks * S;
+  for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < tasks; t += waves) {
+    const int64_t s = t / blocks, b = t - s * blocks;
+    const int64_t k0 = s * chunk, k1 = k0 + chunk < K ? k0 + chunk : K;
+    const int64_t row = b * 16 + li;
+    const bool mrow = row < R, xrow = li < V;
+    const T *mp = static_cast<const T *>(M) + (mrow ? row : 0) * ldm + kg * VEC;
+    const T *xp = static_cast<const T *>(X) + (xrow ? li : 0) * ldx + kg * VEC;
+    f4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto step = [&](const u4_t &mv, const u4_t &xv) {
+      if constexpr (DT == SK_F32) {
+        const f4_t mf = __builtin_bit_cast(f4_t, mv), xf = __builtin_bit_cast(f4_t, xv);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[q], mf[q], acc, 0, 0, 0);
+      } else if constexpr (DT == SK_F16) {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv), __builtin_bit_cast(h8_t, mv),
+                                                     acc, 0, 0, 0);
+      } else {
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, xv), __builtin_bit_cast(b8_t, mv),
+                                                      acc, 0, 0, 0);
+      }
+    };
+    const u4_t zero = {0u, 0u, 0u, 0u};
+    const int64_t kfull = k0 + (k1 - k0) / SLAB * SLAB;  // whole slabs of this chunk
+    int64_t k = k0;
+    for (; k + 4 * SLAB <= kfull; k += 4 * SLAB) {
+      u4_t mv[4], xv[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        mv[u] = mrow ? *reinterpret_cast<const u4_t *>(mp + k + u * SLAB) : zero;
+        xv[u] = xrow ? *reinterpret_cast<const u4_t *>(xp + k + u * SLAB) : zero;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) step(mv[u], xv[u]);
+    }
+    for (; k < kfull; k += SLAB) {
+      const u4_t mv = mrow ? *reinterpret_cast<const u4_t *>(mp + k) : zero;
+      const u4_t xv = xrow ? *reinterpret_cast<const u4_t *>(xp + k) : zero;
+      step(mv, xv);
+    }
+    if (k < k1) {  // the slab holding the end of k
+      T me[VEC], xe[VEC];
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) {
+        const bool in = k + kg * VEC + e < k1;
+        me[e] = mrow && in ? mp[k + e] : (T)0.f;
+        xe[e] = xrow && in ? xp[k + e] : (T)0.f;
+      }
+      step(__builtin_bit_cast(u4_t, me), __builtin_bit_cast(u4_t, xe));
+    }
+    const int64_t r = b * 16 + li;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * kg + e;
+      if (i >= V || r >= R) continue;
+      if (S > 1) {
+        part[s * (int64_t)V * R + i * R + r] = acc[e];
+      } else {
+        T *dst = static_cast<T *>(out) + i * ld_v + r * ld_r;
+        float o = alpha * acc[e];
+        if (beta != 0.f) o += beta * (float)*dst;
+        *dst = (T)o;
+      }
+    }
   }
 }
 
 }  // namespace dev
 
 namespace {
+void launch_reduce_parts(int dtype, const float *part, int64_t NO, int64_t R, int64_t S, void *out, int64_t ld_i,
+                         int64_t ld_j, float alpha, float beta, hipStream_t stream) {
+  const int64_t rb = (NO + 63) / 64;
+  const dim3 g((unsigned)(rb < 8192 ? rb : 8192)), b(256);
+  if (dtype == SK_F32)
+    hipLaunchKernelGGL(dev::gemv_part_reduce_kernel<SK_F32>, g, b, 0, stream, part, NO, R, S, out, ld_i, ld_j, alpha,
+                       beta);
+  else if (dtype == SK_F16)
+    hipLaunchKernelGGL(dev::gemv_part_reduce_kernel<SK_F16>, g, b, 0, stream, part, NO, R, S, out, ld_i, ld_j, alpha,
+                       beta);
+  else
+    hipLaunchKernelGGL(dev::gemv_part_reduce_kernel<SK_BF16>, g, b, 0, stream, part, NO, R, S, out, ld_i, ld_j,
+                       alpha, beta);
+}
+
 template <int DT>
 void launch_axpy(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
   hipLaunchKernelGGL(dev::gemv_axpy_kernel<DT>, dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.incv, g.R,
                      g.K, g.chunk, g.S, part, g.out, g.ldo, alpha, beta);
-  if (g.S > 1 && hipPeekAtLastError() == hipSuccess) {
-    const int64_t rb = (g.R + 63) / 64;
-    hipLaunchKernelGGL(dev::gemv_axpy_reduce_kernel<DT>, dim3((unsigned)(rb < 8192 ? rb : 8192)), dim3(256), 0,
-                       stream, part, g.R, g.S, g.out, g.ldo, alpha, beta);
-  }
+  if (g.S > 1 && hipPeekAtLastError() == hipSuccess)
+    launch_reduce_parts(DT, part, g.R, g.R, g.S, g.out, 0, g.ldo, alpha, beta, stream);
+}
+
+template <int DT>
+void launch_multi(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
+  hipLaunchKernelGGL(dev::gemv_multi_kernel<DT>, dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.ldv, g.V,
+                     g.R, g.K, g.chunk, g.S, part, g.out, g.ld_v, g.ld_r, alpha, beta);
+  if (g.S > 1 && hipPeekAtLastError() == hipSuccess)
+    launch_reduce_parts(DT, part, (int64_t)g.V * g.R, g.R, g.S, g.out, g.ld_v, g.ld_r, alpha, beta, stream);
 }
 
 template <int DT>
@@ -281,13 +399,23 @@ void launch_dot(const GemvPlan &g, float *part, float alpha, float beta, hipStre
 
 }  // namespace
 
+template <int DT>
+void launch_form(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
+  if (g.form == kGemvAxpy)
+    launch_axpy<DT>(g, part, alpha, beta, stream);
+  else if (g.form == kGemvMulti)
+    launch_multi<DT>(g, part, alpha, beta, stream);
+  else
+    launch_dot<DT>(g, part, alpha, beta, stream);
+}
+
 int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
   if (dtype == SK_F32)
-    g.axpy ? launch_axpy<SK_F32>(g, part, alpha, beta, stream) : launch_dot<SK_F32>(g, part, alpha, beta, stream);
+    launch_form<SK_F32>(g, part, alpha, beta, stream);
   else if (dtype == SK_F16)
-    g.axpy ? launch_axpy<SK_F16>(g, part, alpha, beta, stream) : launch_dot<SK_F16>(g, part, alpha, beta, stream);
+    launch_form<SK_F16>(g, part, alpha, beta, stream);
   else
-    g.axpy ? launch_axpy<SK_BF16>(g, part, alpha, beta, stream) : launch_dot<SK_BF16>(g, part, alpha, beta, stream);
+    launch_form<SK_BF16>(g, part, alpha, beta, stream);
   return (int)hipGetLastError();
 }
 

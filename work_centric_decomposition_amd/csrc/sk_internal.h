@@ -265,28 +265,36 @@ struct Plan {
   }
 };
 
-// Matrix-vector path (SK_SCHED_GEMV_SPLIT), in one of two forms:
-//  dot (axpy == 0): out[r * ldo] = alpha * (M row r) . v + beta * out[r * ldo]
-//    for r < R, M rows of K elements (k-contiguous, stride ldm), v
-//    contiguous; each row split in S chunks of `chunk` elements;
-//  axpy (axpy == 1): out[j * ldo] = alpha * sum_r v[r * incv] M[r, j] +
+// Matrix-vector path (SK_SCHED_GEMV_SPLIT), in one of three forms:
+//  kGemvDot: out[r * ldo] = alpha * (M row r) . v + beta * out[r * ldo] for
+//    r < R, M rows of K elements (k-contiguous, stride ldm), v contiguous;
+//    each row split in S chunks of `chunk` elements;
+//  kGemvAxpy: out[j * ldo] = alpha * sum_r v[r * incv] M[r, j] +
 //    beta * out[j * ldo] for j < R, M rows of R elements (contiguous along
-//    the output, stride ldm), r < K; the output is cut in blocks of one wave's
-//    width and the K rows in S chunks of `chunk` rows.
+//    the output, stride ldm), r < K; the output is cut in blocks of one
+//    wave's width and the K rows in S chunks of `chunk` rows;
+//  kGemvMulti: V (2 .. 16) vectors, rows of v with stride ldv, against the R
+//    k-contiguous rows of M: out[i * ld_v + r * ld_r] = alpha * (v row i) .
+//    (M row r) + beta * (the same) for i < V, r < R; tasks are blocks of 16
+//    rows times S chunks of `chunk` k.
 // `grid` workgroups of 256 threads.
+enum { kGemvDot = 0, kGemvAxpy = 1, kGemvMulti = 2 };
 struct GemvPlan {
   const void *M, *v;
   void *out;
   int64_t ldm, ldo, incv, R, K, chunk, S;
-  int axpy;
+  int64_t ldv, ld_v, ld_r;  // kGemvMulti
+  int V;                    // kGemvMulti
+  int form;
   int grid;
 };
 // Fills `g` and returns true if the call is a matrix-vector product the
-// path takes (m == 1 or n == 1; dot form: the matrix operand k-contiguous
+// path takes: m == 1 or n == 1 (dot form: the matrix operand k-contiguous
 // with 16-byte aligned base and rows, the vector contiguous and 16-byte
 // aligned; axpy form, when the matrix operand is contiguous along the
-// output instead: 16-byte aligned base and rows, any vector stride); cus:
-// compute units.
+// output instead: 16-byte aligned base and rows, any vector stride), or
+// 2 <= m or n <= 16 with both operands k-contiguous and 16-byte aligned
+// (multi form); cus: compute units.
 bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g);
 int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream);
 

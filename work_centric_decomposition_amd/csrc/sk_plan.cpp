@@ -430,28 +430,58 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Pl
 }
 
 bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
-  if (d.k <= 0 || (d.m != 1 && d.n != 1) || cus <= 0) return false;
+  if (d.k <= 0 || d.m <= 0 || d.n <= 0 || cus <= 0) return false;
   const int64_t es = d.dtype == SK_F32 ? 4 : 2, vec = 16 / es;
   const bool ak = d.layout == SK_A_ROW_B_ROW || d.layout == SK_A_ROW_B_COL;
   const bool bk = d.layout == SK_A_ROW_B_COL || d.layout == SK_A_COL_B_COL;
-  g.axpy = 0;
+  g.form = kGemvDot;
   g.incv = 1;
+  g.V = 1;
+  g.ldv = g.ld_v = g.ld_r = 0;
+  if (d.k <= 0) return false;
+  // 2 .. 16 vectors against k-contiguous rows (neither m nor n 1): the
+  // multi form
+  const bool few_m = d.m >= 2 && d.m <= 16, few_n = d.n >= 2 && d.n <= 16;
+  if ((few_m || few_n) && d.m >= 2 && d.n >= 2 && ak && bk) {
+    g.form = kGemvMulti;
+    if (few_m) {  // rows of A against the rows of column-major B
+      g.V = (int)d.m; g.v = d.A; g.ldv = d.lda; g.M = d.B; g.ldm = d.ldb; g.R = d.n;
+      g.ld_v = d.ldc; g.ld_r = 1;
+    } else {  // columns of B against the rows of row-major A
+      g.V = (int)d.n; g.v = d.B; g.ldv = d.ldb; g.M = d.A; g.ldm = d.lda; g.R = d.m;
+      g.ld_v = 1; g.ld_r = d.ldc;
+    }
+    g.out = d.C; g.ldo = 0; g.K = d.k;
+    if (reinterpret_cast<uintptr_t>(g.M) % 16 || reinterpret_cast<uintptr_t>(g.v) % 16) return false;
+    if ((g.ldm * es) % 16 || (g.ldv * es) % 16) return false;
+    // k slabs of one load per lane (64 bytes of every row per wave load);
+    // chunks of at least eight slabs, about 8 (row block, chunk) tasks per CU
+    const int64_t slab = 64 / es;
+    const int64_t blocks = cdiv(g.R, 16);
+    const int64_t want = cdiv((int64_t)8 * cus, blocks);
+    int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (8 * slab)));
+    g.chunk = cdiv(cdiv(g.K, S), slab) * slab;
+    g.S = cdiv(g.K, g.chunk);
+    g.grid = (int)std::min<int64_t>(cdiv(blocks * g.S, 4), (int64_t)8 * cus);
+    return true;
+  }
+  if (d.m != 1 && d.n != 1) return false;
   if (d.n == 1 && ak && (bk || d.ldb == 1 || d.k == 1)) {  // rows of A against the column B
     g.M = d.A; g.ldm = d.lda; g.v = d.B; g.R = d.m; g.out = d.C; g.ldo = d.ldc;
   } else if (d.m == 1 && bk && (ak || d.lda == 1 || d.k == 1)) {  // the row A against columns of B
     g.M = d.B; g.ldm = d.ldb; g.v = d.A; g.R = d.n; g.out = d.C; g.ldo = 1;
   } else if (d.m == 1 && !bk) {  // C row = sum_k A[0, k] B[k, :], B rows contiguous along n
-    g.axpy = 1;
+    g.form = kGemvAxpy;
     g.M = d.B; g.ldm = d.ldb; g.v = d.A; g.incv = ak ? 1 : d.lda; g.R = d.n; g.out = d.C; g.ldo = 1;
   } else if (d.n == 1 && !ak) {  // C column = sum_k A[:, k] B[k, 0], A columns contiguous along m
-    g.axpy = 1;
+    g.form = kGemvAxpy;
     g.M = d.A; g.ldm = d.lda; g.v = d.B; g.incv = bk ? 1 : d.ldb; g.R = d.m; g.out = d.C; g.ldo = d.ldc;
   } else {
     return false;
   }
   g.K = d.k;
   if (reinterpret_cast<uintptr_t>(g.M) % 16) return false;
-  if (!g.axpy) {
+  if (g.form == kGemvDot) {
     if (reinterpret_cast<uintptr_t>(g.v) % 16) return false;
     if (g.R > 1 && (g.ldm * es) % 16) return false;
     // enough chunks to keep every CU busy (about 32 per CU), none shorter
