@@ -171,10 +171,11 @@ def library_gemm(torch, sk, S, steps, warmup):
 
 
 # (m, n, k, dtype, layout): k-contiguous matrix operand (dot-product form),
-# then the matrix contiguous along the output (axpy form)
+# the matrix contiguous along the output (axpy form), eight vectors (multi
+# form)
 GEMV_SHAPES = [(1, 16384, 16384, "f16", 1), (16384, 1, 16384, "f16", 1), (1, 16384, 16384, "f32", 1),
                (1, 1, 1 << 24, "f32", 1), (1, 16384, 16384, "f16", 0), (16384, 1, 16384, "f16", 3),
-               (1, 16384, 16384, "f32", 0)]
+               (1, 16384, 16384, "f32", 0), (8, 16384, 16384, "f16", 1), (8, 16384, 16384, "f32", 1)]
 
 
 def gemv_leg(torch, sk, S, reps=20):
@@ -213,7 +214,8 @@ def gemv_leg(torch, sk, S, reps=20):
         by = es * (m * k + k * n + m * n)
         out.append({"shape": [m, n, k], "dtype": name, "layout": ["A row, B row", "A row, B col", "A col, B row",
                                                                   "A col, B col"][layout],
-                    "form": "axpy" if p.tile_n > 0 else "dot", "schedule": int(p.schedule),
+                    "form": "multi" if p.tile_m > 0 else ("axpy" if p.tile_n > 0 else "dot"),
+                    "schedule": int(p.schedule),
                     "chunks": int(p.sk_blocks), "grid": int(p.grid), "us": round(us, 2),
                     "GB_s": round(by / us / 1e3, 1), "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
                     "torch_matmul_us": round(lib_us, 2)})

@@ -447,10 +447,12 @@ def test_matrix_vector_output_contiguous_form(dtype, m, n, k):
 @pytest.mark.parametrize("m,n,k", [(8, 16384, 16384), (16384, 2, 4096), (16, 16, 16), (3, 1000, 4097),
                                    (2, 5, 100003)])
 def test_matrix_vector_few_vectors_form(dtype, m, n, k):
-    """2 .. 16 vectors against k-contiguous rows (both operands k-contiguous)
-    take the multi form: tasks are blocks of 16 rows times chunks of whole
-    64-byte slabs of k (the last chunk ends at k), at least eight slabs each
-    unless there is only one chunk, and enough of them for every CU."""
+    """2 .. 16 vectors (fp16/bf16: 8) against k-contiguous rows (both
+    operands k-contiguous, neither m nor n 1) take the multi form: tasks are
+    blocks of 64 (fp32) or 16 rows times chunks of whole 64-byte slabs of k
+    (the last chunk ends at k), at least eight slabs each unless there is
+    only one chunk, and enough of them for every CU; more vectors keep the
+    tiled schedules."""
     es = 4 if dtype == sk.F32 else 2
     slab = 64 // es
     slots = 512 if dtype == sk.F32 else 256
@@ -458,16 +460,20 @@ def test_matrix_vector_few_vectors_form(dtype, m, n, k):
     d = sk.make_desc(m, n, k, 1.0, 1 << 20, kp, 1 << 21, kp, 0.0, 1 << 22, n, dtype, sk.A_ROW_B_COL)
     p = sk.plan_query(d, None, slots)
     V, R = (m, n) if m <= 16 else (n, m)
-    assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_m == V and p.tile_n == 16
-    S, chunk, blocks = p.sk_blocks, p.tile_k, -(-R // 16)
+    if V > (16 if dtype == sk.F32 else 8):
+        assert p.schedule != sk.SCHED_GEMV_SPLIT
+        return
+    rows = 64 if dtype == sk.F32 else 16
+    assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_m == V and p.tile_n == rows
+    S, chunk, blocks = p.sk_blocks, p.tile_k, -(-R // rows)
     assert p.tiles == V * R and p.total_iters == blocks * S
     assert chunk % slab == 0 and S * chunk >= k > (S - 1) * chunk
     assert chunk >= 8 * slab or S == 1
-    assert 2 * blocks * S >= min(8 * 256, blocks * max(1, k // (8 * slab)))  # chunks round up to slabs
-    # any other operand order, or ABFT, keeps the tiled schedules
+    per_cu = 8 if dtype == sk.F32 else 16
+    assert 2 * blocks * S >= min(per_cu * 256, blocks * max(1, k // (8 * slab)))  # chunks round up to slabs
+    # any other operand order keeps the tiled schedules
     other = sk.make_desc(m, n, k, 1.0, 1 << 20, kp, 1 << 21, n, 0.0, 1 << 22, n, dtype, sk.A_ROW_B_ROW)
-    if min(m, n) > 1:
-        assert sk.plan_query(other, None, slots).schedule != sk.SCHED_GEMV_SPLIT
+    assert sk.plan_query(other, None, slots).schedule != sk.SCHED_GEMV_SPLIT
 
 
 def test_matrix_vector_fallbacks():

@@ -440,14 +440,14 @@ def test_matrix_vector_output_contiguous_large(dtype, m, n, k, layout):
 
 
 def _multi_cases(dtype):
-    """(m, n, k, pad, alpha, beta): 2 .. 16 vectors (m, or n with m > 16)
-    against k-contiguous rows (A row-major, B column-major); pad aligns the
-    rows for a ragged k and strides C."""
+    """(m, n, k, pad, alpha, beta): 2 .. 16 vectors (fp16/bf16: 8; m, or n
+    with m > 16) against k-contiguous rows (A row-major, B column-major); pad
+    aligns the rows for a ragged k and strides C."""
     vec = 4 if dtype == sk.F32 else 8
     out = []
     for k in (1, 5, 31, 64, 1000, 4097):
         pad = (-k) % vec
-        for V in (2, 5, 16):
+        for V in ((2, 5, 16) if dtype == sk.F32 else (2, 5, 8)):
             for R in ((7, 4099) if k <= 1000 else (300,)):
                 out.append((V, R, k, pad, 1.0, 0.0))
                 out.append((R + 16, V, k, pad + vec, 0.5, -1.5))
@@ -456,8 +456,8 @@ def _multi_cases(dtype):
 
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_matrix_vector_few_vectors_against_oracle(dtype):
-    """2 .. 16 vectors against k-contiguous rows take the multi form (MFMA
-    over 16-row blocks and k-chunks; k tails, rows and vectors past the end,
+    """A few vectors against k-contiguous rows take the multi form (MFMA
+    over row blocks and k-chunks; k tails, rows and vectors past the end,
     strided C, alpha/beta) and match the oracle; repeated calls are bitwise
     equal."""
     for (m, n, k, pad, alpha, beta) in _multi_cases(dtype):
@@ -465,7 +465,7 @@ def test_matrix_vector_few_vectors_against_oracle(dtype):
         c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 17 + m + 3 * n + k, pad=pad)
         d = sk.make_desc(m, n, k, alpha, c.dA, c.lda, c.dB, c.ldb, beta, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
         p = sk.plan_query(d)
-        assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_n == 16, (m, n, k)
+        assert p.schedule == sk.SCHED_GEMV_SPLIT and p.tile_n == (64 if dtype == sk.F32 else 16), (m, n, k)
         got = c.run(alpha, beta)
         ref, bound = c.reference(alpha, beta)
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)

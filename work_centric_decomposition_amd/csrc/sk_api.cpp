@@ -343,11 +343,11 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       if (g.form == kGemvAxpy) {  // outputs per task: one wave's width
         out->tile_n = (desc->dtype == SK_F32 ? 4 : 8) * 64;
         out->total_iters = (g.R + out->tile_n - 1) / out->tile_n * g.S;
-      } else if (g.form == kGemvMulti) {  // vectors x 16 rows per task
+      } else if (g.form == kGemvMulti) {  // vectors x rows per task
         out->tile_m = g.V;
-        out->tile_n = 16;
+        out->tile_n = desc->dtype == SK_F32 ? 64 : 16;
         out->tiles = (int64_t)g.V * g.R;
-        out->total_iters = (g.R + 15) / 16 * g.S;
+        out->total_iters = (g.R + out->tile_n - 1) / out->tile_n * g.S;
       } else {
         out->total_iters = g.R * g.S;
       }

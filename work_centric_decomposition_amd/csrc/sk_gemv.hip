@@ -258,18 +258,20 @@ __global__ __launch_bounds__(256) void gemv_part_reduce_kernel(const float *part
 
 // The multi form: D[i][r] = sum_k X[i][k] M[r][k] for vectors i < V (<= 16),
 // rows r < R, both k-contiguous (16-byte aligned base and rows).  Task
-// t = s * blocks + b takes rows [16 b, 16 b + 16) over k-chunk s in slabs of
-// one 16-byte load per lane: lane l loads row 16 b + (l & 15) of M and row
-// (l & 15) of X at k offset VEC (l >> 4) of the slab, rows or vectors past
-// the end as zeros, and the MFMA sums over the slab (fp16/bf16:
-// v_mfma_f32_16x16x32 with X as the first operand, one per 32-k slab;
-// fp32: four v_mfma_f32_16x16x4 steps per 16-k slab, step q taking the
-// q-th element of every lane's four, so that the lane groups cover
-// k = 4 (l >> 4) + q).  Lane l then holds D for vectors 4 (l >> 4) + e and
-// row 16 b + (l & 15).  A slab holding the end of k loads element by
-// element, zeros past k.  The 16 x 16 partial goes to part[s * V R + i R + r]
-// (S > 1) or, with alpha and beta, to out[i ld_v + r ld_r] (S == 1).
-template <int DT>
+// t = s * blocks + b takes rows [16 NB b, 16 NB (b + 1)) (NB blocks of 16)
+// over k-chunk s, in slabs of one 16-byte load per lane and block: lane l
+// loads row 16 (NB b + q) + (l & 15) of M for each block q and row (l & 15)
+// of X (once for the NB blocks) at k offset VEC (l >> 4) of the slab, rows or
+// vectors past the end as zeros, and the MFMAs sum over the slab (fp16 and
+// bf16: one v_mfma_f32_16x16x32 per block and 32-k slab with X as the first
+// operand; fp32: four v_mfma_f32_16x16x4 steps per block and 16-k slab, step
+// e taking the e-th of every lane's four values, so that the lane groups
+// cover k = 4 (l >> 4) + e).  U slabs' loads are in flight.  Lane l then
+// holds D for vectors 4 (l >> 4) + e and rows 16 (NB b + q) + (l & 15).  A slab
+// holding the end of k loads element by element, zeros past k.  The
+// partials go to part[s * V R + i R + r] (S > 1) or, with alpha and beta, to
+// out[i ld_v + r ld_r] (S == 1).
+template <int DT, int NB, int U>
 __global__ __launch_bounds__(256) void gemv_multi_kernel(const void *M, int64_t ldm, const void *X, int64_t ldx,
                                                          int V, int64_t R, int64_t K, int64_t chunk, int64_t S,
                                                          float *part, void *out, int64_t ld_v, int64_t ld_r,
@@ -279,68 +281,84 @@ __global__ __launch_bounds__(256) void gemv_multi_kernel(const void *M, int64_t 
   constexpr int64_t SLAB = 4 * VEC;
   const int lane = threadIdx.x & 63, li = lane & 15, kg = lane >> 4;
   const int64_t waves = (int64_t)gridDim.x * (blockDim.x / 64);
-  const int64_t blocks = (R + 15) / 16, tasks = blocks * S;
+  const int64_t blocks = (R + 16 * NB - 1) / (16 * NB), tasks = blocks * S;
+  const bool xrow = li < V;
+  const T *xp = static_cast<const T *>(X) + (xrow ? li : 0) * ldx + kg * VEC;
   for (int64_t t = (int64_t)blockIdx.x * (blockDim.x / 64) + (threadIdx.x >> 6); t < tasks; t += waves) {
     const int64_t s = t / blocks, b = t - s * blocks;
     const int64_t k0 = s * chunk, k1 = k0 + chunk < K ? k0 + chunk : K;
-    const int64_t row = b * 16 + li;
-    const bool mrow = row < R, xrow = li < V;
-    const T *mp = static_cast<const T *>(M) + (mrow ? row : 0) * ldm + kg * VEC;
-    const T *xp = static_cast<const T *>(X) + (xrow ? li : 0) * ldx + kg * VEC;
-    f4_t acc = {0.f, 0.f, 0.f, 0.f};
-    auto step = [&](const u4_t &mv, const u4_t &xv) {
+    bool mrow[NB];
+    const T *mp[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int64_t row = b * 16 * NB + 16 * q + li;
+      mrow[q] = row < R;
+      mp[q] = static_cast<const T *>(M) + (mrow[q] ? row : 0) * ldm + kg * VEC;
+    }
+    f4_t acc[NB];
+#pragma unroll
+    for (int q = 0; q < NB; ++q) acc[q] = f4_t{0.f, 0.f, 0.f, 0.f};
+    auto step = [&](f4_t &c, const u4_t &mv, const u4_t &xv) {
       if constexpr (DT == SK_F32) {
         const f4_t mf = __builtin_bit_cast(f4_t, mv), xf = __builtin_bit_cast(f4_t, xv);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[q], mf[q], acc, 0, 0, 0);
+        for (int e = 0; e < 4; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(xf[e], mf[e], c, 0, 0, 0);
       } else if constexpr (DT == SK_F16) {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv), __builtin_bit_cast(h8_t, mv),
-                                                     acc, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(h8_t, xv), __builtin_bit_cast(h8_t, mv), c, 0,
+                                                   0, 0);
       } else {
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, xv), __builtin_bit_cast(b8_t, mv),
-                                                      acc, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(b8_t, xv), __builtin_bit_cast(b8_t, mv), c,
+                                                    0, 0, 0);
       }
     };
     const u4_t zero = {0u, 0u, 0u, 0u};
     const int64_t kfull = k0 + (k1 - k0) / SLAB * SLAB;  // whole slabs of this chunk
     int64_t k = k0;
-    for (; k + 4 * SLAB <= kfull; k += 4 * SLAB) {
-      u4_t mv[4], xv[4];
+    for (; k + U * SLAB <= kfull; k += U * SLAB) {
+      u4_t mv[U][NB], xv[U];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        mv[u] = mrow ? *reinterpret_cast<const u4_t *>(mp + k + u * SLAB) : zero;
+      for (int u = 0; u < U; ++u) {
         xv[u] = xrow ? *reinterpret_cast<const u4_t *>(xp + k + u * SLAB) : zero;
+#pragma unroll
+        for (int q = 0; q < NB; ++q) mv[u][q] = mrow[q] ? *reinterpret_cast<const u4_t *>(mp[q] + k + u * SLAB) : zero;
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) step(mv[u], xv[u]);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int q = 0; q < NB; ++q) step(acc[q], mv[u][q], xv[u]);
     }
     for (; k < kfull; k += SLAB) {
-      const u4_t mv = mrow ? *reinterpret_cast<const u4_t *>(mp + k) : zero;
       const u4_t xv = xrow ? *reinterpret_cast<const u4_t *>(xp + k) : zero;
-      step(mv, xv);
+#pragma unroll
+      for (int q = 0; q < NB; ++q) step(acc[q], mrow[q] ? *reinterpret_cast<const u4_t *>(mp[q] + k) : zero, xv);
     }
     if (k < k1) {  // the slab holding the end of k
-      T me[VEC], xe[VEC];
+      T xe[VEC];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        const bool in = k + kg * VEC + e < k1;
-        me[e] = mrow && in ? mp[k + e] : (T)0.f;
-        xe[e] = xrow && in ? xp[k + e] : (T)0.f;
+      for (int e = 0; e < VEC; ++e) xe[e] = xrow && k + kg * VEC + e < k1 ? xp[k + e] : (T)0.f;
+#pragma unroll
+      for (int q = 0; q < NB; ++q) {
+        T me[VEC];
+#pragma unroll
+        for (int e = 0; e < VEC; ++e) me[e] = mrow[q] && k + kg * VEC + e < k1 ? mp[q][k + e] : (T)0.f;
+        step(acc[q], __builtin_bit_cast(u4_t, me), __builtin_bit_cast(u4_t, xe));
       }
-      step(__builtin_bit_cast(u4_t, me), __builtin_bit_cast(u4_t, xe));
     }
-    const int64_t r = b * 16 + li;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int i = 4 * kg + e;
-      if (i >= V || r >= R) continue;
-      if (S > 1) {
-        part[s * (int64_t)V * R + i * R + r] = acc[e];
-      } else {
-        T *dst = static_cast<T *>(out) + i * ld_v + r * ld_r;
-        float o = alpha * acc[e];
-        if (beta != 0.f) o += beta * (float)*dst;
-        *dst = (T)o;
+    for (int q = 0; q < NB; ++q) {
+      const int64_t r = b * 16 * NB + 16 * q + li;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 4 * kg + e;
+        if (i >= V || r >= R) continue;
+        if (S > 1) {
+          part[s * (int64_t)V * R + i * R + r] = acc[q][e];
+        } else {
+          T *dst = static_cast<T *>(out) + i * ld_v + r * ld_r;
+          float o = alpha * acc[q][e];
+          if (beta != 0.f) o += beta * (float)*dst;
+          *dst = (T)o;
+        }
       }
     }
   }
@@ -372,9 +390,13 @@ void launch_axpy(const GemvPlan &g, float *part, float alpha, float beta, hipStr
     launch_reduce_parts(DT, part, g.R, g.R, g.S, g.out, 0, g.ldo, alpha, beta, stream);
 }
 
+// Rows per task and slabs in flight, per element type: fp32 shares each
+// vector load among four 16-row blocks (its vector loads otherwise rival the
+// matrix's); fp16 and bf16 keep one block and eight slabs in flight.
 template <int DT>
 void launch_multi(const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream) {
-  hipLaunchKernelGGL(dev::gemv_multi_kernel<DT>, dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.ldv, g.V,
+  constexpr int NB = DT == SK_F32 ? 4 : 1, U = DT == SK_F32 ? 4 : 8;
+  hipLaunchKernelGGL((dev::gemv_multi_kernel<DT, NB, U>), dim3(g.grid), dim3(256), 0, stream, g.M, g.ldm, g.v, g.ldv, g.V,
                      g.R, g.K, g.chunk, g.S, part, g.out, g.ld_v, g.ld_r, alpha, beta);
   if (g.S > 1 && hipPeekAtLastError() == hipSuccess)
     launch_reduce_parts(DT, part, (int64_t)g.V * g.R, g.R, g.S, g.out, g.ld_v, g.ld_r, alpha, beta, stream);

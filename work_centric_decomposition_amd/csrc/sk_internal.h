@@ -273,10 +273,11 @@ struct Plan {
 //    beta * out[j * ldo] for j < R, M rows of R elements (contiguous along
 //    the output, stride ldm), r < K; the output is cut in blocks of one
 //    wave's width and the K rows in S chunks of `chunk` rows;
-//  kGemvMulti: V (2 .. 16) vectors, rows of v with stride ldv, against the R
-//    k-contiguous rows of M: out[i * ld_v + r * ld_r] = alpha * (v row i) .
-//    (M row r) + beta * (the same) for i < V, r < R; tasks are blocks of 16
-//    rows times S chunks of `chunk` k.
+//  kGemvMulti: V (2 .. 16 for fp32, 2 .. 8 for fp16/bf16) vectors, rows of v
+//    with stride ldv, against the R k-contiguous rows of M:
+//    out[i * ld_v + r * ld_r] = alpha * (v row i) . (M row r) + beta * (the
+//    same) for i < V, r < R; tasks are blocks of 64 (fp32) or 16 rows times
+//    S chunks of `chunk` k.
 // `grid` workgroups of 256 threads.
 enum { kGemvDot = 0, kGemvAxpy = 1, kGemvMulti = 2 };
 struct GemvPlan {
@@ -293,8 +294,8 @@ struct GemvPlan {
 // with 16-byte aligned base and rows, the vector contiguous and 16-byte
 // aligned; axpy form, when the matrix operand is contiguous along the
 // output instead: 16-byte aligned base and rows, any vector stride), or
-// 2 <= m or n <= 16 with both operands k-contiguous and 16-byte aligned
-// (multi form); cus: compute units.
+// 2 <= m or n <= 16 (fp16/bf16: 8), neither 1, with both operands
+// k-contiguous and 16-byte aligned (multi form); cus: compute units.
 bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g);
 int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float beta, hipStream_t stream);
 

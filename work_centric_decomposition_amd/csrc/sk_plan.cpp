@@ -441,7 +441,9 @@ bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
   if (d.k <= 0) return false;
   // 2 .. 16 vectors against k-contiguous rows (neither m nor n 1): the
   // multi form
-  const bool few_m = d.m >= 2 && d.m <= 16, few_n = d.n >= 2 && d.n <= 16;
+  // (fp16 and bf16: up to 8; beyond that the tiled kernels are as fast)
+  const int64_t vmax = d.dtype == SK_F32 ? 16 : 8;
+  const bool few_m = d.m >= 2 && d.m <= vmax, few_n = d.n >= 2 && d.n <= vmax;
   if ((few_m || few_n) && d.m >= 2 && d.n >= 2 && ak && bk) {
     g.form = kGemvMulti;
     if (few_m) {  // rows of A against the rows of column-major B
@@ -455,10 +457,12 @@ bool gemv_plan(const sk_gemm_desc &d, int cus, GemvPlan &g) {
     if (reinterpret_cast<uintptr_t>(g.M) % 16 || reinterpret_cast<uintptr_t>(g.v) % 16) return false;
     if ((g.ldm * es) % 16 || (g.ldv * es) % 16) return false;
     // k slabs of one load per lane (64 bytes of every row per wave load);
-    // chunks of at least eight slabs, about 8 (row block, chunk) tasks per CU
+    // chunks of at least eight slabs; tasks of 64 rows (fp32) or 16, about 8
+    // (fp32) or 16 of them per CU
     const int64_t slab = 64 / es;
-    const int64_t blocks = cdiv(g.R, 16);
-    const int64_t want = cdiv((int64_t)8 * cus, blocks);
+    const int64_t rows = d.dtype == SK_F32 ? 64 : 16;
+    const int64_t blocks = cdiv(g.R, rows);
+    const int64_t want = cdiv((int64_t)(d.dtype == SK_F32 ? 8 : 16) * cus, blocks);
     int64_t S = std::max<int64_t>(1, std::min<int64_t>(want, g.K / (8 * slab)));
     g.chunk = cdiv(cdiv(g.K, S), slab) * slab;
     g.S = cdiv(g.K, g.chunk);
