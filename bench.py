@@ -46,11 +46,11 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "da26b8555459ad4e",
+TRAFFIC = {"kernel_hash": "ca8108144a0c362b",
            # mean over the six launches of one step (1024^3 ... 6144^3)
-           "sgemm-sweep": 985046357,
+           "sgemm-sweep": 1227751763,
            # fp16 8192^3 launch
-           "hgemm-8192": 1762027546}
+           "hgemm-8192": 1781558212}
 
 
 def kernel_hash():
