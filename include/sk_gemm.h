@@ -8,6 +8,10 @@
  * "two-tile Stream-K + data-parallel" hybrid of its section 5.2, optionally
  * with threadblock-level ABFT checksums ("Anatomy of High-Performance GEMM
  * with Online Fault Tolerance on GPUs", threadblock-level scheme, Figs. 5-7).
+ * Matrix-vector products (m or n = 1) and a few vectors at once (up to 16,
+ * fp16/bf16 up to 8) take the even split of "KBLAS: An Optimized Library for
+ * Dense Matrix-Vector Multiplication on GPU Accelerators" (section 6.2)
+ * instead of output tiles (SK_SCHED_GEMV_SPLIT).
  *
  * Conventions shared by every entry point:
  *  - A is m x k, B is k x n, C is m x n.  Storage order of A and B is given by
@@ -87,11 +91,16 @@ typedef enum {
  *                     the matrix operand contiguous along the output instead
  *                     (16-byte aligned base and rows, any vector stride),
  *                     each workgroup wave accumulates a block of outputs over
- *                     a chunk of the k rows.  Chunk sums are added in a fixed
- *                     order by a second kernel, so results are reproducible.
- *                     Chosen explicitly, it returns SK_ERR_UNSUPPORTED for
- *                     other shapes or alignments, and with ABFT.
- *  SK_SCHED_AUTO      SK_SCHED_GEMV_SPLIT for eligible matrix-vector shapes
+ *                     a chunk of the k rows.  A few vectors (2 <= m <= 16, or
+ *                     2 <= n <= 16 with m > 16; fp16/bf16 up to 8) against
+ *                     k-contiguous rows, both operands k-contiguous and
+ *                     16-byte aligned, are split the same way into blocks of
+ *                     rows and k-chunks on MFMA.  Chunk sums are added in a
+ *                     fixed order by a second kernel, so results are
+ *                     reproducible.  Chosen explicitly, it returns
+ *                     SK_ERR_UNSUPPORTED for other shapes or alignments, and
+ *                     with ABFT.
+ *  SK_SCHED_AUTO      SK_SCHED_GEMV_SPLIT for the shapes it takes (above)
  *                     (with default tile, grid and ABFT options); otherwise
  *                     SK_SCHED_XCD_ALIGNED with the tile instance, quantum and
  *                     grid chosen by the runtime model, or its data-parallel
@@ -182,12 +191,15 @@ typedef struct {
 
 /* Plan of one call, for inspection (host only, needs no GPU when
  * sk_plan_query is given an explicit slot count).  For SK_SCHED_GEMV_SPLIT:
- * tiles = the number of outputs (m or n), tile_k = the k-chunk length
- * in elements, sk_blocks = chunks per output, iters_per_tile = 1, tile_n =
- * 0 for the dot-product form, else the outputs one task covers (64 x the
- * elements in 16 bytes), total_iters = the tasks (outputs or output blocks
- * times chunks), grid = workgroups of 256 threads; the other fields that
- * describe GEMM tiles are 0, and sk_plan_segments lists no segments. */
+ * tiles = the number of outputs, tile_k = the k-chunk length in elements,
+ * sk_blocks = chunks per output, iters_per_tile = 1; tile_m = tile_n = 0
+ * for the dot-product form; tile_m = 0 and tile_n = the outputs one task
+ * covers (64 x the elements in 16 bytes) for the form with the matrix
+ * contiguous along the output; tile_m = the vectors and tile_n = the rows
+ * one task covers for a few vectors; total_iters = the tasks (outputs or
+ * output blocks times chunks), grid = workgroups of 256 threads; the other
+ * fields that describe GEMM tiles are 0, and sk_plan_segments lists no
+ * segments. */
 typedef struct {
   int32_t tile_m, tile_n, tile_k; /* BLK_M, BLK_N, BLK_K of the kernel */
   int32_t slots;                  /* p: workgroups resident at once */
