@@ -64,9 +64,6 @@ template <int DT> struct Elem;
 template <> struct Elem<SK_F16> {
   using T = _Float16;
   using V8 = h8_t;
-  static __device__ __forceinline__ f4_t mfma(V8 a, V8 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ float ld(const void *p, int64_t i) {
     return (float)static_cast<const T *>(p)[i];
   }
@@ -85,9 +82,6 @@ template <> struct Elem<SK_F16> {
 template <> struct Elem<SK_BF16> {
   using T = __bf16;
   using V8 = b8_t;
-  static __device__ __forceinline__ f4_t mfma(V8 a, V8 b, f4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-  }
   static __device__ __forceinline__ float ld(const void *p, int64_t i) {
     return (float)static_cast<const T *>(p)[i];
   }
