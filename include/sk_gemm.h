@@ -7,7 +7,10 @@
  * work-centric decomposition of that page's section 4 (Algorithm 5) and the
  * "two-tile Stream-K + data-parallel" hybrid of its section 5.2, optionally
  * with threadblock-level ABFT checksums ("Anatomy of High-Performance GEMM
- * with Online Fault Tolerance on GPUs", threadblock-level scheme, Figs. 5-7).
+ * with Online Fault Tolerance on GPUs", threadblock-level scheme, Figs. 5-7;
+ * the column and row encodings of each tile row of A and tile column of B
+ * are formed once per call by a separate kernel, and the MAC loop keeps
+ * only the checksum updates).
  * Matrix-vector products (m or n = 1) and a few vectors at once (up to 16,
  * fp16/bf16 up to 8) take the even split of "KBLAS: An Optimized Library for
  * Dense Matrix-Vector Multiplication on GPU Accelerators" (section 6.2)
@@ -252,7 +255,11 @@ int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t
  * chosen explicitly whose positions or quanta products would reach 2^31
  * (k of several million with the XCD-aware schedule) returns
  * SK_ERR_UNSUPPORTED; AUTO then takes the two-tile hybrid, else the
- * data-parallel order. */
+ * data-parallel order.  Stream-ordered temporaries (hipMallocAsync, freed
+ * on the stream after the GEMM; SK_ERR_NO_MEMORY when one cannot be had):
+ * the k-contiguous copy of an operand the kernels cannot read in place
+ * (plan packs bits), and in ABFT mode the operands' checksum encodings,
+ * (tiles_m + tiles_n) * ceil(k/32) * 256 bytes for 128 x 128 tiles. */
 int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
                hipStream_t stream);
 

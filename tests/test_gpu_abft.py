@@ -167,6 +167,37 @@ def test_two_faults_in_one_domain_are_uncorrectable():
     assert rep.detected == 1 and rep.uncorrectable == 1 and rep.corrected == 0
 
 
+def test_faults_on_ragged_edges_are_corrected():
+    """Faults in partial tiles at the matrix edge, every layout: rows of A and
+    columns of B past the matrix are left out of the encodings."""
+    for layout in range(4):
+        c = Case(200, 150, 300, sk.F32, layout, 93 + layout)
+        faults = [(199, 149, 0, 0, 0, 1000.0), (130, 20, 0, 0, 0, -1000.0)]
+        got, rep = _run_abft(c, faults)
+        _check_corrected(c, got, faults, rep)
+
+
+def test_abft_on_repacked_operands():
+    """k-major rows that are not 16-byte aligned are repacked before the GEMM;
+    the encodings are formed from the copies the kernel reads."""
+    for layout in range(4):
+        c = Case(300, 260, 333, sk.F32, layout, 95 + layout, pad=1)
+        d = sk.make_desc(c.m, c.n, c.k, 1.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc, sk.F32,
+                         layout)
+        p = sk.plan_query(d, sk.make_options(abft=True))
+        ref, bound = c.reference()
+        c.reset_c()
+        got, rep = _run_abft(c)
+        assert (rep.detected, rep.n_records) == (0, 0), (layout, p.packs, _records(rep))
+        assert rel_err(got, sk.F32, ref, bound) <= TOL[sk.F32]
+        if layout == sk.A_ROW_B_COL:
+            assert p.packs == 3, p.packs
+        c.reset_c()
+        faults = [(123, 201, 0, 0, 0, 1000.0)]
+        got, rep = _run_abft(c, faults)
+        _check_corrected(c, got, faults, rep)
+
+
 @pytest.mark.parametrize("bit", [31, 30, 29, 28, 27, 26, 25, 24, 23, 22, 21])
 def test_bit_flips_of_large_effect(bit):
     c = Case(512, 512, 1024, sk.F32, sk.A_ROW_B_ROW, 300 + bit)

@@ -272,7 +272,35 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   a.abft = o.abft; a.n_faults = o.n_faults; a.faults = o.faults; a.report = report;
   a.abft_tau = o.abft_tau > 0 ? o.abft_tau : 1.0f;
 
+  // ABFT: the encodings of every tile row of A and tile column of B, formed
+  // once from the operands the kernel reads
+  float *enc = nullptr;
+  if (o.abft) {
+    const int64_t kb = P.ipt;
+    const int64_t a_floats = P.tiles_m * kb * 64;
+    e = hipMallocAsync(reinterpret_cast<void **>(&enc), (size_t)(a_floats + P.tiles_n * kb * 64) * sizeof(float),
+                       stream);
+    if (e != hipSuccess) {
+      (void)hipGetLastError();
+      if (pa) (void)hipFreeAsync(pa, stream);
+      if (pb) (void)hipFreeAsync(pb, stream);
+      return SK_ERR_NO_MEMORY;
+    }
+    rc = launch_abft_encode(static_cast<const float *>(a.A), a.lda, a.a_kmajor != 0, d.m, d.k, kb, enc, stream);
+    if (rc == hipSuccess)
+      rc = launch_abft_encode(static_cast<const float *>(a.B), a.ldb, a.b_kmajor != 0, d.n, d.k, kb,
+                              enc + a_floats, stream);
+    if (rc != hipSuccess) {
+      (void)hipFreeAsync(enc, stream);
+      if (pa) (void)hipFreeAsync(pa, stream);
+      if (pb) (void)hipFreeAsync(pb, stream);
+      return hip_fail((hipError_t)rc, "ABFT encoding kernel");
+    }
+    a.enc_a = enc; a.enc_b = enc + a_floats; a.enc_kb = (int32_t)kb;
+  }
+
   rc = launch_gemm(P, a, stream);
+  if (enc) (void)hipFreeAsync(enc, stream);
   if (pa) (void)hipFreeAsync(pa, stream);
   if (pb) (void)hipFreeAsync(pb, stream);
   if (rc != hipSuccess) return hip_fail((hipError_t)rc, "GEMM kernel launch");

@@ -337,6 +337,10 @@ struct KernelArgs {
   const sk_fault *faults;
   sk_abft_report *report;
   float abft_tau;
+  // ABFT encodings (abft_encode_kernel): per 128-row tile of A and 128-column
+  // tile of B and per k-iteration of 32, the 32 sums then the 32 absolute sums
+  const float *enc_a, *enc_b;
+  int32_t enc_kb;      // k-iterations per tile in the encoding arrays
 };
 
 // Kernel launchers (sk_kernels.hip).  Return a hipError_t value.
@@ -349,6 +353,13 @@ int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t l
 int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_t rows,
                 int64_t k, void *dst, int64_t ldd, hipStream_t stream);
 int launch_zero_report(sk_abft_report *report, hipStream_t stream);
+// ABFT encodings of an fp32 operand of `rows` rows (m for A, n for B) and k
+// columns: for each 128-row tile and each k < 32*kb, the sum of the tile's
+// rows and of their absolute values (rows past `rows` left out, k past `k`
+// zero), written to out[(tile*kb + k/32)*64 + k%32] and [... + 32].
+// Element (r, l) is X[r*ld + l] when kmajor, else X[l*ld + r].
+int launch_abft_encode(const float *X, int64_t ld, bool kmajor, int64_t rows, int64_t k, int64_t kb,
+                       float *out, hipStream_t stream);
 // Occupancy query for the GEMM kernel of `dtype` (fp32: with or without ABFT).
 int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu);
 

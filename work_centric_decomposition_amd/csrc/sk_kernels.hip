@@ -716,24 +716,28 @@ __device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (
 
 // ---------------------------------------------------------------- ABFT
 //
-// Threadblock-level ABFT of the fault-tolerant GEMM page, per work segment.
-// Each k-iteration, from the tiles already staged in LDS:
+// Threadblock-level ABFT of the fault-tolerant GEMM page, per work segment:
 //   encodings   (e^T A)_k = sum_i A_ik,  (B e)_k = sum_j B_kj   (and |.| sums)
+//               over the tile's rows of A and columns of B;
 //   checksums   rc_i += sum_k A_ik (B e)_k     -- row checksum of C = A B
 //               cc_j += sum_k (e^T A)_k B_kj   -- column checksum
 //               ra_i, ca_j: the same with |A|, |B| (detection threshold).
-// At the end of the segment (before its partial store, or before the owner
-// adds its peers' partials) the row and column sums of the accumulators are
-// compared with the checksums: a row mismatches when |sum - rc_i| exceeds
-// tau * 2^-24 * sqrt(k_seg) * ra_i or is not finite (likewise columns), where
-// k_seg is the number of k values the segment accumulated: the rounding
-// error of an fp32 dot product of length k grows like sqrt(k) u sum|a||b|.  One mismatching
-// row and one mismatching column locate the fault; the element is recomputed
-// from its row checksum, c_ij = rc_i - sum_{l != j} c_il.  Any other pattern
-// is reported as uncorrectable.  All reductions run in a fixed order.
+// The encodings depend only on the operands, and every workgroup of a tile
+// row (column) needs the same ones, so they are formed once per call by
+// abft_encode_kernel, read from memory into LDS with the tiles two
+// iterations ahead, and only the checksum updates run in the MAC loop, from
+// the staged tiles.  At the end of the segment (before its partial store, or
+// before the owner adds its peers' partials) the row and column sums of the
+// accumulators are compared with the checksums: a row mismatches when
+// |sum - rc_i| exceeds tau * 2^-24 * sqrt(k_seg) * ra_i or is not finite
+// (likewise columns), where k_seg is the number of k values the segment
+// accumulated: the rounding error of an fp32 dot product of length k grows
+// like sqrt(k) u sum|a||b|.  One mismatching row and one mismatching column
+// locate the fault; the element is recomputed from its row checksum,
+// c_ij = rc_i - sum_{l != j} c_il.  Any other pattern is reported as
+// uncorrectable.  All reductions run in a fixed order.
 struct AbftLds {
-  alignas(16) float enc[4][16][SCfg::BK];  // per-part encodings: e^T A, e^T|A|, B e, |B| e
-  alignas(16) float e[4][SCfg::BK];  // encodings of the iteration
+  alignas(16) float e[2][4][SCfg::BK];  // per stage: e^T A, e^T|A|, B e, |B| e
   float part[4][2][128];      // rc, ra, cc, ca: two k-halves
   float sums[2][2][128];      // row sums per wave column, column sums per wave row
   float others[SCfg::NT / 64];
@@ -748,15 +752,6 @@ struct AbftPart {
 __device__ __forceinline__ AbftLds &abft_lds() {
   __shared__ AbftLds L;
   return L;
-}
-
-template <bool KMAJOR>
-__device__ __forceinline__ float s_elem(int base_off, int mn, int k) {
-  if (KMAJOR) {
-    const int c = k >> 2;
-    return *reinterpret_cast<const float *>(smem + base_off + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4) + (k & 3) * 4);
-  }
-  return s_mn_elem(base_off, mn, k);
 }
 
 // The 16 k values 16 h .. 16 h + 15 of row (m or n) `mn` of a staged tile:
@@ -778,99 +773,39 @@ __device__ __forceinline__ void s_row16(int base_off, int mn, int h, float (&v)[
   }
 }
 
-// Partial encodings of one staged operand tile (128 rows of the operand by
-// BK = 32 values of k): sums over the rows and of their absolute values, by
-// 128 threads u, written to L.enc[q0] and L.enc[q0 + 1] as [part][k].
-//  k-major: part p = u >> 3 sums rows 8p .. 8p+7 of 16-byte chunk c = u & 7
-//    (k = 4c .. 4c+3) with 128-bit reads (16 parts); rows past the matrix
-//    were loaded as zeros.
-//  mn-major: thread u sums row k = u & 31 over columns 32p .. 32p+31
-//    (p = u >> 5, 4 parts); each lane starts at a different chunk so that the
-//    32 rows read at once fall in distinct bank groups; columns past the
-//    matrix in a partial chunk are masked.
-template <bool KMAJOR>
-__device__ __forceinline__ void enc_part(AbftLds &L, int q0, int base, int u, int valid) {
-  if (KMAJOR) {
-    const int c = u & 7, p = u >> 3;
-    f4_t sm = {0.f, 0.f, 0.f, 0.f}, sa = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int r = 0; r < 8; ++r) {
-      const int row = 8 * p + r;
-      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base + row * 128 + ((c ^ ((row >> 1) & 7)) << 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) { sm[e] += x[e]; sa[e] += fabsf(x[e]); }
-    }
-    *reinterpret_cast<f4_t *>(&L.enc[q0][p][4 * c]) = sm;
-    *reinterpret_cast<f4_t *>(&L.enc[q0 + 1][p][4 * c]) = sa;
-  } else {
-    const int k = u & 31, p = u >> 5;
-    float sm = 0.f, sa = 0.f;
-#pragma unroll
-    for (int cc = 0; cc < 8; ++cc) {
-      const int c = 8 * p + ((cc + k) & 7);
-      const int pos = c ^ (4 * ((k >> 2) & 3));
-      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base + k * 512 + pos * 16);
-#pragma unroll
-      for (int e = 0; e < 4; ++e)
-        if (4 * c + e < valid) { sm += x[e]; sa += fabsf(x[e]); }
-    }
-    L.enc[q0][p][k] = sm;
-    L.enc[q0 + 1][p][k] = sa;
-  }
-}
-
+// Checksum update of one staged k-iteration: thread t covers row and column
+// t % 128 of the tile over half of the k range (entries past the end of k
+// are zero in the staged tiles and in the encodings).
 template <bool AK, bool BKM>
-__device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, int n_valid, int k_valid,
-                                            AbftPart &pt) {
+__device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, int n_valid, AbftPart &pt) {
   const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
   const int t = threadIdx.x;
-  {  // encodings: threads 0-127 form e^T A and e^T|A|, threads 128-255 B e and |B| e
-    const int u = t & 127;
-    const bool is_b = t >= 128;
-    if (is_b) enc_part<BKM>(L, 2, Bs, u, n_valid);
-    else enc_part<AK>(L, 0, As, u, m_valid);
-  }
-  __syncthreads();
-  if (t < 4 * SCfg::BK) {
-    const int q = t / SCfg::BK, k = t % SCfg::BK;
-    const bool kmaj = q < 2 ? AK : BKM;
-    const int parts = kmaj ? 16 : 4;
-    float v = 0.f;
+  const int i = t & 127, h = t >> 7;
+  if (i < m_valid) {
+    float v[16];
+    s_row16<AK>(As, i, h, v);
 #pragma unroll
-    for (int p = 0; p < 16; ++p)
-      if (p < parts) v += L.enc[q][p][k];
-    L.e[q][k] = v;
-  }
-  __syncthreads();
-  {  // checksums: thread t covers row / column t % 128 over half of the k range
-    // (entries past k_valid are zero in the staged tiles)
-    const int i = t & 127, h = t >> 7;
-    if (i < m_valid) {
-      float v[16];
-      s_row16<AK>(As, i, h, v);
+    for (int c = 0; c < 4; ++c) {
+      const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[stage][2][16 * h + 4 * c]);
+      const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[stage][3][16 * h + 4 * c]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[2][16 * h + 4 * c]);
-        const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[3][16 * h + 4 * c]);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pt.rc += v[4 * c + e] * eb[e];
-          pt.ra += fabsf(v[4 * c + e]) * eba[e];
-        }
+      for (int e = 0; e < 4; ++e) {
+        pt.rc += v[4 * c + e] * eb[e];
+        pt.ra += fabsf(v[4 * c + e]) * eba[e];
       }
     }
-    if (i < n_valid) {
-      float v[16];
-      s_row16<BKM>(Bs, i, h, v);
+  }
+  if (i < n_valid) {
+    float v[16];
+    s_row16<BKM>(Bs, i, h, v);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[0][16 * h + 4 * c]);
-        const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[1][16 * h + 4 * c]);
+    for (int c = 0; c < 4; ++c) {
+      const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[stage][0][16 * h + 4 * c]);
+      const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[stage][1][16 * h + 4 * c]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          pt.cc += ea[e] * v[4 * c + e];
-          pt.ca += eaa[e] * fabsf(v[4 * c + e]);
-        }
+      for (int e = 0; e < 4; ++e) {
+        pt.cc += ea[e] * v[4 * c + e];
+        pt.ca += eaa[e] * fabsf(v[4 * c + e]);
       }
     }
   }
@@ -1048,6 +983,22 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   const int n = le - lb;
   if (n <= 0) return;
   AbftPart pt{0.f, 0.f, 0.f, 0.f};
+  // ABFT: threads 0-127 carry the encodings of a k-iteration (64 floats of
+  // the tile row's A encodings, then 64 of the tile column's B encodings)
+  // from memory to the stage's LDS slot: loaded with the stage's tiles,
+  // stored after the next wait for them, read after the barrier after that.
+  const bool enc_lane = ABFT && threadIdx.x < 128;
+  const float *esrc = nullptr;
+  float ev = 0.f, ev1 = 0.f;
+  if constexpr (ABFT) {
+    const int t = threadIdx.x;
+    esrc = t < 64 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 64 + t
+                  : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 64 + (t - 64);
+    if (enc_lane) {
+      ev = esrc[(int64_t)lb * 64];
+      if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 64];
+    }
+  }
   SLoader<AK> la;
   SLoader<BKM> lbd;
   la.init(a.A, a.lda, m0, a.m, a.k, a.a_kext);
@@ -1063,6 +1014,13 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
+  if constexpr (ABFT) {
+    if (enc_lane) {
+      AbftLds &L = abft_lds();
+      (&L.e[0][0][0])[threadIdx.x] = ev;
+      if (n > 1) (&L.e[1][0][0])[threadIdx.x] = ev1;
+    }
+  }
   __syncthreads();
   f4_t a0[SCfg::MB], b0[SCfg::NB], a1[SCfg::MB], b1[SCfg::NB];
   s_frags<AK, BKM>(0, 0, wm, wn, a0, b0);
@@ -1072,13 +1030,20 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     __builtin_amdgcn_sched_barrier(0);
     s_mfmas(a0, b0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ABFT) {
-      const int kv = a.k - (lb + i) * SCfg::BK;
-      abft_update<AK, BKM>(abft_lds(), buf, a.m - m0, a.n - n0, kv < SCfg::BK ? kv : SCfg::BK, pt);
-    }
+    if constexpr (ABFT) abft_update<AK, BKM>(abft_lds(), buf, a.m - m0, a.n - n0, pt);
     __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (ABFT) {
+      // the encodings of iteration i+1, loaded at iteration i-1 (the
+      // prologue stored those of iterations 0 and 1)
+      if (enc_lane && i >= 1 && i + 1 < n) (&abft_lds().e[buf ^ 1][0][0])[threadIdx.x] = ev;
+    }
     __syncthreads();
-    if (i + 2 < n) load(buf, lb + i + 2);
+    if (i + 2 < n) {
+      load(buf, lb + i + 2);
+      if constexpr (ABFT) {
+        if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 64];
+      }
+    }
     if (i + 1 < n) s_frags<AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
     s_mfmas(a1, b1, acc);
@@ -1267,6 +1232,33 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
   }
 }
 
+// ABFT encodings of one fp32 operand (rows x k): thread (tile, l) sums the
+// tile's 128 rows at k = l in row order, and their absolute values.  Threads
+// of a wave take consecutive l, so a k-contiguous operand is read coalesced.
+__global__ __launch_bounds__(256) void abft_encode_kernel(const float *X, int64_t ld, int kmajor, int64_t rows,
+                                                         int64_t k, int64_t kb, float *out) {
+  const int64_t kp = kb * 32;
+  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t tiles = (rows + 127) / 128;
+  if (g >= tiles * kp) return;
+  const int64_t tile = g / kp, l = g % kp;
+  float sm = 0.f, sa = 0.f;
+  if (l < k) {
+    const int64_t r0 = tile * 128, r1 = rows < r0 + 128 ? rows : r0 + 128;
+    const float *p = kmajor ? X + r0 * ld + l : X + l * ld + r0;
+    const int64_t step = kmajor ? ld : 1;
+#pragma unroll 8
+    for (int64_t r = r0; r < r1; ++r, p += step) {
+      const float x = *p;
+      sm += x;
+      sa += fabsf(x);
+    }
+  }
+  float *o = out + (tile * kb + l / 32) * 64 + (l % 32);
+  o[0] = sm;
+  o[32] = sa;
+}
+
 __global__ void zero_words_kernel(int32_t *p, int64_t words) {
   for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < words;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -1351,6 +1343,16 @@ int launch_zero_report(sk_abft_report *report, hipStream_t stream) {
   const int64_t words = (int64_t)(sizeof(sk_abft_report) / 4);
   hipLaunchKernelGGL(dev::zero_words_kernel, dim3(1), dim3(256), 0, stream,
                      reinterpret_cast<int32_t *>(report), words);
+  return (int)hipGetLastError();
+}
+
+int launch_abft_encode(const float *X, int64_t ld, bool kmajor, int64_t rows, int64_t k, int64_t kb,
+                       float *out, hipStream_t stream) {
+  const int64_t threads = (rows + 127) / 128 * kb * 32;
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks <= 0 || blocks > INT32_MAX) return (int)hipErrorInvalidValue;
+  hipLaunchKernelGGL(dev::abft_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, ld,
+                     kmajor ? 1 : 0, rows, k, kb, out);
   return (int)hipGetLastError();
 }
 
