@@ -46,7 +46,7 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "8c330a6304972d36",
+TRAFFIC = {"kernel_hash": "642ef77c9ee44326",
            # mean over the six launches of one step (1024^3 ... 6144^3)
            "sgemm-sweep": 1227751763,
            # fp16 8192^3 launch
@@ -87,6 +87,8 @@ def parse():
                    help="measure the sustained MFMA rates and the HBM read rate only")
     p.add_argument("--gemv", action="store_true",
                    help="time the matrix-vector products only (m == 1 or n == 1 shapes)")
+    p.add_argument("--abft", action="store_true",
+                   help="time the fp32 4096^3 GEMM with and without ABFT only")
     p.add_argument("--compare-schedules", action="store_true",
                    help="time AUTO, the page's schedules and data-parallel on a few fp16 shapes "
                         "(one launch each with --steps 1, e.g. under rocprofv3 --pmc)")
@@ -743,6 +745,9 @@ def main():
         return
     if args.peaks:
         print(json.dumps(measured_peaks(torch, sk)), flush=True)
+        return
+    if args.abft:
+        print(json.dumps(abft_overhead(torch, sk, S, steps=args.steps)), flush=True)
         return
     if args.skinny:
         for r in skinny_leg(torch, sk, S, reps=args.steps):

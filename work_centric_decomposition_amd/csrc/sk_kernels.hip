@@ -1232,31 +1232,63 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
   }
 }
 
-// ABFT encodings of one fp32 operand (rows x k): thread (tile, l) sums the
-// tile's 128 rows at k = l in row order, and their absolute values.  Threads
-// of a wave take consecutive l, so a k-contiguous operand is read coalesced.
+// ABFT encodings of one fp32 operand (rows x k): workgroup (tile, chunk)
+// stages the tile's 128 rows at 64 values of k in LDS (a wave reads 64
+// consecutive elements of the operand in either storage order), then four
+// threads per k sum 32 rows each in row order and the four sums are added
+// in order; likewise for the absolute values.
 __global__ __launch_bounds__(256) void abft_encode_kernel(const float *X, int64_t ld, int kmajor, int64_t rows,
                                                          int64_t k, int64_t kb, float *out) {
-  const int64_t kp = kb * 32;
-  const int64_t g = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t tiles = (rows + 127) / 128;
-  if (g >= tiles * kp) return;
-  const int64_t tile = g / kp, l = g % kp;
-  float sm = 0.f, sa = 0.f;
-  if (l < k) {
-    const int64_t r0 = tile * 128, r1 = rows < r0 + 128 ? rows : r0 + 128;
-    const float *p = kmajor ? X + r0 * ld + l : X + l * ld + r0;
-    const int64_t step = kmajor ? ld : 1;
+  __shared__ float T[64][129];
+  __shared__ float P[2][4][64];
+  const int t = threadIdx.x;
+  const int64_t chunks = (kb * 32 + 63) / 64;
+  const int64_t tile = blockIdx.x / chunks, k0 = (blockIdx.x % chunks) * 64;
+  const int64_t r0 = tile * 128;
+  const int64_t rv = rows - r0 < 128 ? rows - r0 : 128;  // valid rows of the tile
+  if (kmajor) {
+    const int kk = t & 63, rr = t >> 6;
+    const bool kok = k0 + kk < k;
+    const float *p = X + r0 * ld + k0 + kk;
 #pragma unroll 8
-    for (int64_t r = r0; r < r1; ++r, p += step) {
-      const float x = *p;
+    for (int q = 0; q < 32; ++q) {
+      const int r = 4 * q + rr;
+      T[kk][r] = kok && r < rv ? p[(int64_t)r * ld] : 0.f;
+    }
+  } else {
+    const int r = t & 127, kq = t >> 7;
+    const bool rok = r < rv;
+    const float *p = X + k0 * ld + r0 + r;
+#pragma unroll 8
+    for (int q = 0; q < 32; ++q) {
+      const int kk = 2 * q + kq;
+      T[kk][r] = rok && k0 + kk < k ? p[(int64_t)kk * ld] : 0.f;
+    }
+  }
+  __syncthreads();
+  {
+    const int kk = t & 63, g = t >> 6;
+    float sm = 0.f, sa = 0.f;
+#pragma unroll 8
+    for (int r = 32 * g; r < 32 * g + 32; ++r) {
+      const float x = T[kk][r];
       sm += x;
       sa += fabsf(x);
     }
+    P[0][g][kk] = sm;
+    P[1][g][kk] = sa;
   }
-  float *o = out + (tile * kb + l / 32) * 64 + (l % 32);
-  o[0] = sm;
-  o[32] = sa;
+  __syncthreads();
+  if (t < 64) {
+    const int64_t l = k0 + t;
+    if (l < kb * 32) {
+      const float sm = ((P[0][0][t] + P[0][1][t]) + P[0][2][t]) + P[0][3][t];
+      const float sa = ((P[1][0][t] + P[1][1][t]) + P[1][2][t]) + P[1][3][t];
+      float *o = out + (tile * kb + l / 32) * 64 + (l % 32);
+      o[0] = sm;
+      o[32] = sa;
+    }
+  }
 }
 
 __global__ void zero_words_kernel(int32_t *p, int64_t words) {
@@ -1348,8 +1380,7 @@ int launch_zero_report(sk_abft_report *report, hipStream_t stream) {
 
 int launch_abft_encode(const float *X, int64_t ld, bool kmajor, int64_t rows, int64_t k, int64_t kb,
                        float *out, hipStream_t stream) {
-  const int64_t threads = (rows + 127) / 128 * kb * 32;
-  const int64_t blocks = (threads + 255) / 256;
+  const int64_t blocks = (rows + 127) / 128 * ((kb * 32 + 63) / 64);
   if (blocks <= 0 || blocks > INT32_MAX) return (int)hipErrorInvalidValue;
   hipLaunchKernelGGL(dev::abft_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, ld,
                      kmajor ? 1 : 0, rows, k, kb, out);
