@@ -50,7 +50,9 @@ TRAFFIC = {"kernel_hash": "642ef77c9ee44326",
            # mean over the six launches of one step (1024^3 ... 6144^3)
            "sgemm-sweep": 1227751763,
            # fp16 8192^3 launch
-           "hgemm-8192": 1781558212}
+           "hgemm-8192": 1781558212,
+           # bf16 8192^3 launch (same counter runs)
+           "hgemm-8192-bf16": 1760224688}
 
 
 def kernel_hash():
@@ -801,7 +803,7 @@ def main():
                                            "peak": PEAK_TFLOPS[name], "unit": "TFLOP/s",
                                            "frac": round(achieved / PEAK_TFLOPS[name], 4),
                                            # counters were taken on the fp16 launch only
-                                           "traffic": traffic_for(wl) if name == "f16" else None,
+                                           "traffic": traffic_for(wl if name == "f16" else wl + "-bf16"),
                                            "kernel": f"hgemm_kernel<{name}>",
                                            "launch_ms": round(per_launch[0], 4)})
                 del h
