@@ -738,14 +738,16 @@ __device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (
 // uncorrectable.  All reductions run in a fixed order.
 struct AbftLds {
   alignas(16) float e[2][4][SCfg::BK];  // per stage: e^T A, e^T|A|, B e, |B| e
-  float part[4][2][128];      // rc, ra, cc, ca: two k-halves
+  float part[4][4][128];      // rc, ra, cc, ca: per wave (a quarter of the k range)
   float sums[2][2][128];      // row sums per wave column, column sums per wave row
   float others[SCfg::NT / 64];
   int bad[4];                 // mismatching rows, one such row, columns, one such column
 };
 
+// Checksums of one thread: rows (columns) 4 (t % 32) .. + 3 of the tile over
+// its k values.
 struct AbftPart {
-  float rc, ra, cc, ca;
+  float rc[4], ra[4], cc[4], ca[4];
 };
 
 // The ABFT working set in LDS (allocated only in kernels that use it).
@@ -754,58 +756,61 @@ __device__ __forceinline__ AbftLds &abft_lds() {
   return L;
 }
 
-// The 16 k values 16 h .. 16 h + 15 of row (m or n) `mn` of a staged tile:
-// four 128-bit reads in the k-major format, sixteen 32-bit reads in the
-// mn-major one.
+// The 4 x 4 block of a staged operand tile at rows (m or n) 4 g .. 4 g + 3
+// and k = 4 kq .. 4 kq + 3, as v[row][k]: one 128-bit read per row in the
+// k-major format, one per k in the mn-major one.
 template <bool KMAJOR>
-__device__ __forceinline__ void s_row16(int base_off, int mn, int h, float (&v)[16]) {
+__device__ __forceinline__ void s_blk4(int base_off, int g, int kq, float (&v)[4][4]) {
 #pragma unroll
-  for (int c = 0; c < 4; ++c) {
+  for (int j = 0; j < 4; ++j) {
     if (KMAJOR) {
-      const int cc = 4 * h + c;
-      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + mn * 128 + ((cc ^ ((mn >> 1) & 7)) << 4));
+      const int mn = 4 * g + j;
+      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + mn * 128 + ((kq ^ ((mn >> 1) & 7)) << 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * c + e] = x[e];
+      for (int e = 0; e < 4; ++e) v[j][e] = x[e];
     } else {
+      const int k = 4 * kq + j;
+      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + k * 512 + ((g ^ (4 * (kq & 3))) << 4));
 #pragma unroll
-      for (int e = 0; e < 4; ++e) v[4 * c + e] = s_mn_elem(base_off, mn, 16 * h + 4 * c + e);
+      for (int e = 0; e < 4; ++e) v[e][j] = x[e];
     }
   }
 }
 
-// Checksum update of one staged k-iteration: thread t covers row and column
-// t % 128 of the tile over half of the k range (entries past the end of k
-// are zero in the staged tiles and in the encodings).
+// Checksum update of one staged k-iteration: thread t covers rows and
+// columns 4 (t % 32) .. + 3 of the tile at k = 4 (t / 32) .. + 3 (entries
+// past the end of k are zero in the staged tiles and in the encodings; rows
+// and columns past the matrix give checksums that are never verified).
 template <bool AK, bool BKM>
-__device__ __forceinline__ void abft_update(AbftLds &L, int stage, int m_valid, int n_valid, AbftPart &pt) {
+__device__ __forceinline__ void abft_update(AbftLds &L, int stage, AbftPart &pt) {
   const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
-  const int t = threadIdx.x;
-  const int i = t & 127, h = t >> 7;
-  if (i < m_valid) {
-    float v[16];
-    s_row16<AK>(As, i, h, v);
+  const int t = threadIdx.x, g = t & 31, kq = t >> 5;
+  {  // rows (the A side), then columns: one side's values live at a time
+    const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[stage][2][4 * kq]);
+    const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[stage][3][4 * kq]);
+    float va[4][4];
+    s_blk4<AK>(As, g, kq, va);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[stage][2][16 * h + 4 * c]);
-      const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[stage][3][16 * h + 4 * c]);
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pt.rc += v[4 * c + e] * eb[e];
-        pt.ra += fabsf(v[4 * c + e]) * eba[e];
+        pt.rc[j] += va[j][e] * eb[e];
+        pt.ra[j] += fabsf(va[j][e]) * eba[e];
       }
     }
   }
-  if (i < n_valid) {
-    float v[16];
-    s_row16<BKM>(Bs, i, h, v);
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[stage][0][4 * kq]);
+    const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[stage][1][4 * kq]);
+    float vb[4][4];
+    s_blk4<BKM>(Bs, g, kq, vb);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[stage][0][16 * h + 4 * c]);
-      const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[stage][1][16 * h + 4 * c]);
+    for (int j = 0; j < 4; ++j) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        pt.cc += ea[e] * v[4 * c + e];
-        pt.ca += eaa[e] * fabsf(v[4 * c + e]);
+        pt.cc[j] += ea[e] * vb[j][e];
+        pt.ca[j] += eaa[e] * fabsf(vb[j][e]);
       }
     }
   }
@@ -829,8 +834,17 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
   const int wm = w / 2, wn = w % 2;
   const int m_valid = a.m - m0, n_valid = a.n - n0;
   {
-    const int i = t & 127, h = t >> 7;
-    L.part[0][h][i] = pt.rc; L.part[1][h][i] = pt.ra; L.part[2][h][i] = pt.cc; L.part[3][h][i] = pt.ca;
+    // the two k-quarters of a wave (lanes l and l ^ 32) are added, then each
+    // wave stores its rows' and columns' checksums
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float rc = pt.rc[j] + __shfl_xor(pt.rc[j], 32), ra = pt.ra[j] + __shfl_xor(pt.ra[j], 32);
+      const float cc = pt.cc[j] + __shfl_xor(pt.cc[j], 32), ca = pt.ca[j] + __shfl_xor(pt.ca[j], 32);
+      if (lane < 32) {
+        const int x = 4 * lane + j;
+        L.part[0][w][x] = rc; L.part[1][w][x] = ra; L.part[2][w][x] = cc; L.part[3][w][x] = ca;
+      }
+    }
   }
   if (t < 4) L.bad[t] = t == 0 || t == 2 ? 0 : -1;
   // injected faults (testing): applied to the accumulator before verification
@@ -896,8 +910,8 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
     const bool valid = is_row ? x < m_valid : x < n_valid;
     if (valid) {
       const int q = is_row ? 0 : 2;
-      const float ck = L.part[q][0][x] + L.part[q][1][x];
-      const float ab = L.part[q + 1][0][x] + L.part[q + 1][1][x];
+      const float ck = ((L.part[q][0][x] + L.part[q][1][x]) + L.part[q][2][x]) + L.part[q][3][x];
+      const float ab = ((L.part[q + 1][0][x] + L.part[q + 1][1][x]) + L.part[q + 1][2][x]) + L.part[q + 1][3][x];
       const float sm = L.sums[is_row ? 0 : 1][0][x] + L.sums[is_row ? 0 : 1][1][x];
       const float r = sm - ck;
       if (!(fabsf(r) <= a.abft_tau * u * ab)) {
@@ -942,7 +956,7 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
       float others = 0.f;
 #pragma unroll
       for (int v = 0; v < SCfg::NT / 64; ++v) others += L.others[v];
-      const float rc = L.part[0][0][bi] + L.part[0][1][bi];
+      const float rc = ((L.part[0][0][bi] + L.part[0][1][bi]) + L.part[0][2][bi]) + L.part[0][3][bi];
       const float fixed = rc - others;
       float delta = 0.f;
 #pragma unroll
@@ -982,21 +996,22 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   for (int i = 0; i < SCfg::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int n = le - lb;
   if (n <= 0) return;
-  AbftPart pt{0.f, 0.f, 0.f, 0.f};
+  AbftPart pt{};
   // ABFT: threads 0-127 carry the encodings of a k-iteration (64 floats of
   // the tile row's A encodings, then 64 of the tile column's B encodings)
   // from memory to the stage's LDS slot: loaded with the stage's tiles,
   // stored after the next wait for them, read after the barrier after that.
-  const bool enc_lane = ABFT && threadIdx.x < 128;
-  const float *esrc = nullptr;
+  const int wv = wave_id();
+  const bool enc_lane = ABFT && wv < 2;  // waves 0 (A) and 1 (B)
+  const float *esrc = nullptr;           // wave-uniform base of the wave's encodings
   float ev = 0.f, ev1 = 0.f;
   if constexpr (ABFT) {
-    const int t = threadIdx.x;
-    esrc = t < 64 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 64 + t
-                  : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 64 + (t - 64);
+    esrc = wv == 0 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 64
+                   : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 64;
     if (enc_lane) {
-      ev = esrc[(int64_t)lb * 64];
-      if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 64];
+      const int lane = threadIdx.x & 63;
+      ev = esrc[(int64_t)lb * 64 + lane];
+      if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 64 + lane];
     }
   }
   SLoader<AK> la;
@@ -1030,7 +1045,7 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     __builtin_amdgcn_sched_barrier(0);
     s_mfmas(a0, b0, acc);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ABFT) abft_update<AK, BKM>(abft_lds(), buf, a.m - m0, a.n - n0, pt);
+    if constexpr (ABFT) abft_update<AK, BKM>(abft_lds(), buf, pt);
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (ABFT) {
       // the encodings of iteration i+1, loaded at iteration i-1 (the
@@ -1041,7 +1056,7 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     if (i + 2 < n) {
       load(buf, lb + i + 2);
       if constexpr (ABFT) {
-        if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 64];
+        if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 64 + (threadIdx.x & 63)];
       }
     }
     if (i + 1 < n) s_frags<AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
