@@ -90,7 +90,7 @@ def _flip(v, bit):
     return float(x.view(np.float32)[0])
 
 
-def _check_corrected(c, got, faults, rep, ref=None):
+def _check_corrected(c, got, faults, rep, ref=None, alpha=1.0, beta=0.0):
     assert rep.detected == len(faults), (rep.detected, rep.corrected, rep.uncorrectable, _records(rep))
     assert rep.corrected == len(faults) and rep.uncorrectable == 0
     assert sorted((r, cc) for r, cc, st in _records(rep)) == sorted((f[0], f[1]) for f in faults)
@@ -98,7 +98,7 @@ def _check_corrected(c, got, faults, rep, ref=None):
     cols = np.array([f[1] for f in faults], np.int64)
     srow, scol = sample_indices(c.m, c.n, 500, 17)
     rows, cols = np.concatenate([rows, srow]), np.concatenate([cols, scol])
-    want, bound = c.reference_entries(rows, cols)
+    want, bound = c.reference_entries(rows, cols, alpha, beta)
     g = decode(got[rows, cols], c.dtype)
     assert np.all(np.isfinite(g))
     assert np.max(np.abs(g - want) / bound) <= TOL[sk.F32]
@@ -175,6 +175,16 @@ def test_faults_on_ragged_edges_are_corrected():
         faults = [(199, 149, 0, 0, 0, 1000.0), (130, 20, 0, 0, 0, -1000.0)]
         got, rep = _run_abft(c, faults)
         _check_corrected(c, got, faults, rep)
+
+
+def test_faults_corrected_before_alpha_and_beta_are_applied():
+    """The checksums cover A B; a fault is corrected in the accumulators, and
+    the epilogue then applies alpha and beta (C read) as without ABFT."""
+    for layout in range(4):
+        c = Case(300, 260, 640, sk.F32, layout, 97 + layout)
+        faults = [(123, 201, 0, 0, 0, 1000.0), (7, 3, 0, 0, 0, -500.0)]
+        got, rep = _run_abft(c, faults, alpha=1.5, beta=-0.75)
+        _check_corrected(c, got, faults, rep, alpha=1.5, beta=-0.75)
 
 
 def test_abft_on_repacked_operands():
