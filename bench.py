@@ -46,7 +46,7 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "d4317562001950fb",
+TRAFFIC = {"kernel_hash": "7c5cae1c083c9144",
            # mean over the six launches of one step (1024^3 ... 6144^3)
            "sgemm-sweep": 1227751763,
            # fp16 8192^3 launch

@@ -1261,23 +1261,49 @@ __global__ __launch_bounds__(256) void abft_encode_kernel(const float *X, int64_
   const int64_t tile = blockIdx.x / chunks, k0 = (blockIdx.x % chunks) * 64;
   const int64_t r0 = tile * 128;
   const int64_t rv = rows - r0 < 128 ? rows - r0 : 128;  // valid rows of the tile
+  // 16-byte loads where all four elements are inside the operand (rows of
+  // a k-major operand and k-lines of an mn-major one start 16-byte aligned:
+  // the leading dimension is a multiple of four and the base is aligned),
+  // single elements at the edges
   if (kmajor) {
-    const int kk = t & 63, rr = t >> 6;
-    const bool kok = k0 + kk < k;
-    const float *p = X + r0 * ld + k0 + kk;
-#pragma unroll 8
-    for (int q = 0; q < 32; ++q) {
-      const int r = 4 * q + rr;
-      T[kk][r] = kok && r < rv ? p[(int64_t)r * ld] : 0.f;
+    const int kc = t & 15, rr = t >> 4;  // k = k0 + 4 kc .. + 3, rows rr + 16 q
+    const int64_t kk0 = k0 + 4 * kc;
+#pragma unroll 4
+    for (int q = 0; q < 8; ++q) {
+      const int r = rr + 16 * q;
+      f4_t x = {0.f, 0.f, 0.f, 0.f};
+      if (r < rv) {
+        const float *p = X + (r0 + r) * ld + kk0;
+        if (kk0 + 3 < k) {
+          x = *reinterpret_cast<const f4_t *>(p);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (kk0 + e < k) x[e] = p[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[4 * kc + e][r] = x[e];
     }
   } else {
-    const int r = t & 127, kq = t >> 7;
-    const bool rok = r < rv;
-    const float *p = X + k0 * ld + r0 + r;
-#pragma unroll 8
-    for (int q = 0; q < 32; ++q) {
-      const int kk = 2 * q + kq;
-      T[kk][r] = rok && k0 + kk < k ? p[(int64_t)kk * ld] : 0.f;
+    const int rc = t & 31, kr = t >> 5;  // rows 4 rc .. + 3, k = k0 + kr + 8 q
+#pragma unroll 4
+    for (int q = 0; q < 8; ++q) {
+      const int kk = kr + 8 * q;
+      const int r = 4 * rc;
+      f4_t x = {0.f, 0.f, 0.f, 0.f};
+      if (k0 + kk < k) {
+        const float *p = X + (k0 + kk) * ld + r0 + r;
+        if (r + 3 < rv) {
+          x = *reinterpret_cast<const f4_t *>(p);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (r + e < rv) x[e] = p[e];
+        }
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[kk][r + e] = x[e];
     }
   }
   __syncthreads();
