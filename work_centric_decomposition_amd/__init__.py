@@ -7,7 +7,8 @@ kernels.  Device memory and streams may come from PyTorch: any object with
 may be a ``torch.cuda.Stream``, a raw ``hipStream_t`` value (int) or None (the
 current PyTorch stream if torch is loaded, else the default stream).
 
-If the built library is missing the import fails loudly: there is no fallback.
+The library is loaded on first use; if it is not built, that first call
+raises ImportError: there is no fallback.
 """
 from __future__ import annotations
 
@@ -30,9 +31,6 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT,
     0, -1, -2, -3, -4, -5, -6
 ABFT_MAX_RECORDS = 64
 
-if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m work_centric_decomposition_amd.build`")
-
 # PyTorch-ROCm ships its own HIP runtime, which its libraries reference by the
 # unversioned file name.  If libskgemm.so (which needs libamdhip64.so.7) were
 # loaded first, torch would then load a second runtime into the process and
@@ -40,8 +38,6 @@ if not os.path.exists(LIB_PATH):
 # bind to the runtime torch already holds.
 if importlib.util.find_spec("torch") is not None:
     import torch  # noqa: F401
-
-_lib = ctypes.CDLL(LIB_PATH)
 
 i64, i32, f32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_float, ctypes.c_void_p
 
@@ -88,26 +84,48 @@ class Segment(ctypes.Structure):
                 ("ended", i32), ("last_peer", i64)]
 
 
-_lib.sk_gemm.argtypes = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, ctypes.c_int,
-                         ctypes.c_int, vp]
-_lib.sk_gemm.restype = ctypes.c_int
-_lib.sk_gemm_ex.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), vp, vp]
-_lib.sk_gemm_ex.restype = ctypes.c_int
-_lib.sk_plan_query.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), i32,
-                               ctypes.POINTER(Plan)]
-_lib.sk_plan_query.restype = ctypes.c_int
-_lib.sk_plan_segments.argtypes = [ctypes.POINTER(Plan), i64, ctypes.POINTER(Segment), i64]
-_lib.sk_plan_segments.restype = i64
-_lib.sk_device_status.argtypes = []
-_lib.sk_device_status.restype = ctypes.c_int
-_lib.sk_strerror.argtypes = [ctypes.c_int]
-_lib.sk_strerror.restype = ctypes.c_char_p
-_lib.sk_last_hip_error.argtypes = []
-_lib.sk_last_hip_error.restype = ctypes.c_char_p
-_lib.sk_release_workspace.argtypes = []
-_lib.sk_release_workspace.restype = ctypes.c_int
-_lib.sk_version.argtypes = []
-_lib.sk_version.restype = ctypes.c_char_p
+class _Library:
+    """libskgemm.so, loaded on first use: importing the package (for example
+    to build the library) never needs it, while every call through the ABI
+    fails loudly when it is missing.  There is no fallback of any kind."""
+
+    def __init__(self):
+        self._cdll = None
+
+    def _load(self):
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run "
+                              f"`python -m work_centric_decomposition_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.sk_gemm.argtypes = [i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64, ctypes.c_int,
+                                 ctypes.c_int, vp]
+        lib.sk_gemm.restype = ctypes.c_int
+        lib.sk_gemm_ex.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), vp, vp]
+        lib.sk_gemm_ex.restype = ctypes.c_int
+        lib.sk_plan_query.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), i32,
+                                       ctypes.POINTER(Plan)]
+        lib.sk_plan_query.restype = ctypes.c_int
+        lib.sk_plan_segments.argtypes = [ctypes.POINTER(Plan), i64, ctypes.POINTER(Segment), i64]
+        lib.sk_plan_segments.restype = i64
+        lib.sk_device_status.argtypes = []
+        lib.sk_device_status.restype = ctypes.c_int
+        lib.sk_strerror.argtypes = [ctypes.c_int]
+        lib.sk_strerror.restype = ctypes.c_char_p
+        lib.sk_last_hip_error.argtypes = []
+        lib.sk_last_hip_error.restype = ctypes.c_char_p
+        lib.sk_release_workspace.argtypes = []
+        lib.sk_release_workspace.restype = ctypes.c_int
+        lib.sk_version.argtypes = []
+        lib.sk_version.restype = ctypes.c_char_p
+        self._cdll = lib
+        return lib
+
+    def __getattr__(self, name):
+        lib = self.__dict__.get("_cdll") or self._load()
+        return getattr(lib, name)
+
+
+_lib = _Library()
 
 
 class SkError(RuntimeError):
@@ -121,7 +139,7 @@ class SkError(RuntimeError):
 
 def library():
     """The loaded ctypes library (for tests of the exported symbols)."""
-    return _lib
+    return _lib._cdll or _lib._load()
 
 
 def header_functions():
