@@ -26,6 +26,8 @@ padding) hold a NaN pattern, so any read of them poisons the result.
 from __future__ import annotations
 
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -142,7 +144,8 @@ def matrix(seed: int, stream: int, rows: int, cols: int, dtype: int, dist: str =
     view = np.lib.stride_tricks.as_strided(out, shape=(outer, contig),
                                            strides=(ld * out.itemsize, out.itemsize))
     total = rows * cols
-    for start in range(0, total, _CHUNK):
+
+    def fill(start):
         cnt = min(_CHUNK, total - start)
         enc = encode(values(seed, stream, start, cnt, dist, scale, int_range), dtype)
         li = np.arange(start, start + cnt, dtype=np.int64)
@@ -151,7 +154,24 @@ def matrix(seed: int, stream: int, rows: int, cols: int, dtype: int, dist: str =
             view[i, j] = enc
         else:
             view[j, i] = enc
+
+    starts = range(0, total, _CHUNK)
+    if len(starts) == 1:
+        fill(0)
+    else:
+        # chunks are independent (counter-based draws into disjoint cells);
+        # numpy releases the interpreter lock in this arithmetic
+        with ThreadPoolExecutor(max_workers=_workers()) as ex:
+            list(ex.map(fill, starts))
     return out
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def signs(seed: int, stream: int, n: int) -> np.ndarray:

@@ -136,3 +136,73 @@ def sample_indices(m, n, count, seed):
     rows = np.concatenate([rows, [0, 0, m - 1, m - 1]])
     cols = np.concatenate([cols, [0, n - 1, 0, n - 1]])
     return rows, cols
+
+
+# ------------------------------------------------- per-tile sampling
+#
+# Freivalds' check (C x against A (B x) for random sign vectors x) cannot
+# gate fp16/bf16 results element by element: its bound normalises each row
+# by sum_j D_ij |x_j| over all n columns, so an error as large as D_ij in
+# every element of one 256-wide tile moves the ratio by about sqrt(256)/n
+# (2e-3 at n = 8192), under the 5e-3 tolerance.  The parity tests therefore
+# compare sampled entries with the oracle entry by entry, sampled so that
+# every output tile is seen, and keep Freivalds only as a supplement.
+
+def split_tiles(plan) -> np.ndarray:
+    """Linear indices (in the plan's tile size) of the tiles whose k range
+    is split over more than one workgroup under `plan`."""
+    out = set()
+    for wg in range(plan.grid):
+        for (tile, _b, _e, started, ended, _lp) in sk.plan_segments(plan, wg):
+            if not (started and ended):
+                out.add(int(tile))
+    return np.array(sorted(out), dtype=np.int64)
+
+
+def tile_sample_indices(m, n, seed, tile=128, extra=2, split=None, split_tm=256, split_tn=256,
+                        tiles_n=None):
+    """Entries of an m x n output such that every `tile` x `tile` output
+    tile (128 refines both fp16/bf16 instances' tiles and the fp32 tile) is
+    checked at its first and its last row (each at a seeded column of the
+    tile), its first and last column (each at a seeded row), and at `extra`
+    seeded entries.  Every tile listed in `split` (linear indices of
+    split_tm x split_tn tiles, row-major over tiles_n tile columns: the
+    tiles a schedule splits over workgroups) is also checked at a seeded
+    permutation that meets each of its rows and each of its columns once.
+    Returns (rows, cols) without duplicates."""
+    if m == 0 or n == 0:
+        return np.zeros(0, np.int64), np.zeros(0, np.int64)
+    tm, tn = -(-m // tile), -(-n // tile)
+    ti = np.repeat(np.arange(tm, dtype=np.int64), tn)
+    tj = np.tile(np.arange(tn, dtype=np.int64), tm)
+    r0, c0 = ti * tile, tj * tile
+    h = np.minimum(m - r0, tile)
+    w = np.minimum(n - c0, tile)
+    T = tm * tn
+    u = S.u64(seed, 556, 0, (4 + 2 * extra) * T).reshape(4 + 2 * extra, T)
+    rnd_r = lambda q: r0 + (u[q] % h.astype(np.uint64)).astype(np.int64)  # noqa: E731
+    rnd_c = lambda q: c0 + (u[q] % w.astype(np.uint64)).astype(np.int64)  # noqa: E731
+    rows = [r0, r0 + h - 1, rnd_r(0), rnd_r(1)]
+    cols = [rnd_c(2), rnd_c(3), c0, c0 + w - 1]
+    for e in range(extra):
+        rows.append(rnd_r(4 + 2 * e))
+        cols.append(rnd_c(5 + 2 * e))
+    if split is not None and len(split):
+        tiles_n = tiles_n or -(-n // split_tn)
+        for idx, t in enumerate(np.asarray(split, np.int64)):
+            a, b = int(t) // tiles_n, int(t) % tiles_n
+            sr0, sc0 = a * split_tm, b * split_tn
+            sh, sw = min(m - sr0, split_tm), min(n - sc0, split_tn)
+            L = max(sh, sw)
+            perm = np.argsort(S.u64(seed, 557 + idx, 0, L), kind="stable")
+            i = np.arange(L, dtype=np.int64)
+            rows.append(sr0 + i % sh)
+            cols.append(sc0 + perm % sw)
+    rows, cols = np.concatenate(rows), np.concatenate(cols)
+    lin = np.unique(rows * n + cols)
+    return lin // n, lin % n
+
+
+def sampled_err(got: np.ndarray, dtype: int, rows, cols, ref64, bound) -> float:
+    """The parity metric over the sampled entries."""
+    return rel_err(got[rows, cols], dtype, ref64, bound)

@@ -5,6 +5,8 @@ Tolerances (max |C - C_ref| / (|alpha||A||B| + |beta||C_in|)): 1e-5 for
 fp32, 5e-3 for fp16/bf16 inputs with fp32 accumulation.  Schedule
 equivalences are bitwise.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -14,7 +16,8 @@ import work_centric_decomposition_amd as sk
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-from gemm_check import TOL, Case, decode, rel_err, sample_indices  # noqa: E402
+from gemm_check import (TOL, Case, decode, rel_err, sampled_err, split_tiles,  # noqa: E402
+                        tile_sample_indices)
 
 DTYPES = [sk.F32, sk.F16, sk.BF16]
 LAYOUTS = [sk.A_ROW_B_ROW, sk.A_ROW_B_COL, sk.A_COL_B_ROW, sk.A_COL_B_COL]
@@ -181,17 +184,23 @@ def test_hybrid_schedule_hgemm_against_oracle():
 
 def test_auto_hybrid_on_a_long_k_shape_against_oracle():
     """272 tiles with k = 8192: AUTO keeps a Stream-K region of one wave plus
-    the 16 leftover tiles, split in XCD lock-step quanta."""
+    the 16 leftover tiles, split in XCD lock-step quanta.  Every 128 x 128
+    output tile is checked at its first and last rows and columns and two
+    more entries, and every split tile at a permutation meeting each of its
+    rows and columns (tile_sample_indices); Freivalds as a supplement."""
     m, n, k = 256 * 17, 256 * 16, 8192
     c = Case(m, n, k, sk.BF16, sk.A_ROW_B_COL, 16, dist="normal", scale=1 / np.sqrt(8192),
              with_c=False)
     p = sk.plan_query(sk.make_desc(m, n, k, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, sk.BF16,
                                    sk.A_ROW_B_COL))
     assert p.schedule == sk.SCHED_XCD_ALIGNED and p.sk_tiles == 272 and p.phase_div > 0
+    split = split_tiles(p)
+    assert len(split) > 0
     got = c.run(1.0, 0.0)
-    rows, cols = sample_indices(m, n, 1500, 16)
+    rows, cols = tile_sample_indices(m, n, 16, split=split, split_tm=p.tile_m, split_tn=p.tile_n,
+                                     tiles_n=p.tiles_n)
     ref, bound = c.reference_entries(rows, cols)
-    assert np.max(np.abs(decode(got[rows, cols], sk.BF16) - ref) / bound) <= TOL[sk.BF16]
+    assert sampled_err(got, sk.BF16, rows, cols, ref, bound) <= TOL[sk.BF16]
     assert c.freivalds(got) <= TOL[sk.BF16]
 
 
@@ -240,67 +249,138 @@ def test_hybrid_schedule_sgemm_against_oracle():
 
 @pytest.mark.parametrize("nsq", [1024, 2048, 3072, 4096, 5120, 6144])
 def test_sgemm_square_sweep_sampled(nsq):
-    """Square SGEMM, row-major, U[-1,1], C_in U[-1,1], alpha=1 beta=1."""
+    """Square SGEMM, row-major, U[-1,1], C_in U[-1,1], alpha=1 beta=1.  Up to
+    2n^3 = 2^36 every output element is compared with the oracle; above,
+    every 128 x 128 tile at its first and last rows and columns and two more
+    entries, plus every split tile of the plan at a permutation meeting each
+    of its rows and columns; Freivalds as a supplement."""
     _say("case sgemm square", nsq)
     c = Case(nsq, nsq, nsq, sk.F32, sk.A_ROW_B_ROW, S.SEED_SGEMM_SQUARE)
     got = c.run(1.0, 1.0)
-    rows, cols = sample_indices(nsq, nsq, 1500, nsq)
+    if 2 * nsq ** 3 <= 2 ** 36:
+        ref, bound = c.reference(1.0, 1.0)
+        assert rel_err(got, sk.F32, ref, bound) <= TOL[sk.F32]
+        return
+    p = sk.plan_query(sk.make_desc(nsq, nsq, nsq, 1, c.dA, c.lda, c.dB, c.ldb, 1, c.dC, c.ldc, sk.F32,
+                                   sk.A_ROW_B_ROW))
+    rows, cols = tile_sample_indices(nsq, nsq, nsq, split=split_tiles(p), split_tm=p.tile_m,
+                                     split_tn=p.tile_n, tiles_n=p.tiles_n)
     ref, bound = c.reference_entries(rows, cols, 1.0, 1.0)
-    g = decode(got[rows, cols], sk.F32)
-    assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F32]
+    assert sampled_err(got, sk.F32, rows, cols, ref, bound) <= TOL[sk.F32]
     assert c.freivalds(got, 1.0, 1.0) <= TOL[sk.F32]
 
 
 @pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
 def test_hgemm_8192_sampled(dtype):
     """8192^3, A row-major and B column-major (both k-contiguous), entries
-    N(0,1)/sqrt(k), alpha=1 beta=0, fp32 accumulation."""
+    N(0,1)/sqrt(k), alpha=1 beta=0, fp32 accumulation.  Every 128 x 128
+    output tile (4096 of them) is checked at its first and last rows and
+    columns and two more entries; Freivalds as a supplement."""
     _say("case hgemm 8192", dtype)
     n = 8192
     c = Case(n, n, n, dtype, sk.A_ROW_B_COL, S.SEED_HGEMM_LARGE, dist="normal",
              scale=1 / np.sqrt(n), with_c=False)
     got = c.run(1.0, 0.0)
-    rows, cols = sample_indices(n, n, 1500, 8192 + dtype)
+    p = sk.plan_query(sk.make_desc(n, n, n, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
+                                   sk.A_ROW_B_COL))
+    rows, cols = tile_sample_indices(n, n, 8192 + dtype, split=split_tiles(p), split_tm=p.tile_m,
+                                     split_tn=p.tile_n, tiles_n=p.tiles_n)
     ref, bound = c.reference_entries(rows, cols)
-    g = decode(got[rows, cols], dtype)
-    assert np.max(np.abs(g - ref) / bound) <= TOL[dtype]
+    assert sampled_err(got, dtype, rows, cols, ref, bound) <= TOL[dtype]
     assert c.freivalds(got) <= TOL[dtype]
 
 
 # ------------------------------------------------- Stream-K sweep shapes
 
-def _sweep_subset(per_kind=8, max_elems=None):
-    # adversarial shapes have more than one full wave of 256 x 256 tiles, so
-    # their output alone is ~17M elements
-    max_elems = max_elems or {"random": 1.2e7, "skinny": 1.2e7, "adversarial": 4.5e7}
-    probe = sk.plan_query(sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, sk.F16,
-                                       sk.A_ROW_B_COL))
-    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, probe.tile_m, probe.tile_n, probe.slots)
-    out, seen = [], {}
+# Strata of the 2000-shape fp16 sweep: (kind, AUTO's tile instance, whether
+# AUTO keeps a Stream-K region) -> shapes taken.  These are all the kinds of
+# plan AUTO resolves to on the sweep (planned for 256 slots, one MI355X).
+SWEEP_STRATA = {
+    ("random", 128, False): 9, ("random", 128, True): 9,
+    ("random", 256, False): 6, ("random", 256, True): 6,
+    ("skinny", 128, True): 8, ("skinny", 256, True): 2,
+    ("adversarial", 128, False): 6, ("adversarial", 128, True): 4,
+    ("adversarial", 256, False): 4, ("adversarial", 256, True): 6,
+}
+SWEEP_CASES = sum(SWEEP_STRATA.values())
+FULL_ORACLE_FLOPS = 2 ** 36  # full output against the oracle up to this 2mnk
+
+
+@functools.lru_cache(maxsize=1)
+def _sweep_subset():
+    """A seeded, stratified subset of the sweep: in each stratum, shapes
+    drawn at random among those with at most 2.5e7 operand and output
+    elements (6e7 in the strata with no such shape; the smallest ones when
+    even that leaves too few), so the test's inputs fit in its time."""
+    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, 256, 256, 256)
+    by = {}
     for kind, m, n, k in shapes:
-        if m * k + k * n + m * n > max_elems[kind] or seen.get(kind, 0) >= per_kind:
-            continue
-        seen[kind] = seen.get(kind, 0) + 1
-        out.append((kind, m, n, k))
+        p = sk.plan_query(sk.make_desc(m, n, k, 1.0, 0, k, 0, k, 0.0, 0, n, sk.F16, sk.A_ROW_B_COL),
+                          None, 256)
+        by.setdefault((kind, p.tile_m, p.sk_tiles > 0), []).append((m * k + k * n + m * n, m, n, k))
+    out = []
+    for si, (key, want) in enumerate(SWEEP_STRATA.items()):
+        cands = sorted(by.get(key, []))
+        for cap in (2.5e7, 6e7):
+            pool = [c for c in cands if c[0] <= cap]
+            if len(pool) >= want:
+                break
+        if len(pool) < want:
+            pool = cands[:want]
+        order = np.argsort(S.u64(S.SEED_SWEEP, 900 + si, 0, len(pool)), kind="stable")
+        out += [(key, pool[i][1], pool[i][2], pool[i][3]) for i in sorted(order[:want])]
     return out
 
 
-def test_sweep_shapes_auto_and_dp_against_oracle():
-    """A seeded subset of the Stream-K sweep (random, skinny and tile-count
-    adversarial kinds): AUTO and data-parallel schedules both match the oracle
-    on sampled entries and pass a Freivalds check."""
-    for kind, m, n, k in _sweep_subset():
-        _say("case sweep", kind, m, n, k)
-        c = Case(m, n, k, sk.F16, sk.A_ROW_B_COL, S.SEED_SWEEP + m + n + k, dist="normal",
-                 scale=1 / np.sqrt(k), with_c=False)
-        rows, cols = sample_indices(m, n, 400, m * 7 + n)
+PAGE_SCHEDULES = [sk.SCHED_SK_HYBRID2, sk.SCHED_SK_HYBRID1, sk.SCHED_SK_BASIC]
+
+
+@pytest.mark.parametrize("idx", range(SWEEP_CASES))
+def test_sweep_shapes_against_oracle(idx):
+    """One shape of the stratified sweep subset, fp16, A row-major, B
+    column-major, N(0,1)/sqrt(k), alpha=1 beta=0, run under AUTO, data-parallel
+    on the large tile, AUTO with the small tile, and one of the page's
+    schedules (two-tile hybrid, one-tile hybrid, basic Stream-K, in turn, on
+    either instance).  With 2mnk <= 2^36 every output element of every run
+    is compared with the oracle; above that, every 128 x 128 output tile is
+    checked at its first and last rows and columns and two more entries, and
+    every tile the run's plan splits over workgroups at a permutation that
+    meets each of its rows and columns (tile_sample_indices); Freivalds'
+    check runs beside it as a supplement only."""
+    key, m, n, k = _sweep_subset()[idx]
+    _say("case sweep", idx, key, m, n, k)
+    c = Case(m, n, k, sk.F16, sk.A_ROW_B_COL, S.SEED_SWEEP + m + n + k, dist="normal",
+             scale=1 / np.sqrt(k), with_c=False)
+    runs = [sk.make_options(), sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE),
+            sk.make_options(tile=sk.TILE_SMALL),
+            sk.make_options(schedule=PAGE_SCHEDULES[idx % 3],
+                            tile=(sk.TILE_LARGE, sk.TILE_SMALL)[(idx // 3) % 2])]
+    full = 2 * m * n * k <= FULL_ORACLE_FLOPS
+    plans = []
+    for o in runs:
+        plans.append(sk.plan_query(sk.make_desc(m, n, k, 1.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc,
+                                                sk.F16, sk.A_ROW_B_COL), o))
+    assert (plans[0].tile_m, plans[0].sk_tiles > 0) == key[1:], (plans[0].tile_m, plans[0].sk_tiles)
+    if full:
+        ref, bound = c.reference()
+    else:
+        rr, cc = [], []
+        for i, p in enumerate(plans):
+            r, q = tile_sample_indices(m, n, m + 3 * n + i, split=split_tiles(p), split_tm=p.tile_m,
+                                       split_tn=p.tile_n, tiles_n=p.tiles_n)
+            rr.append(r)
+            cc.append(q)
+        lin = np.unique(np.concatenate(rr) * n + np.concatenate(cc))
+        rows, cols = lin // n, lin % n
         ref, bound = c.reference_entries(rows, cols)
-        for opts in (None, sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE),
-                     sk.make_options(tile=sk.TILE_SMALL)):
-            got = c.run(1.0, 0.0, opts)
-            g = decode(got[rows, cols], sk.F16)
-            assert np.max(np.abs(g - ref) / bound) <= TOL[sk.F16], (kind, m, n, k)
+    for o, p in zip(runs, plans):
+        got = c.run(1.0, 0.0, o)
+        if full:
+            err = rel_err(got, sk.F16, ref, bound)
+        else:
+            err = sampled_err(got, sk.F16, rows, cols, ref, bound)
             assert c.freivalds(got) <= TOL[sk.F16]
+        assert err <= TOL[sk.F16], (key, m, n, k, p.schedule, p.tile_m, err)
 
 
 # ------------------------------------------------ matrix-vector products
