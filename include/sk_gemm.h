@@ -67,7 +67,8 @@ typedef enum {
   SK_ERR_NO_MEMORY = -3,     /* workspace allocation failed */
   SK_ERR_HIP = -4,           /* a HIP runtime call or kernel launch failed; sk_last_hip_error() has the text */
   SK_ERR_FIXUP_TIMEOUT = -5, /* device: a workgroup gave up waiting for a peer's partial tile */
-  SK_ERR_NO_DEVICE = -6      /* no usable gfx950 device */
+  SK_ERR_NO_DEVICE = -6,     /* no usable gfx950 device */
+  SK_ERR_TOO_LARGE = -7      /* sk_gemm_noalloc: the call needs more scratch than it holds */
 } sk_status;
 
 /* Work decompositions.  The first four are the Stream-K page's, with tiles in
@@ -262,6 +263,32 @@ int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t
  * (tiles_m + tiles_n) * ceil(k/32) * 256 bytes for 128 x 128 tiles. */
 int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
                hipStream_t stream);
+
+/* Bytes of partial-tile scratch the allocation-free entry point holds per
+ * GPU (256 partial tiles of 256 x 256 fp32). */
+#define SK_NOALLOC_PARTIAL_BYTES (64u * 1024u * 1024u)
+
+/* Allocation-free form of sk_gemm_ex, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  Same GEMM, plans and kernels as
+ * sk_gemm_ex, but it calls no allocating routine: the partial tiles, flags
+ * and status word of the cross-workgroup fixup live in a static device array
+ * of the library (SK_NOALLOC_PARTIAL_BYTES plus 128 KiB; each GPU the
+ * library runs on holds its own copy until the process ends).  The first
+ * call on a device looks the array up and clears its flags with a fill
+ * kernel on `stream`.  Every call on one GPU shares that array and leaves it
+ * as the call ended: calls that overlap on one GPU (other streams, other
+ * host threads) race and must not be issued.  Refused: ABFT mode and
+ * operands that would need a repacked copy (SK_ERR_UNSUPPORTED; an operand
+ * is read in place when its base is 16-byte aligned, its leading dimension
+ * a multiple of 16 bytes and, if it is k-contiguous, k a multiple of 16
+ * bytes of elements; fp16/bf16 operands must also be k-contiguous: plan
+ * packs bits 0), and plans needing more than 16384
+ * workgroups or more partial-tile bytes than SK_NOALLOC_PARTIAL_BYTES
+ * (SK_ERR_TOO_LARGE: a forced grid above the slot count on the large
+ * fp16/bf16 tile, or a matrix-vector split with more chunk sums).  Time-outs
+ * of the fixup wait are reported by sk_device_status() as for sk_gemm_ex. */
+int sk_gemm_noalloc(const sk_gemm_desc *desc, const sk_options *opts, hipStream_t stream);
 
 /* Plan the call would use.  slots > 0 plans for that many resident
  * workgroups of the fp32 or large-tile fp16/bf16 kernel (the small-tile

@@ -576,3 +576,19 @@ def test_strerror_texts():
     assert "time" in sk.strerror(sk.ERR_FIXUP_TIMEOUT)
     assert sk.version().startswith("sk_gemm")
     assert ctypes.sizeof(sk.AbftReport) == 16 + 64 * ctypes.sizeof(sk.AbftRecord)
+
+
+def test_noalloc_refusals_before_any_gpu_call():
+    """The allocation-free entry point refuses ABFT (its encodings would need
+    an allocation) and bad arguments before touching the GPU; its scratch
+    size is the header's."""
+    d = _desc(256, 256, 256, sk.F32, sk.A_ROW_B_ROW)
+    assert sk.gemm_noalloc(d, sk.make_options(abft=True), check=False) == sk.ERR_UNSUPPORTED
+    bad = _desc(-1, 256, 256)
+    assert sk.gemm_noalloc(bad, None, check=False) == sk.ERR_INVALID_ARG
+    assert sk.library().sk_gemm_noalloc(None, None, None) == sk.ERR_INVALID_ARG
+    import re
+    hdr = open(sk.HEADER_PATH).read()
+    mib = int(re.search(r"#define SK_NOALLOC_PARTIAL_BYTES \((\d+)u \* 1024u \* 1024u\)", hdr).group(1))
+    assert mib * 1024 * 1024 == sk.NOALLOC_PARTIAL_BYTES
+    assert sk.strerror(sk.ERR_TOO_LARGE).startswith("the call needs more scratch")

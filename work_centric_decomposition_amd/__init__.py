@@ -29,6 +29,8 @@ SCHED_XCD_ALIGNED, SCHED_GEMV_SPLIT = 5, 6
 TILE_AUTO, TILE_LARGE, TILE_SMALL = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT, ERR_NO_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
+ERR_TOO_LARGE = -7
+NOALLOC_PARTIAL_BYTES = 64 * 1024 * 1024
 ABFT_MAX_RECORDS = 64
 
 # PyTorch-ROCm ships its own HIP runtime, which its libraries reference by the
@@ -102,6 +104,8 @@ class _Library:
         lib.sk_gemm.restype = ctypes.c_int
         lib.sk_gemm_ex.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), vp, vp]
         lib.sk_gemm_ex.restype = ctypes.c_int
+        lib.sk_gemm_noalloc.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), vp]
+        lib.sk_gemm_noalloc.restype = ctypes.c_int
         lib.sk_plan_query.argtypes = [ctypes.POINTER(GemmDesc), ctypes.POINTER(Options), i32,
                                        ctypes.POINTER(Plan)]
         lib.sk_plan_query.restype = ctypes.c_int
@@ -216,6 +220,16 @@ def gemm_ex(desc: GemmDesc, opts: Options | None = None, report=None, stream=Non
                          _ptr(report), _stream(stream))
     if check and rc != OK:
         raise SkError(rc, "sk_gemm_ex")
+    return rc
+
+
+def gemm_noalloc(desc: GemmDesc, opts: Options | None = None, stream=None, check=True) -> int:
+    """``sk_gemm_noalloc``: the allocation-free form of ``sk_gemm_ex`` (no
+    ABFT; scratch is the library's static per-GPU array)."""
+    rc = _lib.sk_gemm_noalloc(ctypes.byref(desc), ctypes.byref(opts) if opts is not None else None,
+                              _stream(stream))
+    if check and rc != OK:
+        raise SkError(rc, "sk_gemm_noalloc")
     return rc
 
 

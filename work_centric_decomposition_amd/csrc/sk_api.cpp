@@ -99,6 +99,50 @@ __global__ void init_flags_kernel(uint32_t *flags, int n, int32_t *status) {
   if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
 }
 
+// Scratch of the allocation-free entry point (sk_gemm_noalloc): one static
+// device array per GPU, held until the process ends.  Layout: the status
+// word at byte 0, kScratchFlags flags from byte 256, the partial-tile slots
+// from byte kScratchHead.  Host code never uses the array's name as an
+// address (on the host it is only a stand-in for the symbol): its device
+// address is looked up once per device with hipGetSymbolAddress and kept.
+constexpr int kScratchFlags = 16384;
+constexpr size_t kScratchHead = 128 * 1024;
+constexpr size_t kScratchPartialBytes = SK_NOALLOC_PARTIAL_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchHead + kScratchPartialBytes];
+
+struct NoAlloc {
+  char *ptr = nullptr;  // device address of `scratch` on this device
+  uint32_t epoch = 0;
+};
+std::map<int, NoAlloc> g_noalloc;
+
+// Set-up of the scratch on device `dev` (current), once: its address, and
+// the flags and status word cleared by a fill kernel on `stream`.  Caller
+// holds g_mu.
+int noalloc_state(int dev, hipStream_t stream, NoAlloc **out) {
+  NoAlloc &s = g_noalloc[dev];
+  if (s.ptr == nullptr) {
+    void *p = nullptr;
+    hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      g_noalloc.erase(dev);
+      return hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+    }
+    char *base = static_cast<char *>(p);
+    hipLaunchKernelGGL(init_flags_kernel, dim3(16), dim3(256), 0, stream,
+                       reinterpret_cast<uint32_t *>(base + 256), kScratchFlags,
+                       reinterpret_cast<int32_t *>(base));
+    e = hipGetLastError();
+    if (e != hipSuccess) {
+      g_noalloc.erase(dev);
+      return hip_fail(e, "scratch set-up");
+    }
+    s.ptr = base;
+  }
+  *out = &s;
+  return SK_OK;
+}
+
 // Workspace of (dev, stream) with room for `slots` partial tiles of
 // `tile_bytes` each.  Caller holds g_mu.
 int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes, Workspace **out) {
@@ -162,7 +206,13 @@ int validate(const sk_gemm_desc &d, const sk_options &o, const sk_abft_report *r
   return SK_OK;
 }
 
-int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report, hipStream_t stream) {
+// noalloc: the allocation-free form (sk_gemm_noalloc): partials, flags and
+// status come from the static scratch; nothing is allocated, and calls that
+// would need an allocation (ABFT encodings, repacked operands) or more
+// scratch than it holds are refused.
+int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report, hipStream_t stream,
+              bool noalloc = false) {
+  if (noalloc && o.abft) return SK_ERR_UNSUPPORTED;
   int rc = validate(d, o, report);
   if (rc != SK_OK) return rc;
   if (d.m == 0 || d.n == 0) return SK_OK;  // nothing to compute or write
@@ -173,6 +223,11 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   DeviceInfo *info = nullptr;
   rc = device_info(dev, &info);
   if (rc != SK_OK) return rc;
+  NoAlloc *na = nullptr;
+  if (noalloc) {
+    rc = noalloc_state(dev, stream, &na);
+    if (rc != SK_OK) return rc;
+  }
   if (o.abft) {
     rc = launch_zero_report(report, stream);
     if (rc != hipSuccess) return hip_fail((hipError_t)rc, "report reset");
@@ -188,10 +243,16 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     if (!o.abft && gemv_plan(d, info->cus, g)) {
       float *part = nullptr;
       if (g.S > 1) {
-        Workspace *ws = nullptr;
-        rc = get_workspace(dev, stream, 1, (size_t)(g.S * g.R * g.V) * sizeof(float), &ws);
-        if (rc != SK_OK) return rc;
-        part = ws->partials;
+        const size_t need = (size_t)(g.S * g.R * g.V) * sizeof(float);
+        if (noalloc) {
+          if (need > kScratchPartialBytes) return SK_ERR_TOO_LARGE;
+          part = reinterpret_cast<float *>(na->ptr + kScratchHead);
+        } else {
+          Workspace *ws = nullptr;
+          rc = get_workspace(dev, stream, 1, need, &ws);
+          if (rc != SK_OK) return rc;
+          part = ws->partials;
+        }
       }
       rc = launch_gemv(d.dtype, g, part, d.alpha, d.beta, stream);
       return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "matrix-vector kernel launch");
@@ -205,6 +266,11 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   if (rc != SK_OK) return rc;
   const int es = d.dtype == SK_F32 ? 4 : 2;
   const bool ak = a_kmajor_of(d.layout), bk = b_kmajor_of(d.layout);
+  if (noalloc) {
+    if (P.pack_a || P.pack_b) return SK_ERR_UNSUPPORTED;
+    if (P.grid > kScratchFlags || (size_t)P.grid * P.cfg.bm * P.cfg.bn * 4 > kScratchPartialBytes)
+      return SK_ERR_TOO_LARGE;
+  }
 
   // operands: direct, or repacked into a k-contiguous copy
   const int64_t kp = (d.k + 63) / 64 * 64;
@@ -250,15 +316,27 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     return SK_ERR_UNSUPPORTED;
   }
 
-  Workspace *ws = nullptr;
-  const int64_t slots_needed = P.grid;
-  rc = get_workspace(dev, stream, slots_needed, (size_t)c.bm * c.bn * 4, &ws);
-  if (rc != SK_OK) {
-    if (pa) (void)hipFreeAsync(pa, stream);
-    if (pb) (void)hipFreeAsync(pb, stream);
-    return rc;
+  float *partials = nullptr;
+  uint32_t *flags = nullptr, epoch = 0;
+  int32_t *status = nullptr;
+  if (noalloc) {
+    partials = reinterpret_cast<float *>(na->ptr + kScratchHead);
+    flags = reinterpret_cast<uint32_t *>(na->ptr + 256);
+    status = reinterpret_cast<int32_t *>(na->ptr);
+    if (++na->epoch == 0) na->epoch = 1;
+    epoch = na->epoch;
+  } else {
+    Workspace *ws = nullptr;
+    const int64_t slots_needed = P.grid;
+    rc = get_workspace(dev, stream, slots_needed, (size_t)c.bm * c.bn * 4, &ws);
+    if (rc != SK_OK) {
+      if (pa) (void)hipFreeAsync(pa, stream);
+      if (pb) (void)hipFreeAsync(pb, stream);
+      return rc;
+    }
+    if (++ws->epoch == 0) ws->epoch = 1;
+    partials = ws->partials; flags = ws->flags; status = ws->status; epoch = ws->epoch;
   }
-  if (++ws->epoch == 0) ws->epoch = 1;
 
   a.C = d.C; a.ldc = d.ldc;
   a.m = (int32_t)d.m; a.n = (int32_t)d.n; a.k = (int32_t)d.k;
@@ -266,7 +344,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   a.tiles_m = (int32_t)P.tiles_m; a.tiles_n = (int32_t)P.tiles_n;
   a.tiles = (int32_t)P.tiles; a.ipt = (int32_t)P.ipt;
   a.sched = P.sched();
-  a.partials = ws->partials; a.flags = ws->flags; a.epoch = ws->epoch; a.status = ws->status;
+  a.partials = partials; a.flags = flags; a.epoch = epoch; a.status = status;
   const int64_t us = o.spin_limit_us > 0 ? o.spin_limit_us : 2000000;
   a.spin_limit = us * info->wall_khz / 1000;
   a.abft = o.abft; a.n_faults = o.n_faults; a.faults = o.faults; a.report = report;
@@ -332,6 +410,15 @@ int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report 
   if (!desc) return SK_ERR_INVALID_ARG;
   try {
     return gemm_impl(*desc, opts ? *opts : kDefaultOpts, report, stream);
+  } catch (...) {
+    return SK_ERR_NO_MEMORY;
+  }
+}
+
+int sk_gemm_noalloc(const sk_gemm_desc *desc, const sk_options *opts, hipStream_t stream) {
+  if (!desc) return SK_ERR_INVALID_ARG;
+  try {
+    return gemm_impl(*desc, opts ? *opts : kDefaultOpts, nullptr, stream, true);
   } catch (...) {
     return SK_ERR_NO_MEMORY;
   }
@@ -409,15 +496,19 @@ int sk_device_status(void) {
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
   int result = SK_OK;
-  for (auto &kv : g_ws) {
-    if (kv.first.first != dev || !kv.second.status) continue;
+  std::vector<int32_t *> words;
+  for (auto &kv : g_ws)
+    if (kv.first.first == dev && kv.second.status) words.push_back(kv.second.status);
+  auto na = g_noalloc.find(dev);
+  if (na != g_noalloc.end() && na->second.ptr) words.push_back(reinterpret_cast<int32_t *>(na->second.ptr));
+  for (int32_t *w : words) {
     int32_t v = 0;
-    e = hipMemcpy(&v, kv.second.status, sizeof(v), hipMemcpyDeviceToHost);
+    e = hipMemcpy(&v, w, sizeof(v), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "status read");
     if (v & 1) result = SK_ERR_FIXUP_TIMEOUT;
     if (v) {
       const int32_t zero = 0;
-      e = hipMemcpy(kv.second.status, &zero, sizeof(zero), hipMemcpyHostToDevice);
+      e = hipMemcpy(w, &zero, sizeof(zero), hipMemcpyHostToDevice);
       if (e != hipSuccess) return hip_fail(e, "status clear");
     }
   }
@@ -433,6 +524,7 @@ const char *sk_strerror(int status) {
     case SK_ERR_HIP: return "HIP runtime error";
     case SK_ERR_FIXUP_TIMEOUT: return "a workgroup timed out waiting for a partial tile";
     case SK_ERR_NO_DEVICE: return "no usable gfx950 device";
+    case SK_ERR_TOO_LARGE: return "the call needs more scratch than the allocation-free entry point holds";
     default: return "unknown status";
   }
 }
