@@ -33,7 +33,10 @@
  *    time (they would share one workspace).
  *  - Return value: SK_OK (0) or a negative sk_status.  No exception crosses
  *    this interface.  Errors found on the device (a fixup wait that timed
- *    out) are reported by sk_device_status().
+ *    out, the result of that call being wrong) are reported once: by the
+ *    next sk_gemm / sk_gemm_ex call on the device that starts after the
+ *    kernel wrote its error word (that call returns SK_ERR_FIXUP_TIMEOUT and
+ *    launches nothing), or by sk_device_status(), whichever comes first.
  */
 #ifndef SK_GEMM_H
 #define SK_GEMM_H
@@ -191,7 +194,14 @@ typedef struct {
   float model_a, model_b, model_c, model_d;
   int32_t spin_limit_us;    /* fixup wait time-out in microseconds (0 = 2 s) */
   int32_t tile;             /* sk_tile: fp16/bf16 tile instance (ignored for SK_F32) */
+  int32_t test_flags;       /* testing only (0 otherwise): SK_TEST_NO_SIGNAL */
 } sk_options;
+
+/* test_flags bit: workgroups store their partial tiles but never signal
+ * them, so every fixup wait of the call gives up after spin_limit_us (the
+ * result is then wrong and the time-out is reported); forces the error path
+ * of the bounded wait from the host.  Kernels always exit normally. */
+#define SK_TEST_NO_SIGNAL 1
 
 /* Plan of one call, for inspection (host only, needs no GPU when
  * sk_plan_query is given an explicit slot count).  For SK_SCHED_GEMV_SPLIT:
@@ -302,8 +312,9 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
  * cap), or a negative sk_status. */
 int64_t sk_plan_segments(const sk_plan *plan, int64_t wg, sk_segment *out, int64_t cap);
 
-/* Device-side status word of the current device's workspaces: SK_OK or
- * SK_ERR_FIXUP_TIMEOUT; reading it synchronises the device and clears it. */
+/* Error words of the current device's workspaces and of the allocation-free
+ * entry point's scratch: SK_OK or SK_ERR_FIXUP_TIMEOUT (a time-out not yet
+ * reported by a later call); synchronises the device and clears them. */
 int sk_device_status(void);
 
 /* Text of a status code, and of the last HIP error seen by the library. */

@@ -592,3 +592,20 @@ def test_noalloc_refusals_before_any_gpu_call():
     mib = int(re.search(r"#define SK_NOALLOC_PARTIAL_BYTES \((\d+)u \* 1024u \* 1024u\)", hdr).group(1))
     assert mib * 1024 * 1024 == sk.NOALLOC_PARTIAL_BYTES
     assert sk.strerror(sk.ERR_TOO_LARGE).startswith("the call needs more scratch")
+
+
+def test_forced_grid_beyond_the_slots_is_refused_when_a_wait_could_target_an_undispatched_workgroup():
+    """A grid above the resident slot count relies on in-order dispatch as
+    slots free up; it is planned only while every owner's last peer is fewer
+    than slots - 8 workgroups after it."""
+    d = _desc(128, 128, 32 * 600, sk.F32, sk.A_ROW_B_ROW)  # one tile of 600 iterations
+    p = sk.plan_query(d, sk.make_options(forced_grid=200), 256)  # within the slots: any reach
+    assert p.grid == 200 and p.max_peers == 199
+    p = sk.plan_query(d, sk.make_options(forced_grid=300), 512)  # above 256 would be refused
+    assert p.grid == 300
+    with pytest.raises(sk.SkError) as e:
+        sk.plan_query(d, sk.make_options(forced_grid=300), 256)
+    assert e.value.status == sk.ERR_UNSUPPORTED
+    d2 = _desc(8192, 8192, 8192, sk.F16)  # 1024 tiles: g = t is data-parallel, no waits
+    assert sk.plan_query(d2, sk.make_options(forced_grid=1024), 256).max_peers == 0
+    assert sk.gemm_ex(d, sk.make_options(test_flags=2), check=False) == sk.ERR_INVALID_ARG

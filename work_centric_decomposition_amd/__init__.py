@@ -30,6 +30,7 @@ TILE_AUTO, TILE_LARGE, TILE_SMALL = 0, 1, 2
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT, ERR_NO_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 ERR_TOO_LARGE = -7
+TEST_NO_SIGNAL = 1
 NOALLOC_PARTIAL_BYTES = 64 * 1024 * 1024
 ABFT_MAX_RECORDS = 64
 
@@ -69,7 +70,7 @@ class Options(ctypes.Structure):
     _fields_ = [("schedule", i32), ("forced_grid", i32), ("abft", i32), ("hybrid_min_waves", i32),
                 ("faults", vp), ("n_faults", i32), ("abft_tau", f32), ("model_a", f32),
                 ("model_b", f32), ("model_c", f32), ("model_d", f32), ("spin_limit_us", i32),
-                ("tile", i32)]
+                ("tile", i32), ("test_flags", i32)]
 
 
 class Plan(ctypes.Structure):
@@ -197,7 +198,7 @@ def gemm(m, n, k, alpha, A, lda, B, ldb, beta, C, ldc, dtype, layout, stream=Non
 
 def make_options(schedule=SCHED_AUTO, forced_grid=0, abft=False, hybrid_min_waves=0,
                  faults=None, n_faults=0, abft_tau=0.0, model=(0.0, 0.0, 0.0, 0.0),
-                 spin_limit_us=0, tile=0) -> Options:
+                 spin_limit_us=0, tile=0, test_flags=0) -> Options:
     o = Options()
     o.schedule, o.forced_grid, o.abft, o.hybrid_min_waves = schedule, forced_grid, int(abft), \
         hybrid_min_waves
@@ -205,6 +206,7 @@ def make_options(schedule=SCHED_AUTO, forced_grid=0, abft=False, hybrid_min_wave
     o.model_a, o.model_b, o.model_c, o.model_d = model
     o.spin_limit_us = spin_limit_us
     o.tile = tile
+    o.test_flags = test_flags
     return o
 
 

@@ -43,7 +43,10 @@ struct Workspace {
   size_t partial_bytes = 0;
   uint32_t *flags = nullptr;
   int flag_count = 0;
-  int32_t *status = nullptr;
+  // the error word, in pinned host memory mapped into the device's address
+  // space: a kernel's time-out is seen by the host without a synchronisation
+  int32_t *status_host = nullptr;
+  int32_t *status = nullptr;  // its device address
   uint32_t epoch = 0;
 };
 
@@ -96,7 +99,7 @@ int device_info(int dev, DeviceInfo **out) {
 
 __global__ void init_flags_kernel(uint32_t *flags, int n, int32_t *status) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) flags[i] = 0;
-  if (blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
+  if (status != nullptr && blockIdx.x == 0 && threadIdx.x == 0) *status = 0;
 }
 
 // Scratch of the allocation-free entry point (sk_gemm_noalloc): one static
@@ -150,20 +153,39 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
   const size_t need = (size_t)slots * tile_bytes;
   const size_t base = (size_t)256 * 256 * 256 * 4;  // 256 slots of the largest tile: 64 MiB
   if (w.partials == nullptr || w.partial_bytes < need || w.flag_count < slots) {
+    int32_t *keep_host = nullptr, *keep_dev = nullptr;
     if (w.partials) {  // growth: wait for work that may still use the old buffers
       hipError_t e = hipStreamSynchronize(stream);
       if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
       (void)hipFree(w.partials);
       (void)hipFree(w.flags);
-      (void)hipFree(w.status);
+      keep_host = w.status_host;  // the error word survives growth (it may hold a report)
+      keep_dev = w.status;
       w = Workspace{};
     }
     size_t bytes = need > base ? need : base;
     int nflags = slots > 1024 ? (int)slots : 1024;
     hipError_t e = hipMalloc(&w.partials, bytes);
-    if (e != hipSuccess) { w = Workspace{}; (void)hipGetLastError(); return SK_ERR_NO_MEMORY; }
+    if (e != hipSuccess) {
+      w = Workspace{};
+      w.status_host = keep_host;
+      w.status = keep_dev;
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
     e = hipMalloc(&w.flags, sizeof(uint32_t) * nflags);
-    if (e == hipSuccess) e = hipMalloc(&w.status, sizeof(int32_t));
+    if (e == hipSuccess && keep_host == nullptr) {
+      e = hipHostMalloc(reinterpret_cast<void **>(&keep_host), sizeof(int32_t),
+                        hipHostMallocMapped | hipHostMallocCoherent);
+      if (e == hipSuccess) {
+        *keep_host = 0;
+        e = hipHostGetDevicePointer(reinterpret_cast<void **>(&keep_dev), keep_host, 0);
+        if (e != hipSuccess) {
+          (void)hipHostFree(keep_host);
+          keep_host = nullptr;
+        }
+      }
+    }
     if (e != hipSuccess) {
       (void)hipFree(w.partials);
       (void)hipFree(w.flags);
@@ -171,14 +193,32 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
       (void)hipGetLastError();
       return SK_ERR_NO_MEMORY;
     }
+    w.status_host = keep_host;
+    w.status = keep_dev;
     w.partial_bytes = bytes;
     w.flag_count = nflags;
     w.epoch = 0;
-    hipLaunchKernelGGL(init_flags_kernel, dim3(4), dim3(256), 0, stream, w.flags, nflags, w.status);
+    hipLaunchKernelGGL(init_flags_kernel, dim3(4), dim3(256), 0, stream, w.flags, nflags, nullptr);
     e = hipGetLastError();
     if (e != hipSuccess) return hip_fail(e, "workspace init");
   }
   *out = &w;
+  return SK_OK;
+}
+
+// A fixup time-out that a kernel of this device has written to a
+// workspace's (host-mapped) error word since the last report: reported once,
+// by the next call that starts after the word was written (the call then
+// launches nothing), or by sk_device_status.  Caller holds g_mu.
+int take_timeout_report(int dev) {
+  for (auto &kv : g_ws) {
+    if (kv.first.first != dev || kv.second.status_host == nullptr) continue;
+    volatile int32_t *w = kv.second.status_host;
+    if (*w & 1) {
+      *w = 0;
+      return SK_ERR_FIXUP_TIMEOUT;
+    }
+  }
   return SK_OK;
 }
 
@@ -193,6 +233,7 @@ int validate(const sk_gemm_desc &d, const sk_options &o, const sk_abft_report *r
   if (o.forced_grid < 0 || o.hybrid_min_waves < 0 || o.n_faults < 0 || o.spin_limit_us < 0)
     return SK_ERR_INVALID_ARG;
   if (o.n_faults > 0 && o.faults == nullptr) return SK_ERR_INVALID_ARG;
+  if (o.test_flags & ~SK_TEST_NO_SIGNAL) return SK_ERR_INVALID_ARG;
   if (o.abft && d.dtype != SK_F32) return SK_ERR_UNSUPPORTED;
   if (o.abft && report == nullptr) return SK_ERR_INVALID_ARG;
   if (d.m == 0 || d.n == 0) return SK_OK;
@@ -226,6 +267,9 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   NoAlloc *na = nullptr;
   if (noalloc) {
     rc = noalloc_state(dev, stream, &na);
+    if (rc != SK_OK) return rc;
+  } else {
+    rc = take_timeout_report(dev);
     if (rc != SK_OK) return rc;
   }
   if (o.abft) {
@@ -347,6 +391,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   a.partials = partials; a.flags = flags; a.epoch = epoch; a.status = status;
   const int64_t us = o.spin_limit_us > 0 ? o.spin_limit_us : 2000000;
   a.spin_limit = us * info->wall_khz / 1000;
+  a.no_signal = (o.test_flags & SK_TEST_NO_SIGNAL) ? 1 : 0;
   a.abft = o.abft; a.n_faults = o.n_faults; a.faults = o.faults; a.report = report;
   a.abft_tau = o.abft_tau > 0 ? o.abft_tau : 1.0f;
 
@@ -495,13 +540,15 @@ int sk_device_status(void) {
   if (hipGetDevice(&dev) != hipSuccess) return SK_ERR_HIP;
   hipError_t e = hipDeviceSynchronize();
   if (e != hipSuccess) return hip_fail(e, "hipDeviceSynchronize");
-  int result = SK_OK;
-  std::vector<int32_t *> words;
-  for (auto &kv : g_ws)
-    if (kv.first.first == dev && kv.second.status) words.push_back(kv.second.status);
+  int result = take_timeout_report(dev);
+  for (auto &kv : g_ws)  // every workspace's word is read and cleared
+    if (kv.first.first == dev && kv.second.status_host) {
+      if (*static_cast<volatile int32_t *>(kv.second.status_host) & 1) result = SK_ERR_FIXUP_TIMEOUT;
+      *static_cast<volatile int32_t *>(kv.second.status_host) = 0;
+    }
   auto na = g_noalloc.find(dev);
-  if (na != g_noalloc.end() && na->second.ptr) words.push_back(reinterpret_cast<int32_t *>(na->second.ptr));
-  for (int32_t *w : words) {
+  if (na != g_noalloc.end() && na->second.ptr) {  // the allocation-free entry point's word: device memory
+    int32_t *w = reinterpret_cast<int32_t *>(na->second.ptr);
     int32_t v = 0;
     e = hipMemcpy(&v, w, sizeof(v), hipMemcpyDeviceToHost);
     if (e != hipSuccess) return hip_fail(e, "status read");
@@ -541,7 +588,7 @@ int sk_release_workspace(void) {
     (void)hipSetDevice(kv.first.first);
     (void)hipFree(kv.second.partials);
     (void)hipFree(kv.second.flags);
-    (void)hipFree(kv.second.status);
+    (void)hipHostFree(kv.second.status_host);
     (void)hipSetDevice(cur);
   }
   g_ws.clear();

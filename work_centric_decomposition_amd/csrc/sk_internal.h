@@ -329,8 +329,9 @@ struct KernelArgs {
   float *partials;     // grid slots of BM*BN floats
   uint32_t *flags;     // grid flags
   uint32_t epoch;
-  int32_t *status;     // device error word (bit 0: fixup time-out)
+  int32_t *status;     // error word (bit 0: fixup time-out): mapped host memory, or device memory
   int64_t spin_limit;  // time-out in ticks of the 100 MHz real-time counter
+  int32_t no_signal;   // testing: producers store partials without signalling them
   // ABFT (fp32 only)
   int32_t abft;
   int32_t n_faults;

@@ -122,10 +122,14 @@ template <> struct Elem<SK_F32> {
 // coherent with the others, and an agent-scope release or acquire in the
 // language memory model writes back or invalidates the entire L2 of the XCD
 // (disturbing every workgroup that shares it, and costing tens of
-// microseconds per fixup on a busy chip).  Instead, the partial tile is
-// written and read with agent-coherent (sc1) 128-bit buffer accesses, which
-// the L2 passes through to the memory side, so only the order of the
-// accesses matters:
+// microseconds per fixup on a busy chip).  In the LLVM AMDGPU memory model
+// for GFX942 (followed by gfx950), relaxed agent-scope atomics are plain
+// accesses with the sc1 bit, coherent across the XCDs' L2 caches, and the
+// release/acquire maintenance (write-back before, invalidation after) exists
+// only for data accessed without sc1.  Here the partial tile is written and
+// read with agent-coherent (sc1) 128-bit buffer accesses, which the L2
+// passes through to the memory side, so only the order of the accesses
+// matters:
 //   producer: sc1 stores; wait for this wave's stores to complete; workgroup
 //     barrier; thread 0 stores the flag (relaxed, agent scope, also sc1);
 //   owner: thread 0 reads the flag (relaxed, agent scope) until it holds the
@@ -145,7 +149,7 @@ __device__ __forceinline__ void store_partial(const KernelArgs &a, int x, const 
   }
   __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
   __syncthreads();
-  if (t == 0) __hip_atomic_store(a.flags + x, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0 && !a.no_signal) __hip_atomic_store(a.flags + x, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Returns false if the wait timed out (the status word is set).
@@ -157,7 +161,8 @@ __device__ __forceinline__ bool wait_flag(const KernelArgs &a, int peer) {
     while (__hip_atomic_load(a.flags + peer, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != a.epoch) {
       __builtin_amdgcn_s_sleep(1);
       if ((int64_t)(__builtin_amdgcn_s_memrealtime() - t0) > a.spin_limit) {
-        atomicOr(a.status, 1);
+        // the error word may be host memory: a plain system-scope store
+        __hip_atomic_store(a.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         ok = 0;
         break;
       }

@@ -385,6 +385,18 @@ static std::pair<InstKey, int> g_inst[64];
 static bool g_inst_valid[64];
 static unsigned g_inst_next = 0;
 
+// A grid above the resident slot count runs only if workgroups are
+// dispatched in index order (per XCD) as slots free up.  Owners wait only on
+// higher-numbered peers whose partial is their first segment, so the
+// smallest resident workgroup can block only on a peer at least slots - 8
+// workgroups after it (eight XCDs, each dispatching its share in order);
+// plans whose owners reach that far could wait on a workgroup that cannot
+// be dispatched before they finish, and are refused.
+static int forced_grid_ok(int rc, const Plan &P) {
+  if (rc != SK_OK || P.grid <= P.slots) return rc;
+  return plan_max_peers(P) < P.slots - 8 ? SK_OK : SK_ERR_UNSUPPORTED;
+}
+
 int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &P) {
   std::memset(&P, 0, sizeof(P));
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
@@ -398,8 +410,8 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Pl
   if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
   // a forced grid is a count of large-tile workgroups unless a tile is given
   if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE || (o.tile == SK_TILE_AUTO && o.forced_grid > 0))
-    return plan_inst(d, o, 0, slots[0], P);
-  if (o.tile == SK_TILE_SMALL) return plan_inst(d, o, 1, slots[1], P);
+    return forced_grid_ok(plan_inst(d, o, 0, slots[0], P), P);
+  if (o.tile == SK_TILE_SMALL) return forced_grid_ok(plan_inst(d, o, 1, slots[1], P), P);
   // AUTO: whichever instance the model predicts faster (cached per shape
   // class); measured on the fp16 shape sweep, the small tile wins on most
   // shapes below one wave of large tiles and on short-k shapes up to about
