@@ -77,11 +77,13 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-extra", action="store_true", help="skip the other workload")
     p.add_argument("--sweep", type=int, default=0, metavar="COUNT",
-                   help="run the Stream-K shape sweep (first COUNT of the 2000 seeded fp16 "
-                        "shapes), Stream-K (AUTO) vs data-parallel, and print its summary")
+                   help="only the Stream-K shape sweep on COUNT shapes (2000: all) and print its summary")
     p.add_argument("--sweep-out", default="", help="CSV file for the per-shape sweep results")
-    p.add_argument("--sweep-tiles", action="store_true",
-                   help="also time each sweep shape with each fp16 tile instance (AUTO schedule)")
+    p.add_argument("--sweep-legs", default="auto,dp",
+                   help="schedules timed per sweep shape: auto, dp, page, large, small, basic, hybrid2, "
+                        "hybrid2_w2, hybrid1, xcd_w2")
+    p.add_argument("--sweep-count", type=int, default=300,
+                   help="shapes of the sweep leg in the default run (0: no sweep leg)")
     p.add_argument("--skinny", action="store_true",
                    help="time eight memory-bound skinny fp16 shapes of the sweep (AUTO and DP), "
                         "--steps launches each")
@@ -559,133 +561,202 @@ def _spin_cycles(torch, seconds):
     return max(1000, int(seconds / per_cycle))
 
 
-def shape_sweep(torch, sk, S, count, out_path, reps=5, tile_legs=False):
-    """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
-    contiguous along k; alpha=1, beta=0) on the seeded shape list; each shape
-    runs three schedules of the same kernel: AUTO (the XCD-aware split), the
-    page's own choice (two-tile hybrid with a wave or more of tiles, basic
-    Stream-K below a wave, data-parallel when the tiles fill whole waves) and
-    data-parallel in linear tile order.
+def _spin_for(torch, seconds, _cache={}):
+    """Queues a spin kernel that keeps the GPU busy for about `seconds`."""
+    if "per_cycle" not in _cache:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(1000)
+        e0.record()
+        torch.cuda._sleep(1000000)
+        e1.record()
+        torch.cuda.synchronize()
+        _cache["per_cycle"] = e0.elapsed_time(e1) * 1e-3 / 1e6
+    torch.cuda._sleep(max(1000, int(seconds / _cache["per_cycle"])))
 
-    Per shape: median time of `reps` launches after one warm-up; a spin
-    kernel queued ahead of the timed launches keeps the GPU busy while the
-    host enqueues them, so each event pair brackets the GEMM alone and not
-    the host's launch cost (which for the smallest shapes exceeds the kernel
-    time; it is reported separately as the plan+launch latency); roofline time
-    T_min = max(2mnk / P_fp16, 2(mk + kn + mn) / BW_HBM); utilisation =
-    T_min / T.  Inputs: N(0,1)/sqrt(k)-scaled normal values drawn on the GPU
-    from a generator seeded with the sweep seed (timing only; parity of sweep
-    shapes is covered by the tests)."""
+
+def back_to_back_us(torch, launch, min_ms=20.0, max_launches=4096):
+    """Mean time of one launch, from R launches timed back to back between
+    one pair of HIP events, R chosen so that the measurement spans at least
+    `min_ms` (at least 5 launches).  A spin kernel queued ahead keeps the GPU
+    busy while the host enqueues the R launches, so they run back to back on
+    the GPU and the host's cost of a call (planning, argument marshalling)
+    is not charged to the kernel.  Returns (microseconds, R, host
+    microseconds per call)."""
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    host = []
+    for _ in range(3):  # warm-up (plan cache, clocks), and the host's cost of a call
+        h0 = time.perf_counter()
+        launch()
+        host.append(time.perf_counter() - h0)
+    torch.cuda.synchronize()
+    h = min(host)
+    _spin_for(torch, 4 * h + 2e-4)
+    e0.record()
+    launch()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = max(e0.elapsed_time(e1), 1e-4)  # ms
+    R = int(min(max_launches, max(5, math.ceil(min_ms / t1))))
+    spin_s = 1.3 * R * h + 5e-4
+    _spin_for(torch, spin_s)
+    e0.record()
+    h0 = time.perf_counter()
+    for _ in range(R):
+        launch()
+    enq = time.perf_counter() - h0
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / R
+    # the launches ran back to back on the GPU only if the host had queued
+    # them all before the spin ended (a full queue would block the host)
+    back_to_back_us.last = {"enqueue_ms": enq * 1e3, "spin_ms": spin_s * 1e3, "host_bound": enq > spin_s}
+    return us, R, h * 1e6
+
+
+def sweep_subset(S, count, tile_m=256, tile_n=256, slots=256):
+    """`count` shapes of the seeded 2000-shape Stream-K sweep in its
+    proportions (3/4 random, 1/8 skinny, 1/8 tile-count adversarial): every
+    (2000/count)-th shape of the list, which holds the kinds in that order."""
+    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, tile_m, tile_n, slots)
+    if count >= len(shapes):
+        return shapes
+    return [shapes[int(i * len(shapes) / count)] for i in range(count)]
+
+
+def sweep_legs(sk, names, page_sched):
+    """Options of each named leg (the schedule of the same kernels)."""
+    L = sk.TILE_LARGE
+    table = {
+        "auto": sk.make_options(),
+        "dp": sk.make_options(schedule=sk.SCHED_DP, tile=L),
+        "page": sk.make_options(schedule=page_sched, tile=L),
+        "large": sk.make_options(tile=L),
+        "small": sk.make_options(tile=sk.TILE_SMALL),
+        "basic": sk.make_options(schedule=sk.SCHED_SK_BASIC, tile=L),
+        "hybrid2": sk.make_options(schedule=sk.SCHED_SK_HYBRID2, tile=L),
+        "hybrid2_w2": sk.make_options(schedule=sk.SCHED_SK_HYBRID2, tile=L, hybrid_min_waves=2),
+        "hybrid1": sk.make_options(schedule=sk.SCHED_SK_HYBRID1, tile=L),
+        "xcd_w2": sk.make_options(schedule=sk.SCHED_XCD_ALIGNED, tile=L, hybrid_min_waves=2),
+    }
+    return [(n, table[n]) for n in names]
+
+
+def shape_sweep(torch, sk, S, count, out_path="", legs=("auto", "dp"), min_ms=20.0):
+    """Stream-K shape sweep: fp16 GEMMs (A row-major, B column-major, both
+    contiguous along k; alpha=1, beta=0) on `count` shapes of the seeded
+    sweep list (sweep_subset), each run under the named schedules of the
+    same kernels ("dp": data-parallel on the large tile, the baseline).
+
+    Per shape and leg: back_to_back_us (R launches back to back, at least
+    20 ms per measurement).  Roofline time T_min = max(2mnk / P_fp16,
+    2(mk + kn + mn) / BW_HBM); utilisation = T_min / T.  Inputs:
+    N(0,1)-scaled normal values drawn on the GPU from a generator seeded with
+    the sweep seed (timing only; parity of sweep shapes is in the tests)."""
     import statistics
     probe = sk.make_desc(256, 256, 256, 1.0, 0, 256, 0, 256, 0.0, 0, 256, sk.F16, sk.A_ROW_B_COL)
-    tile = sk.plan_query(probe)
-    shapes = S.sweep_shapes(2000, S.SEED_SWEEP, tile.tile_m, tile.tile_n, tile.slots)[:count]
+    tile = sk.plan_query(probe, sk.make_options(tile=sk.TILE_LARGE))
+    shapes = sweep_subset(S, count, tile.tile_m, tile.tile_n, tile.slots)
     mx = max(max(m * k, k * n, m * n) for _, m, n, k in shapes)
     g = torch.Generator(device="cuda")
     g.manual_seed(S.SEED_SWEEP)
     A = torch.randn(mx, generator=g, device="cuda", dtype=torch.float32).to(torch.float16)
     B = torch.randn(mx, generator=g, device="cuda", dtype=torch.float32).to(torch.float16)
     C = torch.empty(mx, device="cuda", dtype=torch.float16)
-    peak, bw = PEAK_TFLOPS["f16"] * 1e12, 8.0e12
+    peak, bw = PEAK_TFLOPS["f16"] * 1e12, PEAK_HBM_GBS * 1e9
     rows = []
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for _ in range(reps)]
-    spin = _spin_cycles(torch, 40e-6 * (reps + 1))
     for idx, (kind, m, n, k) in enumerate(shapes):
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
-        p = sk.plan_query(d)
-        large = sk.TILE_LARGE
-        pl = sk.plan_query(d, sk.make_options(tile=large))
+        pl = sk.plan_query(d, sk.make_options(tile=sk.TILE_LARGE))
         t, slots = pl.tiles, pl.slots
         w, r = divmod(t, slots)
         page = sk.SCHED_DP if r == 0 else sk.SCHED_SK_HYBRID2 if w >= 1 else sk.SCHED_SK_BASIC
-        res = {}
-        legs = [("auto", sk.make_options()), ("page", sk.make_options(schedule=page, tile=large)),
-                ("dp", sk.make_options(schedule=sk.SCHED_DP, tile=large))]
-        if tile_legs:
-            legs += [("large", sk.make_options(tile=large)), ("small", sk.make_options(tile=sk.TILE_SMALL))]
+        lg = sweep_legs(sk, legs, page)
         # rotate the order per shape so that clock ramps do not favour one leg
-        legs = legs[idx % len(legs):] + legs[:idx % len(legs)]
-        for sched_name, opts in legs:
-            sk.gemm_ex(d, opts)
-            torch.cuda._sleep(spin)
-            host = []
-            for e0, e1 in ev:
-                e0.record()
-                h0 = time.perf_counter()
-                sk.gemm_ex(d, opts)
-                host.append(time.perf_counter() - h0)
-                e1.record()
-            torch.cuda.synchronize()
-            res[sched_name] = statistics.median(e0.elapsed_time(e1) for e0, e1 in ev) * 1e-3
-            res["host_" + sched_name] = statistics.median(host)
+        lg = lg[idx % len(lg):] + lg[:idx % len(lg)]
         fl = 2.0 * m * n * k
         by = 2.0 * (m * k + k * n + m * n)
         tmin = max(fl / peak, by / bw)
-        rows.append(dict(kind=kind, m=m, n=n, k=k, tiles=t, schedule=p.schedule, grid=p.grid,
-                         sk_tiles=p.sk_tiles, phase_div=p.phase_div, page_schedule=page,
-                         t_auto_us=res["auto"] * 1e6, t_page_us=res["page"] * 1e6,
-                         t_dp_us=res["dp"] * 1e6,
-                         tflops_auto=fl / res["auto"] / 1e12, tflops_page=fl / res["page"] / 1e12,
-                         tflops_dp=fl / res["dp"] / 1e12,
-                         util_auto=tmin / res["auto"], util_page=tmin / res["page"],
-                         util_dp=tmin / res["dp"],
-                         dp_quant_eff=t / (slots * -(-t // slots)), mem_bound=int(by / bw > fl / peak),
-                         tmin_us=tmin * 1e6,
-                         host_auto_us=res["host_auto"] * 1e6, host_dp_us=res["host_dp"] * 1e6,
-                         tile_auto=p.tile_m,
-                         **({"t_large_us": res["large"] * 1e6, "t_small_us": res["small"] * 1e6} if tile_legs else {})))
-        if idx % 100 == 0:
+        row = dict(kind=kind, m=m, n=n, k=k, tiles=t, waves=w, tail=r, tmin_us=tmin * 1e6,
+                   mem_bound=int(by / bw > fl / peak), dp_quant_eff=t / (slots * -(-t // slots)))
+        for name, opts in lg:
+            us, R, host_us = back_to_back_us(torch, lambda: sk.gemm_ex(d, opts), min_ms)
+            pq = sk.plan_query(d, opts)
+            row[f"t_{name}_us"] = us
+            row[f"launches_{name}"] = R
+            row[f"host_{name}_us"] = host_us
+            row[f"util_{name}"] = tmin * 1e6 / us
+            row[f"tflops_{name}"] = fl / (us * 1e-6) / 1e12
+            row[f"schedule_{name}"] = pq.schedule
+            row[f"tile_{name}"] = pq.tile_m
+            row[f"enqueue_ms_{name}"] = back_to_back_us.last["enqueue_ms"]
+            row[f"spin_ms_{name}"] = back_to_back_us.last["spin_ms"]
+            row[f"host_bound_{name}"] = int(back_to_back_us.last["host_bound"])
+        rows.append(row)
+        if idx % 50 == 0:
             print(f"sweep {idx}/{len(shapes)}", file=sys.stderr, flush=True)
     if out_path:
         with open(out_path, "w") as f:
-            f.write(",".join(rows[0].keys()) + "\n")
+            keys = list(rows[0].keys())
+            f.write(",".join(keys) + "\n")
             for r in rows:
-                f.write(",".join(f"{v:.6g}" if isinstance(v, float) else str(v) for v in r.values()) + "\n")
+                f.write(",".join(f"{r[k]:.6g}" if isinstance(r[k], float) else str(r[k]) for k in keys) + "\n")
+    return sweep_summary(rows, legs)
+
+
+def sweep_summary(rows, legs):
+    import statistics
 
     def cv(xs):
         mu = statistics.fmean(xs)
         return statistics.pstdev(xs) / mu if mu > 0 else float("nan")
 
-    def speed(sel, name):
-        sp = [r["t_dp_us"] / r[f"t_{name}_us"] for r in sel]
-        return {"mean": round(statistics.fmean(sp), 4),
-                "geomean": round(math.exp(statistics.fmean(math.log(x) for x in sp)), 4),
-                "median": round(statistics.median(sp), 4),
-                "max": round(max(sp), 3), "min": round(min(sp), 3),
-                "frac_not_slower": round(sum(x >= 0.98 for x in sp) / len(sp), 4)}
-
     def summary(sel):
         if not sel:
             return None
         out = {"shapes": len(sel)}
-        for name in ("auto", "page"):
-            out[f"speedup_{name}_over_dp"] = speed(sel, name)
-        for name in ("auto", "page", "dp"):
-            out[f"util_{name}"] = {"mean": round(statistics.fmean(r[f"util_{name}"] for r in sel), 4),
-                                   "cv": round(cv([r[f"util_{name}"] for r in sel]), 4)}
-            out[f"tflops_{name}_mean"] = round(statistics.fmean(r[f"tflops_{name}"] for r in sel), 2)
-        out["dp_quant_eff_mean"] = round(statistics.fmean(r["dp_quant_eff"] for r in sel), 4)
-        u = sorted(r["util_auto"] for r in sel)
-        out["util_auto_p5_p95"] = [round(u[int(0.05 * (len(u) - 1))], 4), round(u[int(0.95 * (len(u) - 1))], 4)]
-        # host time of one sk_gemm call from Python (plan + launch)
-        out["host_launch_us_median"] = {name: round(statistics.median(r[f"host_{name}_us"] for r in sel), 2)
-                                        for name in ("auto", "dp")}
+        for name in legs:
+            if name == "dp" or "dp" not in legs:
+                continue
+            sp = [r["t_dp_us"] / r[f"t_{name}_us"] for r in sel]
+            out[f"{name}_over_dp"] = {
+                "geomean": round(math.exp(statistics.fmean(math.log(x) for x in sp)), 4),
+                "median": round(statistics.median(sp), 4), "min": round(min(sp), 3),
+                "max": round(max(sp), 3), "frac_not_slower": round(sum(x >= 0.98 for x in sp) / len(sp), 4)}
+        for name in legs:
+            u = [r[f"util_{name}"] for r in sel]
+            us = sorted(u)
+            out[f"util_{name}"] = {"mean": round(statistics.fmean(u), 4), "cv": round(cv(u), 4),
+                                   "p5_p95": [round(us[int(0.05 * (len(us) - 1))], 4),
+                                              round(us[int(0.95 * (len(us) - 1))], 4)]}
+        if "auto" in legs:
+            out["host_call_us_median"] = round(statistics.median(r["host_auto_us"] for r in sel), 2)
+        out["host_bound_measurements"] = sum(r[f"host_bound_{name}"] for r in sel for name in legs)
         return out
 
-    return {"sweep": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0",
-            "all": summary(rows),
-            "compute_bound": summary([r for r in rows if not r["mem_bound"]]),
-            # shapes whose roofline time is at least 100 us: the fixed cost of
-            # a launch (8-12 us) no longer dominates them
-            "compute_bound_tmin_100us": summary([r for r in rows if not r["mem_bound"]
-                                                 and r["tmin_us"] >= 100.0]),
-            "memory_bound": summary([r for r in rows if r["mem_bound"]]),
-            "random": summary([r for r in rows if r["kind"] == "random"]),
-            "skinny": summary([r for r in rows if r["kind"] == "skinny"]),
-            "adversarial": summary([r for r in rows if r["kind"] == "adversarial"]),
-            "roofline": {"peak_tflops": PEAK_TFLOPS["f16"], "hbm_tb_s": 8.0,
-                         "t_min": "max(2mnk/peak, 2(mk+kn+mn)/bw)"}}
+    classes = {
+        "all": rows,
+        "compute_bound": [r for r in rows if not r["mem_bound"]],
+        "memory_bound": [r for r in rows if r["mem_bound"]],
+        "random": [r for r in rows if r["kind"] == "random"],
+        "skinny": [r for r in rows if r["kind"] == "skinny"],
+        "adversarial": [r for r in rows if r["kind"] == "adversarial"],
+        # by the roofline time: below 10 us the fixed cost of a launch dominates
+        "tmin_lt_10us": [r for r in rows if r["tmin_us"] < 10.0],
+        "tmin_10_100us": [r for r in rows if 10.0 <= r["tmin_us"] < 100.0],
+        "tmin_ge_100us": [r for r in rows if r["tmin_us"] >= 100.0],
+        "compute_bound_tmin_ge_100us": [r for r in rows if not r["mem_bound"] and r["tmin_us"] >= 100.0],
+        # full waves of large tiles: the page's hybrids differ only from one wave on
+        "waves_0": [r for r in rows if r["waves"] == 0],
+        "waves_1_tail": [r for r in rows if r["waves"] == 1 and r["tail"] > 0],
+        "waves_2plus_tail": [r for r in rows if r["waves"] >= 2 and r["tail"] > 0],
+    }
+    return {"workload": "Stream-K shape sweep, fp16, A row-major / B column-major, alpha=1 beta=0; "
+                        f"{len(rows)} shapes of the seeded 2000-shape list in its proportions",
+            "timing": "R launches back to back between one event pair, >= 20 ms per measurement",
+            "legs": list(legs),
+            "roofline": {"peak_tflops": PEAK_TFLOPS["f16"], "hbm_tb_s": PEAK_HBM_GBS / 1000,
+                         "t_min": "max(2mnk/peak, 2(mk+kn+mn)/bw)"},
+            "classes": {name: summary(sel) for name, sel in classes.items()}}
 
 
 def cpu_baseline(S, budget_s=25.0):
@@ -732,8 +803,8 @@ def main():
         calibrate_copy(torch)
         return
     if args.sweep:
-        print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out, tile_legs=args.sweep_tiles)),
-              flush=True)
+        print(json.dumps(shape_sweep(torch, sk, S, args.sweep, args.sweep_out,
+                                     legs=tuple(args.sweep_legs.split(",")))), flush=True)
         return
     if args.calibrate_model:
         print(json.dumps(calibrate_model(torch, sk, S, args.calibrate_model)), flush=True)
@@ -826,6 +897,8 @@ def main():
         line["per_shape_tflops"] = m["per_shape"]
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(S)
+    if not args.no_extra and args.sweep_count > 0:
+        line["sweep"] = shape_sweep(torch, sk, S, args.sweep_count)
     if not args.no_extra:
         line["abft"] = abft_overhead(torch, sk, S)
         line["gemv"] = gemv_leg(torch, sk, S)

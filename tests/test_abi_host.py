@@ -609,3 +609,20 @@ def test_forced_grid_beyond_the_slots_is_refused_when_a_wait_could_target_an_und
     d2 = _desc(8192, 8192, 8192, sk.F16)  # 1024 tiles: g = t is data-parallel, no waits
     assert sk.plan_query(d2, sk.make_options(forced_grid=1024), 256).max_peers == 0
     assert sk.gemm_ex(d, sk.make_options(test_flags=2), check=False) == sk.ERR_INVALID_ARG
+
+
+def test_two_tile_hybrid_honours_min_waves():
+    """hybrid_min_waves = 2 (the page's "w >= 2"): with one full wave and
+    leftover tiles the page's two-tile hybrid becomes basic Stream-K over all
+    tiles, planned exactly as the oracle's Algorithm 5 on the slot count;
+    from two waves on it is the two-tile hybrid again."""
+    d = _desc(256 * 17, 256 * 16, 2048)  # 272 tiles on 256 slots: w = 1, r = 16
+    p1 = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_HYBRID2), 256)
+    assert p1.schedule == sk.SCHED_SK_HYBRID2 and p1.sk_tiles == 272
+    p2 = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_HYBRID2, hybrid_min_waves=2), 256)
+    assert p2.schedule == sk.SCHED_SK_BASIC and p2.grid == 256 and p2.sk_tiles == p2.tiles
+    assert _lib_plan_records(p2) == _oracle_records(256 * 17, 256 * 16, 2048, p2.tile_m, p2.tile_n,
+                                                    p2.tile_k, oracle.SK, 256)
+    d3 = _desc(256 * 33, 256 * 16, 2048)  # 528 tiles: w = 2, r = 16
+    p3 = sk.plan_query(d3, sk.make_options(schedule=sk.SCHED_SK_HYBRID2, hybrid_min_waves=2), 256)
+    assert p3.schedule == sk.SCHED_SK_HYBRID2 and p3.sk_tiles == 16 + 256

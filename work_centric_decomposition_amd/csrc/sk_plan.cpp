@@ -251,7 +251,11 @@ static int plan_inst(const sk_gemm_desc &d, const sk_options &o, int inst, int s
     sk_tiles = P.tiles;
   } else {
     if (sched == SK_SCHED_AUTO) sched = SK_SCHED_XCD_ALIGNED;
-    if (sched == SK_SCHED_SK_HYBRID2 && (P.w < 1 || P.r == 0))
+    // the page's two-tile hybrid needs hybrid_min_waves full waves (reading
+    // of its "w >= 2" against the mechanism, which works from one wave);
+    // with fewer it is basic Stream-K over all tiles, with no leftover tiles
+    // data-parallel
+    if (sched == SK_SCHED_SK_HYBRID2 && (P.w < min_waves || P.r == 0))
       sched = P.r == 0 ? SK_SCHED_DP : SK_SCHED_SK_BASIC;
     switch (sched) {
       case SK_SCHED_DP:
