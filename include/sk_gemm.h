@@ -169,6 +169,9 @@ typedef struct {
   int32_t uncorrectable; /* domains whose mismatch could not be located */
   int32_t n_records;     /* records produced; the first SK_ABFT_MAX_RECORDS are stored */
   sk_abft_record records[SK_ABFT_MAX_RECORDS];
+  float max_ratio;       /* largest |checksum residual| / threshold over every row and column
+                          * checked (a fault-free margin: below 1 nothing is flagged) */
+  int32_t checked;       /* rows and columns checked */
 } sk_abft_report;
 
 /* fp16/bf16 tile instances.  LARGE: 256 x 256 x 64 tiles, one 512-thread
@@ -266,11 +269,15 @@ int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t
  * chosen explicitly whose positions or quanta products would reach 2^31
  * (k of several million with the XCD-aware schedule) returns
  * SK_ERR_UNSUPPORTED; AUTO then takes the two-tile hybrid, else the
- * data-parallel order.  Stream-ordered temporaries (hipMallocAsync, freed
- * on the stream after the GEMM; SK_ERR_NO_MEMORY when one cannot be had):
- * the k-contiguous copy of an operand the kernels cannot read in place
- * (plan packs bits), and in ABFT mode the operands' checksum encodings,
- * (tiles_m + tiles_n) * ceil(k/32) * 256 bytes for 128 x 128 tiles. */
+ * data-parallel order.  Stream-ordered temporary (hipMallocAsync, freed on
+ * the stream after the GEMM; SK_ERR_NO_MEMORY when it cannot be had): the
+ * k-contiguous copy of an operand the kernels cannot read in place (plan
+ * packs bits).  In ABFT mode the operands' checksum encodings and
+ * detection-threshold inputs, at most about 4 * ((tiles_m + tiles_n) * 32 *
+ * ceil(k/32) + (m + n) * (ceil(k/64) + 1)) bytes for 128 x 128 tiles (at
+ * least 4 MiB), and one 32-bit counter per tile of A and B, are kept in the
+ * stream's workspace (grown when a call needs more, after synchronising the
+ * stream; freed by sk_release_workspace). */
 int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report *report,
                hipStream_t stream);
 

@@ -575,7 +575,9 @@ def test_strerror_texts():
     assert sk.strerror(0) == "success"
     assert "time" in sk.strerror(sk.ERR_FIXUP_TIMEOUT)
     assert sk.version().startswith("sk_gemm")
-    assert ctypes.sizeof(sk.AbftReport) == 16 + 64 * ctypes.sizeof(sk.AbftRecord)
+    # four counters, the records, then max_ratio and checked
+    assert ctypes.sizeof(sk.AbftReport) == 16 + 64 * ctypes.sizeof(sk.AbftRecord) + 8
+    assert sk.AbftReport.max_ratio.offset == 16 + 64 * ctypes.sizeof(sk.AbftRecord)
 
 
 def test_noalloc_refusals_before_any_gpu_call():

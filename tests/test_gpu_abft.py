@@ -73,13 +73,16 @@ def _logical(c: Case):
 
 
 def _thresholds(Al, Bl, i, j, tile=128):
-    """Detection thresholds of row i and column j of the verification domain
-    (a full tile here): used only to re-draw undetectable bit flips."""
+    """Detection thresholds the kernel applies to row i and column j of a
+    full-k verification domain (a whole tile): 2^-24 sqrt(k) times the bound
+    ||a_i||_1 max_k (|B| e)_k of the row's absolute checksum (likewise
+    max_k (e^T|A|)_k ||b_j||_1 for the column); used only to re-draw bit
+    flips too small to detect."""
     r0, c0 = (i // tile) * tile, (j // tile) * tile
     Ba = np.abs(Bl[:, c0:c0 + tile])
     Aa = np.abs(Al[r0:r0 + tile, :])
-    ra = np.abs(Al[i]) @ Ba.sum(axis=1)
-    ca = Aa.sum(axis=0) @ np.abs(Bl[:, j])
+    ra = np.abs(Al[i]).sum() * Ba.sum(axis=1).max()
+    ca = Aa.sum(axis=0).max() * np.abs(Bl[:, j]).sum()
     scale = U * np.sqrt(Al.shape[1])
     return scale * ra, scale * ca
 
@@ -269,3 +272,34 @@ def test_abft_4096_seeded_fault_runs():
         _check_corrected(c, got, faults, rep)
         total += len(faults)
     assert total >= 50
+
+
+def test_abft_4096_fault_free_runs_margin():
+    """100 fault-free 4096^3 fp32 runs (10 seeds, 5 with beta = 0 and 5 with
+    beta = 1 each; U[-1,1] inputs): zero detections in every run, every row
+    and column of every tile checked, and the largest |residual| / threshold
+    seen over all of them (the margin of the sqrt(k_seg) threshold) is
+    printed and must stay below 1."""
+    n, runs, worst = 4096, 0, 0.0
+    for seed in range(10):
+        c = Case(n, n, n, sk.F32, sk.A_ROW_B_ROW, S.SEED_ABFT + 100 + seed)
+        rep_dev = _report_dev()
+        opts = sk.make_options(abft=True)
+        d = sk.make_desc(n, n, n, 1.0, c.dA, c.lda, c.dB, c.ldb, 0.0, c.dC, c.ldc, sk.F32, sk.A_ROW_B_ROW)
+        for r in range(10):
+            beta = 0.0 if r < 5 else 1.0
+            d.beta = beta
+            c.reset_c()
+            sk.gemm_ex(d, opts, rep_dev)
+            torch.cuda.synchronize()
+            rep = sk.read_report(rep_dev)
+            assert (rep.detected, rep.corrected, rep.uncorrectable, rep.n_records) == (0, 0, 0, 0), \
+                (seed, r, _records(rep))
+            assert rep.checked == (n // 128) ** 2 * 256, rep.checked
+            worst = max(worst, rep.max_ratio)
+            runs += 1
+        got = c.result()
+        assert c.freivalds(got, 1.0, 1.0) <= TOL[sk.F32]  # the last run (beta = 1) is right
+        print(f"seed {seed}: largest |residual| / threshold so far {worst:.4f}", flush=True)
+    print(f"{runs} fault-free 4096^3 runs: largest |residual| / threshold = {worst:.4f}", flush=True)
+    assert runs == 100 and 0.0 < worst < 1.0

@@ -63,7 +63,7 @@ class AbftRecord(ctypes.Structure):
 
 class AbftReport(ctypes.Structure):
     _fields_ = [("detected", i32), ("corrected", i32), ("uncorrectable", i32), ("n_records", i32),
-                ("records", AbftRecord * ABFT_MAX_RECORDS)]
+                ("records", AbftRecord * ABFT_MAX_RECORDS), ("max_ratio", f32), ("checked", i32)]
 
 
 class Options(ctypes.Structure):

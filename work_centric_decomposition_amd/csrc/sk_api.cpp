@@ -48,6 +48,14 @@ struct Workspace {
   int32_t *status_host = nullptr;
   int32_t *status = nullptr;  // its device address
   uint32_t epoch = 0;
+  // ABFT preparation: one completion counter per tile of A and of B, zero
+  // between calls (the kernel's last workgroup of a tile clears its own),
+  // and the encodings and threshold inputs (calls on one stream run in
+  // order, so each reuses them)
+  uint32_t *abft_ctr = nullptr;
+  int64_t abft_ctr_count = 0;
+  float *abft_buf = nullptr;
+  int64_t abft_floats = 0;
 };
 
 std::mutex g_mu;
@@ -161,13 +169,18 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
       (void)hipFree(w.flags);
       keep_host = w.status_host;  // the error word survives growth (it may hold a report)
       keep_dev = w.status;
-      w = Workspace{};
+      Workspace keep_abft;  // so do the ABFT buffers (the counters are zero)
+      keep_abft.abft_ctr = w.abft_ctr;
+      keep_abft.abft_ctr_count = w.abft_ctr_count;
+      keep_abft.abft_buf = w.abft_buf;
+      keep_abft.abft_floats = w.abft_floats;
+      w = keep_abft;
     }
     size_t bytes = need > base ? need : base;
     int nflags = slots > 1024 ? (int)slots : 1024;
     hipError_t e = hipMalloc(&w.partials, bytes);
     if (e != hipSuccess) {
-      w = Workspace{};
+      w.partials = nullptr;
       w.status_host = keep_host;
       w.status = keep_dev;
       (void)hipGetLastError();
@@ -189,7 +202,8 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
     if (e != hipSuccess) {
       (void)hipFree(w.partials);
       (void)hipFree(w.flags);
-      w = Workspace{};
+      w.partials = nullptr;
+      w.flags = nullptr;
       (void)hipGetLastError();
       return SK_ERR_NO_MEMORY;
     }
@@ -203,6 +217,54 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
     if (e != hipSuccess) return hip_fail(e, "workspace init");
   }
   *out = &w;
+  return SK_OK;
+}
+
+// Workgroups of the ABFT preparation launch (four per compute unit): enough
+// loads in flight to stream the operands, each workgroup walking several
+// chunks so that its completion count is paid once per group.
+constexpr int64_t kPrepBlocks = 1024;
+
+// At least `count` zeroed ABFT counters and `floats` floats of ABFT buffer
+// in workspace `w` of `stream`.  Caller holds g_mu.
+int get_abft_buffers(Workspace &w, hipStream_t stream, int64_t count, int64_t floats) {
+  if (count > INT32_MAX) return SK_ERR_TOO_LARGE;
+  const bool grow_ctr = w.abft_ctr == nullptr || w.abft_ctr_count < count;
+  const bool grow_buf = w.abft_buf == nullptr || w.abft_floats < floats;
+  if (!grow_ctr && !grow_buf) return SK_OK;
+  if (w.abft_ctr != nullptr || w.abft_buf != nullptr) {  // growth: wait for work that may still use them
+    hipError_t e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+  }
+  if (grow_buf) {
+    (void)hipFree(w.abft_buf);
+    w.abft_buf = nullptr;
+    w.abft_floats = 0;
+    const int64_t n = floats > (1 << 20) ? floats : (1 << 20);
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&w.abft_buf), sizeof(float) * (size_t)n);
+    if (e != hipSuccess) {
+      w.abft_buf = nullptr;
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
+    w.abft_floats = n;
+  }
+  if (grow_ctr) {
+    (void)hipFree(w.abft_ctr);
+    w.abft_ctr = nullptr;
+    w.abft_ctr_count = 0;
+    const int64_t n = count > 1024 ? count : 1024;
+    hipError_t e = hipMalloc(reinterpret_cast<void **>(&w.abft_ctr), sizeof(uint32_t) * n);
+    if (e != hipSuccess) {
+      w.abft_ctr = nullptr;
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
+    hipLaunchKernelGGL(init_flags_kernel, dim3(4), dim3(256), 0, stream, w.abft_ctr, (int)n, nullptr);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "ABFT counter init");
+    w.abft_ctr_count = n;
+  }
   return SK_OK;
 }
 
@@ -272,11 +334,11 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     rc = take_timeout_report(dev);
     if (rc != SK_OK) return rc;
   }
-  if (o.abft) {
-    rc = launch_zero_report(report, stream);
-    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "report reset");
-  }
   if (d.k == 0 || d.alpha == 0.f) {  // C = beta * C
+    if (o.abft) {  // (the GEMM path zeroes the report in its ABFT preparation)
+      rc = launch_zero_report(report, stream);
+      if (rc != hipSuccess) return hip_fail((hipError_t)rc, "report reset");
+    }
     rc = launch_scale(d.dtype, d.m, d.n, d.beta, d.C, d.ldc, stream);
     return rc == hipSuccess ? SK_OK : hip_fail((hipError_t)rc, "scale kernel");
   }
@@ -363,6 +425,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   float *partials = nullptr;
   uint32_t *flags = nullptr, epoch = 0;
   int32_t *status = nullptr;
+  Workspace *ws = nullptr;  // (every call but the allocation-free one)
   if (noalloc) {
     partials = reinterpret_cast<float *>(na->ptr + kScratchHead);
     flags = reinterpret_cast<uint32_t *>(na->ptr + 256);
@@ -370,7 +433,6 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     if (++na->epoch == 0) na->epoch = 1;
     epoch = na->epoch;
   } else {
-    Workspace *ws = nullptr;
     const int64_t slots_needed = P.grid;
     rc = get_workspace(dev, stream, slots_needed, (size_t)c.bm * c.bn * 4, &ws);
     if (rc != SK_OK) {
@@ -395,35 +457,47 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   a.abft = o.abft; a.n_faults = o.n_faults; a.faults = o.faults; a.report = report;
   a.abft_tau = o.abft_tau > 0 ? o.abft_tau : 1.0f;
 
-  // ABFT: the encodings of every tile row of A and tile column of B, formed
-  // once from the operands the kernel reads
-  float *enc = nullptr;
+  // ABFT: the encodings of every tile row of A and tile column of B and the
+  // detection-threshold inputs, formed once from the operands the kernel
+  // reads, in the stream's workspace, by one preparation launch
   if (o.abft) {
-    const int64_t kb = P.ipt;
-    const int64_t a_floats = P.tiles_m * kb * 64;
-    e = hipMallocAsync(reinterpret_cast<void **>(&enc), (size_t)(a_floats + P.tiles_n * kb * 64) * sizeof(float),
-                       stream);
-    if (e != hipSuccess) {
-      (void)hipGetLastError();
+    const int64_t kb = P.ipt, chunks = (kb * 32 + 63) / 64;
+    // about kPrepBlocks workgroups, each walking a group of chunks
+    const int64_t tiles2 = P.tiles_m + P.tiles_n;
+    int64_t groups = (kPrepBlocks + tiles2 - 1) / tiles2;
+    if (groups > chunks) groups = chunks;
+    const int64_t gsize = (chunks + groups - 1) / groups;
+    groups = (chunks + gsize - 1) / gsize;
+    const int64_t ea = P.tiles_m * kb * 32, eb = P.tiles_n * kb * 32;
+    const int64_t ra_ = d.m * groups, rb_ = d.n * groups, ta = P.tiles_m * groups, tb = P.tiles_n * groups;
+    const int64_t floats = ea + eb + ra_ + rb_ + ta + tb + d.m + d.n + P.tiles_m + P.tiles_n;
+    rc = get_abft_buffers(*ws, stream, P.tiles_m + P.tiles_n, floats);
+    if (rc != SK_OK) {
       if (pa) (void)hipFreeAsync(pa, stream);
       if (pb) (void)hipFreeAsync(pb, stream);
-      return SK_ERR_NO_MEMORY;
+      return rc;
     }
-    rc = launch_abft_encode(static_cast<const float *>(a.A), a.lda, a.a_kmajor != 0, d.m, d.k, kb, enc, stream);
-    if (rc == hipSuccess)
-      rc = launch_abft_encode(static_cast<const float *>(a.B), a.ldb, a.b_kmajor != 0, d.n, d.k, kb,
-                              enc + a_floats, stream);
+    float *p_ea = ws->abft_buf, *p_eb = p_ea + ea, *p_ra = p_eb + eb, *p_rb = p_ra + ra_, *p_ta = p_rb + rb_,
+          *p_tb = p_ta + ta, *p_na = p_tb + tb, *p_nb = p_na + d.m, *p_ma = p_nb + d.n, *p_mb = p_ma + P.tiles_m;
+    AbftPrepArgs pr;
+    pr.op[0] = AbftPrepOperand{static_cast<const float *>(a.A), a.lda, a.a_kmajor, d.m, P.tiles_m,
+                               p_ea, p_ra, p_ta, p_na, p_ma};
+    pr.op[1] = AbftPrepOperand{static_cast<const float *>(a.B), a.ldb, a.b_kmajor, d.n, P.tiles_n,
+                               p_eb, p_rb, p_tb, p_nb, p_mb};
+    pr.k = d.k; pr.kb = kb; pr.chunks = chunks; pr.group_chunks = gsize; pr.groups = groups;
+    pr.counters = ws->abft_ctr;
+    pr.report = report;
+    rc = launch_abft_prep(pr, stream);
     if (rc != hipSuccess) {
-      (void)hipFreeAsync(enc, stream);
       if (pa) (void)hipFreeAsync(pa, stream);
       if (pb) (void)hipFreeAsync(pb, stream);
-      return hip_fail((hipError_t)rc, "ABFT encoding kernel");
+      return hip_fail((hipError_t)rc, "ABFT preparation kernel");
     }
-    a.enc_a = enc; a.enc_b = enc + a_floats; a.enc_kb = (int32_t)kb;
+    a.enc_a = p_ea; a.enc_b = p_eb; a.enc_kb = (int32_t)kb;
+    a.norm_a = p_na; a.norm_b = p_nb; a.emax_a = p_ma; a.emax_b = p_mb;
   }
 
   rc = launch_gemm(P, a, stream);
-  if (enc) (void)hipFreeAsync(enc, stream);
   if (pa) (void)hipFreeAsync(pa, stream);
   if (pb) (void)hipFreeAsync(pb, stream);
   if (rc != hipSuccess) return hip_fail((hipError_t)rc, "GEMM kernel launch");
@@ -588,6 +662,8 @@ int sk_release_workspace(void) {
     (void)hipSetDevice(kv.first.first);
     (void)hipFree(kv.second.partials);
     (void)hipFree(kv.second.flags);
+    (void)hipFree(kv.second.abft_ctr);
+    (void)hipFree(kv.second.abft_buf);
     (void)hipHostFree(kv.second.status_host);
     (void)hipSetDevice(cur);
   }

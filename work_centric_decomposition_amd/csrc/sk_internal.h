@@ -338,10 +338,13 @@ struct KernelArgs {
   const sk_fault *faults;
   sk_abft_report *report;
   float abft_tau;
-  // ABFT encodings (abft_encode_kernel): per 128-row tile of A and 128-column
-  // tile of B and per k-iteration of 32, the 32 sums then the 32 absolute sums
+  // ABFT encodings (abft_prep_kernel): per 128-row tile of A and 128-column
+  // tile of B and per k-iteration of 32, the 32 sums
   const float *enc_a, *enc_b;
   int32_t enc_kb;      // k-iterations per tile in the encoding arrays
+  // detection-threshold inputs: per row of A and column of B the sum of |x|
+  // over all of k; per tile the largest column (row) sum of |x| over k
+  const float *norm_a, *norm_b, *emax_a, *emax_b;
 };
 
 // Kernel launchers (sk_kernels.hip).  Return a hipError_t value.
@@ -354,13 +357,34 @@ int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t l
 int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_t rows,
                 int64_t k, void *dst, int64_t ldd, hipStream_t stream);
 int launch_zero_report(sk_abft_report *report, hipStream_t stream);
-// ABFT encodings of an fp32 operand of `rows` rows (m for A, n for B) and k
-// columns: for each 128-row tile and each k < 32*kb, the sum of the tile's
-// rows and of their absolute values (rows past `rows` left out, k past `k`
-// zero), written to out[(tile*kb + k/32)*64 + k%32] and [... + 32].
-// Element (r, l) is X[r*ld + l] when kmajor, else X[l*ld + r].
-int launch_abft_encode(const float *X, int64_t ld, bool kmajor, int64_t rows, int64_t k, int64_t kb,
-                       float *out, hipStream_t stream);
+// ABFT preparation of an fp32 GEMM, in one launch over both operands.  For
+// operand X of `rows` rows (m for A, n for B) and k columns, element (r, l)
+// at X[r*ld + l] when kmajor, else X[l*ld + r]:
+//   enc[(tile*kb + l/32)*32 + l%32]  the sum of the 128-row tile's rows at
+//                                    k = l < 32*kb (rows past `rows` left
+//                                    out, l >= k zero);
+//   norm[r]    sum over k of |X(r, k)|;
+//   emax[tile] max over k of the tile's sum of |X(r, k)| over its rows;
+// k is cut into chunks of 64 (chunks = ceil(32*kb / 64)) and the chunks
+// into `groups` groups of group_chunks, one workgroup per (tile, group);
+// scratch arrays rowabs (groups * rows) and tmax (tiles * groups).  The last
+// workgroup of a tile to finish reduces the tile's norms and emax (counters:
+// one per tile of A, then of B, zero before the call and left zero after
+// it).  The first workgroup zeroes the report (if not null).
+struct AbftPrepOperand {
+  const float *X;
+  int64_t ld;
+  int32_t kmajor;
+  int64_t rows, tiles;
+  float *enc, *rowabs, *tmax, *norm, *emax;
+};
+struct AbftPrepArgs {
+  AbftPrepOperand op[2];  // A, B
+  int64_t k, kb, chunks, group_chunks, groups;
+  uint32_t *counters;     // tiles of A + tiles of B
+  sk_abft_report *report;
+};
+int launch_abft_prep(const AbftPrepArgs &args, hipStream_t stream);
 // Occupancy query for the GEMM kernel of `dtype` (fp32: with or without ABFT).
 int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu);
 

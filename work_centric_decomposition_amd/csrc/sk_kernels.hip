@@ -265,6 +265,11 @@ struct HPolicy {
   static constexpr int A_BYTES = BM * ROW, B_BYTES = BN * ROW;
   static constexpr int STAGE = A_BYTES + B_BYTES;
   static constexpr int LDS_BYTES = NSTAGE * STAGE;
+  // LDS holds the A tiles of all stages, then the B tiles of all stages, so
+  // that every fragment read lies within 64 KiB (the reach of an LDS
+  // instruction's offset field) of one A base and one B base
+  static __device__ __forceinline__ constexpr int a_off(int stage) { return stage * A_BYTES; }
+  static __device__ __forceinline__ constexpr int b_off(int stage) { return NSTAGE * A_BYTES + stage * B_BYTES; }
   static constexpr int LOADS = A_BYTES / 1024 / (NT / 64);  // per operand per wave and stage
   static constexpr int ROWS_PER_LOAD = 1024 / ROW;
   // 16-byte chunk c of LDS row r is stored at chunk position c ^ swz(r):
@@ -300,10 +305,15 @@ template <class P>
 struct HLoader {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[P::LOADS], vb[P::LOADS];
-  int chunk[P::LOADS];  // 16-byte k-chunk each load fetches (same for A and B)
+  // 16-byte k-chunk load j fetches (same for A and B): rows of load j are
+  // 8 j further on, which with 128-byte rows changes the swizzle only with
+  // the parity of j, so two values hold every load's chunk
+  int chunk2[2];
+  __device__ __forceinline__ int chunk(int j) const { return chunk2[j & 1]; }
   int lds_a;            // LDS byte offset of this wave's first A load (stage 0)
 
   __device__ __forceinline__ void init(const KernelArgs &a, int m0, int n0) {
+    static_assert(P::ROW == 128 && P::LOADS % 2 == 0, "chunk of load j depends only on j & 1");
     constexpr int ES = 2;
     const int w = wave_id(), lane = threadIdx.x & 63;
     const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
@@ -316,7 +326,7 @@ struct HLoader {
     for (int j = 0; j < P::LOADS; ++j) {
       const int row = (w * P::LOADS + j) * P::ROWS_PER_LOAD + lane / CPR;
       const int c = (lane % CPR) ^ P::swz(row);
-      chunk[j] = c;
+      if (j < 2) chunk2[j] = c;
       va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
       vb[j] = row < a.n - n0 ? (uint32_t)(row * ldb_b + c * 16) : kOOB;
     }
@@ -331,8 +341,8 @@ struct HLoader {
     const int j = q >> 1;
     const int k0b = kit * P::BK * 2;
     const int left = live ? (a.k - kit * P::BK) * 2 : 0;
-    const bool ok = chunk[j] * 16 < left;
-    const int dst = stage * P::STAGE + lds_a + (q & 1) * P::A_BYTES + j * 1024;
+    const bool ok = chunk(j) * 16 < left;
+    const int dst = ((q & 1) ? P::b_off(stage) : P::a_off(stage)) + lds_a + j * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds((q & 1) ? rb : ra, (lds_vptr)(smem + dst), 16,
                                              ok ? ((q & 1) ? vb[j] : va[j]) : kOOB, k0b, 0, 0);
   }
@@ -340,21 +350,21 @@ struct HLoader {
   __device__ __forceinline__ void load(const KernelArgs &a, int stage, int kit) const {
     const int k0b = kit * P::BK * 2;
     const int left = (a.k - kit * P::BK) * 2;  // bytes of k from k0
-    const int base = stage * P::STAGE + lds_a;
+    const int abase = P::a_off(stage) + lds_a, bbase = P::b_off(stage) + lds_a;
     if (left >= P::BK * 2) {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + base + j * 1024), 16, va[j], k0b, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + base + P::A_BYTES + j * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16, va[j], k0b, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
                                                  vb[j], k0b, 0, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
-        const bool ok = chunk[j] * 16 < left;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + base + j * 1024), 16,
+        const bool ok = chunk(j) * 16 < left;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16,
                                                  ok ? va[j] : kOOB, k0b, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + base + P::A_BYTES + j * 1024), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
                                                  ok ? vb[j] : kOOB, k0b, 0, 0);
       }
     }
@@ -395,7 +405,7 @@ template <class P>
 __device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, int q, HFrag<P> &F) {
   using V8 = typename Elem<P::ET>::V8;
   const int lane = threadIdx.x & 63;
-  const int As = stage * P::STAGE, Bs = As + P::A_BYTES;
+  const int As = P::a_off(stage), Bs = P::b_off(stage);
   const int c = sub * 2 + (lane >> 5);
   if (q < P::NB) {
     const int row = wn * P::WTN + q * 32 + (lane & 31);
@@ -722,37 +732,41 @@ __device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (
 // ---------------------------------------------------------------- ABFT
 //
 // Threadblock-level ABFT of the fault-tolerant GEMM page, per work segment:
-//   encodings   (e^T A)_k = sum_i A_ik,  (B e)_k = sum_j B_kj   (and |.| sums)
+//   encodings   (e^T A)_k = sum_i A_ik,  (B e)_k = sum_j B_kj
 //               over the tile's rows of A and columns of B;
 //   checksums   rc_i += sum_k A_ik (B e)_k     -- row checksum of C = A B
-//               cc_j += sum_k (e^T A)_k B_kj   -- column checksum
-//               ra_i, ca_j: the same with |A|, |B| (detection threshold).
+//               cc_j += sum_k (e^T A)_k B_kj   -- column checksum.
 // The encodings depend only on the operands, and every workgroup of a tile
 // row (column) needs the same ones, so they are formed once per call by
-// abft_encode_kernel, read from memory into LDS with the tiles two
-// iterations ahead, and only the checksum updates run in the MAC loop, from
-// the staged tiles.  At the end of the segment (before its partial store, or
-// before the owner adds its peers' partials) the row and column sums of the
-// accumulators are compared with the checksums: a row mismatches when
-// |sum - rc_i| exceeds tau * 2^-24 * sqrt(k_seg) * ra_i or is not finite
-// (likewise columns), where k_seg is the number of k values the segment
-// accumulated: the rounding error of an fp32 dot product of length k grows
-// like sqrt(k) u sum|a||b|.  One mismatching row and one mismatching column
-// locate the fault; the element is recomputed from its row checksum,
-// c_ij = rc_i - sum_{l != j} c_il.  Any other pattern is reported as
-// uncorrectable.  All reductions run in a fixed order.
+// abft_prep_kernel, read from memory into LDS with the tiles two iterations
+// ahead, and only the checksum updates run in the MAC loop, from the MFMA
+// fragments already in registers.  At the end of the segment (before its
+// partial store, or before the owner adds its peers' partials) the row and
+// column sums of the accumulators are compared with the checksums: a row
+// mismatches when |sum - rc_i| exceeds tau * 2^-24 * sqrt(k_seg) * ra_i or
+// is not finite (likewise columns), where k_seg is the number of k values
+// the segment accumulated: the rounding error of an fp32 dot product of
+// length k grows like sqrt(k) u sum|a||b|.  ra_i stands for
+// sum_k |a_ik| (|B| e)_k; the kernel uses its bound ||a_i||_1 max_k (|B| e)_k
+// (row norm and tile maximum over all of k, formed once per call with the
+// encodings), and likewise max_k (e^T|A|)_k ||b_j||_1 for columns, so the
+// MAC loop carries no absolute checksums.  One mismatching row and one
+// mismatching column locate the fault; the element is recomputed from its
+// row checksum, c_ij = rc_i - sum_{l != j} c_il.  Any other pattern is
+// reported as uncorrectable.  All reductions run in a fixed order.
 struct AbftLds {
-  alignas(16) float e[2][4][SCfg::BK];  // per stage: e^T A, e^T|A|, B e, |B| e
-  float part[4][4][128];      // rc, ra, cc, ca: per wave (a quarter of the k range)
+  alignas(16) float e[2][2][SCfg::BK];  // per stage: e^T A, B e
+  float part[2][4][128];      // rc, cc: per lane group l >> 4 (a quarter of k)
   float sums[2][2][128];      // row sums per wave column, column sums per wave row
   float others[SCfg::NT / 64];
   int bad[4];                 // mismatching rows, one such row, columns, one such column
 };
 
-// Checksums of one thread: rows (columns) 4 (t % 32) .. + 3 of the tile over
-// its k values.
+// Checksums of one lane (rows wm*64 + mb*16 + (l & 15) in a row wave,
+// columns wn*64 + nb*16 + (l & 15) in a column wave) over the k values
+// 4 (l >> 4) .. + 3 modulo 16.
 struct AbftPart {
-  float rc[4], ra[4], cc[4], ca[4];
+  float c[4];
 };
 
 // The ABFT working set in LDS (allocated only in kernels that use it).
@@ -761,64 +775,50 @@ __device__ __forceinline__ AbftLds &abft_lds() {
   return L;
 }
 
-// The 4 x 4 block of a staged operand tile at rows (m or n) 4 g .. 4 g + 3
-// and k = 4 kq .. 4 kq + 3, as v[row][k]: one 128-bit read per row in the
-// k-major format, one per k in the mn-major one.
-template <bool KMAJOR>
-__device__ __forceinline__ void s_blk4(int base_off, int g, int kq, float (&v)[4][4]) {
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    if (KMAJOR) {
-      const int mn = 4 * g + j;
-      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + mn * 128 + ((kq ^ ((mn >> 1) & 7)) << 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[j][e] = x[e];
-    } else {
-      const int k = 4 * kq + j;
-      const f4_t x = *reinterpret_cast<const f4_t *>(smem + base_off + k * 512 + ((g ^ (4 * (kq & 3))) << 4));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e][j] = x[e];
-    }
-  }
+// Checksum update from the MFMA fragments already in registers.  Lane l
+// holds A at rows wm*64 + mb*16 + (l & 15) and B at columns
+// wn*64 + nb*16 + (l & 15), at k = 16 g + 4 (l >> 4) + q of k-group g, so
+//   rows:     c[mb] += sum_q A(row, k) (B e)_k
+//   columns:  c[nb] += sum_q (e^T A)_k B(k, col).
+// Both waves of a wave row hold the same rows of A (and both of a wave
+// column the same columns of B): waves (0, 1) and (1, 0) form the row
+// checksums of their wave rows, waves (0, 0) and (1, 1) the column checksums
+// of their wave columns.  Entries past the end of k are zero in the staged
+// tiles and in the encodings; rows and columns past the matrix give
+// checksums that are never verified.
+__device__ __forceinline__ bool abft_rows_wave(int wm, int wn) { return wm != wn; }
+
+// The encodings that meet a lane's fragments of k-group g (B e for a row
+// wave, e^T A for a column wave), at k = 16 g + 4 (l >> 4) + q, q = 0..3.
+__device__ __forceinline__ f4_t abft_read_e(AbftLds &L, int stage, int g, bool rows) {
+  const int h = (threadIdx.x & 63) >> 4;
+  return *reinterpret_cast<const f4_t *>(&L.e[stage][rows ? 1 : 0][16 * g + 4 * h]);
 }
 
-// Checksum update of one staged k-iteration: thread t covers rows and
-// columns 4 (t % 32) .. + 3 of the tile at k = 4 (t / 32) .. + 3 (entries
-// past the end of k are zero in the staged tiles and in the encodings; rows
-// and columns past the matrix give checksums that are never verified).
-template <bool AK, bool BKM>
-__device__ __forceinline__ void abft_update(AbftLds &L, int stage, AbftPart &pt) {
-  const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
-  const int t = threadIdx.x, g = t & 31, kq = t >> 5;
-  {  // rows (the A side), then columns: one side's values live at a time
-    const f4_t eb = *reinterpret_cast<const f4_t *>(&L.e[stage][2][4 * kq]);
-    const f4_t eba = *reinterpret_cast<const f4_t *>(&L.e[stage][3][4 * kq]);
-    float va[4][4];
-    s_blk4<AK>(As, g, kq, va);
+__device__ __forceinline__ void abft_fma(const f4_t (&x)[4], f4_t e, AbftPart &pt) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
+  for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pt.rc[j] += va[j][e] * eb[e];
-        pt.ra[j] += fabsf(va[j][e]) * eba[e];
-      }
-    }
+    for (int j = 0; j < 4; ++j) pt.c[j] += x[j][q] * e[q];
+}
+
+// One MFMA group and, in the ABFT kernels, the wave's checksum FMAs of that
+// k-group, issued before the group (measured: the FMAs cost least there; set
+// among the MFMAs they slow the group down).  The empty asm takes the
+// checksums as operands, so that the compiler cannot sink the FMAs below the
+// group.
+template <bool ABFT>
+__device__ __forceinline__ void s_group(const f4_t (&av)[SCfg::MB], const f4_t (&bv)[SCfg::NB],
+                                        f4_t (&acc)[SCfg::NACC], bool rows, f4_t e, AbftPart &pt) {
+  if constexpr (ABFT) {
+    if (rows)  // uniform over the wave
+      abft_fma(av, e, pt);
+    else
+      abft_fma(bv, e, pt);
+    asm volatile("" : "+v"(pt.c[0]), "+v"(pt.c[1]), "+v"(pt.c[2]), "+v"(pt.c[3]));
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_barrier(0);
-  {
-    const f4_t ea = *reinterpret_cast<const f4_t *>(&L.e[stage][0][4 * kq]);
-    const f4_t eaa = *reinterpret_cast<const f4_t *>(&L.e[stage][1][4 * kq]);
-    float vb[4][4];
-    s_blk4<BKM>(Bs, g, kq, vb);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        pt.cc[j] += ea[e] * vb[j][e];
-        pt.ca[j] += eaa[e] * fabsf(vb[j][e]);
-      }
-    }
-  }
+  s_mfmas(av, bv, acc);
 }
 
 __device__ __forceinline__ void abft_record(const KernelArgs &a, int64_t row, int64_t col, float delta,
@@ -839,17 +839,13 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
   const int wm = w / 2, wn = w % 2;
   const int m_valid = a.m - m0, n_valid = a.n - n0;
   {
-    // the two k-quarters of a wave (lanes l and l ^ 32) are added, then each
-    // wave stores its rows' and columns' checksums
+    // one partial per lane group: row checksums from the row waves, column
+    // checksums from the column waves
+    const int h = lane >> 4, li = lane & 15;
+    const bool rows = abft_rows_wave(wm, wn);
+    const int x0 = rows ? wm * SCfg::WTM + li : wn * SCfg::WTN + li;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float rc = pt.rc[j] + __shfl_xor(pt.rc[j], 32), ra = pt.ra[j] + __shfl_xor(pt.ra[j], 32);
-      const float cc = pt.cc[j] + __shfl_xor(pt.cc[j], 32), ca = pt.ca[j] + __shfl_xor(pt.ca[j], 32);
-      if (lane < 32) {
-        const int x = 4 * lane + j;
-        L.part[0][w][x] = rc; L.part[1][w][x] = ra; L.part[2][w][x] = cc; L.part[3][w][x] = ca;
-      }
-    }
+    for (int j = 0; j < 4; ++j) L.part[rows ? 0 : 1][h][x0 + j * 16] = pt.c[j];
   }
   if (t < 4) L.bad[t] = t == 0 || t == 2 ? 0 : -1;
   // injected faults (testing): applied to the accumulator before verification
@@ -913,17 +909,28 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
     const int x = t & 127;
     const bool is_row = t < 128;
     const bool valid = is_row ? x < m_valid : x < n_valid;
+    float ratio = 0.f;  // margin of the checks that pass: |residual| / tau
     if (valid) {
-      const int q = is_row ? 0 : 2;
+      const int q = is_row ? 0 : 1;
       const float ck = ((L.part[q][0][x] + L.part[q][1][x]) + L.part[q][2][x]) + L.part[q][3][x];
-      const float ab = ((L.part[q + 1][0][x] + L.part[q + 1][1][x]) + L.part[q + 1][2][x]) + L.part[q + 1][3][x];
+      // bound of sum_k |a_ik| (|B| e)_k (row) or sum_k (e^T|A|)_k |b_kj| (column)
+      const float ab = is_row ? a.norm_a[m0 + x] * a.emax_b[n0 / SCfg::BN]
+                              : a.emax_a[m0 / SCfg::BM] * a.norm_b[n0 + x];
       const float sm = L.sums[is_row ? 0 : 1][0][x] + L.sums[is_row ? 0 : 1][1][x];
       const float r = sm - ck;
-      if (!(fabsf(r) <= a.abft_tau * u * ab)) {
-        atomicAdd(&L.bad[q], 1);
-        L.bad[q + 1] = x;
+      const float tau = a.abft_tau * u * ab;
+      if (!(fabsf(r) <= tau)) {
+        atomicAdd(&L.bad[2 * q], 1);
+        L.bad[2 * q + 1] = x;
+      } else if (tau > 0.f) {
+        ratio = fabsf(r) / tau;
       }
     }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) ratio = fmaxf(ratio, __shfl_xor(ratio, o));
+    // non-negative floats order like their bit patterns
+    if ((t & 63) == 0 && ratio > 0.f) atomicMax(reinterpret_cast<int *>(&a.report->max_ratio), __float_as_int(ratio));
+    if (t == 0) atomicAdd(&a.report->checked, min(m_valid, SCfg::BM) + min(n_valid, SCfg::BN));
   }
   __syncthreads();
   const int nbr = L.bad[0], nbc = L.bad[2];
@@ -988,10 +995,10 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
 
 // MacLoop of the fp32 kernel, same two-stage pipeline as the HGEMM one:
 // the fragments of k-group 1 are read while the MFMAs of group 0 run; then
-// (ABFT: the checksum update of this stage;) wait for this wave's loads of
-// the next stage, barrier, issue the loads of iteration i+2 into this
-// stage's buffer and read group 0 of the next stage while the MFMAs of
-// group 1 run.
+// wait for this wave's loads of the next stage, barrier, issue the loads of
+// iteration i+2 into this stage's buffer and read group 0 of the next stage
+// while the MFMAs of group 1 run.  ABFT: each group's checksum FMAs run
+// just before its MFMAs, from the same fragments.
 template <bool AK, bool BKM, bool ABFT>
 __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
                                           f4_t (&acc)[SCfg::NACC]) {
@@ -1002,21 +1009,21 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   const int n = le - lb;
   if (n <= 0) return;
   AbftPart pt{};
-  // ABFT: threads 0-127 carry the encodings of a k-iteration (64 floats of
-  // the tile row's A encodings, then 64 of the tile column's B encodings)
-  // from memory to the stage's LDS slot: loaded with the stage's tiles,
-  // stored after the next wait for them, read after the barrier after that.
+  // ABFT: wave 0 carries the encodings of a k-iteration (lanes 0-31: the
+  // tile row's e^T A, lanes 32-63: the tile column's B e) from memory to the
+  // stage's LDS slot: loaded with the stage's tiles, stored after the next
+  // wait for them, read after the barrier after that.
   const int wv = wave_id();
-  const bool enc_lane = ABFT && wv < 2;  // waves 0 (A) and 1 (B)
-  const float *esrc = nullptr;           // wave-uniform base of the wave's encodings
+  const bool enc_lane = ABFT && wv == 0;
+  const float *esrc = nullptr;  // this lane's encodings
   float ev = 0.f, ev1 = 0.f;
   if constexpr (ABFT) {
-    esrc = wv == 0 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 64
-                   : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 64;
+    const int lane = threadIdx.x & 63;
+    esrc = (lane < 32 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 32
+                      : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 32) + (lane & 31);
     if (enc_lane) {
-      const int lane = threadIdx.x & 63;
-      ev = esrc[(int64_t)lb * 64 + lane];
-      if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 64 + lane];
+      ev = esrc[(int64_t)lb * 32];
+      if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 32];
     }
   }
   SLoader<AK> la;
@@ -1045,12 +1052,20 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   f4_t a0[SCfg::MB], b0[SCfg::NB], a1[SCfg::MB], b1[SCfg::NB];
   s_frags<AK, BKM>(0, 0, wm, wn, a0, b0);
   int buf = 0;
+  const bool rows = abft_rows_wave(wm, wn);
+  f4_t e0{}, e1{};  // ABFT: the wave's encodings for the two k-groups of this stage
   for (int i = 0; i < n; ++i) {
+    // ABFT: both groups' encodings are read before the barrier (wave 0
+    // stores those of iteration i+2 into this slot after it), and before
+    // the fragments, so that the first FMAs wait for them alone
+    if constexpr (ABFT) {
+      e0 = abft_read_e(abft_lds(), buf, 0, rows);
+      e1 = abft_read_e(abft_lds(), buf, 1, rows);
+    }
     s_frags<AK, BKM>(buf, 1, wm, wn, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    s_mfmas(a0, b0, acc);
+    s_group<ABFT>(a0, b0, acc, rows, e0, pt);
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ABFT) abft_update<AK, BKM>(abft_lds(), buf, pt);
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (ABFT) {
       // the encodings of iteration i+1, loaded at iteration i-1 (the
@@ -1061,12 +1076,12 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     if (i + 2 < n) {
       load(buf, lb + i + 2);
       if constexpr (ABFT) {
-        if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 64 + (threadIdx.x & 63)];
+        if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 32];
       }
     }
     if (i + 1 < n) s_frags<AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    s_mfmas(a1, b1, acc);
+    s_group<ABFT>(a1, b1, acc, rows, e1, pt);
     __builtin_amdgcn_sched_barrier(0);
     buf ^= 1;
   }
@@ -1252,87 +1267,173 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
   }
 }
 
-// ABFT encodings of one fp32 operand (rows x k): workgroup (tile, chunk)
-// stages the tile's 128 rows at 64 values of k in LDS (a wave reads 64
-// consecutive elements of the operand in either storage order), then four
-// threads per k sum 32 rows each in row order and the four sums are added
-// in order; likewise for the absolute values.
-__global__ __launch_bounds__(256) void abft_encode_kernel(const float *X, int64_t ld, int kmajor, int64_t rows,
-                                                         int64_t k, int64_t kb, float *out) {
-  __shared__ float T[64][129];
-  __shared__ float P[2][4][64];
+// ABFT preparation (both operands in one launch).  Workgroup (operand,
+// tile, group) walks the group's chunks of 64 values of k in order; the
+// next chunk's loads are in flight while the current one is reduced.  Per
+// chunk the tile's 128 rows are staged in LDS (a wave reads 64 consecutive
+// elements of the operand in either storage order), four threads per k sum
+// 32 rows each in row order and the four sums are added in order (the
+// encoding e^T X of the tile per k, rows past the matrix left out, k past
+// the end zero), and likewise for the absolute values.  Over the group, each
+// row's sum of absolute values (chunks in order, k in order) goes to
+// rowabs[group][row] and the largest column sum of absolute values to
+// tmax[tile][group].  The last workgroup of a tile to finish (a counter per
+// tile) adds each row's group sums in order into norm[row] and takes the
+// largest tmax of the tile into emax[tile].
+template <bool KMAJOR>
+__device__ __forceinline__ void prep_load(const float *X, int64_t ld, int64_t r0, int64_t rv, int64_t k0, int64_t k,
+                                          f4_t (&x)[8]) {
   const int t = threadIdx.x;
-  const int64_t chunks = (kb * 32 + 63) / 64;
-  const int64_t tile = blockIdx.x / chunks, k0 = (blockIdx.x % chunks) * 64;
-  const int64_t r0 = tile * 128;
-  const int64_t rv = rows - r0 < 128 ? rows - r0 : 128;  // valid rows of the tile
   // 16-byte loads where all four elements are inside the operand (rows of
   // a k-major operand and k-lines of an mn-major one start 16-byte aligned:
   // the leading dimension is a multiple of four and the base is aligned),
   // single elements at the edges
-  if (kmajor) {
-    const int kc = t & 15, rr = t >> 4;  // k = k0 + 4 kc .. + 3, rows rr + 16 q
-    const int64_t kk0 = k0 + 4 * kc;
-#pragma unroll 4
-    for (int q = 0; q < 8; ++q) {
-      const int r = rr + 16 * q;
-      f4_t x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    x[q] = f4_t{0.f, 0.f, 0.f, 0.f};
+    if (KMAJOR) {
+      const int kc = t & 15, r = (t >> 4) + 16 * q;  // k = k0 + 4 kc .. + 3
+      const int64_t kk0 = k0 + 4 * kc;
       if (r < rv) {
-        const float *p = X + (r0 + r) * ld + kk0;
+        const float *src = X + (r0 + r) * ld + kk0;
         if (kk0 + 3 < k) {
-          x = *reinterpret_cast<const f4_t *>(p);
+          x[q] = *reinterpret_cast<const f4_t *>(src);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (kk0 + e < k) x[e] = p[e];
+            if (kk0 + e < k) x[q][e] = src[e];
         }
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) T[4 * kc + e][r] = x[e];
-    }
-  } else {
-    const int rc = t & 31, kr = t >> 5;  // rows 4 rc .. + 3, k = k0 + kr + 8 q
-#pragma unroll 4
-    for (int q = 0; q < 8; ++q) {
-      const int kk = kr + 8 * q;
-      const int r = 4 * rc;
-      f4_t x = {0.f, 0.f, 0.f, 0.f};
+    } else {
+      const int r = 4 * (t & 31), kk = (t >> 5) + 8 * q;  // rows r .. r + 3
       if (k0 + kk < k) {
-        const float *p = X + (k0 + kk) * ld + r0 + r;
+        const float *src = X + (k0 + kk) * ld + r0 + r;
         if (r + 3 < rv) {
-          x = *reinterpret_cast<const f4_t *>(p);
+          x[q] = *reinterpret_cast<const f4_t *>(src);
         } else {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
-            if (r + e < rv) x[e] = p[e];
+            if (r + e < rv) x[q][e] = src[e];
         }
       }
+    }
+  }
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ void prep_stage(float (&T)[64][129], const f4_t (&x)[8]) {
+  const int t = threadIdx.x;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) T[kk][r + e] = x[e];
+  for (int q = 0; q < 8; ++q) {
+    if (KMAJOR) {
+      const int kc = t & 15, r = (t >> 4) + 16 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[4 * kc + e][r] = x[q][e];
+    } else {
+      const int r = 4 * (t & 31), kk = (t >> 5) + 8 * q;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) T[kk][r + e] = x[q][e];
     }
   }
-  __syncthreads();
-  {
-    const int kk = t & 63, g = t >> 6;
-    float sm = 0.f, sa = 0.f;
+}
+
+template <bool KMAJOR>
+__device__ __forceinline__ void prep_walk(const AbftPrepArgs &p, const AbftPrepOperand &o, int64_t tile,
+                                          int64_t c_begin, int64_t c_end, float (&T)[64][129],
+                                          float (&P)[2][4][64], float &rowsum, float &tmx) {
+  const int t = threadIdx.x;
+  const int64_t r0 = tile * 128, rows = o.rows, k = p.k, kb = p.kb;
+  const int64_t rv = rows - r0 < 128 ? rows - r0 : 128;  // valid rows of the tile
+  f4_t x[8];
+  prep_load<KMAJOR>(o.X, o.ld, r0, rv, c_begin * 64, k, x);
+  for (int64_t c = c_begin; c < c_end; ++c) {
+    __syncthreads();  // the previous chunk's readers of T and P are done
+    prep_stage<KMAJOR>(T, x);
+    if (c + 1 < c_end) prep_load<KMAJOR>(o.X, o.ld, r0, rv, (c + 1) * 64, k, x);
+    __syncthreads();
+    {
+      const int kk = t & 63, g = t >> 6;
+      float sm = 0.f, sa = 0.f;
 #pragma unroll 8
-    for (int r = 32 * g; r < 32 * g + 32; ++r) {
-      const float x = T[kk][r];
-      sm += x;
-      sa += fabsf(x);
+      for (int r = 32 * g; r < 32 * g + 32; ++r) {
+        const float v = T[kk][r];
+        sm += v;
+        sa += fabsf(v);
+      }
+      P[0][g][kk] = sm;
+      P[1][g][kk] = sa;
     }
-    P[0][g][kk] = sm;
-    P[1][g][kk] = sa;
+    if (t < 128) {
+#pragma unroll 8
+      for (int kk = 0; kk < 64; ++kk) rowsum += fabsf(T[kk][t]);
+    }
+    __syncthreads();
+    if (t < 64) {
+      const int64_t l = c * 64 + t;
+      const float sm = ((P[0][0][t] + P[0][1][t]) + P[0][2][t]) + P[0][3][t];
+      float sa = ((P[1][0][t] + P[1][1][t]) + P[1][2][t]) + P[1][3][t];
+      if (l < kb * 32) o.enc[(tile * kb + l / 32) * 32 + (l % 32)] = sm;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) sa = fmaxf(sa, __shfl_xor(sa, off));
+      tmx = fmaxf(tmx, sa);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256, 4) void abft_prep_kernel(AbftPrepArgs p) {
+  __shared__ float T[64][129];
+  __shared__ float P[2][4][64];
+  __shared__ int last;
+  const int t = threadIdx.x;
+  const int64_t groups = p.groups, gsize = p.group_chunks;
+  const int64_t blocks_a = p.op[0].tiles * groups;
+  const int which = blockIdx.x < blocks_a ? 0 : 1;
+  const AbftPrepOperand &o = p.op[which];
+  const int64_t b = blockIdx.x - (which ? blocks_a : 0);
+  const int64_t tile = b / groups, grp = b % groups;
+  const int64_t c_begin = grp * gsize, c_end = c_begin + gsize < p.chunks ? c_begin + gsize : p.chunks;
+  const int64_t r0 = tile * 128, rows = o.rows;
+  const int64_t rv = rows - r0 < 128 ? rows - r0 : 128;
+  if (blockIdx.x == 0 && p.report != nullptr) {
+    int32_t *w = reinterpret_cast<int32_t *>(p.report);
+    for (int i = t; i < (int)(sizeof(sk_abft_report) / 4); i += 256) w[i] = 0;
+  }
+  float rowsum = 0.f, tmx = 0.f;
+  if (o.kmajor)
+    prep_walk<true>(p, o, tile, c_begin, c_end, T, P, rowsum, tmx);
+  else
+    prep_walk<false>(p, o, tile, c_begin, c_end, T, P, rowsum, tmx);
+  // The last workgroup of the tile reads what the others wrote to rowabs
+  // and tmax.  As in the Stream-K fixup, no release or acquire (each would
+  // write back or invalidate a whole L2): those arrays are written and read
+  // with agent-coherent relaxed atomics (sc1 accesses), and the count
+  // follows this workgroup's completed stores (wait, barrier).
+  if (t < rv) __hip_atomic_store(&o.rowabs[grp * rows + r0 + t], rowsum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (t == 0) __hip_atomic_store(&o.tmax[tile * groups + grp], tmx, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_s_waitcnt(vmcnt_le(0));
+  __syncthreads();
+  uint32_t *ctr = p.counters + (which ? p.op[0].tiles : 0) + tile;
+  if (t == 0) {
+    const uint32_t done = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = done + 1 == (uint32_t)groups;
   }
   __syncthreads();
+  if (!last) return;
+  if (t < rv) {
+    float s = 0.f;
+    for (int64_t g = 0; g < groups; ++g)
+      s += __hip_atomic_load(&o.rowabs[g * rows + r0 + t], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    o.norm[r0 + t] = s;
+  }
   if (t < 64) {
-    const int64_t l = k0 + t;
-    if (l < kb * 32) {
-      const float sm = ((P[0][0][t] + P[0][1][t]) + P[0][2][t]) + P[0][3][t];
-      const float sa = ((P[1][0][t] + P[1][1][t]) + P[1][2][t]) + P[1][3][t];
-      float *o = out + (tile * kb + l / 32) * 64 + (l % 32);
-      o[0] = sm;
-      o[32] = sa;
+    float mx = 0.f;
+    for (int64_t g = t; g < groups; g += 64)
+      mx = fmaxf(mx, __hip_atomic_load(&o.tmax[tile * groups + g], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    if (t == 0) {
+      o.emax[tile] = mx;
+      __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);  // ready for the next call
     }
   }
 }
@@ -1424,12 +1525,12 @@ int launch_zero_report(sk_abft_report *report, hipStream_t stream) {
   return (int)hipGetLastError();
 }
 
-int launch_abft_encode(const float *X, int64_t ld, bool kmajor, int64_t rows, int64_t k, int64_t kb,
-                       float *out, hipStream_t stream) {
-  const int64_t blocks = (rows + 127) / 128 * ((kb * 32 + 63) / 64);
+int launch_abft_prep(const AbftPrepArgs &args, hipStream_t stream) {
+  const int64_t blocks = (args.op[0].tiles + args.op[1].tiles) * args.groups;
+  if (args.group_chunks <= 0 || args.groups != (args.chunks + args.group_chunks - 1) / args.group_chunks)
+    return (int)hipErrorInvalidValue;
   if (blocks <= 0 || blocks > INT32_MAX) return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(dev::abft_encode_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, X, ld,
-                     kmajor ? 1 : 0, rows, k, kb, out);
+  hipLaunchKernelGGL(dev::abft_prep_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, args);
   return (int)hipGetLastError();
 }
 
