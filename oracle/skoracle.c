@@ -412,20 +412,22 @@ static int64_t cta_segments(const or_decomp *d, int64_t x, or_seg *out, int64_t 
     else PUSH(tile, lb, le, 1, le == d->ipt, d->s == 1 ? -1 : tile * d->s + d->s - 1);
     return c;
   }
-  /* Stream-K region (Algorithm 5) */
+  /* Stream-K region.  CTA x holds the contiguous iteration range
+   * [first(x), first(x+1)) of the even split of the region's iterations
+   * (Stream-K page, Algorithm 5).  Its segments are the intersections of
+   * that range with the tiles it meets, in tile order: a segment holding a
+   * tile's first iteration has started the tile, one holding its last
+   * iteration has ended it, and a tile started but not ended here is
+   * finished by the CTA whose range holds the tile's last iteration. */
   if (d->sk_tiles > 0 && x < d->sk_g) {
-    int64_t iter = cta_first_iter(d, x);
-    int64_t iter_end = cta_first_iter(d, x + 1);
-    while (iter < iter_end) {
-      int64_t tile = iter / d->ipt;
-      int64_t tile_iter = tile * d->ipt, tile_iter_end = tile_iter + d->ipt;
-      int64_t lb = iter - tile_iter;
-      int64_t le = (iter_end < tile_iter_end ? iter_end : tile_iter_end) - tile_iter;
-      int64_t started = iter == tile_iter, ended = iter_end >= tile_iter_end;
-      int64_t last_peer = -1;
-      if (started && !ended) last_peer = cta_of_iter(d, tile_iter_end - 1);
-      PUSH(tile, lb, le, started, ended, last_peer);
-      iter = tile_iter_end;
+    const int64_t r_lo = cta_first_iter(d, x), r_hi = cta_first_iter(d, x + 1);
+    if (r_lo < r_hi) {
+      for (int64_t tile = r_lo / d->ipt; tile <= (r_hi - 1) / d->ipt; ++tile) {
+        const int64_t t_lo = tile * d->ipt, t_hi = t_lo + d->ipt;
+        const int64_t lo = r_lo > t_lo ? r_lo : t_lo, hi = r_hi < t_hi ? r_hi : t_hi;
+        const int64_t started = lo == t_lo, ended = hi == t_hi;
+        PUSH(tile, lo - t_lo, hi - t_lo, started, ended, started && !ended ? cta_of_iter(d, t_hi - 1) : -1);
+      }
     }
   }
   /* data-parallel region */
@@ -620,9 +622,11 @@ int or_sk_execute(int64_t m, int64_t n, int64_t k, double alpha, const void *A, 
  * Verify: row residual dr_i = sum_j C_ij - rc_i, column residual dc_j likewise;
  * a row/column mismatches when |residual| > tau or the residual is not finite.
  * Locate: the intersection of the single mismatching row and column.
- * Correct: C_ij <- rc_i - sum_{l != j} C_il (recomputed from the row checksum,
- * reading of "the correction value is determined by the offset in the
- * checksums", stable when the fault made C_ij huge, Inf or NaN).
+ * Correct: C_ij <- rc_i - sum_{l != j} C_il (recomputed from the row checksum:
+ * the page derives the size of the fix from the checksums' discrepancy,
+ * "Anatomy of High-Performance GEMM with Online Fault Tolerance on GPUs",
+ * Fig. 3; recomputing instead of subtracting the discrepancy stays correct
+ * when the fault made C_ij huge, Inf or NaN).
  * Returns 0 clean, 1 corrected (fills *fi, *fj, *fdelta = faulty - corrected),
  * 2 mismatch that cannot be located to one element, -1 bad arguments.
  */
