@@ -245,12 +245,12 @@ def skinny_shapes(S, count=8, min_tmin_us=20.0):
     return out
 
 
-def skinny_leg(torch, sk, S, reps=7):
+def skinny_leg(torch, sk, S, min_ms=20.0):
     """Skinny fp16 GEMMs (A row-major, B column-major, alpha=1, beta=0) under
-    AUTO and under data-parallel on the 256x256 tile, in that order per
-    shape, one warm-up and `reps` launches each (queued behind a spin kernel;
-    median).  Bytes = 2(mk + kn + mn), read and written once each."""
-    spin = _spin_cycles(torch, 300e-6)
+    AUTO, on the narrow-m tile (Stream-K, XCD-aware split) and data-parallel
+    on the 256x256 tile, each timed as R launches back to back between one
+    event pair (at least `min_ms` per measurement, host enqueue hidden behind
+    a spin kernel).  Bytes = 2(mk + kn + mn), read and written once each."""
     out = []
     g = torch.Generator(device="cuda")
     g.manual_seed(S.SEED_SWEEP)
@@ -264,12 +264,13 @@ def skinny_leg(torch, sk, S, reps=7):
         tmin = max(fl / (PEAK_TFLOPS["f16"] * 1e6), by / (PEAK_HBM_GBS * 1e3))
         row = {"shape": [m, n, k], "bytes": int(by), "tmin_us": round(tmin, 2)}
         for name, opts in (("auto", sk.make_options()),
+                           ("narrow", sk.make_options(tile=sk.TILE_NARROW)),
                            ("dp", sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE))):
-            us = _gpu_time_us(torch, sk, d, opts, spin, reps)
+            us, R, _ = back_to_back_us(torch, lambda: sk.gemm_ex(d, opts), min_ms=min_ms)
             p = sk.plan_query(d, opts)
             row[name] = {"us": round(us, 2), "GB_s": round(by / us / 1e3, 1), "tflops": round(fl / us / 1e6, 1),
-                         "util": round(tmin / us, 4), "tile": int(p.tile_m), "grid": int(p.grid),
-                         "schedule": int(p.schedule)}
+                         "util": round(tmin / us, 4), "tile": [int(p.tile_m), int(p.tile_n)], "grid": int(p.grid),
+                         "schedule": int(p.schedule), "launches": R}
         out.append(row)
         del A, B, C
     return out
@@ -823,7 +824,8 @@ def main():
         print(json.dumps(abft_overhead(torch, sk, S, steps=args.steps)), flush=True)
         return
     if args.skinny:
-        for r in skinny_leg(torch, sk, S, reps=args.steps):
+        # (--steps below 5: five launches per leg, for counter runs)
+        for r in skinny_leg(torch, sk, S, min_ms=20.0 if args.steps >= 5 else 0.0):
             print(json.dumps(r), flush=True)
         return
     if args.compare_schedules:

@@ -178,8 +178,12 @@ typedef struct {
  * workgroup per CU.  SMALL: 128 x 128 x 64 tiles, two 256-thread workgroups
  * per CU, for GEMMs with few large tiles (the page's observation that a
  * large tile loses on small, bandwidth-bound shapes, evaluation section).
- * AUTO picks the one the runtime model predicts faster. */
-typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2 } sk_tile;
+ * NARROW: for m <= 256 (SK_ERR_UNSUPPORTED above), BM x 256 x 64 tiles with
+ * BM = 64, 128, 192 or 256, the smallest that holds m, so that B is read
+ * once; B streams into registers three iterations ahead (memory-bound
+ * shapes with long k, the page's evaluation section).  AUTO picks among
+ * them. */
+typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2, SK_TILE_NARROW = 3 } sk_tile;
 
 /* Options for sk_gemm_ex.  Zero-initialised options mean: AUTO schedule, no
  * forced grid, ABFT off, default model constants, AUTO tile instance. */

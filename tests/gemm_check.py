@@ -75,9 +75,12 @@ class Case:
         self.dC.copy_(to_dev(self.Cin if self.Cin.size else np.zeros(1, self.Cin.dtype),
                              self.dtype))
 
+    def desc(self, alpha=1.0, beta=0.0):
+        return sk.make_desc(self.m, self.n, self.k, alpha, self.dA, self.lda, self.dB, self.ldb, beta,
+                            self.dC, self.ldc, self.dtype, self.layout)
+
     def run(self, alpha=1.0, beta=0.0, opts=None, report=None):
-        d = sk.make_desc(self.m, self.n, self.k, alpha, self.dA, self.lda, self.dB, self.ldb, beta,
-                         self.dC, self.ldc, self.dtype, self.layout)
+        d = self.desc(alpha, beta)
         if opts is None and report is None:
             sk.gemm(self.m, self.n, self.k, alpha, self.dA, self.lda, self.dB, self.ldb, beta,
                     self.dC, self.ldc, self.dtype, self.layout)

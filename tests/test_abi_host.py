@@ -628,3 +628,24 @@ def test_two_tile_hybrid_honours_min_waves():
     d3 = _desc(256 * 33, 256 * 16, 2048)  # 528 tiles: w = 2, r = 16
     p3 = sk.plan_query(d3, sk.make_options(schedule=sk.SCHED_SK_HYBRID2, hybrid_min_waves=2), 256)
     assert p3.schedule == sk.SCHED_SK_HYBRID2 and p3.sk_tiles == 16 + 256
+
+
+def test_narrow_tile_plans():
+    """The narrow-m instance: the smallest BM of 64, 128, 192, 256 that holds
+    m, 256 columns, one tile row; refused above m = 256; fp32 ignores the
+    tile option; AUTO never picks it."""
+    for m, bm in ((1, 64), (64, 64), (65, 128), (128, 128), (129, 192), (192, 192), (193, 256), (256, 256)):
+        for dt in (sk.F16, sk.BF16):
+            p = sk.plan_query(_desc(m, 5000, 9000, dt), sk.make_options(tile=sk.TILE_NARROW), slots=256)
+            assert (p.tile_m, p.tile_n, p.tile_k, p.tiles_m, p.tiles_n) == (bm, 256, 64, 1, 20), (m, dt)
+            auto = sk.plan_query(_desc(m, 5000, 9000, dt), sk.make_options(), slots=256)
+            assert auto.tile_n != 256 or auto.tile_m == 256
+    with pytest.raises(sk.SkError) as e:
+        sk.plan_query(_desc(257, 5000, 9000), sk.make_options(tile=sk.TILE_NARROW), slots=256)
+    assert e.value.status == sk.ERR_UNSUPPORTED
+    p = sk.plan_query(_desc(100, 5000, 9000, sk.F32, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW),
+                      slots=512)
+    assert (p.tile_m, p.tile_n) == (128, 128)
+    with pytest.raises(sk.SkError) as e:
+        sk.plan_query(_desc(100, 500, 900), sk.make_options(tile=4), slots=256)
+    assert e.value.status == sk.ERR_INVALID_ARG

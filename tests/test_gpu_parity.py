@@ -82,6 +82,52 @@ def test_k_not_multiple_of_vector_width_and_odd_ld(dtype):
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
 
 
+# ------------------------------------------------ the narrow-m instance
+
+# m, n, k, layout, pad, alpha, beta: every row-block count (BM = 64, 128,
+# 192, 256 and the edges of each), ragged n and k (k below one iteration,
+# not a multiple of the 16-byte chunk, several iterations with a tail),
+# operands read in place and repacked (layouts with a non-k-contiguous
+# operand), alpha and beta applied
+NARROW_CASES = [(1, 300, 200, sk.A_ROW_B_COL, 0, 1.0, 0.0), (17, 513, 1000, sk.A_ROW_B_COL, 8, 0.5, -1.5),
+                (64, 256, 64, sk.A_ROW_B_COL, 0, 1.0, 1.0), (65, 700, 4100, sk.A_ROW_B_ROW, 0, 1.0, 0.0),
+                (100, 1000, 777, sk.A_COL_B_COL, 3, 2.0, 0.0), (128, 520, 136, sk.A_ROW_B_COL, 0, 1.0, 0.0),
+                (144, 2000, 3000, sk.A_ROW_B_COL, 0, 1.0, 0.0), (192, 257, 5000, sk.A_COL_B_ROW, 0, 0.75, 1.25),
+                (200, 3000, 1234, sk.A_ROW_B_COL, 0, 1.0, 0.0), (256, 512, 640, sk.A_ROW_B_COL, 0, 1.0, -1.0),
+                (250, 1300, 17, sk.A_ROW_B_COL, 1, 1.0, 0.0)]
+
+
+@pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
+@pytest.mark.parametrize("sched", ["auto", "dp", "forced7", "forced255"])
+def test_narrow_instance_against_oracle(dtype, sched):
+    """The narrow-m tile (m <= 256) against the full oracle output on every
+    case, under the XCD-aware split (AUTO), data-parallel, and basic
+    Stream-K with 7 and 255 workgroups (owners adding several peers)."""
+    kw = {"auto": {}, "dp": {"schedule": sk.SCHED_DP}, "forced7": {"forced_grid": 7},
+          "forced255": {"forced_grid": 255}}[sched]
+    for (m, n, k, layout, pad, alpha, beta) in NARROW_CASES:
+        _say("case narrow", dtype, sched, m, n, k, layout, pad)
+        c = Case(m, n, k, dtype, layout, 300 + m + k, pad=pad)
+        opts = sk.make_options(tile=sk.TILE_NARROW, **kw)
+        p = sk.plan_query(c.desc(alpha, beta), opts)
+        want_bm = 64 if m <= 64 else 128 if m <= 128 else 192 if m <= 192 else 256
+        assert (p.tile_m, p.tile_n, p.tiles_m) == (want_bm, 256, 1)
+        got = c.run(alpha, beta, opts)
+        ref, bound = c.reference(alpha, beta)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
+
+
+@pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
+def test_narrow_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype):
+    m, n, k = 176, 4000, 3000
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 17)
+    t = sk.plan_query(c.desc(1.0, 0.0), sk.make_options(tile=sk.TILE_NARROW)).tiles
+    dp = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_NARROW))
+    c.reset_c()
+    skg = c.run(1.0, 0.0, sk.make_options(forced_grid=t, tile=sk.TILE_NARROW))
+    assert np.array_equal(dp.view(np.uint8), skg.view(np.uint8))
+
+
 # ----------------------------------------------------------------- edges
 
 @pytest.mark.parametrize("dtype", DTYPES)

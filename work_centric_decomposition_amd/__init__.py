@@ -26,7 +26,7 @@ F32, F16, BF16 = 0, 1, 2
 A_ROW_B_ROW, A_ROW_B_COL, A_COL_B_ROW, A_COL_B_COL = 0, 1, 2, 3
 SCHED_AUTO, SCHED_DP, SCHED_SK_BASIC, SCHED_SK_HYBRID2, SCHED_SK_HYBRID1 = 0, 1, 2, 3, 4
 SCHED_XCD_ALIGNED, SCHED_GEMV_SPLIT = 5, 6
-TILE_AUTO, TILE_LARGE, TILE_SMALL = 0, 1, 2
+TILE_AUTO, TILE_LARGE, TILE_SMALL, TILE_NARROW = 0, 1, 2, 3
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_NO_MEMORY, ERR_HIP, ERR_FIXUP_TIMEOUT, ERR_NO_DEVICE = \
     0, -1, -2, -3, -4, -5, -6
 ERR_TOO_LARGE = -7

@@ -9,6 +9,7 @@
 
 #include <cstdio>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <mutex>
 #include <string>
@@ -34,6 +35,7 @@ struct DeviceInfo {
   int cus = 0;
   int slots[3] = {0, 0, 0};        // per dtype (fp16/bf16: large tiles)
   int slots_small[3] = {0, 0, 0};  // fp16/bf16 small-tile instance
+  int slots_narrow[3] = {0, 0, 0}; // fp16/bf16 narrow-m instances (the fewest of the four)
   int slots_abft = 0;              // fp32 with ABFT
   int64_t wall_khz = 100000;
 };
@@ -99,6 +101,22 @@ int device_info(int dev, DeviceInfo **out) {
       return SK_ERR_HIP;
     }
     (dt == 3 ? d.slots_abft : dt > 3 ? d.slots_small[dtype] : d.slots[dt]) = d.cus * (occ < want ? occ : want);
+  }
+  // fp16, bf16 narrow-m instances: one workgroup per CU each
+  for (int dtype = SK_F16; dtype <= SK_BF16; ++dtype) {
+    int fewest = 1 << 30;
+    for (int inst = 2; inst <= 5; ++inst) {
+      int occ = 0;
+      e = (hipError_t)kernel_occupancy(dtype, false, inst, &occ);
+      if (e != hipSuccess) return hip_fail(e, "occupancy query");
+      if (occ < 1) {
+        g_last_hip_error = "kernel does not fit on a CU";
+        return SK_ERR_HIP;
+      }
+      const int want = tile_cfg(dtype, inst).occupancy;
+      fewest = std::min(fewest, occ < want ? occ : want);
+    }
+    d.slots_narrow[dtype] = d.cus * fewest;
   }
   d.ok = true;
   forget.armed = false;
@@ -366,8 +384,9 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     if (o.schedule == SK_SCHED_GEMV_SPLIT) return SK_ERR_UNSUPPORTED;
   }
   Plan P;
-  const int slots[2] = {o.abft && d.dtype == SK_F32 ? info->slots_abft : info->slots[d.dtype],
-                        d.dtype == SK_F32 ? 1 : info->slots_small[d.dtype]};
+  const int slots[3] = {o.abft && d.dtype == SK_F32 ? info->slots_abft : info->slots[d.dtype],
+                        d.dtype == SK_F32 ? 1 : info->slots_small[d.dtype],
+                        d.dtype == SK_F32 ? 1 : info->slots_narrow[d.dtype]};
   rc = make_plan(d, o, slots, P);
   if (rc != SK_OK) return rc;
   const int es = d.dtype == SK_F32 ? 4 : 2;
@@ -547,7 +566,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
   if (!desc || !out || slots < 0) return SK_ERR_INVALID_ARG;
   const sk_options &o = opts ? *opts : kDefaultOpts;
   try {
-    int slots2 = 0;  // small-tile instance
+    int slots2 = 0, slots3 = 0;  // small-tile and narrow-m instances
     if (slots == 0) {
       int dev = 0;
       hipError_t e = hipGetDevice(&dev);
@@ -559,8 +578,10 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       if (desc->dtype < 0 || desc->dtype > 2) return SK_ERR_INVALID_ARG;
       slots = o.abft && desc->dtype == SK_F32 ? info->slots_abft : info->slots[desc->dtype];
       slots2 = desc->dtype == SK_F32 ? 1 : info->slots_small[desc->dtype];
+      slots3 = desc->dtype == SK_F32 ? 1 : info->slots_narrow[desc->dtype];
     }
     if (slots2 == 0) slots2 = 2 * slots;
+    if (slots3 == 0) slots3 = slots;
     GemvPlan g;
     if ((o.schedule == SK_SCHED_GEMV_SPLIT ||
          (o.schedule == SK_SCHED_AUTO && !o.abft && o.forced_grid == 0 && o.tile == SK_TILE_AUTO)) &&
@@ -587,7 +608,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       }
       return SK_OK;
     }
-    const int both[2] = {slots, slots2};
+    const int both[3] = {slots, slots2, slots3};
     Plan P;
     int rc = make_plan(*desc, o, both, P);
     if (rc != SK_OK) return rc;

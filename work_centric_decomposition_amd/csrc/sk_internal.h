@@ -23,7 +23,8 @@ struct TileCfg {
   int lds_bytes;     // dynamic LDS per workgroup
   // default grid-size model constants, in units of one MAC iteration
   float a, b, c, d;
-  int inst;          // HGEMM tile instance (0: 256 x 256, 1: 128 x 128)
+  int inst;          // HGEMM tile instance (0: 256 x 256, 1: 128 x 128,
+                     // 2-5: narrow-m, 64/128/192/256 x 256)
   // the tile-instance choice, microseconds (least-squares fit, relative
   // error, to the fp16 shape sweep timed on each instance): fixed cost of a
   // launch (start, first loads, epilogue), one level of partial exchange,
@@ -40,6 +41,14 @@ struct TileCfg {
 // with few large tiles.  Model constants in units of one MAC iteration of
 // the instance.
 inline TileCfg tile_cfg(int dtype, int inst = 0) {
+  // narrow-m fp16/bf16 (m up to 256): BM = 64 (inst - 1) rows by 256
+  // columns, 8 waves, one workgroup per CU, four A stages of BM x 64 in LDS;
+  // a BM x 256 fp32 partial against one iteration's 32 KiB of B
+  if (dtype != SK_F32 && inst >= 2 && inst <= 5) {
+    const int bm = 64 * (inst - 1);
+    return TileCfg{bm, 256, 64, 512, 1, 4 * bm * 128, 4.f, 4.f * bm / 256, 1.f, 4.f * bm / 256, inst,
+                   13.8f, 8.45f, 0.745f, 1.153f};
+  }
   // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
   if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f, 0, 8.3f, 3.3f, 2.f, 2.f};
   // 128 x 128 fp16: a 64 KiB partial against a quarter of the large tile's
@@ -301,7 +310,10 @@ int launch_gemv(int dtype, const GemvPlan &g, float *part, float alpha, float be
 
 // Fills `plan` (except max_peers); returns SK_OK or an sk_status.  slots:
 // resident workgroups of the large (or fp32) and of the small-tile instance.
-int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &plan);
+// The narrow-m instance for m rows (m <= 256): the smallest BM that holds m.
+inline int narrow_inst(int64_t m) { return m <= 64 ? 2 : m <= 128 ? 3 : m <= 192 ? 4 : 5; }
+// slots: resident workgroups of the large, small and narrow-m instances
+int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[3], Plan &plan);
 // The runtime model's predicted time of a plan, in microseconds.
 double plan_cost_us(const Plan &plan);
 // Most partials any owner adds under `plan` (O(tiles); for inspection).

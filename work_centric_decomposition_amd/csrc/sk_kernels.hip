@@ -591,6 +591,194 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
                    P::get4(acc, (mb * P::NB + nb) * 4 + g));
 }
 
+// ========================================================= narrow-m HGEMM
+// GEMMs with m of at most 256 and long k (HBM-bound once n and k are large:
+// the Stream-K page's evaluation singles out such memory-bound shapes).  One
+// tile covers every row of C, so B -- the large operand -- is read once, and
+// it streams straight into registers D iterations ahead rather than through
+// LDS.  Tiles of BM = 32 MB rows (MB = 2, 4, 6 or 8: the smallest that holds
+// m) by 256 columns, 8 waves of 32 columns each, every wave over all BM
+// rows: per iteration of 64 k a wave holds its 32 x 64 slice of B in
+// registers (four 16-byte loads per lane, issued D iterations ahead) and
+// reads the tile's A, staged in LDS for all waves (D + 1 stages), one
+// 32-row fragment per MFMA.  Order of k inside an iteration: lane half h at
+// k-step s takes the 16-byte chunk 4 h + s (8 values of k) of the 64, in A
+// and B alike, so that a lane's four B loads cover 64 contiguous bytes of
+// its column.  The MFMA is the HGEMM kernels' 32x32x16 (C^T = B^T A^T, the
+// same accumulator layout), one 32 x 32 block per row block.
+template <int DT, int MB_>
+struct NPolicy {
+  static constexpr int ET = DT;
+  static constexpr int MB = MB_, NB = 1;
+  static constexpr int BM = 32 * MB, BN = 256, BK = 64;
+  static constexpr int WAVES = 8, NT = 64 * WAVES, WPE = 1;
+  static constexpr int D = 3;           // iterations of B and A in flight
+  static constexpr int NSTAGE = D + 1;  // A stages in LDS
+  static constexpr int ROW = BK * 2;    // bytes of one A row in a stage
+  static constexpr int A_BYTES = BM * ROW;
+  static constexpr int LDS_BYTES = NSTAGE * A_BYTES;
+  static constexpr int LA = A_BYTES / 1024 / WAVES;  // A loads per wave and iteration
+  static constexpr int NACC4 = MB * 4;
+  static_assert(LA >= 1 && A_BYTES % (1024 * WAVES) == 0, "A staging");
+  // 16-byte chunk c of A row r sits at chunk position c ^ swz(r): the 16
+  // lanes of one LDS cycle (16 consecutive rows, one chunk) hit 16 distinct
+  // 16-byte bank groups
+  static __device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
+  struct Acc { f16v_t v[MB]; };
+  static __device__ __forceinline__ f4_t get4(const Acc &c, int i) {
+    const f16v_t &b = c.v[i >> 2];
+    const int g = i & 3;
+    return f4_t{b[4 * g], b[4 * g + 1], b[4 * g + 2], b[4 * g + 3]};
+  }
+  static __device__ __forceinline__ void add4(Acc &c, int i, f4_t x) {
+    f16v_t &b = c.v[i >> 2];
+    const int g = i & 3;
+    b[4 * g] += x[0]; b[4 * g + 1] += x[1]; b[4 * g + 2] += x[2]; b[4 * g + 3] += x[3];
+  }
+  static __device__ __forceinline__ void zero(Acc &c) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) c.v[i][e] = 0.f;
+  }
+};
+
+// Per-lane offsets of the narrow-m kernel's loads, computed once per tile.
+// A: load j of wave w fills rows (w LA + j) * 8 + lane / 8 of a stage
+// (direct-to-LDS, 1 KiB per load).  B: lane l reads column w * 32 + (l & 31)
+// at bytes 64 (l >> 5) + 16 s of each 128-byte k-slice.  Rows and columns
+// past the matrix, and chunks at or past k, are fetched out of range (zeros).
+template <class P>
+struct NLoader {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[P::LA];
+  int ca[P::LA];  // k-chunk of A load j
+  uint32_t vb;
+  int lds_a;      // this wave's first A load within a stage
+
+  __device__ __forceinline__ void init(const KernelArgs &a, int m0, int n0) {
+    constexpr int ES = 2;
+    const int w = wave_id(), lane = threadIdx.x & 63;
+    const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
+    const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * lda_b;
+    const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * ldb_b;
+    ra = make_rsrc(Ab, (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)a.a_kext * ES);
+    rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
+#pragma unroll
+    for (int j = 0; j < P::LA; ++j) {
+      const int row = (w * P::LA + j) * 8 + lane / 8;
+      const int c = (lane % 8) ^ P::swz(row);
+      ca[j] = c;
+      va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
+    }
+    const int col = w * 32 + (lane & 31);
+    vb = col < a.n - n0 ? (uint32_t)(col * ldb_b + (lane >> 5) * 64) : kOOB;
+    lds_a = w * P::LA * 1024;
+  }
+
+  // A of iteration kit into `stage`; every chunk when `live` is false is
+  // fetched out of range
+  __device__ __forceinline__ void load_a(const KernelArgs &a, int stage, int kit, bool live) const {
+    const int k0b = kit * P::BK * 2;
+    const int left = live ? (a.k - kit * P::BK) * 2 : 0;
+    const int dst = stage * P::A_BYTES + lds_a;
+#pragma unroll
+    for (int j = 0; j < P::LA; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + dst + j * 1024), 16,
+                                               ca[j] * 16 < left ? va[j] : kOOB, k0b, 0, 0);
+  }
+
+  // this lane's B of iteration kit, one 16-byte chunk per k-step
+  __device__ __forceinline__ void load_b(const KernelArgs &a, int kit, bool live,
+                                         typename Elem<P::ET>::V8 (&b)[4]) const {
+    using V8 = typename Elem<P::ET>::V8;
+    const int k0b = kit * P::BK * 2;
+    const int left = live ? (a.k - kit * P::BK) * 2 : 0;
+    const int h = (threadIdx.x & 63) >> 5;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const bool ok = (4 * h + s) * 16 < left;
+      b[s] = __builtin_bit_cast(V8, __builtin_amdgcn_raw_buffer_load_b128(rb, ok ? vb + s * 16 : kOOB, k0b, 0));
+    }
+  }
+};
+
+// Iteration i (= PH mod D) of the narrow-m MAC loop.  On entry this wave
+// has issued the loads of iterations up to i + D - 1, A then B per
+// iteration; those of iteration i have landed once at most D - 1
+// iterations' loads are outstanding.  The barrier then publishes A stage
+// i mod (D + 1) and frees stage (i - 1) mod (D + 1), whose readers (the
+// MFMAs of iteration i - 1) are done, for A of iteration i + D; B of
+// iteration i + D goes into the registers this iteration's MFMAs have just
+// read.
+template <class P, int PH>
+__device__ __forceinline__ void n_iter(const KernelArgs &a, const NLoader<P> &ld, int i, int n, int lb,
+                                       typename Elem<P::ET>::V8 (&B)[P::D][4], typename P::Acc &acc) {
+  using V8 = typename Elem<P::ET>::V8;
+  __builtin_amdgcn_s_waitcnt(vmcnt_le((P::D - 1) * (P::LA + 4)));
+  // a plain barrier: __syncthreads() would also wait for every load in
+  // flight; the memory clobber keeps the compiler from moving LDS accesses
+  // across it
+  asm volatile("s_barrier" ::: "memory");
+  ld.load_a(a, (i + P::D) % P::NSTAGE, lb + i + P::D, i + P::D < n);
+  const int lane = threadIdx.x & 63, h = lane >> 5, r = lane & 31;
+  const char *As = smem + (i % P::NSTAGE) * P::A_BYTES + r * P::ROW;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    V8 af[P::MB];
+    const int pos = ((4 * h + s) ^ P::swz(r)) << 4;  // swz(mb * 32 + r) = swz(r)
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) af[mb] = *reinterpret_cast<const V8 *>(As + mb * 32 * P::ROW + pos);
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) acc.v[mb] = h_mfma<P::ET>(B[PH][s], af[mb], acc.v[mb]);
+  }
+  ld.load_b(a, lb + i + P::D, i + P::D < n, B[PH]);
+}
+
+template <class P>
+__device__ __forceinline__ void n_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
+                                          typename P::Acc &acc) {
+  using V8 = typename Elem<P::ET>::V8;
+  static_assert(P::D == 3, "the loop below is unrolled for three iterations in flight");
+  P::zero(acc);
+  const int n = le - lb;
+  if (n <= 0) return;
+  NLoader<P> ld;
+  ld.init(a, m0, n0);
+  V8 B[P::D][4];
+#pragma unroll
+  for (int d = 0; d < P::D; ++d) {
+    ld.load_a(a, d, lb + d, d < n);
+    ld.load_b(a, lb + d, d < n, B[d]);
+  }
+  int i = 0;
+  for (; i + 3 <= n; i += 3) {
+    n_iter<P, 0>(a, ld, i, n, lb, B, acc);
+    n_iter<P, 1>(a, ld, i + 1, n, lb, B, acc);
+    n_iter<P, 2>(a, ld, i + 2, n, lb, B, acc);
+  }
+  if (i < n) n_iter<P, 0>(a, ld, i, n, lb, B, acc);
+  if (i + 1 < n) n_iter<P, 1>(a, ld, i + 1, n, lb, B, acc);
+  // every wave's loads (the last ones fetch nothing) and LDS reads are done
+  // before the caller reuses LDS
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Epilogue of a narrow-m tile: lane l of wave w holds rows mb * 32 + (l & 31)
+// and columns w * 32 + 8 g + 4 (l >> 5) + e of the tile.
+template <class P>
+__device__ __forceinline__ void n_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
+                                           const typename P::Acc &acc) {
+  const int w = wave_id(), lane = threadIdx.x & 63;
+  const int c0 = n0 + w * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int mb = 0; mb < P::MB; ++mb)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      store4<P::ET>(a, vec_ok, m0 + mb * 32 + (lane & 31), c0 + 8 * g, P::get4(acc, mb * 4 + g));
+}
+
 // ============================================================== SGEMM
 // 128 x 128 x 32 tiles, 4 waves as 2 x 2, wave tile 64 x 64,
 // v_mfma_f32_16x16x4_f32: 4 x 4 blocks per wave.  Within a group of 16 k,
@@ -1217,6 +1405,13 @@ __global__ __launch_bounds__(P::NT, P::WPE) void hgemm_kernel(KernelArgs a, int 
       [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
 }
 
+template <class P>
+__global__ __launch_bounds__(P::NT, 1) void ngemm_kernel(KernelArgs a, int vec_ok) {
+  run_workgroup<P>(
+      a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { n_macloop<P>(a, m0, n0, lb, le, acc); },
+      [&](int m0, int n0, const typename P::Acc &acc) { n_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
+}
+
 template <bool AK, bool BKM, bool ABFT>
 __global__ __launch_bounds__(SCfg::NT, 2) void sgemm_kernel(KernelArgs a, int vec_ok) {
   using P = SPolicy<AK, BKM>;
@@ -1470,8 +1665,20 @@ static const void *sgemm_entry(bool ak, bool bk, bool abft) {
 }
 
 // Entry point of an fp16/bf16 tile instance.
+template <int DT>
+static const void *ngemm_entry(int inst) {
+  using namespace dev;
+  switch (inst) {
+    case 2: return reinterpret_cast<const void *>(&ngemm_kernel<NPolicy<DT, 2>>);
+    case 3: return reinterpret_cast<const void *>(&ngemm_kernel<NPolicy<DT, 4>>);
+    case 4: return reinterpret_cast<const void *>(&ngemm_kernel<NPolicy<DT, 6>>);
+    default: return reinterpret_cast<const void *>(&ngemm_kernel<NPolicy<DT, 8>>);
+  }
+}
+
 static const void *hgemm_entry(int dtype, int inst) {
   using namespace dev;
+  if (inst >= 2) return dtype == SK_F16 ? ngemm_entry<SK_F16>(inst) : ngemm_entry<SK_BF16>(inst);
   if (inst == 1)
     return dtype == SK_F16 ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_F16, 128>>)
                            : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_BF16, 128>>);

@@ -401,21 +401,25 @@ static int forced_grid_ok(int rc, const Plan &P) {
   return plan_max_peers(P) < P.slots - 8 ? SK_OK : SK_ERR_UNSUPPORTED;
 }
 
-int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[2], Plan &P) {
+int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[3], Plan &P) {
   std::memset(&P, 0, sizeof(P));
   if (d.m < 0 || d.n < 0 || d.k < 0) return SK_ERR_INVALID_ARG;
   if (d.dtype != SK_F32 && d.dtype != SK_F16 && d.dtype != SK_BF16) return SK_ERR_INVALID_ARG;
   if (d.layout < SK_A_ROW_B_ROW || d.layout > SK_A_COL_B_COL) return SK_ERR_INVALID_ARG;
   if (o.schedule < SK_SCHED_AUTO || o.schedule > SK_SCHED_GEMV_SPLIT) return SK_ERR_INVALID_ARG;
   if (o.schedule == SK_SCHED_GEMV_SPLIT) return SK_ERR_UNSUPPORTED;  // not a matrix-vector call
-  if (o.tile < SK_TILE_AUTO || o.tile > SK_TILE_SMALL) return SK_ERR_INVALID_ARG;
-  if (o.forced_grid < 0 || slots[0] <= 0 || slots[1] <= 0) return SK_ERR_INVALID_ARG;
+  if (o.tile < SK_TILE_AUTO || o.tile > SK_TILE_NARROW) return SK_ERR_INVALID_ARG;
+  if (o.forced_grid < 0 || slots[0] <= 0 || slots[1] <= 0 || slots[2] <= 0) return SK_ERR_INVALID_ARG;
   // 32-bit indices inside the kernels
   if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
   // a forced grid is a count of large-tile workgroups unless a tile is given
   if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE || (o.tile == SK_TILE_AUTO && o.forced_grid > 0))
     return forced_grid_ok(plan_inst(d, o, 0, slots[0], P), P);
   if (o.tile == SK_TILE_SMALL) return forced_grid_ok(plan_inst(d, o, 1, slots[1], P), P);
+  if (o.tile == SK_TILE_NARROW) {
+    if (d.m > 256) return SK_ERR_UNSUPPORTED;
+    return forced_grid_ok(plan_inst(d, o, narrow_inst(d.m), slots[2], P), P);
+  }
   // AUTO: whichever instance the model predicts faster (cached per shape
   // class); measured on the fp16 shape sweep, the small tile wins on most
   // shapes below one wave of large tiles and on short-k shapes up to about
