@@ -681,6 +681,7 @@ def shape_sweep(torch, sk, S, count, out_path="", legs=("auto", "dp"), min_ms=20
                    mem_bound=int(by / bw > fl / peak), dp_quant_eff=t / (slots * -(-t // slots)))
         for name, opts in lg:
             us, R, host_us = back_to_back_us(torch, lambda: sk.gemm_ex(d, opts), min_ms)
+            row[f"err_{name}"] = _sampled_check(torch, A, B, C, m, n, k, idx)
             pq = sk.plan_query(d, opts)
             row[f"t_{name}_us"] = us
             row[f"launches_{name}"] = R
@@ -702,6 +703,22 @@ def shape_sweep(torch, sk, S, count, out_path="", legs=("auto", "dp"), min_ms=20
             for r in rows:
                 f.write(",".join(f"{r[k]:.6g}" if isinstance(r[k], float) else str(r[k]) for k in keys) + "\n")
     return sweep_summary(rows, legs)
+
+
+def _sampled_check(torch, A, B, C, m, n, k, seed, count=64):
+    """The timed launches' result on `count` seeded entries against fp32
+    dot products of the same fp16 inputs on the GPU (torch, not this
+    library): max |C_ij - ref_ij| / sum_l |a_il||b_lj|."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000003 + seed)
+    ii = torch.randint(0, m, (count,), generator=g, device="cuda")
+    jj = torch.randint(0, n, (count,), generator=g, device="cuda")
+    a = A[: m * k].view(m, k)[ii].float()
+    b = B[: n * k].view(n, k)[jj].float()
+    ref = (a * b).sum(1)
+    bound = (a.abs() * b.abs()).sum(1).clamp_min(1e-30)
+    got = C[: m * n].view(m, n)[ii, jj].float()
+    return float(((got - ref).abs() / bound).max())
 
 
 def sweep_summary(rows, legs):
@@ -757,6 +774,12 @@ def sweep_summary(rows, legs):
             "legs": list(legs),
             "roofline": {"peak_tflops": PEAK_TFLOPS["f16"], "hbm_tb_s": PEAK_HBM_GBS / 1000,
                          "t_min": "max(2mnk/peak, 2(mk+kn+mn)/bw)"},
+            # every timed leg's result, 64 seeded entries per shape against
+            # fp32 dot products of the same inputs (torch), error / bound
+            "result_check": {"entries": 64 * len(rows) * len(legs),
+                             "max_err": max(r[f"err_{name}"] for r in rows for name in legs),
+                             "gate": 5e-3,
+                             "failed": sum(r[f"err_{name}"] > 5e-3 for r in rows for name in legs)},
             "classes": {name: summary(sel) for name, sel in classes.items()}}
 
 
