@@ -303,3 +303,31 @@ def test_abft_4096_fault_free_runs_margin():
         print(f"seed {seed}: largest |residual| / threshold so far {worst:.4f}", flush=True)
     print(f"{runs} fault-free 4096^3 runs: largest |residual| / threshold = {worst:.4f}", flush=True)
     assert runs == 100 and 0.0 < worst < 1.0
+
+
+def test_abft_workspace_buffers_grow_between_calls():
+    """The encodings, threshold inputs and per-tile counters live in the
+    stream's workspace and grow when a call needs more: a small call, one
+    whose encodings pass the initial 4 MiB (16384 x 16384 x 4096, 256 + 256
+    tiles at 128 k-iterations), one with more tiles than the initial 1024
+    counters (n = 140000: 1094 tile columns), then the small one again.
+    Fault-free, each equals the same call without ABFT bit for bit (the
+    checksum updates do not touch the accumulators) and reports nothing."""
+    g = torch.Generator(device="cuda")
+    g.manual_seed(4242)
+    for (m, n, k) in [(300, 260, 640), (16384, 16384, 4096), (64, 140000, 96), (300, 260, 640)]:
+        print("case abft growth", m, n, k, flush=True)
+        A = torch.rand(m * k, generator=g, device="cuda") * 2 - 1
+        B = torch.rand(k * n, generator=g, device="cuda") * 2 - 1
+        C0 = torch.zeros(m * n, device="cuda")
+        C1 = torch.zeros(m * n, device="cuda")
+        rep = _report_dev()
+        for C, opts, r in ((C0, sk.make_options(), None), (C1, sk.make_options(abft=True), rep)):
+            d = sk.make_desc(m, n, k, 1.0, A, k, B, n, 0.0, C, n, sk.F32, sk.A_ROW_B_ROW)
+            sk.gemm_ex(d, opts, r)
+        torch.cuda.synchronize()
+        r = sk.read_report(rep)
+        assert (r.detected, r.n_records) == (0, 0), (m, n, k, _records(r))
+        assert r.checked > 0 and r.max_ratio < 1.0, (m, n, k, r.checked, r.max_ratio)
+        assert torch.equal(C0.view(torch.int32), C1.view(torch.int32)), (m, n, k)
+        del A, B, C0, C1
