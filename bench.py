@@ -873,6 +873,12 @@ def main():
             step_flops = sum(2.0 * c["n"] ** 3 + 3.0 * c["n"] ** 2 for c in cases)
             kern_ms = sum(per_launch)
             achieved = sum(flops) / (kern_ms * 1e-3) / 1e12
+            tiles = {}
+            for c in cases:  # the tile instance AUTO runs each shape on
+                n = c["n"]
+                d = sk.make_desc(n, n, n, 1.0, c["A"], n, c["B"], n, 1.0, c["C"], n, sk.F32, sk.A_ROW_B_ROW)
+                p = sk.plan_query(d)
+                tiles[str(n)] = f"{p.tile_m}x{p.tile_n}"
             results[wl] = dict(
                 value=step_flops / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype="f32",
                 per_shape={str(c["n"]): round(f / (t * 1e-3) / 1e12, 2)
@@ -882,6 +888,7 @@ def main():
                           "frac": round(achieved / PEAK_TFLOPS["f32"], 4),
                           "traffic": traffic_for(wl),
                           "kernel": "sgemm_kernel<k-major A, n-major B>",
+                          "tile_per_shape": tiles,
                           "launch_ms": round(kern_ms / len(cases), 4)},
                 config={"workload": "SGEMM fp32 square sweep m=n=k in {1024,2048,3072,4096,5120,6144},"
                                     " row-major A and B, U[-1,1] inputs, C pre-filled U[-1,1],"

@@ -174,15 +174,20 @@ typedef struct {
   int32_t checked;       /* rows and columns checked */
 } sk_abft_report;
 
-/* fp16/bf16 tile instances.  LARGE: 256 x 256 x 64 tiles, one 512-thread
- * workgroup per CU.  SMALL: 128 x 128 x 64 tiles, two 256-thread workgroups
- * per CU, for GEMMs with few large tiles (the page's observation that a
- * large tile loses on small, bandwidth-bound shapes, evaluation section).
- * NARROW: for m <= 256 (SK_ERR_UNSUPPORTED above), BM x 256 x 64 tiles with
- * BM = 64, 128, 192 or 256, the smallest that holds m, so that B is read
- * once; B streams into registers three iterations ahead (memory-bound
- * shapes with long k, the page's evaluation section).  AUTO picks among
- * them. */
+/* Tile instances.  fp16/bf16 -- LARGE: 256 x 256 x 64 tiles, one
+ * 512-thread workgroup per CU.  SMALL: 128 x 128 x 64 tiles, two 256-thread
+ * workgroups per CU, for GEMMs with few large tiles (the page's observation
+ * that a large tile loses on small, bandwidth-bound shapes, evaluation
+ * section).  NARROW: for m <= 256 (SK_ERR_UNSUPPORTED above), BM x 256 x 64
+ * tiles with BM = 64, 128, 192 or 256, the smallest that holds m, so that B
+ * is read once; B streams into registers three iterations ahead
+ * (memory-bound shapes with long k, the page's evaluation section).  AUTO
+ * picks LARGE or SMALL by the runtime model.
+ * fp32 -- LARGE: 128 x 128 x 32 tiles, two 256-thread workgroups per CU.
+ * SMALL: 64 x 64 x 32 tiles, four 256-thread workgroups per CU (1024^3 is
+ * one such tile per CU, with no partial exchange); not with ABFT
+ * (SK_ERR_UNSUPPORTED), which runs on LARGE.  NARROW: SK_ERR_UNSUPPORTED.
+ * AUTO picks LARGE or SMALL by the runtime model (LARGE with ABFT). */
 typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2, SK_TILE_NARROW = 3 } sk_tile;
 
 /* Options for sk_gemm_ex.  Zero-initialised options mean: AUTO schedule, no
@@ -190,7 +195,7 @@ typedef enum { SK_TILE_AUTO = 0, SK_TILE_LARGE = 1, SK_TILE_SMALL = 2, SK_TILE_N
 typedef struct {
   int32_t schedule;         /* sk_schedule */
   int32_t forced_grid;      /* > 0: basic Stream-K with exactly this many workgroups (on the
-                             * large fp16/bf16 tile unless `tile` names one) */
+                             * large tile unless `tile` names one) */
   int32_t abft;             /* nonzero: ABFT mode (checksums, verify, correct); SK_F32 only */
   int32_t hybrid_min_waves; /* full waves needed before the two-tile hybrid is used (default 1) */
   const sk_fault *faults;   /* device array of injected faults (testing), or NULL */
@@ -200,7 +205,7 @@ typedef struct {
    * fixed cost a, partial-output cost b, per-iteration cost c, per-peer cost d */
   float model_a, model_b, model_c, model_d;
   int32_t spin_limit_us;    /* fixup wait time-out in microseconds (0 = 2 s) */
-  int32_t tile;             /* sk_tile: fp16/bf16 tile instance (ignored for SK_F32) */
+  int32_t tile;             /* sk_tile: tile instance */
   int32_t test_flags;       /* testing only (0 otherwise): SK_TEST_NO_SIGNAL */
 } sk_options;
 
@@ -312,10 +317,9 @@ int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report 
 int sk_gemm_noalloc(const sk_gemm_desc *desc, const sk_options *opts, hipStream_t stream);
 
 /* Plan the call would use.  slots > 0 plans for that many resident
- * workgroups of the fp32 or large-tile fp16/bf16 kernel (the small-tile
- * instance runs two workgroups where the large one runs one, so it is
- * planned for 2 * slots) without touching the GPU; slots == 0 asks the
- * current device. */
+ * workgroups of the large-tile kernel (the small-tile instance runs two
+ * workgroups where the large one runs one, so it is planned for 2 * slots)
+ * without touching the GPU; slots == 0 asks the current device. */
 int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slots, sk_plan *out);
 
 /* Segments of workgroup `wg` under `plan`, in execution order.  Writes at

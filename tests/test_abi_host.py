@@ -102,14 +102,16 @@ TILES = [sk.TILE_LARGE, sk.TILE_SMALL]
 def test_page_schedules_match_oracle_decomposition(shape, dtype, slots, tile):
     """The page's decompositions, chosen explicitly, against the oracle's own
     construction of Algorithms 2 and 5 and section 5.2's hybrids (both fp16
-    tile instances; the small one runs two workgroups per slot)."""
+    tile instances of each type; the small one runs two workgroups per
+    large-tile slot)."""
     m, n, k = shape
     d = _desc(m, n, k, dtype)
     for sched, mode in [(sk.SCHED_DP, oracle.DP_PERSISTENT), (sk.SCHED_SK_BASIC, oracle.SK),
                         (sk.SCHED_SK_HYBRID2, oracle.HYBRID2), (sk.SCHED_SK_HYBRID1, oracle.HYBRID1)]:
         p = sk.plan_query(d, sk.make_options(schedule=sched, tile=tile), slots)
-        assert p.slots == (2 * slots if dtype != sk.F32 and tile == sk.TILE_SMALL else slots)
-        assert p.tile_m == (128 if dtype == sk.F32 or tile == sk.TILE_SMALL else 256)
+        assert p.slots == (2 * slots if tile == sk.TILE_SMALL else slots)
+        large, small = (128, 64) if dtype == sk.F32 else (256, 128)
+        assert p.tile_m == p.tile_n == (small if tile == sk.TILE_SMALL else large)
         slots = p.slots
         t, ipt = p.tiles, p.iters_per_tile
         assert t == -(-m // p.tile_m) * -(-n // p.tile_n) and ipt == -(-k // p.tile_k)
@@ -234,12 +236,14 @@ def test_forced_grid_and_explicit_schedules_match_oracle(shape):
         assert p.schedule == sk.SCHED_SK_BASIC and p.grid == g
         assert _lib_plan_records(p) == _oracle_records(m, n, k, p.tile_m, p.tile_n, p.tile_k,
                                                        oracle.SK, g)
+    # explicit schedules on either instance (AUTO tile may pick the small
+    # one, whose slot count is twice the large one's)
     p = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_SK_HYBRID1), 256)
     assert _lib_plan_records(p) == _oracle_records(m, n, k, p.tile_m, p.tile_n, p.tile_k,
-                                                   oracle.HYBRID1, 256)
+                                                   oracle.HYBRID1, p.slots)
     p = sk.plan_query(d, sk.make_options(schedule=sk.SCHED_DP), 256)
     assert _lib_plan_records(p) == _oracle_records(m, n, k, p.tile_m, p.tile_n, p.tile_k,
-                                                   oracle.DP_PERSISTENT, min(256, p.tiles))
+                                                   oracle.DP_PERSISTENT, min(p.slots, p.tiles))
 
 
 def test_forced_grid_equal_tiles_is_data_parallel_plan():
@@ -372,8 +376,9 @@ def test_auto_below_a_wave_needs_a_clear_iteration_gain():
 def test_auto_tile_instance():
     """fp16 AUTO keeps the large tile once its tiles fill the grid and takes
     the small one where the runtime model predicts it faster (few large
-    tiles of few iterations); an explicit instance is always honoured, and
-    fp32 has one instance."""
+    tiles of few iterations); an explicit instance is always honoured.
+    fp32 likewise between 128 x 128 and 64 x 64 (1024^3 is one 64 x 64 tile
+    per CU), and ABFT keeps the 128 x 128 tile."""
     big = sk.plan_query(_desc(8192, 8192, 8192), None, 256)
     assert (big.tile_m, big.slots) == (256, 256)
     small = sk.plan_query(_desc(512, 512, 512), None, 256)
@@ -381,7 +386,16 @@ def test_auto_tile_instance():
     for shape in [(512, 512, 512), (8192, 8192, 8192), (300, 5000, 700)]:
         for tile, bm in [(sk.TILE_LARGE, 256), (sk.TILE_SMALL, 128)]:
             assert sk.plan_query(_desc(*shape), sk.make_options(tile=tile), 256).tile_m == bm
-        assert sk.plan_query(_desc(*shape, sk.F32), sk.make_options(tile=sk.TILE_SMALL), 512).tile_m == 128
+        for tile, bm in [(sk.TILE_LARGE, 128), (sk.TILE_SMALL, 64)]:
+            assert sk.plan_query(_desc(*shape, sk.F32), sk.make_options(tile=tile), 512).tile_m == bm
+        with pytest.raises(sk.SkError) as e:
+            sk.plan_query(_desc(*shape, sk.F32), sk.make_options(tile=sk.TILE_SMALL, abft=True), 512)
+        assert e.value.status == sk.ERR_UNSUPPORTED
+        assert sk.plan_query(_desc(*shape, sk.F32), sk.make_options(abft=True), 512).tile_m == 128
+    f32_big = sk.plan_query(_desc(6144, 6144, 6144, sk.F32), None, 512)
+    assert (f32_big.tile_m, f32_big.slots) == (128, 512)
+    f32_small = sk.plan_query(_desc(1024, 1024, 1024, sk.F32), None, 512)
+    assert (f32_small.tile_m, f32_small.slots, f32_small.tiles) == (64, 1024, 256)
     with pytest.raises(sk.SkError):
         sk.plan_query(_desc(512, 512, 512), sk.make_options(tile=3), 256)
 
@@ -632,8 +646,8 @@ def test_two_tile_hybrid_honours_min_waves():
 
 def test_narrow_tile_plans():
     """The narrow-m instance: the smallest BM of 64, 128, 192, 256 that holds
-    m, 256 columns, one tile row; refused above m = 256; fp32 ignores the
-    tile option; AUTO never picks it."""
+    m, 256 columns, one tile row; refused above m = 256 and for fp32 (no
+    such instance); AUTO never picks it."""
     for m, bm in ((1, 64), (64, 64), (65, 128), (128, 128), (129, 192), (192, 192), (193, 256), (256, 256)):
         for dt in (sk.F16, sk.BF16):
             p = sk.plan_query(_desc(m, 5000, 9000, dt), sk.make_options(tile=sk.TILE_NARROW), slots=256)
@@ -643,9 +657,10 @@ def test_narrow_tile_plans():
     with pytest.raises(sk.SkError) as e:
         sk.plan_query(_desc(257, 5000, 9000), sk.make_options(tile=sk.TILE_NARROW), slots=256)
     assert e.value.status == sk.ERR_UNSUPPORTED
-    p = sk.plan_query(_desc(100, 5000, 9000, sk.F32, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW),
+    with pytest.raises(sk.SkError) as e:
+        sk.plan_query(_desc(100, 5000, 9000, sk.F32, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW),
                       slots=512)
-    assert (p.tile_m, p.tile_n) == (128, 128)
+    assert e.value.status == sk.ERR_UNSUPPORTED
     with pytest.raises(sk.SkError) as e:
         sk.plan_query(_desc(100, 500, 900), sk.make_options(tile=4), slots=256)
     assert e.value.status == sk.ERR_INVALID_ARG

@@ -58,8 +58,6 @@ TILES = [sk.TILE_AUTO, sk.TILE_LARGE, sk.TILE_SMALL]
 @pytest.mark.parametrize("layout", LAYOUTS)
 @pytest.mark.parametrize("tile", TILES)
 def test_ragged_shapes_all_layouts(dtype, layout, tile):
-    if dtype == sk.F32 and tile != sk.TILE_AUTO:
-        pytest.skip("fp32 has one tile instance")
     # (520, 264, 320): interior tiles with vector-aligned rows and alpha, beta
     # not 1, 0 (the epilogue's straight-line path) next to edge tiles
     for (m, n, k, pad, alpha, beta) in [(300, 520, 200, 0, 1.0, 0.0), (513, 257, 1000, 8, 0.5, -1.5),
@@ -160,8 +158,8 @@ def test_beta_zero_does_not_read_c(dtype):
 
 # ------------------------------------------------- schedule equivalences
 
-@pytest.mark.parametrize("dtype,tile", [(sk.F32, sk.TILE_AUTO), (sk.F16, sk.TILE_LARGE),
-                                        (sk.F16, sk.TILE_SMALL)])
+@pytest.mark.parametrize("dtype,tile", [(sk.F32, sk.TILE_LARGE), (sk.F32, sk.TILE_SMALL),
+                                        (sk.F16, sk.TILE_LARGE), (sk.F16, sk.TILE_SMALL)])
 def test_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype, tile):
     m, n, k = (1024, 768, 2048) if dtype != sk.F32 else (640, 512, 1024)
     c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 11)
@@ -177,12 +175,12 @@ def test_stream_k_with_g_equal_t_is_bitwise_data_parallel(dtype, tile):
 @pytest.mark.parametrize("dtype", DTYPES)
 def test_every_grid_size_exact_on_integer_inputs(dtype):
     """Small integers make every partial sum exact in fp32, so every
-    decomposition, and both fp16/bf16 tile instances, give the same bits."""
+    decomposition, and both tile instances of each type, give the same
+    bits."""
     m, n, k = (700, 600, 1024) if dtype == sk.F32 else (600, 520, 2048)
     c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 12, dist="int")
     ref = c.run(1.0, 0.0, sk.make_options(schedule=sk.SCHED_DP))
-    tiles = [sk.TILE_AUTO] if dtype == sk.F32 else [sk.TILE_LARGE, sk.TILE_SMALL]
-    for tile in tiles:
+    for tile in [sk.TILE_LARGE, sk.TILE_SMALL]:
         for g in [1, 2, 3, 5, 7, 13, 31, 100, 255, 256, 300]:
             c.reset_c()
             got = c.run(1.0, 0.0, sk.make_options(forced_grid=g, tile=tile))
@@ -267,8 +265,6 @@ XCD_CASES = [
 @pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
 def test_xcd_aligned_schedule_against_oracle(case, tile):
     m, n, k, dtype, layout = case
-    if dtype == sk.F32 and tile == sk.TILE_SMALL:
-        pytest.skip("fp32 has one tile instance")
     _say("case xcd aligned", case, tile)
     c = Case(m, n, k, dtype, layout, 21, dist="normal", scale=1 / np.sqrt(k))
     opts = sk.make_options(schedule=sk.SCHED_XCD_ALIGNED, tile=tile)

@@ -33,8 +33,8 @@ int hip_fail(hipError_t e, const char *what) {
 struct DeviceInfo {
   bool ok = false;
   int cus = 0;
-  int slots[3] = {0, 0, 0};        // per dtype (fp16/bf16: large tiles)
-  int slots_small[3] = {0, 0, 0};  // fp16/bf16 small-tile instance
+  int slots[3] = {0, 0, 0};        // per dtype, large tiles
+  int slots_small[3] = {0, 0, 0};  // per dtype, small tiles
   int slots_narrow[3] = {0, 0, 0}; // fp16/bf16 narrow-m instances (the fewest of the four)
   int slots_abft = 0;              // fp32 with ABFT
   int64_t wall_khz = 100000;
@@ -88,19 +88,26 @@ int device_info(int dev, DeviceInfo **out) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     d.wall_khz = khz;
-  // 0-2: per dtype; 3: fp32 with ABFT; 4, 5: fp16, bf16 small tiles
-  for (int dt = 0; dt < 6; ++dt) {
+  // large and small tiles per dtype, and fp32 with ABFT (large tiles)
+  struct Query {
+    int dtype, inst;
+    bool abft;
+    int *slots;
+  };
+  const Query queries[] = {{SK_F32, 0, false, &d.slots[SK_F32]},        {SK_F16, 0, false, &d.slots[SK_F16]},
+                           {SK_BF16, 0, false, &d.slots[SK_BF16]},      {SK_F32, 0, true, &d.slots_abft},
+                           {SK_F32, 1, false, &d.slots_small[SK_F32]},  {SK_F16, 1, false, &d.slots_small[SK_F16]},
+                           {SK_BF16, 1, false, &d.slots_small[SK_BF16]}};
+  for (const Query &q : queries) {
     int occ = 0;
-    const int dtype = dt == 3 ? SK_F32 : dt > 3 ? dt - 3 : dt;
-    const int inst = dt > 3 ? 1 : 0;
-    e = (hipError_t)kernel_occupancy(dtype, dt == 3, inst, &occ);
+    e = (hipError_t)kernel_occupancy(q.dtype, q.abft, q.inst, &occ);
     if (e != hipSuccess) return hip_fail(e, "occupancy query");
-    const int want = tile_cfg(dtype, inst).occupancy;
+    const int want = tile_cfg(q.dtype, q.inst).occupancy;
     if (occ < 1) {
       g_last_hip_error = "kernel does not fit on a CU";
       return SK_ERR_HIP;
     }
-    (dt == 3 ? d.slots_abft : dt > 3 ? d.slots_small[dtype] : d.slots[dt]) = d.cus * (occ < want ? occ : want);
+    *q.slots = d.cus * (occ < want ? occ : want);
   }
   // fp16, bf16 narrow-m instances: one workgroup per CU each
   for (int dtype = SK_F16; dtype <= SK_BF16; ++dtype) {
@@ -385,8 +392,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   }
   Plan P;
   const int slots[3] = {o.abft && d.dtype == SK_F32 ? info->slots_abft : info->slots[d.dtype],
-                        d.dtype == SK_F32 ? 1 : info->slots_small[d.dtype],
-                        d.dtype == SK_F32 ? 1 : info->slots_narrow[d.dtype]};
+                        info->slots_small[d.dtype], d.dtype == SK_F32 ? 1 : info->slots_narrow[d.dtype]};
   rc = make_plan(d, o, slots, P);
   if (rc != SK_OK) return rc;
   const int es = d.dtype == SK_F32 ? 4 : 2;
@@ -577,7 +583,7 @@ int sk_plan_query(const sk_gemm_desc *desc, const sk_options *opts, int32_t slot
       if (rc != SK_OK) return rc;
       if (desc->dtype < 0 || desc->dtype > 2) return SK_ERR_INVALID_ARG;
       slots = o.abft && desc->dtype == SK_F32 ? info->slots_abft : info->slots[desc->dtype];
-      slots2 = desc->dtype == SK_F32 ? 1 : info->slots_small[desc->dtype];
+      slots2 = info->slots_small[desc->dtype];
       slots3 = desc->dtype == SK_F32 ? 1 : info->slots_narrow[desc->dtype];
     }
     if (slots2 == 0) slots2 = 2 * slots;

@@ -15,7 +15,8 @@ namespace sk {
 //   2 x 4, two per SIMD, each owning a 128 x 64 block of C), two LDS stages
 //   of 64 KiB, one workgroup per CU.
 //   SGEMM (fp32): 128 x 128 x 32 tiles, 256 threads (4 wave64s, 2 x 2, each
-//   64 x 64), two LDS stages of 32 KiB, two workgroups per CU.
+//   64 x 64), two LDS stages of 32 KiB, two workgroups per CU; and 64 x 64 x
+//   32 tiles (32 x 32 per wave, stages of 16 KiB, four workgroups per CU).
 struct TileCfg {
   int bm, bn, bk;
   int threads;
@@ -23,8 +24,9 @@ struct TileCfg {
   int lds_bytes;     // dynamic LDS per workgroup
   // default grid-size model constants, in units of one MAC iteration
   float a, b, c, d;
-  int inst;          // HGEMM tile instance (0: 256 x 256, 1: 128 x 128,
-                     // 2-5: narrow-m, 64/128/192/256 x 256)
+  int inst;          // tile instance: fp16/bf16 0: 256 x 256, 1: 128 x 128,
+                     // 2-5: narrow-m, 64/128/192/256 x 256; fp32 0: 128 x 128,
+                     // 1: 64 x 64
   // the tile-instance choice, microseconds (least-squares fit, relative
   // error, to the fp16 shape sweep timed on each instance): fixed cost of a
   // launch (start, first loads, epilogue), one level of partial exchange,
@@ -33,10 +35,15 @@ struct TileCfg {
   // (a partly idle chip runs at a higher clock); with two, iter_a while
   // every workgroup has a CU to itself and iter_b once two share one
   float fixed_us, level_us, iter_a_us, iter_b_us;
+  // the grid-size model's iteration cost when every one of the
+  // `occupancy` workgroup slots of each CU is busy, in units of c (a
+  // workgroup alone on its CU: 1), interpolated linearly in between
+  float c_shared = 1.f;
 };
 
-// Tile instances.  fp32: 128 x 128 x 32, 4 waves, two workgroups per CU.
-// fp16/bf16: instance 0, 256 x 256 x 64 with 8 waves and one workgroup per
+// Tile instances.  fp32: instance 0, 128 x 128 x 32, 4 waves, two
+// workgroups per CU; instance 1, 64 x 64 x 32, 4 waves, four per CU, for
+// shapes with few 128 x 128 tiles.  fp16/bf16: instance 0, 256 x 256 x 64 with 8 waves and one workgroup per
 // CU; instance 1, 128 x 128 x 64 with 4 waves and two per CU, for shapes
 // with few large tiles.  Model constants in units of one MAC iteration of
 // the instance.
@@ -49,8 +56,17 @@ inline TileCfg tile_cfg(int dtype, int inst = 0) {
     return TileCfg{bm, 256, 64, 512, 1, 4 * bm * 128, 4.f, 4.f * bm / 256, 1.f, 4.f * bm / 256, inst,
                    13.8f, 8.45f, 0.745f, 1.153f};
   }
-  // fp32: a 64 KiB partial costs about one and a half 32-deep iterations
-  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 2.f, 1.5f, 1.f, 1.5f, 0, 8.3f, 3.3f, 2.f, 2.f};
+  // fp32 constants measured on MI355X (1024-4096 cubes and one-wave
+  // data-parallel and split grids, fp32 row-major): 64 x 64 x 32, 4 waves,
+  // four workgroups per CU -- 0.68 us per iteration alone on a CU, 2.08 with
+  // four per CU (3.06 times), 2 us per exchange of a 16 KiB partial (three
+  // iterations), 5.5 us fixed
+  if (dtype == SK_F32 && inst == 1)
+    return TileCfg{64, 64, 32, 256, 4, 2 * 2 * 64 * 32 * 4, 8.f, 1.5f, 1.f, 1.5f, 1, 5.5f, 2.f, 0.68f, 2.08f, 3.06f};
+  // 128 x 128 x 32, two workgroups per CU -- 2.08 us per iteration alone,
+  // 3.79 with two per CU (1.82 times), 5 us per exchange of a 64 KiB
+  // partial (two and a half iterations), 12 us fixed
+  if (dtype == SK_F32) return TileCfg{128, 128, 32, 256, 2, 2 * 2 * 128 * 32 * 4, 6.f, 1.2f, 1.f, 1.2f, 0, 12.f, 5.f, 2.08f, 3.79f, 1.82f};
   // 128 x 128 fp16: a 64 KiB partial against a quarter of the large tile's
   // iteration work
   if (inst == 1) return TileCfg{128, 128, 64, 256, 2, 2 * 2 * 128 * 64 * 2, 4.f, 5.f, 1.f, 4.f, 1, 9.16f, 3.39f, 0.413f, 1.2f};

@@ -780,31 +780,40 @@ __device__ __forceinline__ void n_epilogue(const KernelArgs &a, bool vec_ok, int
 }
 
 // ============================================================== SGEMM
-// 128 x 128 x 32 tiles, 4 waves as 2 x 2, wave tile 64 x 64,
-// v_mfma_f32_16x16x4_f32: 4 x 4 blocks per wave.  Within a group of 16 k,
-// MFMA step q of lane group h = lane >> 4 multiplies k = 16 g + 4 h + q for
-// both operands; a k-major operand reads its 4 values with one 128-bit LDS
-// read, an mn-major operand reads one 32-bit value per step.
-struct SCfg {
-  static constexpr int BM = 128, BN = 128, BK = 32, NT = 256;
-  static constexpr int WTM = 64, WTN = 64, MB = 4, NB = 4, NACC = MB * NB;
+// TILE x TILE x 32 tiles, 4 waves as 2 x 2, wave tile TILE/2 x TILE/2,
+// v_mfma_f32_16x16x4_f32: (TILE/32)^2 blocks per wave.  Two instances:
+// 128 x 128 (4 x 4 blocks per wave, two workgroups per CU) and 64 x 64
+// (2 x 2 blocks, for shapes with few 128 x 128 tiles: 1024^3 is one 64 x 64
+// tile per CU with no partial exchange).  Within a group of 16 k, MFMA step
+// q of lane group h = lane >> 4 multiplies k = 16 g + 4 h + q for both
+// operands; a k-major operand reads its 4 values with one 128-bit LDS read,
+// an mn-major operand reads one 32-bit value per step.
+template <int TILE>
+struct SCfgT {
+  static_assert(TILE == 128 || TILE == 64, "fp32 tile");
+  static constexpr int BM = TILE, BN = TILE, BK = 32, NT = 256;
+  static constexpr int WTM = TILE / 2, WTN = TILE / 2, MB = WTM / 16, NB = WTN / 16, NACC = MB * NB;
   static constexpr int A_BYTES = BM * BK * 4, B_BYTES = BN * BK * 4;
   static constexpr int STAGE = A_BYTES + B_BYTES;
+  static constexpr int MN_ROW = TILE * 4;  // bytes of one k row of an mn-major slice
 };
+using SCfg = SCfgT<128>;  // the instance ABFT runs on
 
 // Direct-to-LDS loads of one operand's tile slices (fp32), with per-lane
 // offsets computed once per tile; each k-iteration advances a scalar base.
 //  k-major: BM rows (m or n) of BK fp32 (128 bytes), chunk c of row r at
 //    position c ^ ((r >> 1) & 7); one 1 KiB load covers 8 rows; the base
 //    of iteration kit is kit * BK * 4 bytes further.
-//  mn-major: BK rows (k) of 128 fp32 (512 bytes), chunk c of row k at
-//    position c ^ (4 * ((k >> 2) & 3)); one load covers 2 rows; the base
-//    advances kit * BK * ld * 4 bytes.
+//  mn-major: BK rows (k) of TILE fp32 (MN_ROW bytes), chunk c of row k at
+//    position c ^ (4 * ((k >> 2) & 3)); one load covers 1024 / MN_ROW rows;
+//    the base advances kit * BK * ld * 4 bytes.
 // Rows past the matrix (and, in the iteration holding the end of k, k
 // chunks or rows at or past k) are fetched out of range, i.e. as zeros.
-template <bool KMAJOR>
+template <class C, bool KMAJOR>
 struct SLoader {
-  static constexpr int LOADS = SCfg::BM * SCfg::BK * 4 / 1024 / (SCfg::NT / 64);
+  static constexpr int LOADS = C::BM * C::BK * 4 / 1024 / (C::NT / 64);
+  static constexpr int LPR = C::MN_ROW / 16;  // mn-major: lanes per k row
+  static_assert(LOADS >= 1 && 64 % LPR == 0, "fp32 staging");
   const char *base;     // element (mn0, 0) of the operand
   int64_t range;        // bytes from base to the end of the operand
   int64_t kstep;        // bytes the slice advances per k-iteration
@@ -820,7 +829,7 @@ struct SLoader {
     if (KMAJOR) {
       base = static_cast<const char *>(ptr) + (int64_t)mn0 * ldb;
       range = (int64_t)(mn_total - 1 - mn0) * ldb + (int64_t)k_ext * 4;
-      kstep = SCfg::BK * 4;
+      kstep = C::BK * 4;
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) {
         const int row = (w * LOADS + j) * 8 + (lane >> 3);
@@ -831,11 +840,11 @@ struct SLoader {
     } else {
       base = static_cast<const char *>(ptr) + (int64_t)mn0 * 4;
       range = (int64_t)(k_total - 1) * ldb + (int64_t)(mn_total - mn0) * 4;
-      kstep = SCfg::BK * ldb;
+      kstep = C::BK * ldb;
 #pragma unroll
       for (int j = 0; j < LOADS; ++j) {
-        const int kr = (w * LOADS + j) * 2 + (lane >> 5);
-        const int c = (lane & 31) ^ (4 * ((kr >> 2) & 3));
+        const int kr = (w * LOADS + j) * (64 / LPR) + lane / LPR;
+        const int c = (lane % LPR) ^ (4 * ((kr >> 2) & 3));
         key[j] = kr;
         v[j] = c * 4 < mn_total - mn0 ? (uint32_t)(kr * ldb + c * 16) : kOOB;
       }
@@ -848,9 +857,9 @@ struct SLoader {
   __device__ __forceinline__ void load(int lds_off, int kit, int k_total) const {
     const int64_t adv = (int64_t)kit * kstep;
     const __amdgpu_buffer_rsrc_t r = make_rsrc(base + adv, range - adv);
-    const int left = k_total - kit * SCfg::BK;  // k values from the slice start
+    const int left = k_total - kit * C::BK;  // k values from the slice start
     const int dst = lds_off + lds_first;
-    if (left >= SCfg::BK) {
+    if (left >= C::BK) {
 #pragma unroll
       for (int j = 0; j < LOADS; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_vptr)(smem + dst + j * 1024), 16, v[j], 0, 0, 0);
@@ -866,55 +875,57 @@ struct SLoader {
 };
 
 // Element (mn, k) of an mn-major fp32 stage area.
+template <class C>
 __device__ __forceinline__ float s_mn_elem(int base_off, int mn, int k) {
   const int c = mn >> 2, e = mn & 3;
   const int p = c ^ (4 * ((k >> 2) & 3));
-  return *reinterpret_cast<const float *>(smem + base_off + k * 512 + p * 16 + e * 4);
+  return *reinterpret_cast<const float *>(smem + base_off + k * C::MN_ROW + p * 16 + e * 4);
 }
 
 // Fragments of k-group g (16 values of k) of an LDS stage.  Within the
 // group, MFMA step q of lane group h = lane >> 4 multiplies k = 16 g + 4 h + q
 // for both operands: a k-major operand reads its four values with one
 // 128-bit LDS read, an mn-major operand with one 32-bit read per step.
-template <bool AK, bool BKM>
-__device__ __forceinline__ void s_frags(int stage, int g, int wm, int wn, f4_t (&av)[SCfg::MB],
-                                        f4_t (&bv)[SCfg::NB]) {
+template <class C, bool AK, bool BKM>
+__device__ __forceinline__ void s_frags(int stage, int g, int wm, int wn, f4_t (&av)[C::MB],
+                                        f4_t (&bv)[C::NB]) {
   const int lane = threadIdx.x & 63;
-  const int As = stage * SCfg::STAGE, Bs = As + SCfg::A_BYTES;
+  const int As = stage * C::STAGE, Bs = As + C::A_BYTES;
   const int h = lane >> 4, li = lane & 15;
   const int c = 4 * g + h;
 #pragma unroll
-  for (int mb = 0; mb < SCfg::MB; ++mb) {
-    const int mn = wm * SCfg::WTM + mb * 16 + li;
+  for (int mb = 0; mb < C::MB; ++mb) {
+    const int mn = wm * C::WTM + mb * 16 + li;
     if (AK) {
       av[mb] = *reinterpret_cast<const f4_t *>(smem + As + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4));
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) av[mb][q] = s_mn_elem(As, mn, 16 * g + 4 * h + q);
+      for (int q = 0; q < 4; ++q) av[mb][q] = s_mn_elem<C>(As, mn, 16 * g + 4 * h + q);
     }
   }
 #pragma unroll
-  for (int nb = 0; nb < SCfg::NB; ++nb) {
-    const int mn = wn * SCfg::WTN + nb * 16 + li;
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int mn = wn * C::WTN + nb * 16 + li;
     if (BKM) {
       bv[nb] = *reinterpret_cast<const f4_t *>(smem + Bs + mn * 128 + ((c ^ ((mn >> 1) & 7)) << 4));
     } else {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) bv[nb][q] = s_mn_elem(Bs, mn, 16 * g + 4 * h + q);
+      for (int q = 0; q < 4; ++q) bv[nb][q] = s_mn_elem<C>(Bs, mn, 16 * g + 4 * h + q);
     }
   }
 }
 
-__device__ __forceinline__ void s_mfmas(const f4_t (&av)[SCfg::MB], const f4_t (&bv)[SCfg::NB],
-                                        f4_t (&acc)[SCfg::NACC]) {
+template <class C>
+__device__ __forceinline__ void s_mfmas(const f4_t (&av)[C::MB], const f4_t (&bv)[C::NB],
+                                        f4_t (&acc)[C::NACC]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int mb = 0; mb < SCfg::MB; ++mb)
+    for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < SCfg::NB; ++nb)
-        acc[mb * SCfg::NB + nb] =
-            __builtin_amdgcn_mfma_f32_16x16x4f32(bv[nb][q], av[mb][q], acc[mb * SCfg::NB + nb], 0, 0, 0);
+      for (int nb = 0; nb < C::NB; ++nb)
+        acc[mb * C::NB + nb] =
+            __builtin_amdgcn_mfma_f32_16x16x4f32(bv[nb][q], av[mb][q], acc[mb * C::NB + nb], 0, 0, 0);
 }
 
 // ---------------------------------------------------------------- ABFT
@@ -995,9 +1006,10 @@ __device__ __forceinline__ void abft_fma(const f4_t (&x)[4], f4_t e, AbftPart &p
 // among the MFMAs they slow the group down).  The empty asm takes the
 // checksums as operands, so that the compiler cannot sink the FMAs below the
 // group.
-template <bool ABFT>
-__device__ __forceinline__ void s_group(const f4_t (&av)[SCfg::MB], const f4_t (&bv)[SCfg::NB],
-                                        f4_t (&acc)[SCfg::NACC], bool rows, f4_t e, AbftPart &pt) {
+template <class C, bool ABFT>
+__device__ __forceinline__ void s_group(const f4_t (&av)[C::MB], const f4_t (&bv)[C::NB],
+                                        f4_t (&acc)[C::NACC], bool rows, f4_t e, AbftPart &pt) {
+  static_assert(!ABFT || C::BM == SCfg::BM, "ABFT runs on the 128 x 128 instance");
   if constexpr (ABFT) {
     if (rows)  // uniform over the wave
       abft_fma(av, e, pt);
@@ -1006,7 +1018,7 @@ __device__ __forceinline__ void s_group(const f4_t (&av)[SCfg::MB], const f4_t (
     asm volatile("" : "+v"(pt.c[0]), "+v"(pt.c[1]), "+v"(pt.c[2]), "+v"(pt.c[3]));
     __builtin_amdgcn_sched_barrier(0);
   }
-  s_mfmas(av, bv, acc);
+  s_mfmas<C>(av, bv, acc);
 }
 
 __device__ __forceinline__ void abft_record(const KernelArgs &a, int64_t row, int64_t col, float delta,
@@ -1187,13 +1199,13 @@ __device__ __forceinline__ void abft_verify(const KernelArgs &a, AbftLds &L, con
 // iteration i+2 into this stage's buffer and read group 0 of the next stage
 // while the MFMAs of group 1 run.  ABFT: each group's checksum FMAs run
 // just before its MFMAs, from the same fragments.
-template <bool AK, bool BKM, bool ABFT>
+template <class C, bool AK, bool BKM, bool ABFT>
 __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, int lb, int le,
-                                          f4_t (&acc)[SCfg::NACC]) {
+                                          f4_t (&acc)[C::NACC]) {
   const int w = wave_id();
   const int wm = w / 2, wn = w % 2;
 #pragma unroll
-  for (int i = 0; i < SCfg::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < C::NACC; ++i) acc[i] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int n = le - lb;
   if (n <= 0) return;
   AbftPart pt{};
@@ -1207,25 +1219,25 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
   float ev = 0.f, ev1 = 0.f;
   if constexpr (ABFT) {
     const int lane = threadIdx.x & 63;
-    esrc = (lane < 32 ? a.enc_a + (int64_t)(m0 / SCfg::BM) * a.enc_kb * 32
-                      : a.enc_b + (int64_t)(n0 / SCfg::BN) * a.enc_kb * 32) + (lane & 31);
+    esrc = (lane < 32 ? a.enc_a + (int64_t)(m0 / C::BM) * a.enc_kb * 32
+                      : a.enc_b + (int64_t)(n0 / C::BN) * a.enc_kb * 32) + (lane & 31);
     if (enc_lane) {
       ev = esrc[(int64_t)lb * 32];
       if (n > 1) ev1 = esrc[(int64_t)(lb + 1) * 32];
     }
   }
-  SLoader<AK> la;
-  SLoader<BKM> lbd;
+  SLoader<C, AK> la;
+  SLoader<C, BKM> lbd;
   la.init(a.A, a.lda, m0, a.m, a.k, a.a_kext);
   lbd.init(a.B, a.ldb, n0, a.n, a.k, a.b_kext);
   auto load = [&](int stage, int kit) {
-    la.load(stage * SCfg::STAGE, kit, a.k);
-    lbd.load(stage * SCfg::STAGE + SCfg::A_BYTES, kit, a.k);
+    la.load(stage * C::STAGE, kit, a.k);
+    lbd.load(stage * C::STAGE + C::A_BYTES, kit, a.k);
   };
   load(0, lb);
   if (n > 1) {
     load(1, lb + 1);
-    __builtin_amdgcn_s_waitcnt(vmcnt_le(SLoader<AK>::LOADS + SLoader<BKM>::LOADS));
+    __builtin_amdgcn_s_waitcnt(vmcnt_le(SLoader<C, AK>::LOADS + SLoader<C, BKM>::LOADS));
   } else {
     __builtin_amdgcn_s_waitcnt(0);
   }
@@ -1237,8 +1249,8 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
     }
   }
   __syncthreads();
-  f4_t a0[SCfg::MB], b0[SCfg::NB], a1[SCfg::MB], b1[SCfg::NB];
-  s_frags<AK, BKM>(0, 0, wm, wn, a0, b0);
+  f4_t a0[C::MB], b0[C::NB], a1[C::MB], b1[C::NB];
+  s_frags<C, AK, BKM>(0, 0, wm, wn, a0, b0);
   int buf = 0;
   const bool rows = abft_rows_wave(wm, wn);
   f4_t e0{}, e1{};  // ABFT: the wave's encodings for the two k-groups of this stage
@@ -1250,9 +1262,9 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
       e0 = abft_read_e(abft_lds(), buf, 0, rows);
       e1 = abft_read_e(abft_lds(), buf, 1, rows);
     }
-    s_frags<AK, BKM>(buf, 1, wm, wn, a1, b1);
+    s_frags<C, AK, BKM>(buf, 1, wm, wn, a1, b1);
     __builtin_amdgcn_sched_barrier(0);
-    s_group<ABFT>(a0, b0, acc, rows, e0, pt);
+    s_group<C, ABFT>(a0, b0, acc, rows, e0, pt);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (ABFT) {
@@ -1267,60 +1279,62 @@ __device__ __forceinline__ void s_macloop(const KernelArgs &a, int m0, int n0, i
         if (enc_lane) ev = esrc[(int64_t)(lb + i + 2) * 32];
       }
     }
-    if (i + 1 < n) s_frags<AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
+    if (i + 1 < n) s_frags<C, AK, BKM>(buf ^ 1, 0, wm, wn, a0, b0);
     __builtin_amdgcn_sched_barrier(0);
-    s_group<ABFT>(a1, b1, acc, rows, e1, pt);
+    s_group<C, ABFT>(a1, b1, acc, rows, e1, pt);
     __builtin_amdgcn_sched_barrier(0);
     buf ^= 1;
   }
   if constexpr (ABFT) abft_verify(a, abft_lds(), pt, acc, m0, n0, lb, le);
 }
 
-template <bool AK, bool BKM>
+template <int TILE>
 struct SPolicy {
-  static constexpr int BM = SCfg::BM, BN = SCfg::BN, NT = SCfg::NT;
-  static constexpr int NACC4 = SCfg::NACC;
-  static constexpr int LDS_BYTES = 2 * SCfg::STAGE;
-  struct Acc { f4_t v[SCfg::NACC]; };
+  using C = SCfgT<TILE>;
+  static constexpr int BM = C::BM, BN = C::BN, NT = C::NT;
+  static constexpr int NACC4 = C::NACC;
+  static constexpr int LDS_BYTES = 2 * C::STAGE;
+  struct Acc { f4_t v[C::NACC]; };
   static __device__ __forceinline__ f4_t get4(const Acc &c, int i) { return c.v[i]; }
   static __device__ __forceinline__ void add4(Acc &c, int i, f4_t x) { c.v[i] += x; }
 };
 
 // 16x16 block layout (SGEMM): lane l of a wave holds, for block (mb, nb),
 // row (l & 15) and columns 4*(l >> 4) + {0..3} of the block.
-template <bool AK, bool BKM>
+template <int TILE>
 __device__ __forceinline__ void s_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
-                                           const typename SPolicy<AK, BKM>::Acc &acc) {
+                                           const typename SPolicy<TILE>::Acc &acc) {
+  using C = SCfgT<TILE>;
   const int w = wave_id(), lane = threadIdx.x & 63;
-  constexpr int WN = SCfg::BN / SCfg::WTN;
-  const int r0 = m0 + (w / WN) * SCfg::WTM, c0 = n0 + (w % WN) * SCfg::WTN;
+  constexpr int WN = C::BN / C::WTN;
+  const int r0 = m0 + (w / WN) * C::WTM, c0 = n0 + (w % WN) * C::WTN;
   // a tile wholly inside C: straight-line stores (as in the HGEMM epilogue)
-  if (vec_ok && m0 + SCfg::BM <= a.m && n0 + SCfg::BN <= a.n) {
+  if (vec_ok && m0 + C::BM <= a.m && n0 + C::BN <= a.n) {
     float *cb = static_cast<float *>(a.C) + (int64_t)(r0 + (lane & 15)) * a.ldc + c0 + 4 * (lane >> 4);
     const int64_t rstep = (int64_t)16 * a.ldc;
     if (a.beta == 0.f) {
 #pragma unroll
-      for (int mb = 0; mb < SCfg::MB; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < SCfg::NB; ++nb)
-          Elem<SK_F32>::st4(cb + mb * rstep, nb * 16, a.alpha * acc.v[mb * SCfg::NB + nb]);
+        for (int nb = 0; nb < C::NB; ++nb)
+          Elem<SK_F32>::st4(cb + mb * rstep, nb * 16, a.alpha * acc.v[mb * C::NB + nb]);
     } else {
 #pragma unroll
-      for (int mb = 0; mb < SCfg::MB; ++mb)
+      for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < SCfg::NB; ++nb) {
+        for (int nb = 0; nb < C::NB; ++nb) {
           float *q = cb + mb * rstep;
-          Elem<SK_F32>::st4(q, nb * 16, a.alpha * acc.v[mb * SCfg::NB + nb] + a.beta * Elem<SK_F32>::ld4(q, nb * 16));
+          Elem<SK_F32>::st4(q, nb * 16, a.alpha * acc.v[mb * C::NB + nb] + a.beta * Elem<SK_F32>::ld4(q, nb * 16));
         }
     }
     return;
   }
 #pragma unroll
-  for (int mb = 0; mb < SCfg::MB; ++mb)
+  for (int mb = 0; mb < C::MB; ++mb)
 #pragma unroll
-    for (int nb = 0; nb < SCfg::NB; ++nb)
+    for (int nb = 0; nb < C::NB; ++nb)
       store4<SK_F32>(a, vec_ok, r0 + mb * 16 + (lane & 15), c0 + nb * 16 + 4 * (lane >> 4),
-                     acc.v[mb * SCfg::NB + nb]);
+                     acc.v[mb * C::NB + nb]);
 }
 
 // ======================================================= work iteration
@@ -1412,15 +1426,15 @@ __global__ __launch_bounds__(P::NT, 1) void ngemm_kernel(KernelArgs a, int vec_o
       [&](int m0, int n0, const typename P::Acc &acc) { n_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
 }
 
-template <bool AK, bool BKM, bool ABFT>
-__global__ __launch_bounds__(SCfg::NT, 2) void sgemm_kernel(KernelArgs a, int vec_ok) {
-  using P = SPolicy<AK, BKM>;
+template <int TILE, bool AK, bool BKM, bool ABFT>
+__global__ __launch_bounds__(SCfgT<TILE>::NT, TILE == 128 ? 2 : 4) void sgemm_kernel(KernelArgs a, int vec_ok) {
+  using P = SPolicy<TILE>;
   run_workgroup<P>(
       a,
       [&](int m0, int n0, int lb, int le, typename P::Acc &acc) {
-        s_macloop<AK, BKM, ABFT>(a, m0, n0, lb, le, acc.v);
+        s_macloop<typename P::C, AK, BKM, ABFT>(a, m0, n0, lb, le, acc.v);
       },
-      [&](int m0, int n0, const typename P::Acc &acc) { s_epilogue<AK, BKM>(a, vec_ok != 0, m0, n0, acc); });
+      [&](int m0, int n0, const typename P::Acc &acc) { s_epilogue<TILE>(a, vec_ok != 0, m0, n0, acc); });
 }
 
 // ========================================================= small kernels
@@ -1649,19 +1663,26 @@ static bool c_vec_ok(const KernelArgs &a, int dtype) {
   return (reinterpret_cast<uintptr_t>(a.C) % align == 0) && (a.ldc % 4 == 0);
 }
 
-// Entry point of the fp32 kernel for the operands' storage orders and mode.
-static const void *sgemm_entry(bool ak, bool bk, bool abft) {
+// Entry point of the fp32 kernel for the tile instance (0: 128 x 128, 1:
+// 64 x 64, no ABFT), the operands' storage orders and the mode.
+static const void *sgemm_entry(int inst, bool ak, bool bk, bool abft) {
   using namespace dev;
-  if (abft) {
-    if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<true, true, true>);
-    if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<true, false, true>);
-    if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<false, true, true>);
-    return reinterpret_cast<const void *>(&sgemm_kernel<false, false, true>);
+  if (inst == 1) {
+    if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<64, true, true, false>);
+    if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<64, true, false, false>);
+    if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<64, false, true, false>);
+    return reinterpret_cast<const void *>(&sgemm_kernel<64, false, false, false>);
   }
-  if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<true, true, false>);
-  if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<true, false, false>);
-  if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<false, true, false>);
-  return reinterpret_cast<const void *>(&sgemm_kernel<false, false, false>);
+  if (abft) {
+    if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<128, true, true, true>);
+    if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<128, true, false, true>);
+    if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<128, false, true, true>);
+    return reinterpret_cast<const void *>(&sgemm_kernel<128, false, false, true>);
+  }
+  if (ak && bk) return reinterpret_cast<const void *>(&sgemm_kernel<128, true, true, false>);
+  if (ak) return reinterpret_cast<const void *>(&sgemm_kernel<128, true, false, false>);
+  if (bk) return reinterpret_cast<const void *>(&sgemm_kernel<128, false, true, false>);
+  return reinterpret_cast<const void *>(&sgemm_kernel<128, false, false, false>);
 }
 
 // Entry point of an fp16/bf16 tile instance.
@@ -1691,7 +1712,7 @@ int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
   const size_t lds = p.cfg.lds_bytes;
   const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst)
-                                    : sgemm_entry(a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
+                                    : sgemm_entry(p.cfg.inst, a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
   void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
   return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
 }
@@ -1750,7 +1771,7 @@ int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu) {
     // smallest occupancy among them
     nb = 1 << 20;
     for (int i = 0; i < 4 && e == hipSuccess; ++i) {
-      const void *f = sgemm_entry(i & 1, (i >> 1) & 1, abft);
+      const void *f = sgemm_entry(inst, i & 1, (i >> 1) & 1, abft);
       e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
       int o = 0;
       if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, f, c.threads, c.lds_bytes);

@@ -62,6 +62,17 @@ namespace sk {
 
 static inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Iteration cost of a grid of g workgroups relative to a workgroup alone on
+// its CU: the instance's c_shared once every slot of a CU is busy, linear in
+// the workgroups per CU in between (the dispatcher spreads a grid over the
+// CUs before it doubles up).
+static double share(const TileCfg &c, int slots, int64_t g) {
+  if (c.occupancy <= 1) return 1.0;
+  const int64_t cus = std::max<int64_t>(1, slots / c.occupancy);
+  const int64_t j = std::min<int64_t>(c.occupancy, cdiv(g, cus));
+  return 1.0 + (c.c_shared - 1.0) * (double)(j - 1) / (c.occupancy - 1);
+}
+
 bool operand_direct(int dtype, bool kmajor, const void *ptr, int64_t ld, int64_t k) {
   const int64_t es = dtype == SK_F32 ? 4 : 2;
   const int64_t vec = 16 / es;  // elements per 128-bit load
@@ -98,7 +109,8 @@ static int split_peers(int64_t tiles, int64_t ipt, int64_t g, bool *any_split) {
 // split unless every workgroup boundary falls on a tile boundary, and a tile
 // of ipt iterations meets at most ceil((ipt - 1) / q) + 1 workgroups whose
 // ranges hold at least q iterations.
-static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, float c, float d) {
+static int64_t model_grid(const TileCfg &cfg, int64_t t, int64_t ipt, int slots, float a, float b, float c,
+                          float d) {
   const int64_t total = t * ipt;
   int64_t hi = std::min<int64_t>(slots, total);
   if (hi <= t) return t;
@@ -108,7 +120,7 @@ static int64_t model_grid(int64_t t, int64_t ipt, int slots, float a, float b, f
     const int64_t q = total / g, r = total % g;
     const bool split = !(r == 0 && q % ipt == 0);
     const int64_t peers = split ? std::max<int64_t>(1, cdiv(ipt - 1, q)) : 0;
-    const double T = a + (split ? b : 0.0) + c * (double)cdiv(total, g) + d * (double)peers;
+    const double T = a + (split ? b : 0.0) + c * (double)cdiv(total, g) * share(cfg, slots, g) + d * (double)peers;
     if (T < best - 1e-9) { best = T; best_g = g; }
   }
   return best_g;
@@ -139,8 +151,8 @@ static void aligned_wave(int64_t sk_tiles, int64_t ipt, int slots, int *D_out, i
 
 // XCD-aware schedule below one wave: D (multiple of 8 dividing p) and s by
 // the runtime model with g = D * ceil(t / s) workgroups.
-static double aligned_small(int64_t t, int64_t ipt, int slots, float a, float b, float c, float d, int *D_out,
-                            int *s_out) {
+static double aligned_small(const TileCfg &cfg, int64_t t, int64_t ipt, int slots, float a, float b, float c,
+                            float d, int *D_out, int *s_out) {
   double best = 1e300;
   for (int64_t D = 8; D <= slots; D *= 2) {
     if (slots % D) continue;
@@ -161,7 +173,7 @@ static double aligned_small(int64_t t, int64_t ipt, int slots, float a, float b,
       }
       int64_t levels = 0;
       while (((int64_t)1 << levels) < pieces) ++levels;
-      const double T = (a + c * (double)work + (b + d) * (double)levels) * phase_charge(D);
+      const double T = (a + c * (double)work * share(cfg, slots, D * J) + (b + d) * (double)levels) * phase_charge(D);
       if (T < best - 1e-9) { best = T; *D_out = (int)D; *s_out = (int)s; }
     }
   }
@@ -263,7 +275,7 @@ static int plan_inst(const sk_gemm_desc &d, const sk_options &o, int inst, int s
         sk_tiles = 0;
         break;
       case SK_SCHED_SK_BASIC:
-        grid = P.tiles >= slots ? slots : model_grid(P.tiles, P.ipt, slots, ma, mb, mc, md);
+        grid = P.tiles >= slots ? slots : model_grid(c, P.tiles, P.ipt, slots, ma, mb, mc, md);
         sk_tiles = P.tiles;
         break;
       case SK_SCHED_SK_HYBRID2:
@@ -278,15 +290,16 @@ static int plan_inst(const sk_gemm_desc &d, const sk_options &o, int inst, int s
         P.group_rows = 8;
         int D = 0, s = 0;
         if (P.w == 0) {
-          const double t_al = aligned_small(P.tiles, P.ipt, slots, ma, mb, mc, md, &D, &s);
+          const double t_al = aligned_small(c, P.tiles, P.ipt, slots, ma, mb, mc, md, &D, &s);
           // the data-parallel form: one tile per workgroup.  Below a wave it
           // leaves p - t CUs idle and the busy ones then run at a higher
           // clock, so the split must also promise at least 15 % fewer
           // iterations per workgroup (measured on the fp16 shape sweep:
           // splits promising 10 % ran 7 % slower than the single wave)
-          const double t_dp = ma + mc * (double)P.ipt;
-          const double work = (double)cdiv((int64_t)s * P.ipt, D);
-          if (o.schedule == SK_SCHED_AUTO && (t_dp <= t_al || (double)P.ipt < kSmallGain * work)) D = 0;
+          const double dp_iter = (double)P.ipt * share(c, slots, P.tiles);
+          const double t_dp = ma + mc * dp_iter;
+          const double work = (double)cdiv((int64_t)s * P.ipt, D) * share(c, slots, (int64_t)D * cdiv(P.tiles, s));
+          if (o.schedule == SK_SCHED_AUTO && (t_dp <= t_al || dp_iter < kSmallGain * work)) D = 0;
         } else if (P.r > 0) {
           sk_tiles = P.w >= min_waves ? P.r + slots : P.tiles;
           aligned_wave(sk_tiles, P.ipt, slots, &D, &s);
@@ -368,8 +381,12 @@ double plan_cost_us(const Plan &P) {
       levels = (double)(pieces - 1);
     }
   }
-  const double iter = c.occupancy == 1 ? c.iter_a_us + c.iter_b_us * (double)P.grid / P.slots
-                                       : (P.grid * c.occupancy <= P.slots ? c.iter_a_us : c.iter_b_us);
+  double iter = c.iter_a_us + c.iter_b_us * (double)P.grid / P.slots;
+  if (c.occupancy > 1) {  // iter_a with a CU to itself, iter_b with every slot busy
+    const int64_t cus = std::max<int64_t>(1, P.slots / c.occupancy);
+    const int64_t j = std::min<int64_t>(c.occupancy, cdiv(P.grid, cus));
+    iter = c.iter_a_us + (c.iter_b_us - c.iter_a_us) * (double)(j - 1) / (c.occupancy - 1);
+  }
   return c.fixed_us + iter * work + c.level_us * levels;
 }
 
@@ -413,7 +430,10 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[3], Pl
   // 32-bit indices inside the kernels
   if (d.m > INT32_MAX / 2 || d.n > INT32_MAX / 2 || d.k > INT32_MAX / 2) return SK_ERR_UNSUPPORTED;
   // a forced grid is a count of large-tile workgroups unless a tile is given
-  if (d.dtype == SK_F32 || o.tile == SK_TILE_LARGE || (o.tile == SK_TILE_AUTO && o.forced_grid > 0))
+  // fp32: no narrow-m instance, and ABFT runs on the 128 x 128 tile only
+  const bool f32 = d.dtype == SK_F32;
+  if (f32 && (o.tile == SK_TILE_NARROW || (o.abft && o.tile == SK_TILE_SMALL))) return SK_ERR_UNSUPPORTED;
+  if ((f32 && o.abft) || o.tile == SK_TILE_LARGE || (o.tile == SK_TILE_AUTO && o.forced_grid > 0))
     return forced_grid_ok(plan_inst(d, o, 0, slots[0], P), P);
   if (o.tile == SK_TILE_SMALL) return forced_grid_ok(plan_inst(d, o, 1, slots[1], P), P);
   if (o.tile == SK_TILE_NARROW) {
@@ -423,7 +443,7 @@ int make_plan(const sk_gemm_desc &d, const sk_options &o, const int slots[3], Pl
   // AUTO: whichever instance the model predicts faster (cached per shape
   // class); measured on the fp16 shape sweep, the small tile wins on most
   // shapes below one wave of large tiles and on short-k shapes up to about
-  // two waves, the large one on long-k and large shapes
+  // two waves, the large one on long-k and large shapes (fp32 likewise)
   int rc = plan_inst(d, o, 0, slots[0], P);
   if (rc != SK_OK || P.tiles == 0 || P.ipt == 0) return rc;
   const InstKey key{d.dtype, cdiv(d.m, 128), cdiv(d.n, 128), P.ipt, slots[0], slots[1], o.schedule,
