@@ -46,13 +46,13 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "3aadad1ea2f71899",
+TRAFFIC = {"kernel_hash": "f44abba16b420c29",
            # mean over the six launches of one step (1024^3 ... 6144^3)
-           "sgemm-sweep": 1143011265,
+           "sgemm-sweep": 1170329025,
            # fp16 8192^3 launch
-           "hgemm-8192": 1775364986,
+           "hgemm-8192": 1790078446,
            # bf16 8192^3 launch (same counter runs)
-           "hgemm-8192-bf16": 1763934350}
+           "hgemm-8192-bf16": 1764158922}
 
 
 def kernel_hash():
