@@ -510,12 +510,14 @@ __device__ __forceinline__ void h_macloop_la2(const KernelArgs &a, int m0, int n
   __syncthreads();
 }
 
-// Epilogue of one tile.  A tile that lies wholly inside C is written with
-// beta == 0 through LDS in whole cache lines (C 16-byte aligned, ldc a
-// multiple of 8), else, with rows that allow 4-element vector accesses, by
-// straight-line accesses; edge tiles take the per-element bounds checks of
-// store4.
-template <class P>
+// Epilogue of one tile.  A tile that lies wholly inside C (16-byte aligned,
+// ldc a multiple of 8) is written through LDS in whole cache lines, else,
+// with rows that allow 4-element vector accesses, by straight-line accesses;
+// edge tiles take the per-element bounds checks of store4.  The kernel is
+// built twice: BZ for beta == 0 (C never read) and !BZ for beta != 0, so
+// that neither carries the other's staging code (the beta != 0 staging
+// would otherwise cost the beta == 0 kernel registers and start-up time).
+template <class P, bool BZ>
 __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int m0, int n0,
                                            const typename P::Acc &acc) {
   using T = typename Elem<P::ET>::T;
@@ -562,9 +564,62 @@ __device__ __forceinline__ void h_epilogue(const KernelArgs &a, bool vec_ok, int
     __syncthreads();
     return;
   }
+  if constexpr (!BZ) {
+  if (full && reinterpret_cast<uintptr_t>(a.C) % 16 == 0 && a.ldc % 8 == 0) {
+    // beta != 0: alpha * acc goes through LDS in fp32, one 32-row block of
+    // the wave at a time, and is read back as whole rows (8 columns per
+    // lane) beside 16-byte loads and stores of C that cover whole cache
+    // lines (the MFMA layout would touch 32 rows per access); alpha * acc +
+    // beta * C is rounded once, as on the other paths.  Rows of RS = 4 WTN +
+    // 16 bytes: the 8 lanes of one LDS cycle of a 16-byte write (8 rows)
+    // start on distinct 4-bank groups.  Same region and barrier rules as
+    // above.
+    using V8 = typename Elem<P::ET>::V8;
+    constexpr int RS = P::WTN * 4 + 16;
+    constexpr int LPR = P::WTN / 8, RPI = 64 / LPR;  // lanes per row, rows per read
+    static_assert(P::NT / 64 * 32 * RS <= P::LDS_BYTES && 32 % RPI == 0, "epilogue staging");
+    // the lane index made opaque here, so that these addresses are formed
+    // here and not hoisted out of the tile loop (where they would hold
+    // registers through the MAC loop)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    char *const wr = smem + w * (32 * RS) + (ln & 31) * RS + 16 * (ln >> 5);
+    const char *const rd = smem + w * (32 * RS) + (ln / LPR) * RS + (ln % LPR) * 32;
+    T *cp = static_cast<T *>(a.C) + (int64_t)(r0 + ln / LPR) * a.ldc + c0 + (ln % LPR) * 8;
+    const int64_t step = (int64_t)RPI * a.ldc;
+#pragma unroll
+    for (int mb = 0; mb < P::MB; ++mb) {
+#pragma unroll
+      for (int nb = 0; nb < P::NB; ++nb)
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          *reinterpret_cast<f4_t *>(wr + (nb * 32 + 8 * g) * 4) = a.alpha * P::get4(acc, (mb * P::NB + nb) * 4 + g);
+      // one row group at a time (a rolled loop: the accumulators of the
+      // other blocks leave no registers for several in flight)
+#pragma unroll 1
+      for (int it = 0; it < 32 / RPI; ++it) {
+        const char *rp = rd + it * RPI * RS;
+        const f4_t x0 = *reinterpret_cast<const f4_t *>(rp), x1 = *reinterpret_cast<const f4_t *>(rp + 16);
+        T *const q = cp;
+        cp += step;
+        const V8 c = *reinterpret_cast<const V8 *>(q);
+        V8 o;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          o[e] = (T)(x0[e] + a.beta * (float)c[e]);
+          o[e + 4] = (T)(x1[e] + a.beta * (float)c[e + 4]);
+        }
+        *reinterpret_cast<V8 *>(q) = o;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads returned
+    __syncthreads();
+    return;
+  }
+  }
   if (vec_ok && full) {
-    // beta != 0 (or C rows not 16-byte aligned): straight-line 4-element
-    // accesses at fixed offsets from one row pointer per 32-row block
+    // C rows not 16-byte aligned: straight-line 4-element accesses at fixed
+    // offsets from one row pointer per 32-row block
     T *cb = static_cast<T *>(a.C) + (int64_t)(r0 + (lane & 31)) * a.ldc + c0 + 4 * (lane >> 5);
     const int64_t rstep = (int64_t)32 * a.ldc;
 #pragma unroll
@@ -1412,11 +1467,11 @@ __device__ __forceinline__ void run_workgroup(const KernelArgs &a, MacLoop maclo
   while (sched_next(S, I, g)) run_segment<P>(a, S, x, g, macloop, epilogue);
 }
 
-template <class P>
+template <class P, bool BZ>
 __global__ __launch_bounds__(P::NT, P::WPE) void hgemm_kernel(KernelArgs a, int vec_ok) {
   run_workgroup<P>(
       a, [&](int m0, int n0, int lb, int le, typename P::Acc &acc) { h_macloop_la2<P>(a, m0, n0, lb, le, acc); },
-      [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<P>(a, vec_ok != 0, m0, n0, acc); });
+      [&](int m0, int n0, const typename P::Acc &acc) { h_epilogue<P, BZ>(a, vec_ok != 0, m0, n0, acc); });
 }
 
 template <class P>
@@ -1697,21 +1752,24 @@ static const void *ngemm_entry(int inst) {
   }
 }
 
-static const void *hgemm_entry(int dtype, int inst) {
+template <int DT, int TILE>
+static const void *hgemm_entry_bz(bool beta_zero) {
   using namespace dev;
+  return beta_zero ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<DT, TILE>, true>)
+                   : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<DT, TILE>, false>);
+}
+
+static const void *hgemm_entry(int dtype, int inst, bool beta_zero) {
   if (inst >= 2) return dtype == SK_F16 ? ngemm_entry<SK_F16>(inst) : ngemm_entry<SK_BF16>(inst);
-  if (inst == 1)
-    return dtype == SK_F16 ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_F16, 128>>)
-                           : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_BF16, 128>>);
-  return dtype == SK_F16 ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_F16, 256>>)
-                         : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<SK_BF16, 256>>);
+  if (inst == 1) return dtype == SK_F16 ? hgemm_entry_bz<SK_F16, 128>(beta_zero) : hgemm_entry_bz<SK_BF16, 128>(beta_zero);
+  return dtype == SK_F16 ? hgemm_entry_bz<SK_F16, 256>(beta_zero) : hgemm_entry_bz<SK_BF16, 256>(beta_zero);
 }
 
 int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   dim3 grid(p.grid), block(p.cfg.threads);
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
   const size_t lds = p.cfg.lds_bytes;
-  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst)
+  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst, a.beta == 0.f)
                                     : sgemm_entry(p.cfg.inst, a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
   void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
   return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
@@ -1778,9 +1836,15 @@ int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu) {
       if (o < nb) nb = o;
     }
   } else {
-    const void *f = hgemm_entry(dtype, inst);
-    e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
-    if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, f, c.threads, c.lds_bytes);
+    // both beta forms: the smaller occupancy
+    nb = 1 << 20;
+    for (int bz = 0; bz < 2 && e == hipSuccess; ++bz) {
+      const void *f = hgemm_entry(dtype, inst, bz != 0);
+      e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
+      int o = 0;
+      if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, f, c.threads, c.lds_bytes);
+      if (o < nb) nb = o;
+    }
   }
   *blocks_per_cu = nb;
   return (int)e;
