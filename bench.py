@@ -46,13 +46,13 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "f44abba16b420c29",
+TRAFFIC = {"kernel_hash": "a1d7da478bc01aa8",
            # mean over the six launches of one step (1024^3 ... 6144^3)
-           "sgemm-sweep": 1170329025,
+           "sgemm-sweep": 1170550910,
            # fp16 8192^3 launch
-           "hgemm-8192": 1790078446,
+           "hgemm-8192": 1775136510,
            # bf16 8192^3 launch (same counter runs)
-           "hgemm-8192-bf16": 1764158922}
+           "hgemm-8192-bf16": 1764242395}
 
 
 def kernel_hash():
@@ -783,6 +783,65 @@ def sweep_summary(rows, legs):
             "classes": {name: summary(sel) for name, sel in classes.items()}}
 
 
+def _sclk_path():
+    """The driver's core-clock file of the GPU (the clock rocm-smi
+    --showclocks reports), or None."""
+    import glob
+    for path in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(path) as f:
+                if "*" in f.read():
+                    return path
+        except OSError:
+            continue
+    return None
+
+
+def _read_sclk(path):
+    try:
+        with open(path) as f:
+            for line in f:
+                if "*" in line:
+                    return float(line.split(":")[1].strip().split("Mhz")[0].split("MHz")[0])
+    except (OSError, ValueError, IndexError):
+        return None
+    return None
+
+
+def sample_clock(torch, step, seconds=0.3, interval=0.004):
+    """Core clock while the workload runs: `step` repeated for about
+    `seconds` after the timed region (so the sampling thread cannot perturb
+    the timing), the clock read every `interval` seconds from the driver."""
+    import statistics
+    import threading
+    path = _sclk_path()
+    if path is None:
+        return None
+    samples, stop = [], threading.Event()
+
+    def run():
+        while not stop.is_set():
+            v = _read_sclk(path)
+            if v:
+                samples.append(v)
+            time.sleep(interval)
+
+    step(None)
+    torch.cuda.synchronize()
+    th = threading.Thread(target=run, daemon=True)
+    th.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        step(None)
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"min": min(samples), "median": statistics.median(samples), "max": max(samples),
+            "samples": len(samples), "source": "pp_dpm_sclk (as rocm-smi --showclocks), repeated steps"}
+
+
 def cpu_baseline(S, budget_s=25.0):
     """The oracle (six-loop fp64 GEMM, full output) on the fp32 sweep's
     shapes, smallest first, on the host's cores, stopping once about
@@ -873,6 +932,7 @@ def main():
             step_flops = sum(2.0 * c["n"] ** 3 + 3.0 * c["n"] ** 2 for c in cases)
             kern_ms = sum(per_launch)
             achieved = sum(flops) / (kern_ms * 1e-3) / 1e12
+            clock = sample_clock(torch, lambda ev: sweep_step(sk, cases, ev))
             tiles = {}
             for c in cases:  # the tile instance AUTO runs each shape on
                 n = c["n"]
@@ -880,7 +940,7 @@ def main():
                 p = sk.plan_query(d)
                 tiles[str(n)] = f"{p.tile_m}x{p.tile_n}"
             results[wl] = dict(
-                value=step_flops / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype="f32",
+                value=step_flops / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype="f32", clock=clock,
                 per_shape={str(c["n"]): round(f / (t * 1e-3) / 1e12, 2)
                            for c, f, t in zip(cases, flops, per_launch)},
                 roofline={"bound": "mfma", "achieved": round(achieved, 2),
@@ -899,9 +959,10 @@ def main():
             for dt, name in ((sk.F16, "f16"), (sk.BF16, "bf16")):
                 h = make_hgemm_inputs(torch, sk, S, dt)
                 ms, per_launch, wall = timed(torch, lambda ev: hgemm_step(sk, h, ev), 1, steps, warmup)
+                clock = sample_clock(torch, lambda ev: hgemm_step(sk, h, ev))
                 fl = 2.0 * 8192 ** 3
                 achieved = fl / (per_launch[0] * 1e-3) / 1e12
-                out[name] = dict(value=fl / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype=name,
+                out[name] = dict(value=fl / (ms * 1e-3) / 1e12, ms=ms, wall_ms=wall, dtype=name, clock=clock,
                                  roofline={"bound": "mfma", "achieved": round(achieved, 2),
                                            "peak": PEAK_TFLOPS[name], "unit": "TFLOP/s",
                                            "frac": round(achieved / PEAK_TFLOPS[name], 4),
@@ -912,7 +973,7 @@ def main():
                 del h
                 torch.cuda.empty_cache()
             r = out["f16"]
-            r["bf16"] = {k: out["bf16"][k] for k in ("value", "ms", "roofline")} if "bf16" in out else None
+            r["bf16"] = {k: out["bf16"][k] for k in ("value", "ms", "roofline", "clock")} if "bf16" in out else None
             r["config"] = {"workload": "HGEMM 8192^3, fp16 in/out (bf16 also timed), fp32 accumulate,"
                                        " A row-major, B column-major, N(0,1)/sqrt(k), alpha=1 beta=0",
                            "schedule": "AUTO"}
@@ -924,7 +985,7 @@ def main():
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(m["ms"], 4),
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": m["dtype"], "data": "synthetic", "config": m["config"],
-            "roofline": m["roofline"]}
+            "roofline": m["roofline"], "clock_mhz": m.get("clock")}
     if "per_shape" in m:
         line["per_shape_tflops"] = m["per_shape"]
     if not args.no_cpu_baseline:
@@ -939,9 +1000,11 @@ def main():
         if wl == args.workload:
             continue
         extra = {"value": round(r["value"], 3), "unit": "TFLOP/s", "ms_per_step": round(r["ms"], 4),
-                 "dtype": r["dtype"], "roofline": r["roofline"], "config": r["config"]}
+                 "dtype": r["dtype"], "roofline": r["roofline"], "clock_mhz": r.get("clock"),
+                 "config": r["config"]}
         if r.get("bf16"):
-            extra["bf16"] = {"value": round(r["bf16"]["value"], 3), "roofline": r["bf16"]["roofline"]}
+            extra["bf16"] = {"value": round(r["bf16"]["value"], 3), "roofline": r["bf16"]["roofline"],
+                             "clock_mhz": r["bf16"].get("clock")}
         if "per_shape" in r:
             extra["per_shape_tflops"] = r["per_shape"]
         line["hgemm" if wl == "hgemm-8192" else "sgemm"] = extra
