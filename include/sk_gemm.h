@@ -278,10 +278,12 @@ int sk_gemm(int64_t m, int64_t n, int64_t k, float alpha, const void *A, int64_t
  * chosen explicitly whose positions or quanta products would reach 2^31
  * (k of several million with the XCD-aware schedule) returns
  * SK_ERR_UNSUPPORTED; AUTO then takes the two-tile hybrid, else the
- * data-parallel order.  Stream-ordered temporary (hipMallocAsync, freed on
- * the stream after the GEMM; SK_ERR_NO_MEMORY when it cannot be had): the
- * k-contiguous copy of an operand the kernels cannot read in place (plan
- * packs bits).  In ABFT mode the operands' checksum encodings and
+ * data-parallel order.  The k-contiguous copy of an operand the kernels
+ * cannot read in place (plan packs bits; rows * ceil(k/64) * 64 elements per
+ * copy) is kept in the stream's workspace, one buffer for A and one for B
+ * (grown when a call needs more, after synchronising the stream; freed by
+ * sk_release_workspace; SK_ERR_NO_MEMORY when it cannot be had).  In ABFT
+ * mode the operands' checksum encodings and
  * detection-threshold inputs, at most about 4 * ((tiles_m + tiles_n) * 32 *
  * ceil(k/32) + (m + n) * (ceil(k/64) + 1)) bytes for 128 x 128 tiles (at
  * least 4 MiB), and one 32-bit counter per tile of A and B, are kept in the

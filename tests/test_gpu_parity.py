@@ -80,6 +80,31 @@ def test_k_not_multiple_of_vector_width_and_odd_ld(dtype):
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k)
 
 
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_repacked_operands_buffers_grow_and_shrink_between_calls(dtype):
+    """Operands the kernels cannot read in place are repacked into copies the
+    stream's workspace keeps from call to call: small, larger (the copies
+    grow), smaller again (the larger copies are reused), in the layouts that
+    repack one or both operands (fp16/bf16: any mn-contiguous operand; fp32:
+    a leading dimension that is not a multiple of four), each against the
+    oracle; the tile edges of the 64 x 64 transposes are exercised by ragged
+    m, n and k."""
+    if dtype == sk.F32:
+        runs = [(130, 70, 77, sk.A_ROW_B_ROW, 1), (1000, 1500, 700, sk.A_COL_B_ROW, 3),
+                (300, 130, 65, sk.A_COL_B_COL, 1)]
+    else:
+        runs = [(130, 70, 77, sk.A_ROW_B_ROW, 0), (1000, 1500, 700, sk.A_COL_B_ROW, 0),
+                (300, 130, 65, sk.A_COL_B_COL, 5), (257, 513, 129, sk.A_ROW_B_ROW, 3)]
+    for (m, n, k, layout, pad) in runs:
+        _say("case repack", dtype, m, n, k, layout, pad)
+        c = Case(m, n, k, dtype, layout, 60 + m + layout, pad=pad)
+        plan = sk.plan_query(c.desc(1.0, 0.5))
+        assert plan.packs != 0, (m, n, k, layout, pad)
+        got = c.run(1.0, 0.5)
+        ref, bound = c.reference(1.0, 0.5)
+        assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
+
+
 # ------------------------------------------------ the narrow-m instance
 
 # m, n, k, layout, pad, alpha, beta: every row-block count (BM = 64, 128,

@@ -58,6 +58,10 @@ struct Workspace {
   int64_t abft_ctr_count = 0;
   float *abft_buf = nullptr;
   int64_t abft_floats = 0;
+  // k-contiguous copies of A and B for operands the kernels cannot read in
+  // place (calls on one stream run in order, so each reuses them)
+  void *pack[2] = {nullptr, nullptr};
+  size_t pack_bytes[2] = {0, 0};
 };
 
 std::mutex g_mu;
@@ -194,11 +198,15 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
       (void)hipFree(w.flags);
       keep_host = w.status_host;  // the error word survives growth (it may hold a report)
       keep_dev = w.status;
-      Workspace keep_abft;  // so do the ABFT buffers (the counters are zero)
+      Workspace keep_abft;  // so do the ABFT buffers (the counters are zero) and the repack copies
       keep_abft.abft_ctr = w.abft_ctr;
       keep_abft.abft_ctr_count = w.abft_ctr_count;
       keep_abft.abft_buf = w.abft_buf;
       keep_abft.abft_floats = w.abft_floats;
+      for (int i = 0; i < 2; ++i) {
+        keep_abft.pack[i] = w.pack[i];
+        keep_abft.pack_bytes[i] = w.pack_bytes[i];
+      }
       w = keep_abft;
     }
     size_t bytes = need > base ? need : base;
@@ -242,6 +250,31 @@ int get_workspace(int dev, hipStream_t stream, int64_t slots, size_t tile_bytes,
     if (e != hipSuccess) return hip_fail(e, "workspace init");
   }
   *out = &w;
+  return SK_OK;
+}
+
+// Repack copy `which` (0: A, 1: B) of at least `bytes` in workspace `w` of
+// `stream`, grown (never shrunk) after the stream's earlier work is done with
+// the old one.  Caller holds g_mu.
+int get_pack_buffer(Workspace &w, hipStream_t stream, int which, size_t bytes, void **out) {
+  if (w.pack[which] == nullptr || w.pack_bytes[which] < bytes) {
+    if (w.pack[which] != nullptr) {
+      hipError_t e = hipStreamSynchronize(stream);
+      if (e != hipSuccess) return hip_fail(e, "hipStreamSynchronize");
+      (void)hipFree(w.pack[which]);
+      w.pack[which] = nullptr;
+      w.pack_bytes[which] = 0;
+    }
+    const size_t n = (bytes + ((size_t)1 << 20) - 1) >> 20 << 20;  // whole MiB
+    hipError_t e = hipMalloc(&w.pack[which], n);
+    if (e != hipSuccess) {
+      w.pack[which] = nullptr;
+      (void)hipGetLastError();
+      return SK_ERR_NO_MEMORY;
+    }
+    w.pack_bytes[which] = n;
+  }
+  *out = w.pack[which];
   return SK_OK;
 }
 
@@ -405,47 +438,19 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
 
   // operands: direct, or repacked into a k-contiguous copy
   const int64_t kp = (d.k + 63) / 64 * 64;
-  void *pa = nullptr, *pb = nullptr;
+  const TileCfg &c = P.cfg;
   KernelArgs a;
   std::memset(&a, 0, sizeof(a));
   a.A = d.A; a.lda = d.lda; a.a_kmajor = ak; a.a_kext = (int32_t)d.k;
   a.B = d.B; a.ldb = d.ldb; a.b_kmajor = bk; a.b_kext = (int32_t)d.k;
-  if (P.pack_a) {
-    e = hipMallocAsync(&pa, (size_t)d.m * kp * es, stream);
-    if (e != hipSuccess) { (void)hipGetLastError(); return SK_ERR_NO_MEMORY; }
-    rc = launch_pack(d.dtype, d.A, d.lda, ak, d.m, d.k, pa, kp, stream);
-    if (rc != hipSuccess) {
-      (void)hipFreeAsync(pa, stream);
-      return hip_fail((hipError_t)rc, "pack A");
-    }
-    a.A = pa; a.lda = kp; a.a_kmajor = 1; a.a_kext = (int32_t)kp;
-  }
-  if (P.pack_b) {
-    e = hipMallocAsync(&pb, (size_t)d.n * kp * es, stream);
-    if (e != hipSuccess) {
-      if (pa) (void)hipFreeAsync(pa, stream);
-      (void)hipGetLastError();
-      return SK_ERR_NO_MEMORY;
-    }
-    rc = launch_pack(d.dtype, d.B, d.ldb, bk, d.n, d.k, pb, kp, stream);
-    if (rc != hipSuccess) {
-      if (pa) (void)hipFreeAsync(pa, stream);
-      (void)hipFreeAsync(pb, stream);
-      return hip_fail((hipError_t)rc, "pack B");
-    }
-    a.B = pb; a.ldb = kp; a.b_kmajor = 1; a.b_kext = (int32_t)kp;
-  }
   // 32-bit buffer offsets inside a k-major tile: rows * ld * es must fit
-  const TileCfg &c = P.cfg;
   auto offsets_fit = [&](bool kmaj, int64_t ld, int rows) {
     const int64_t span = kmaj ? (int64_t)rows * ld * es : (int64_t)c.bk * ld * es;
     return span + 1024 < 0x7FFFFFFF;
   };
-  if (!offsets_fit(a.a_kmajor, a.lda, c.bm) || !offsets_fit(a.b_kmajor, a.ldb, c.bn)) {
-    if (pa) (void)hipFreeAsync(pa, stream);
-    if (pb) (void)hipFreeAsync(pb, stream);
+  if (!offsets_fit(P.pack_a ? true : ak, P.pack_a ? kp : d.lda, c.bm) ||
+      !offsets_fit(P.pack_b ? true : bk, P.pack_b ? kp : d.ldb, c.bn))
     return SK_ERR_UNSUPPORTED;
-  }
 
   float *partials = nullptr;
   uint32_t *flags = nullptr, epoch = 0;
@@ -460,13 +465,25 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
   } else {
     const int64_t slots_needed = P.grid;
     rc = get_workspace(dev, stream, slots_needed, (size_t)c.bm * c.bn * 4, &ws);
-    if (rc != SK_OK) {
-      if (pa) (void)hipFreeAsync(pa, stream);
-      if (pb) (void)hipFreeAsync(pb, stream);
-      return rc;
-    }
+    if (rc != SK_OK) return rc;
     if (++ws->epoch == 0) ws->epoch = 1;
     partials = ws->partials; flags = ws->flags; status = ws->status; epoch = ws->epoch;
+  }
+  if (P.pack_a) {  // (never in the allocation-free form: refused above)
+    void *pa = nullptr;
+    rc = get_pack_buffer(*ws, stream, 0, (size_t)d.m * kp * es, &pa);
+    if (rc != SK_OK) return rc;
+    rc = launch_pack(d.dtype, d.A, d.lda, ak, d.m, d.k, pa, kp, stream);
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack A");
+    a.A = pa; a.lda = kp; a.a_kmajor = 1; a.a_kext = (int32_t)kp;
+  }
+  if (P.pack_b) {
+    void *pb = nullptr;
+    rc = get_pack_buffer(*ws, stream, 1, (size_t)d.n * kp * es, &pb);
+    if (rc != SK_OK) return rc;
+    rc = launch_pack(d.dtype, d.B, d.ldb, bk, d.n, d.k, pb, kp, stream);
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "pack B");
+    a.B = pb; a.ldb = kp; a.b_kmajor = 1; a.b_kext = (int32_t)kp;
   }
 
   a.C = d.C; a.ldc = d.ldc;
@@ -497,11 +514,7 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     const int64_t ra_ = d.m * groups, rb_ = d.n * groups, ta = P.tiles_m * groups, tb = P.tiles_n * groups;
     const int64_t floats = ea + eb + ra_ + rb_ + ta + tb + d.m + d.n + P.tiles_m + P.tiles_n;
     rc = get_abft_buffers(*ws, stream, P.tiles_m + P.tiles_n, floats);
-    if (rc != SK_OK) {
-      if (pa) (void)hipFreeAsync(pa, stream);
-      if (pb) (void)hipFreeAsync(pb, stream);
-      return rc;
-    }
+    if (rc != SK_OK) return rc;
     float *p_ea = ws->abft_buf, *p_eb = p_ea + ea, *p_ra = p_eb + eb, *p_rb = p_ra + ra_, *p_ta = p_rb + rb_,
           *p_tb = p_ta + ta, *p_na = p_tb + tb, *p_nb = p_na + d.m, *p_ma = p_nb + d.n, *p_mb = p_ma + P.tiles_m;
     AbftPrepArgs pr;
@@ -513,18 +526,12 @@ int gemm_impl(const sk_gemm_desc &d, const sk_options &o, sk_abft_report *report
     pr.counters = ws->abft_ctr;
     pr.report = report;
     rc = launch_abft_prep(pr, stream);
-    if (rc != hipSuccess) {
-      if (pa) (void)hipFreeAsync(pa, stream);
-      if (pb) (void)hipFreeAsync(pb, stream);
-      return hip_fail((hipError_t)rc, "ABFT preparation kernel");
-    }
+    if (rc != hipSuccess) return hip_fail((hipError_t)rc, "ABFT preparation kernel");
     a.enc_a = p_ea; a.enc_b = p_eb; a.enc_kb = (int32_t)kb;
     a.norm_a = p_na; a.norm_b = p_nb; a.emax_a = p_ma; a.emax_b = p_mb;
   }
 
   rc = launch_gemm(P, a, stream);
-  if (pa) (void)hipFreeAsync(pa, stream);
-  if (pb) (void)hipFreeAsync(pb, stream);
   if (rc != hipSuccess) return hip_fail((hipError_t)rc, "GEMM kernel launch");
   return SK_OK;
 }
@@ -691,6 +698,8 @@ int sk_release_workspace(void) {
     (void)hipFree(kv.second.flags);
     (void)hipFree(kv.second.abft_ctr);
     (void)hipFree(kv.second.abft_buf);
+    (void)hipFree(kv.second.pack[0]);
+    (void)hipFree(kv.second.pack[1]);
     (void)hipHostFree(kv.second.status_host);
     (void)hipSetDevice(cur);
   }

@@ -36,6 +36,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_vptr;
@@ -1506,28 +1507,78 @@ __global__ void scale_kernel(int64_t m, int64_t n, float beta, void *C, int64_t 
   }
 }
 
-// Repack: dst[r * ldd + l] = src(r, l) for l < k, 0 for k <= l < ldd.  A
-// 64 x 64 tile goes through LDS so that both the read (along the source's
-// contiguous index) and the write (along l) are coalesced.
+// Repack: dst[r * ldd + l] = src(r, l) for l < k, 0 for k <= l < ldd, rows
+// r < rows; src(r, l) is src[r * lds + l] (k-major) or src[l * lds + r]
+// (mn-major).  One workgroup per 64 x 64 block, 16 bytes per lane on both
+// sides where the operands allow it (vec_src: the source base is 16-byte
+// aligned and lds a multiple of the elements in 16 bytes; the destination
+// always is): a k-major source is copied row by row; an mn-major one is
+// transposed through LDS -- loaded along r into tile rows of l (rows of 64
+// elements plus 8 bytes, so that the element reads of the store side fall
+// at most two to a bank), and read back along l.
 template <typename U>
-__global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, int src_kmajor,
+__global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, int src_kmajor, int vec_src,
                                                    int64_t rows, int64_t k, U *dst, int64_t ldd) {
-  __shared__ U tile[64][65];
+  constexpr int EPV = 16 / sizeof(U);         // elements per 16-byte vector
+  constexpr int VPR = 64 / EPV;              // vectors per 64-element row
+  constexpr int RPP = 256 / VPR;             // rows per pass of the workgroup
+  constexpr int PITCH = 64 + 8 / sizeof(U);  // elements per LDS tile row
+  static_assert((PITCH * sizeof(U)) % 8 == 0, "8-byte aligned tile rows");
+  union Vec {
+    u4_t v;
+    u2_t h[2];
+    U e[EPV];
+  };
   const int64_t r0 = (int64_t)blockIdx.y * 64, l0 = (int64_t)blockIdx.x * 64;
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;  // 64 x 4
-  for (int yy = ty; yy < 64; yy += 4) {
-    if (src_kmajor) {  // row r = r0 + yy, l = l0 + tx
-      const int64_t r = r0 + yy, l = l0 + tx;
-      tile[yy][tx] = (r < rows && l < k) ? src[r * lds + l] : U(0);
-    } else {  // src(r, l) at l * lds + r: read along r
-      const int64_t l = l0 + yy, r = r0 + tx;
-      tile[tx][yy] = (r < rows && l < k) ? src[l * lds + r] : U(0);
+  const int t = threadIdx.x, vi = t % VPR, ri = t / VPR;
+  const int64_t l = l0 + vi * EPV;  // this lane's first element along l (k-major copy and store side)
+  if (src_kmajor) {
+    for (int p = 0; p < 64; p += RPP) {
+      const int64_t r = r0 + p + ri;
+      if (r >= rows || l >= ldd) continue;
+      Vec x;
+      if (vec_src && l + EPV <= k) {
+        x.v = *reinterpret_cast<const u4_t *>(src + r * lds + l);
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) x.e[e] = l + e < k ? src[r * lds + l + e] : U(0);
+      }
+      if (l + EPV <= ldd) {
+        *reinterpret_cast<u4_t *>(dst + r * ldd + l) = x.v;
+      } else {
+        for (int e = 0; e < EPV && l + e < ldd; ++e) dst[r * ldd + l + e] = x.e[e];
+      }
     }
+    return;
+  }
+  __shared__ __align__(16) U tile[64 * PITCH];  // tile[li][ri]: element (r0 + ri, l0 + li)
+  for (int p = 0; p < 64; p += RPP) {
+    const int li = p + ri;
+    const int64_t ll = l0 + li, r = r0 + vi * EPV;
+    Vec x;
+    if (ll < k && vec_src && r + EPV <= rows) {
+      x.v = *reinterpret_cast<const u4_t *>(src + ll * lds + r);
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) x.e[e] = ll < k && r + e < rows ? src[ll * lds + r + e] : U(0);
+    }
+    u2_t *d = reinterpret_cast<u2_t *>(tile + li * PITCH + vi * EPV);
+    d[0] = x.h[0];
+    d[1] = x.h[1];
   }
   __syncthreads();
-  for (int yy = ty; yy < 64; yy += 4) {
-    const int64_t r = r0 + yy, l = l0 + tx;
-    if (r < rows && l < ldd) dst[r * ldd + l] = tile[yy][tx];
+  for (int p = 0; p < 64; p += RPP) {
+    const int rr = p + ri;
+    const int64_t r = r0 + rr;
+    if (r >= rows || l >= ldd) continue;
+    Vec x;
+#pragma unroll
+    for (int e = 0; e < EPV; ++e) x.e[e] = tile[(vi * EPV + e) * PITCH + rr];
+    if (l + EPV <= ldd) {
+      *reinterpret_cast<u4_t *>(dst + r * ldd + l) = x.v;
+    } else {
+      for (int e = 0; e < EPV && l + e < ldd; ++e) dst[r * ldd + l + e] = x.e[e];
+    }
   }
 }
 
@@ -1793,13 +1844,17 @@ int launch_scale(int dtype, int64_t m, int64_t n, float beta, void *C, int64_t l
 int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_t rows, int64_t k,
                 void *dst, int64_t ldd, hipStream_t stream) {
   dim3 grid((unsigned)((ldd + 63) / 64), (unsigned)((rows + 63) / 64)), block(256);
+  // the kernel writes 16-byte vectors into dst: 16-byte aligned rows of it
+  const int es = dtype == SK_F32 ? 4 : 2;
+  if (reinterpret_cast<uintptr_t>(dst) % 16 != 0 || (ldd * es) % 16 != 0) return (int)hipErrorInvalidValue;
+  const int vec_src = reinterpret_cast<uintptr_t>(src) % 16 == 0 && (lds * es) % 16 == 0 ? 1 : 0;
   if (dtype == SK_F32)
     hipLaunchKernelGGL(dev::pack_kernel<uint32_t>, grid, block, 0, stream,
-                       static_cast<const uint32_t *>(src), lds, src_kmajor ? 1 : 0, rows, k,
+                       static_cast<const uint32_t *>(src), lds, src_kmajor ? 1 : 0, vec_src, rows, k,
                        static_cast<uint32_t *>(dst), ldd);
   else
     hipLaunchKernelGGL(dev::pack_kernel<uint16_t>, grid, block, 0, stream,
-                       static_cast<const uint16_t *>(src), lds, src_kmajor ? 1 : 0, rows, k,
+                       static_cast<const uint16_t *>(src), lds, src_kmajor ? 1 : 0, vec_src, rows, k,
                        static_cast<uint16_t *>(dst), ldd);
   return (int)hipGetLastError();
 }
