@@ -105,6 +105,9 @@ def parse():
                         "timings) for fp16 and fp32, then compare basic Stream-K at the model's grid "
                         "(default and measured constants) with the best grid of an exhaustive search "
                         "on SHAPES seeded fp16 sweep shapes below one wave")
+    p.add_argument("--layouts", action="store_true",
+                   help="time only 8192^3 fp16 GEMMs with B read in place (beta 0 and 1), B repacked and "
+                        "both operands repacked (--steps calls each after 3 warm-ups)")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="only run a plain 1 GiB device-to-device copy 5 times (calibrates the "
                         "FETCH_SIZE / WRITE_SIZE counters against a kernel of known traffic)")
@@ -148,6 +151,38 @@ def compare_schedules(torch, sk, S, steps):
                         "sk_tiles": p.sk_tiles, "phase_div": p.phase_div, "us": round(us, 1),
                         "tflops": round(2.0 * m * n * k / us / 1e6, 1)})
         del A, B, C
+    return out
+
+
+def layouts_leg(torch, sk, S, steps):
+    """8192^3 fp16 (the hgemm workload's N(0,1)/sqrt(k) operands, alpha = 1)
+    in the storage orders that read B in place (A row-major, B column-major;
+    beta 0 and 1), repack B (both row-major) and repack both operands (A
+    column-major, B row-major): `steps` calls per case between one event pair
+    after 3 warm-ups, and 30 warm-up calls before the first case."""
+    h = make_hgemm_inputs(torch, sk, S, sk.F16)
+    n, A, B, C = h["n"], h["A"], h["B"], h["C"]
+    cases = [("A row, B col: B in place", sk.A_ROW_B_COL, 0.0), ("A row, B col: B in place, beta 1", sk.A_ROW_B_COL, 1.0),
+             ("A row, B row: B repacked", sk.A_ROW_B_ROW, 0.0), ("A col, B row: both repacked", sk.A_COL_B_ROW, 0.0)]
+    d0 = sk.make_desc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+    for _ in range(30):
+        sk.gemm_ex(d0, None)
+    torch.cuda.synchronize()
+    out = []
+    for name, layout, beta in cases:
+        d = sk.make_desc(n, n, n, 1.0, A, n, B, n, beta, C, n, sk.F16, layout)
+        for _ in range(3):
+            sk.gemm_ex(d, None)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            sk.gemm_ex(d, None)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / steps * 1e3
+        out.append({"case": name, "beta": beta, "packs": sk.plan_query(d).packs, "us_per_call": round(us, 1),
+                    "tflops": round(2.0 * n ** 3 / us * 1e-6, 1)})
     return out
 
 
@@ -898,6 +933,10 @@ def main():
         return
     if args.gemv:
         print(json.dumps(gemv_leg(torch, sk, S)), flush=True)
+        return
+    if args.layouts:
+        for r in layouts_leg(torch, sk, S, args.steps):
+            print(json.dumps(r), flush=True)
         return
     if args.peaks:
         print(json.dumps(measured_peaks(torch, sk)), flush=True)
