@@ -224,6 +224,29 @@ def test_every_grid_size_exact_on_integer_inputs(dtype):
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("beta", [1.0, -2.0])
+def test_beta_nonzero_exact_on_integer_inputs(dtype, beta):
+    """beta != 0 (for fp16/bf16 the kernel build that stages alpha*acc
+    through LDS in fp32 and reads C in whole lines) on small integers: every
+    decomposition on both tile instances gives the oracle's rounded result
+    bit for bit (alpha*acc + beta*C is exact in fp32, then rounded once),
+    owners adding split tiles' partials included.  The shape has full
+    interior tiles and ragged edges on both instances."""
+    m, n, k = (700, 600, 1024) if dtype == sk.F32 else (600, 520, 2048)
+    c = Case(m, n, k, dtype, sk.A_ROW_B_COL, 17, dist="int")
+    import oracle
+    _, _, rnd = oracle.gemm(m, n, k, 1.0, c.A, c.lda, c.B, c.ldb, beta, c.Cin, c.ldc, dtype, c.layout)
+    for tile in [sk.TILE_LARGE, sk.TILE_SMALL]:
+        runs = [sk.make_options(schedule=sched, tile=tile)
+                for sched in (sk.SCHED_DP, sk.SCHED_SK_BASIC, sk.SCHED_XCD_ALIGNED, sk.SCHED_AUTO)]
+        runs += [sk.make_options(forced_grid=g, tile=tile) for g in (3, 31, 256)]
+        for o in runs:
+            c.reset_c()
+            got = c.run(1.0, beta, o)
+            assert np.array_equal(got.view(np.uint8), rnd.view(np.uint8)), (tile, o.schedule, o.forced_grid)
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
 def test_forced_grids_against_oracle(dtype):
     m, n, k = 520, 600, 3000
     c = Case(m, n, k, dtype, sk.A_ROW_B_COL if dtype else sk.A_ROW_B_ROW, 13)
