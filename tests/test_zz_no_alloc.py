@@ -43,6 +43,7 @@ CASES = [
     ("fp16 auto small tile", (1000, 1000, 5000, sk.F16, sk.A_ROW_B_COL), dict(tile=sk.TILE_SMALL), 0.5, 1.0),
     ("fp32 forced grid 7", (520, 600, 3000, sk.F32, sk.A_ROW_B_ROW), dict(forced_grid=7), 1.0, 1.0),
     ("fp32 auto", (3000, 2960, 200, sk.F32, sk.A_ROW_B_ROW), {}, 1.0, 0.0),
+    ("fp32 small tile", (1024, 1000, 1024, sk.F32, sk.A_ROW_B_ROW), dict(tile=sk.TILE_SMALL), 1.0, 1.0),
     ("fp32 dot products", (1, 2048, 16384, sk.F32, sk.A_ROW_B_COL), {}, 1.0, 0.0),
 ]
 
