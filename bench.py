@@ -156,14 +156,16 @@ def compare_schedules(torch, sk, S, steps):
 
 def layouts_leg(torch, sk, S, steps):
     """8192^3 fp16 (the hgemm workload's N(0,1)/sqrt(k) operands, alpha = 1)
-    in the storage orders that read B in place (A row-major, B column-major;
-    beta 0 and 1), repack B (both row-major) and repack both operands (A
-    column-major, B row-major): `steps` calls per case between one event pair
-    after 3 warm-ups, and 30 warm-up calls before the first case."""
+    in the storage orders that read both operands in place (A row-major, B
+    column-major, beta 0 and 1; both row-major, B read n-contiguous through
+    transposing LDS reads) and repack A (A column-major, B row-major):
+    `steps` calls per case between one event pair after 3 warm-ups, and 30
+    warm-up calls before the first case."""
     h = make_hgemm_inputs(torch, sk, S, sk.F16)
     n, A, B, C = h["n"], h["A"], h["B"], h["C"]
     cases = [("A row, B col: B in place", sk.A_ROW_B_COL, 0.0), ("A row, B col: B in place, beta 1", sk.A_ROW_B_COL, 1.0),
-             ("A row, B row: B repacked", sk.A_ROW_B_ROW, 0.0), ("A col, B row: both repacked", sk.A_COL_B_ROW, 0.0)]
+             ("A row, B row: B in place, n-contiguous", sk.A_ROW_B_ROW, 0.0),
+             ("A col, B row: A repacked", sk.A_COL_B_ROW, 0.0)]
     d0 = sk.make_desc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
     for _ in range(30):
         sk.gemm_ex(d0, None)

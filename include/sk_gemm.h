@@ -55,7 +55,14 @@ extern "C" {
 typedef enum { SK_F32 = 0, SK_F16 = 1, SK_BF16 = 2 } sk_dtype;
 
 /* Storage order of A and B ("ROW": the second index is contiguous).
- * SK_A_ROW_B_COL keeps both operands contiguous along k. */
+ * SK_A_ROW_B_COL keeps both operands contiguous along k.  Operands are read
+ * in place when the base is 16-byte aligned, the leading dimension a
+ * multiple of 16 bytes, and: for a k-contiguous operand, k a multiple of 16
+ * bytes of elements; fp32, either order; fp16/bf16 A, k-contiguous only;
+ * fp16/bf16 B stored n-contiguous (row-major), n a multiple of 8,
+ * 2 (k + 64) ldb + 1024 below 2^31 - 1 (bytes) and the LARGE or SMALL tile
+ * instance (transposed in LDS).  Any other operand is repacked into a k-contiguous copy first (see
+ * sk_gemm_ex). */
 typedef enum {
   SK_A_ROW_B_ROW = 0,
   SK_A_ROW_B_COL = 1,
@@ -307,11 +314,9 @@ int sk_gemm_ex(const sk_gemm_desc *desc, const sk_options *opts, sk_abft_report 
  * kernel on `stream`.  Every call on one GPU shares that array and leaves it
  * as the call ended: calls that overlap on one GPU (other streams, other
  * host threads) race and must not be issued.  Refused: ABFT mode and
- * operands that would need a repacked copy (SK_ERR_UNSUPPORTED; an operand
- * is read in place when its base is 16-byte aligned, its leading dimension
- * a multiple of 16 bytes and, if it is k-contiguous, k a multiple of 16
- * bytes of elements; fp16/bf16 operands must also be k-contiguous: plan
- * packs bits 0), and plans needing more than 16384
+ * operands that would need a repacked copy (SK_ERR_UNSUPPORTED; the
+ * conditions for reading an operand in place are listed with sk_layout:
+ * plan packs bits 0), and plans needing more than 16384
  * workgroups or more partial-tile bytes than SK_NOALLOC_PARTIAL_BYTES
  * (SK_ERR_TOO_LARGE: a forced grid above the slot count on the large
  * fp16/bf16 tile, or a matrix-vector split with more chunk sums).  Time-outs

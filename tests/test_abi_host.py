@@ -553,8 +553,33 @@ def test_grid_model_regimes():
 
 
 def test_repack_flags():
+    # an n-contiguous 16-bit B is read in place by the 256 and 128 instances
     p = sk.plan_query(_desc(1000, 1000, 1000, sk.F16, sk.A_ROW_B_ROW), None, 256)
-    assert p.packs == 2  # B is n-contiguous: repacked for the fp16 kernel
+    assert p.packs == 0
+    p = sk.plan_query(_desc(1000, 1000, 1000, sk.BF16, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_SMALL), 256)
+    assert p.packs == 0
+    # ... but an m-contiguous A is repacked
+    p = sk.plan_query(_desc(1000, 1000, 1000, sk.F16, sk.A_COL_B_ROW), None, 256)
+    assert p.packs == 1
+    # the narrow-m instance reads k-contiguous B only
+    p = sk.plan_query(_desc(100, 1000, 1000, sk.F16, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW), 256)
+    assert p.packs == 2
+    # n not a multiple of 8: the last 128-bit chunk of a k-row would straddle n
+    d = sk.make_desc(1000, 1004, 1000, 1.0, 1 << 20, 1000, 1 << 21, 1008, 0.0, 1 << 22, 1004, sk.F16,
+                     sk.A_ROW_B_ROW)
+    assert sk.plan_query(d, None, 256).packs == 2
+    # ldb not a multiple of 8, or a misaligned base
+    d = sk.make_desc(1000, 1000, 1000, 1.0, 1 << 20, 1000, 1 << 21, 1004, 0.0, 1 << 22, 1000, sk.F16,
+                     sk.A_ROW_B_ROW)
+    assert sk.plan_query(d, None, 256).packs == 2
+    d = sk.make_desc(1000, 1000, 1000, 1.0, 1 << 20, 1000, (1 << 21) + 8, 1000, 0.0, 1 << 22, 1000, sk.F16,
+                     sk.A_ROW_B_ROW)
+    assert sk.plan_query(d, None, 256).packs == 2
+    # k * ldb beyond a 31-bit byte offset: repacked rather than refused
+    p = sk.plan_query(_desc(256, 32768, 32768, sk.F16, sk.A_ROW_B_ROW), None, 256)
+    assert p.packs == 2
+    p = sk.plan_query(_desc(256, 16384, 32768, sk.F16, sk.A_ROW_B_ROW), None, 256)
+    assert p.packs == 0
     p = sk.plan_query(_desc(1000, 1000, 1000, sk.F32, sk.A_COL_B_ROW), None, 256)
     assert p.packs == 0  # the fp32 kernel reads both orders directly
     p = sk.plan_query(_desc(1000, 1000, 1001, sk.F16, sk.A_ROW_B_COL), None, 256)

@@ -17,7 +17,7 @@ pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
 from gemm_check import (TOL, Case, decode, rel_err, sampled_err, split_tiles,  # noqa: E402
-                        tile_sample_indices)
+                        tile_sample_indices, to_dev)
 
 DTYPES = [sk.F32, sk.F16, sk.BF16]
 LAYOUTS = [sk.A_ROW_B_ROW, sk.A_ROW_B_COL, sk.A_COL_B_ROW, sk.A_COL_B_COL]
@@ -103,6 +103,65 @@ def test_repacked_operands_buffers_grow_and_shrink_between_calls(dtype):
         got = c.run(1.0, 0.5)
         ref, bound = c.reference(1.0, 0.5)
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
+
+
+# ------------------------------ n-contiguous B read in place (fp16/bf16)
+
+# m, n, k, pad, alpha, beta: n a multiple of 8 but of neither tile size (a
+# ragged last tile column), k below one iteration and below one 16-byte
+# chunk, several iterations with a tail of k-rows, padded leading
+# dimensions, alpha and beta applied
+BMN_CASES = [(300, 520, 200, 0, 1.0, 0.0), (513, 264, 1000, 8, 0.5, -1.5), (64, 2048, 64, 0, 1.0, 1.0),
+             (256, 256, 5, 0, 1.0, 0.0), (257, 136, 4100, 16, 1.0, 0.0), (1000, 1000, 1000, 0, 0.75, 1.25)]
+
+
+@pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
+@pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
+@pytest.mark.parametrize("sched", ["auto", "dp", "forced7"])
+def test_b_n_contiguous_read_in_place_against_oracle(dtype, tile, sched):
+    """A row-major (k x n) B read in place by the 256 and 128 instances
+    (transposing LDS reads) against the full oracle output, with A
+    k-contiguous (in place) and m-contiguous (repacked)."""
+    kw = {"auto": {}, "dp": {"schedule": sk.SCHED_DP}, "forced7": {"forced_grid": 7}}[sched]
+    for (m, n, k, pad, alpha, beta) in BMN_CASES:
+        for layout in (sk.A_ROW_B_ROW, sk.A_COL_B_ROW):
+            _say("case b-n-contiguous", dtype, tile, sched, m, n, k, layout, pad)
+            c = Case(m, n, k, dtype, layout, 70 + m + k + layout, pad=pad)
+            opts = sk.make_options(tile=tile, **kw)
+            p = sk.plan_query(c.desc(alpha, beta), opts)
+            assert (p.packs & 2) == 0, p.packs
+            got = c.run(alpha, beta, opts)
+            ref, bound = c.reference(alpha, beta)
+            assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
+
+
+@pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
+@pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
+def test_b_n_contiguous_bitwise_equal_to_k_contiguous(dtype, tile):
+    """The same B stored row-major (read in place, transposed in LDS) and
+    column-major (k-contiguous) feeds the MFMAs the same fragments in the
+    same order: the outputs are bit for bit equal, on random inputs, under
+    data-parallel and split schedules and with beta != 0."""
+    for (m, n, k, pad) in [(300, 520, 200, 0), (1000, 1000, 1000, 0), (257, 136, 4100, 16)]:
+        _say("case b-order bitwise", dtype, tile, m, n, k, pad)
+        c = Case(m, n, k, dtype, sk.A_ROW_B_ROW, 90 + m, pad=pad)
+        Bkn = np.lib.stride_tricks.as_strided(c.B, shape=(k, n), strides=(c.ldb * c.B.itemsize, c.B.itemsize))
+        Bcol = np.ascontiguousarray(Bkn.T).reshape(-1)  # (n x k), ld = k
+        dB2 = to_dev(Bcol, dtype)
+        for kw in ({"schedule": sk.SCHED_DP}, {"forced_grid": 7}, {"forced_grid": 255}):
+            o = sk.make_options(tile=tile, **kw)
+            d1 = c.desc(1.0, 0.5)
+            d2 = sk.make_desc(m, n, k, 1.0, c.dA, c.lda, dB2, k, 0.5, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
+            p1, p2 = sk.plan_query(d1, o), sk.plan_query(d2, o)
+            assert (p1.packs & 2) == 0, p1.packs
+            assert (p1.grid, p1.schedule, p1.tile_m) == (p2.grid, p2.schedule, p2.tile_m)
+            c.reset_c()
+            got1 = c.run(1.0, 0.5, o)
+            c.reset_c()
+            sk.gemm_ex(d2, o)
+            torch.cuda.synchronize()
+            got2 = c.result()
+            assert np.array_equal(got1.view(np.uint8), got2.view(np.uint8)), (m, n, k, kw)
 
 
 # ------------------------------------------------ the narrow-m instance

@@ -40,6 +40,7 @@ typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 h4_t __attribute__((ext_vector_type(4)));
 typedef __bf16 b4_t __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void *lds_vptr;
+typedef short v4s_t __attribute__((ext_vector_type(4)));
 
 constexpr uint32_t kOOB = 0x80000000u;  // offset past every buffer range (ranges are < 2^31)
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
@@ -57,6 +58,27 @@ constexpr int vmcnt_le(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+}
+
+// Transposing 64-bit LDS read of 16-bit values (ds_read_b64_tr_b16): within
+// each group of 16 lanes, lane i receives value i % 4 of the 8 bytes at the
+// addresses of lanes i / 4, 4 + i / 4, 8 + i / 4 and 12 + i / 4 (in that
+// order) of its group.
+//
+// The read goes through a restrict-qualified parameter so that, once
+// inlined, it carries alias-scope information.  Without it the compiler's
+// wait insertion puts a wait for every outstanding vector-memory load in
+// front of each such read (it cannot tell the read from one of LDS bytes a
+// direct-to-LDS load may still be writing), which empties the load
+// pipeline inside the MAC loop; ordinary LDS loads are not held that way.
+// The loop orders its LDS reads after the direct-to-LDS loads of a stage
+// with its own waits and barriers, as it does for the ordinary loads.
+typedef __attribute__((address_space(3))) v4s_t *lds_v4s_t;
+__device__ __attribute__((always_inline)) inline v4s_t ds_read_tr16_at(lds_v4s_t __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+__device__ __forceinline__ v4s_t ds_read_tr16(int byte_off) {
+  return ds_read_tr16_at((lds_v4s_t)(lds_vptr)(smem + byte_off));
 }
 
 // ---------------------------------------------------------------- elements
@@ -250,9 +272,12 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // fragment reads per MFMA) also builds and gives the same bits, but one wave
 // per SIMD cannot hide its own LDS and barrier waits: about 6 % slower on
 // large squares, so it is not instantiated.
-template <int DT, int TILE, int W = (TILE == 256 ? 8 : 4)>
+template <int DT, int TILE, int W = (TILE == 256 ? 8 : 4), bool BMN_ = false>
 struct HPolicy {
   static constexpr int ET = DT;
+  // BMN: B stored n-contiguous (row-major k x n), staged in LDS as BK rows
+  // of BN values and read into the MFMA layout with transposing LDS reads
+  static constexpr bool BMN = BMN_;
   static constexpr int BM = TILE, BN = TILE, BK = 64, NSTAGE = 2;
   static constexpr int WAVES = W, NT = 64 * WAVES;
   // waves per SIMD the register budget is sized for
@@ -278,6 +303,16 @@ struct HPolicy {
   // distinct 16-byte bank groups of gfx950's 64 banks (256 bytes hold
   // 256/ROW rows; consecutive groups of them get distinct XOR masks).
   static __device__ __forceinline__ int swz(int r) { return (r / (256 / ROW)) % (ROW / 16); }
+  // BMN: k-row r of a B stage holds BN values (BN / 8 chunks of 16 bytes);
+  // chunk c sits at position c ^ (4 (r & 3)).  A transposing read fetches a
+  // 4 (k) x 16 (n) block per 16 lanes, 8 bytes per lane; with this XOR the 8
+  // blocks of 32 lanes (two column halves x four rows) fall in distinct
+  // 32-byte bank windows, since a row is a multiple of 256 bytes.
+  static constexpr int BROW = BN * 2;                 // bytes of one k-row of a BMN stage
+  static constexpr int BCPR = BN / 8;                 // chunks per k-row
+  static constexpr int BRPL = 1024 / BROW;            // k-rows per 1 KiB load
+  static __device__ __forceinline__ int bpos(int r, int c) { return c ^ (4 * (r & 3)); }
+  static_assert(!BMN || (BROW % 256 == 0 && BCPR >= 16), "mn-major B stage layout");
   struct Acc { f16v_t v[MB * NB]; };
   static __device__ __forceinline__ f4_t get4(const Acc &c, int i) {
     const f16v_t &b = c.v[i >> 2];
@@ -312,6 +347,10 @@ struct HLoader {
   int chunk2[2];
   __device__ __forceinline__ int chunk(int j) const { return chunk2[j & 1]; }
   int lds_a;            // LDS byte offset of this wave's first A load (stage 0)
+  // BMN: k-row of this lane's first B load within a stage (load j: + j BRPL),
+  // and the bytes B advances per k-iteration
+  int krow0;
+  int bstep;
 
   __device__ __forceinline__ void init(const KernelArgs &a, int m0, int n0) {
     static_assert(P::ROW == 128 && P::LOADS % 2 == 0, "chunk of load j depends only on j & 1");
@@ -319,9 +358,26 @@ struct HLoader {
     const int w = wave_id(), lane = threadIdx.x & 63;
     const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
     const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * lda_b;
-    const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * ldb_b;
+    // BMN: element (k, n) of B at B + (k ldb + n) 2; the descriptor starts
+    // at column n0 and ends at the last element, the iteration's k-rows go
+    // in soffset
+    const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * (P::BMN ? ES : ldb_b);
     ra = make_rsrc(Ab, (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)a.a_kext * ES);
-    rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
+    if constexpr (P::BMN) {
+      rb = make_rsrc(Bb, ((int64_t)(a.k - 1) * a.ldb + (a.n - n0)) * ES);
+      bstep = (int)(P::BK * ldb_b);
+      // lane L of load j fills position L % BCPR of k-row krow0 + j BRPL;
+      // the chunk stored there is the inverse of the XOR
+      krow0 = w * P::LOADS * P::BRPL + lane / P::BCPR;
+#pragma unroll
+      for (int j = 0; j < P::LOADS; ++j) {
+        const int kr = krow0 + j * P::BRPL;
+        const int c = P::bpos(kr, lane % P::BCPR);
+        vb[j] = n0 + c * 8 < a.n ? (uint32_t)((int64_t)kr * ldb_b + c * 16) : kOOB;
+      }
+    } else {
+      rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
+    }
     constexpr int CPR = P::ROW / 16;  // chunks per row
 #pragma unroll
     for (int j = 0; j < P::LOADS; ++j) {
@@ -329,7 +385,7 @@ struct HLoader {
       const int c = (lane % CPR) ^ P::swz(row);
       if (j < 2) chunk2[j] = c;
       va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
-      vb[j] = row < a.n - n0 ? (uint32_t)(row * ldb_b + c * 16) : kOOB;
+      if constexpr (!P::BMN) vb[j] = row < a.n - n0 ? (uint32_t)(row * ldb_b + c * 16) : kOOB;
     }
     lds_a = w * P::LOADS * 1024;
   }
@@ -342,8 +398,14 @@ struct HLoader {
     const int j = q >> 1;
     const int k0b = kit * P::BK * 2;
     const int left = live ? (a.k - kit * P::BK) * 2 : 0;
-    const bool ok = chunk(j) * 16 < left;
     const int dst = ((q & 1) ? P::b_off(stage) : P::a_off(stage)) + lds_a + j * 1024;
+    if (P::BMN && (q & 1)) {  // k-row kr of the iteration: rows at or past k read as zeros
+      const bool ok = (krow0 + j * P::BRPL) * 2 < left;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + dst), 16, ok ? vb[j] : kOOB, kit * bstep, 0,
+                                               0);
+      return;
+    }
+    const bool ok = chunk(j) * 16 < left;
     __builtin_amdgcn_raw_ptr_buffer_load_lds((q & 1) ? rb : ra, (lds_vptr)(smem + dst), 16,
                                              ok ? ((q & 1) ? vb[j] : va[j]) : kOOB, k0b, 0, 0);
   }
@@ -352,21 +414,23 @@ struct HLoader {
     const int k0b = kit * P::BK * 2;
     const int left = (a.k - kit * P::BK) * 2;  // bytes of k from k0
     const int abase = P::a_off(stage) + lds_a, bbase = P::b_off(stage) + lds_a;
+    const int k0bb = P::BMN ? kit * bstep : k0b;  // B's soffset
     if (left >= P::BK * 2) {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16, va[j], k0b, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
-                                                 vb[j], k0b, 0, 0);
+                                                 vb[j], k0bb, 0, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
         const bool ok = chunk(j) * 16 < left;
+        const bool okb = P::BMN ? (krow0 + j * P::BRPL) * 2 < left : ok;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16,
                                                  ok ? va[j] : kOOB, k0b, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
-                                                 ok ? vb[j] : kOOB, k0b, 0, 0);
+                                                 okb ? vb[j] : kOOB, k0bb, 0, 0);
       }
     }
   }
@@ -408,7 +472,19 @@ __device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, i
   const int lane = threadIdx.x & 63;
   const int As = P::a_off(stage), Bs = P::b_off(stage);
   const int c = sub * 2 + (lane >> 5);
-  if (q < P::NB) {
+  if (q < P::NB && P::BMN) {
+    // lane 16 g + j addresses the four values (k, n .. n + 3) with
+    // k = 16 sub + 8 (g / 2) + j / 4 and n = 16 (g % 2) + 4 (j % 4) within
+    // the block; the transposing read hands lane 16 g + i the values
+    // (k0 .. k0 + 3, n0 + i) of its 16-lane group.  A second read 4 rows
+    // further completes the eight k of the k-contiguous fragment.
+    const int g = lane >> 4, j = lane & 15;
+    const int n = wn * P::WTN + q * 32 + 16 * (g & 1) + 4 * (j & 3);
+    const int k = sub * 16 + 8 * (g >> 1) + (j >> 2);
+    const int off = Bs + k * P::BROW + (P::bpos(k, n >> 3) << 4) + (n & 4) * 2;
+    const v4s_t lo = ds_read_tr16(off), hi = ds_read_tr16(off + 4 * P::BROW);
+    F.b[q] = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  } else if (q < P::NB) {
     const int row = wn * P::WTN + q * 32 + (lane & 31);
     F.b[q] = *reinterpret_cast<const V8 *>(smem + Bs + row * P::ROW + ((c ^ P::swz(row)) << 4));
   } else {
@@ -1803,24 +1879,34 @@ static const void *ngemm_entry(int inst) {
   }
 }
 
-template <int DT, int TILE>
+template <int DT, int TILE, bool BMN>
 static const void *hgemm_entry_bz(bool beta_zero) {
   using namespace dev;
-  return beta_zero ? reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<DT, TILE>, true>)
-                   : reinterpret_cast<const void *>(&hgemm_kernel<HPolicy<DT, TILE>, false>);
+  using P = HPolicy<DT, TILE, (TILE == 256 ? 8 : 4), BMN>;
+  return beta_zero ? reinterpret_cast<const void *>(&hgemm_kernel<P, true>)
+                   : reinterpret_cast<const void *>(&hgemm_kernel<P, false>);
 }
 
-static const void *hgemm_entry(int dtype, int inst, bool beta_zero) {
+template <int DT, int TILE>
+static const void *hgemm_entry_b(bool beta_zero, bool b_mn) {
+  return b_mn ? hgemm_entry_bz<DT, TILE, true>(beta_zero) : hgemm_entry_bz<DT, TILE, false>(beta_zero);
+}
+
+// b_mn: B read n-contiguous (instances 0 and 1 only)
+static const void *hgemm_entry(int dtype, int inst, bool beta_zero, bool b_mn) {
   if (inst >= 2) return dtype == SK_F16 ? ngemm_entry<SK_F16>(inst) : ngemm_entry<SK_BF16>(inst);
-  if (inst == 1) return dtype == SK_F16 ? hgemm_entry_bz<SK_F16, 128>(beta_zero) : hgemm_entry_bz<SK_BF16, 128>(beta_zero);
-  return dtype == SK_F16 ? hgemm_entry_bz<SK_F16, 256>(beta_zero) : hgemm_entry_bz<SK_BF16, 256>(beta_zero);
+  if (inst == 1)
+    return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 128>(beta_zero, b_mn) : hgemm_entry_b<SK_BF16, 128>(beta_zero, b_mn);
+  return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 256>(beta_zero, b_mn) : hgemm_entry_b<SK_BF16, 256>(beta_zero, b_mn);
 }
 
 int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   dim3 grid(p.grid), block(p.cfg.threads);
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
   const size_t lds = p.cfg.lds_bytes;
-  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst, a.beta == 0.f)
+  if (p.dtype != SK_F32 && !a.a_kmajor) return (int)hipErrorInvalidValue;  // A is always k-contiguous here
+  if (p.dtype != SK_F32 && !a.b_kmajor && p.cfg.inst >= 2) return (int)hipErrorInvalidValue;
+  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst, a.beta == 0.f, !a.b_kmajor)
                                     : sgemm_entry(p.cfg.inst, a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
   void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
   return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
@@ -1891,10 +1977,10 @@ int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu) {
       if (o < nb) nb = o;
     }
   } else {
-    // both beta forms: the smaller occupancy
+    // both beta forms and both orders of B: the smaller occupancy
     nb = 1 << 20;
-    for (int bz = 0; bz < 2 && e == hipSuccess; ++bz) {
-      const void *f = hgemm_entry(dtype, inst, bz != 0);
+    for (int v = 0; v < 4 && e == hipSuccess; ++v) {
+      const void *f = hgemm_entry(dtype, inst, (v & 1) != 0, inst < 2 && (v & 2) != 0);
       e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
       int o = 0;
       if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, f, c.threads, c.lds_bytes);
