@@ -156,23 +156,29 @@ def compare_schedules(torch, sk, S, steps):
 
 def layouts_leg(torch, sk, S, steps):
     """8192^3 fp16 (the hgemm workload's N(0,1)/sqrt(k) operands, alpha = 1)
-    in the storage orders that read both operands in place (A row-major, B
-    column-major, beta 0 and 1; both row-major, B read n-contiguous through
-    transposing LDS reads) and repack A (A column-major, B row-major):
-    `steps` calls per case between one event pair after 3 warm-ups, and 30
-    warm-up calls before the first case."""
+    in every storage order, all read in place (k-contiguous operands as
+    they are, m-contiguous A and n-contiguous B through transposing LDS
+    reads), beta 0 and, for A row-major and B column-major, 1; and B
+    row-major with a leading dimension of n + 4 (not a multiple of 8
+    elements), which is repacked: `steps` calls per case between one event
+    pair after 3 warm-ups, and 30 warm-up calls before the first case."""
     h = make_hgemm_inputs(torch, sk, S, sk.F16)
     n, A, B, C = h["n"], h["A"], h["B"], h["C"]
-    cases = [("A row, B col: B in place", sk.A_ROW_B_COL, 0.0), ("A row, B col: B in place, beta 1", sk.A_ROW_B_COL, 1.0),
-             ("A row, B row: B in place, n-contiguous", sk.A_ROW_B_ROW, 0.0),
-             ("A col, B row: A repacked", sk.A_COL_B_ROW, 0.0)]
+    Bp = torch.empty(n * (n + 4), dtype=B.dtype, device=B.device)
+    Bp.view(n, n + 4)[:, :n].copy_(B.view(n, n))
+    cases = [("A row, B col: k-contiguous", sk.A_ROW_B_COL, 0.0, B, n),
+             ("A row, B col: k-contiguous, beta 1", sk.A_ROW_B_COL, 1.0, B, n),
+             ("A row, B row: B n-contiguous", sk.A_ROW_B_ROW, 0.0, B, n),
+             ("A col, B col: A m-contiguous", sk.A_COL_B_COL, 0.0, B, n),
+             ("A col, B row: both mn-contiguous", sk.A_COL_B_ROW, 0.0, B, n),
+             ("A row, B row, ldb = n + 4: B repacked", sk.A_ROW_B_ROW, 0.0, Bp, n + 4)]
     d0 = sk.make_desc(n, n, n, 1.0, A, n, B, n, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
     for _ in range(30):
         sk.gemm_ex(d0, None)
     torch.cuda.synchronize()
     out = []
-    for name, layout, beta in cases:
-        d = sk.make_desc(n, n, n, 1.0, A, n, B, n, beta, C, n, sk.F16, layout)
+    for name, layout, beta, Bx, ldb in cases:
+        d = sk.make_desc(n, n, n, 1.0, A, n, Bx, ldb, beta, C, n, sk.F16, layout)
         for _ in range(3):
             sk.gemm_ex(d, None)
         torch.cuda.synchronize()

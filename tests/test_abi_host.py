@@ -558,12 +558,19 @@ def test_repack_flags():
     assert p.packs == 0
     p = sk.plan_query(_desc(1000, 1000, 1000, sk.BF16, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_SMALL), 256)
     assert p.packs == 0
-    # ... but an m-contiguous A is repacked
+    # ... and so is an m-contiguous A
     p = sk.plan_query(_desc(1000, 1000, 1000, sk.F16, sk.A_COL_B_ROW), None, 256)
+    assert p.packs == 0
+    p = sk.plan_query(_desc(1000, 1000, 1000, sk.F16, sk.A_COL_B_COL), sk.make_options(tile=sk.TILE_SMALL), 256)
+    assert p.packs == 0
+    # m not a multiple of 8 (lda = m here): A repacked
+    p = sk.plan_query(_desc(1004, 1000, 1000, sk.F16, sk.A_COL_B_ROW), None, 256)
     assert p.packs == 1
-    # the narrow-m instance reads k-contiguous B only
-    p = sk.plan_query(_desc(100, 1000, 1000, sk.F16, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW), 256)
+    # the narrow-m instance reads k-contiguous operands only
+    p = sk.plan_query(_desc(96, 1000, 1000, sk.F16, sk.A_ROW_B_ROW), sk.make_options(tile=sk.TILE_NARROW), 256)
     assert p.packs == 2
+    p = sk.plan_query(_desc(96, 1000, 1000, sk.F16, sk.A_COL_B_COL), sk.make_options(tile=sk.TILE_NARROW), 256)
+    assert p.packs == 1
     # n not a multiple of 8: the last 128-bit chunk of a k-row would straddle n
     d = sk.make_desc(1000, 1004, 1000, 1.0, 1 << 20, 1000, 1 << 21, 1008, 0.0, 1 << 22, 1004, sk.F16,
                      sk.A_ROW_B_ROW)

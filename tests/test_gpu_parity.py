@@ -105,55 +105,77 @@ def test_repacked_operands_buffers_grow_and_shrink_between_calls(dtype):
         assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
 
 
-# ------------------------------ n-contiguous B read in place (fp16/bf16)
+# ------------------- m-contiguous A, n-contiguous B read in place (fp16/bf16)
 
-# m, n, k, pad, alpha, beta: n a multiple of 8 but of neither tile size (a
-# ragged last tile column), k below one iteration and below one 16-byte
-# chunk, several iterations with a tail of k-rows, padded leading
-# dimensions, alpha and beta applied
-BMN_CASES = [(300, 520, 200, 0, 1.0, 0.0), (513, 264, 1000, 8, 0.5, -1.5), (64, 2048, 64, 0, 1.0, 1.0),
-             (256, 256, 5, 0, 1.0, 0.0), (257, 136, 4100, 16, 1.0, 0.0), (1000, 1000, 1000, 0, 0.75, 1.25)]
+# m, n, k, pad, alpha, beta: m and n multiples of 8 but of neither tile size
+# (ragged last tiles), or not multiples of 8 (those operands repacked), k
+# below one iteration and below one 16-byte chunk, several iterations with a
+# tail of k-rows, padded leading dimensions, alpha and beta applied
+MN_CASES = [(296, 520, 200, 0, 1.0, 0.0), (513, 264, 1000, 8, 0.5, -1.5), (64, 2048, 64, 0, 1.0, 1.0),
+            (256, 256, 5, 0, 1.0, 0.0), (264, 136, 4100, 16, 1.0, 0.0), (1000, 1000, 1000, 0, 0.75, 1.25)]
+
+
+def _expected_packs(c):
+    """Repack bits the planner must choose for a Case on the 256 or 128
+    instance: an operand is read in place when its leading dimension is a
+    multiple of 8 elements and, k-contiguous, k is a multiple of 8, or,
+    mn-contiguous, its m (A) or n (B) is."""
+    a_row = c.layout in (sk.A_ROW_B_ROW, sk.A_ROW_B_COL)
+    b_col = c.layout in (sk.A_ROW_B_COL, sk.A_COL_B_COL)
+    a_ok = c.lda % 8 == 0 and (c.k if a_row else c.m) % 8 == 0
+    b_ok = c.ldb % 8 == 0 and (c.k if b_col else c.n) % 8 == 0
+    return (0 if a_ok else 1) | (0 if b_ok else 2)
 
 
 @pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
 @pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
 @pytest.mark.parametrize("sched", ["auto", "dp", "forced7"])
-def test_b_n_contiguous_read_in_place_against_oracle(dtype, tile, sched):
-    """A row-major (k x n) B read in place by the 256 and 128 instances
-    (transposing LDS reads) against the full oracle output, with A
-    k-contiguous (in place) and m-contiguous (repacked)."""
+def test_mn_contiguous_operands_read_in_place_against_oracle(dtype, tile, sched):
+    """Column-major (m-contiguous) A and row-major (n-contiguous) B read in
+    place by the 256 and 128 instances (transposing LDS reads) against the
+    full oracle output, in the three storage orders with such an operand."""
     kw = {"auto": {}, "dp": {"schedule": sk.SCHED_DP}, "forced7": {"forced_grid": 7}}[sched]
-    for (m, n, k, pad, alpha, beta) in BMN_CASES:
-        for layout in (sk.A_ROW_B_ROW, sk.A_COL_B_ROW):
-            _say("case b-n-contiguous", dtype, tile, sched, m, n, k, layout, pad)
+    for (m, n, k, pad, alpha, beta) in MN_CASES:
+        for layout in (sk.A_ROW_B_ROW, sk.A_COL_B_ROW, sk.A_COL_B_COL):
+            _say("case mn-contiguous", dtype, tile, sched, m, n, k, layout, pad)
             c = Case(m, n, k, dtype, layout, 70 + m + k + layout, pad=pad)
             opts = sk.make_options(tile=tile, **kw)
             p = sk.plan_query(c.desc(alpha, beta), opts)
-            assert (p.packs & 2) == 0, p.packs
+            assert p.packs == _expected_packs(c), (p.packs, m, n, k, layout, pad)
             got = c.run(alpha, beta, opts)
             ref, bound = c.reference(alpha, beta)
             assert rel_err(got, dtype, ref, bound) <= TOL[dtype], (m, n, k, layout)
 
 
+def _storage(arr, rows, cols, ld):
+    """(rows x cols) view of a row-major storage array with leading dim ld."""
+    return np.lib.stride_tricks.as_strided(arr, shape=(rows, cols), strides=(ld * arr.itemsize, arr.itemsize))
+
+
 @pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
 @pytest.mark.parametrize("tile", [sk.TILE_LARGE, sk.TILE_SMALL])
-def test_b_n_contiguous_bitwise_equal_to_k_contiguous(dtype, tile):
-    """The same B stored row-major (read in place, transposed in LDS) and
-    column-major (k-contiguous) feeds the MFMAs the same fragments in the
-    same order: the outputs are bit for bit equal, on random inputs, under
+@pytest.mark.parametrize("layout", [sk.A_ROW_B_ROW, sk.A_COL_B_ROW, sk.A_COL_B_COL])
+def test_mn_contiguous_bitwise_equal_to_k_contiguous(dtype, tile, layout):
+    """The same operands stored mn-contiguous (read in place, transposed in
+    LDS) and k-contiguous feed the MFMAs the same fragments in the same
+    order: the outputs are bit for bit equal, on random inputs, under
     data-parallel and split schedules and with beta != 0."""
-    for (m, n, k, pad) in [(300, 520, 200, 0), (1000, 1000, 1000, 0), (257, 136, 4100, 16)]:
-        _say("case b-order bitwise", dtype, tile, m, n, k, pad)
-        c = Case(m, n, k, dtype, sk.A_ROW_B_ROW, 90 + m, pad=pad)
-        Bkn = np.lib.stride_tricks.as_strided(c.B, shape=(k, n), strides=(c.ldb * c.B.itemsize, c.B.itemsize))
-        Bcol = np.ascontiguousarray(Bkn.T).reshape(-1)  # (n x k), ld = k
-        dB2 = to_dev(Bcol, dtype)
+    for (m, n, k, pad) in [(296, 520, 200, 0), (1000, 1000, 1000, 0), (264, 136, 4104, 16)]:
+        _say("case operand order bitwise", dtype, tile, layout, m, n, k, pad)
+        c = Case(m, n, k, dtype, layout, 90 + m + layout, pad=pad)
+        a_row = layout == sk.A_ROW_B_ROW
+        b_col = layout == sk.A_COL_B_COL
+        # the same logical A (m x k) and B (k x n), both stored k-contiguous
+        Ak = _storage(c.A, m, k, c.lda) if a_row else _storage(c.A, k, m, c.lda).T
+        Bk = _storage(c.B, n, k, c.ldb) if b_col else _storage(c.B, k, n, c.ldb).T
+        dA2 = to_dev(np.ascontiguousarray(Ak).reshape(-1), dtype)
+        dB2 = to_dev(np.ascontiguousarray(Bk).reshape(-1), dtype)
         for kw in ({"schedule": sk.SCHED_DP}, {"forced_grid": 7}, {"forced_grid": 255}):
             o = sk.make_options(tile=tile, **kw)
             d1 = c.desc(1.0, 0.5)
-            d2 = sk.make_desc(m, n, k, 1.0, c.dA, c.lda, dB2, k, 0.5, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
+            d2 = sk.make_desc(m, n, k, 1.0, dA2, k, dB2, k, 0.5, c.dC, c.ldc, dtype, sk.A_ROW_B_COL)
             p1, p2 = sk.plan_query(d1, o), sk.plan_query(d2, o)
-            assert (p1.packs & 2) == 0, p1.packs
+            assert p1.packs == 0 and p2.packs == 0, (p1.packs, p2.packs)
             assert (p1.grid, p1.schedule, p1.tile_m) == (p2.grid, p2.schedule, p2.tile_m)
             c.reset_c()
             got1 = c.run(1.0, 0.5, o)

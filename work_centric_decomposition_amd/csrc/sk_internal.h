@@ -338,7 +338,7 @@ int plan_max_peers(const Plan &plan);
 // Does the kernel read this operand directly (true), or from a repacked
 // k-contiguous copy (false)?  `kmajor` = operand contiguous along k; `mn` =
 // its extent along m (A) or n (B); `mn_ok` = the instance has a 16-bit
-// n-contiguous read for it (B on the 256 and 128 HGEMM instances).
+// m- or n-contiguous read for it (the 256 and 128 HGEMM instances).
 bool operand_direct(int dtype, bool kmajor, const void *ptr, int64_t ld, int64_t k, int64_t mn, bool mn_ok);
 
 // Arguments of the GEMM kernels (passed by value).

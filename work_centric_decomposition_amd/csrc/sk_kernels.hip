@@ -77,8 +77,12 @@ typedef __attribute__((address_space(3))) v4s_t *lds_v4s_t;
 __device__ __attribute__((always_inline)) inline v4s_t ds_read_tr16_at(lds_v4s_t __restrict__ p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
 }
-__device__ __forceinline__ v4s_t ds_read_tr16(int byte_off) {
-  return ds_read_tr16_at((lds_v4s_t)(lds_vptr)(smem + byte_off));
+// (at LDS byte address `addr`)
+__device__ __forceinline__ v4s_t ds_read_tr16_abs(int addr) {
+  return ds_read_tr16_at((lds_v4s_t)(uintptr_t)(uint32_t)addr);
+}
+__device__ __forceinline__ int lds_addr(const char *p) {
+  return (int)(uint32_t)(uintptr_t)(lds_vptr)p;
 }
 
 // ---------------------------------------------------------------- elements
@@ -272,12 +276,13 @@ typedef float f16v_t __attribute__((ext_vector_type(16)));
 // fragment reads per MFMA) also builds and gives the same bits, but one wave
 // per SIMD cannot hide its own LDS and barrier waits: about 6 % slower on
 // large squares, so it is not instantiated.
-template <int DT, int TILE, int W = (TILE == 256 ? 8 : 4), bool BMN_ = false>
+template <int DT, int TILE, int W = (TILE == 256 ? 8 : 4), bool BMN_ = false, bool AMN_ = false>
 struct HPolicy {
   static constexpr int ET = DT;
-  // BMN: B stored n-contiguous (row-major k x n), staged in LDS as BK rows
-  // of BN values and read into the MFMA layout with transposing LDS reads
-  static constexpr bool BMN = BMN_;
+  // BMN / AMN: B stored n-contiguous (row-major k x n) / A stored
+  // m-contiguous (column-major m x k), staged in LDS as BK rows of BN / BM
+  // values and read into the MFMA layout with transposing LDS reads
+  static constexpr bool BMN = BMN_, AMN = AMN_;
   static constexpr int BM = TILE, BN = TILE, BK = 64, NSTAGE = 2;
   static constexpr int WAVES = W, NT = 64 * WAVES;
   // waves per SIMD the register budget is sized for
@@ -303,16 +308,18 @@ struct HPolicy {
   // distinct 16-byte bank groups of gfx950's 64 banks (256 bytes hold
   // 256/ROW rows; consecutive groups of them get distinct XOR masks).
   static __device__ __forceinline__ int swz(int r) { return (r / (256 / ROW)) % (ROW / 16); }
-  // BMN: k-row r of a B stage holds BN values (BN / 8 chunks of 16 bytes);
-  // chunk c sits at position c ^ (4 (r & 3)).  A transposing read fetches a
-  // 4 (k) x 16 (n) block per 16 lanes, 8 bytes per lane; with this XOR the 8
-  // blocks of 32 lanes (two column halves x four rows) fall in distinct
-  // 32-byte bank windows, since a row is a multiple of 256 bytes.
-  static constexpr int BROW = BN * 2;                 // bytes of one k-row of a BMN stage
-  static constexpr int BCPR = BN / 8;                 // chunks per k-row
-  static constexpr int BRPL = 1024 / BROW;            // k-rows per 1 KiB load
-  static __device__ __forceinline__ int bpos(int r, int c) { return c ^ (4 * (r & 3)); }
-  static_assert(!BMN || (BROW % 256 == 0 && BCPR >= 16), "mn-major B stage layout");
+  // mn-contiguous stages (BMN, AMN): k-row r holds TILE values (TILE / 8
+  // chunks of 16 bytes); chunk c sits at position c ^ (4 (r & 3)).  A
+  // transposing read fetches a 4 (k) x 16 (m or n) block per 16 lanes, 8
+  // bytes per lane; with this XOR the 8 blocks of 32 lanes (two column
+  // halves x four rows) fall in distinct 32-byte bank windows, since a row
+  // is a multiple of 256 bytes.  BM == BN, so A and B stages of this form
+  // share the layout and the lanes' load positions.
+  static constexpr int MNROW = BN * 2;                // bytes of one k-row of an mn-contiguous stage
+  static constexpr int MNCPR = BN / 8;                // chunks per k-row
+  static constexpr int MNRPL = 1024 / MNROW;          // k-rows per 1 KiB load
+  static __device__ __forceinline__ int mnpos(int r, int c) { return c ^ (4 * (r & 3)); }
+  static_assert(!(BMN || AMN) || (BM == BN && MNROW % 256 == 0 && MNCPR >= 16), "mn-contiguous stage layout");
   struct Acc { f16v_t v[MB * NB]; };
   static __device__ __forceinline__ f4_t get4(const Acc &c, int i) {
     const f16v_t &b = c.v[i >> 2];
@@ -347,36 +354,46 @@ struct HLoader {
   int chunk2[2];
   __device__ __forceinline__ int chunk(int j) const { return chunk2[j & 1]; }
   int lds_a;            // LDS byte offset of this wave's first A load (stage 0)
-  // BMN: k-row of this lane's first B load within a stage (load j: + j BRPL),
-  // and the bytes B advances per k-iteration
+  // mn-contiguous operands: k-row of this lane's first load within a stage
+  // (load j: + j MNRPL), and the bytes A and B advance per k-iteration
   int krow0;
-  int bstep;
+  int astep, bstep;
+  // does load j of this lane fetch k-row krow0 + j MNRPL of the iteration
+  // (a row before k)?
+  __device__ __forceinline__ bool krow_ok(int j, int left) const { return (krow0 + j * P::MNRPL) * 2 < left; }
 
   __device__ __forceinline__ void init(const KernelArgs &a, int m0, int n0) {
     static_assert(P::ROW == 128 && P::LOADS % 2 == 0, "chunk of load j depends only on j & 1");
     constexpr int ES = 2;
     const int w = wave_id(), lane = threadIdx.x & 63;
     const int64_t lda_b = a.lda * ES, ldb_b = a.ldb * ES;
-    const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * lda_b;
-    // BMN: element (k, n) of B at B + (k ldb + n) 2; the descriptor starts
-    // at column n0 and ends at the last element, the iteration's k-rows go
-    // in soffset
+    // mn-contiguous operands: element (k, n) of B at B + (k ldb + n) 2
+    // (element (i, k) of A at A + (k lda + i) 2); the descriptor starts at
+    // column n0 (row m0) and ends at the last element, the iteration's
+    // k-rows go in soffset
+    const char *Ab = static_cast<const char *>(a.A) + (int64_t)m0 * (P::AMN ? ES : lda_b);
     const char *Bb = static_cast<const char *>(a.B) + (int64_t)n0 * (P::BMN ? ES : ldb_b);
-    ra = make_rsrc(Ab, (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)a.a_kext * ES);
-    if constexpr (P::BMN) {
+    if constexpr (P::AMN)
+      ra = make_rsrc(Ab, ((int64_t)(a.k - 1) * a.lda + (a.m - m0)) * ES);
+    else
+      ra = make_rsrc(Ab, (int64_t)(a.m - 1 - m0) * lda_b + (int64_t)a.a_kext * ES);
+    if constexpr (P::BMN)
       rb = make_rsrc(Bb, ((int64_t)(a.k - 1) * a.ldb + (a.n - n0)) * ES);
+    else
+      rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
+    if constexpr (P::AMN || P::BMN) {
+      astep = (int)(P::BK * lda_b);
       bstep = (int)(P::BK * ldb_b);
-      // lane L of load j fills position L % BCPR of k-row krow0 + j BRPL;
+      // lane L of load j fills position L % MNCPR of k-row krow0 + j MNRPL;
       // the chunk stored there is the inverse of the XOR
-      krow0 = w * P::LOADS * P::BRPL + lane / P::BCPR;
+      krow0 = w * P::LOADS * P::MNRPL + lane / P::MNCPR;
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
-        const int kr = krow0 + j * P::BRPL;
-        const int c = P::bpos(kr, lane % P::BCPR);
-        vb[j] = n0 + c * 8 < a.n ? (uint32_t)((int64_t)kr * ldb_b + c * 16) : kOOB;
+        const int kr = krow0 + j * P::MNRPL;
+        const int c = P::mnpos(kr, lane % P::MNCPR);
+        if constexpr (P::AMN) va[j] = m0 + c * 8 < a.m ? (uint32_t)((int64_t)kr * lda_b + c * 16) : kOOB;
+        if constexpr (P::BMN) vb[j] = n0 + c * 8 < a.n ? (uint32_t)((int64_t)kr * ldb_b + c * 16) : kOOB;
       }
-    } else {
-      rb = make_rsrc(Bb, (int64_t)(a.n - 1 - n0) * ldb_b + (int64_t)a.b_kext * ES);
     }
     constexpr int CPR = P::ROW / 16;  // chunks per row
 #pragma unroll
@@ -384,7 +401,7 @@ struct HLoader {
       const int row = (w * P::LOADS + j) * P::ROWS_PER_LOAD + lane / CPR;
       const int c = (lane % CPR) ^ P::swz(row);
       if (j < 2) chunk2[j] = c;
-      va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
+      if constexpr (!P::AMN) va[j] = row < a.m - m0 ? (uint32_t)(row * lda_b + c * 16) : kOOB;
       if constexpr (!P::BMN) vb[j] = row < a.n - n0 ? (uint32_t)(row * ldb_b + c * 16) : kOOB;
     }
     lds_a = w * P::LOADS * 1024;
@@ -399,10 +416,14 @@ struct HLoader {
     const int k0b = kit * P::BK * 2;
     const int left = live ? (a.k - kit * P::BK) * 2 : 0;
     const int dst = ((q & 1) ? P::b_off(stage) : P::a_off(stage)) + lds_a + j * 1024;
-    if (P::BMN && (q & 1)) {  // k-row kr of the iteration: rows at or past k read as zeros
-      const bool ok = (krow0 + j * P::BRPL) * 2 < left;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + dst), 16, ok ? vb[j] : kOOB, kit * bstep, 0,
-                                               0);
+    if (P::BMN && (q & 1)) {  // k-rows at or past k read as zeros
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + dst), 16, krow_ok(j, left) ? vb[j] : kOOB,
+                                               kit * bstep, 0, 0);
+      return;
+    }
+    if (P::AMN && !(q & 1)) {
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + dst), 16, krow_ok(j, left) ? va[j] : kOOB,
+                                               kit * astep, 0, 0);
       return;
     }
     const bool ok = chunk(j) * 16 < left;
@@ -414,11 +435,12 @@ struct HLoader {
     const int k0b = kit * P::BK * 2;
     const int left = (a.k - kit * P::BK) * 2;  // bytes of k from k0
     const int abase = P::a_off(stage) + lds_a, bbase = P::b_off(stage) + lds_a;
-    const int k0bb = P::BMN ? kit * bstep : k0b;  // B's soffset
+    const int k0ba = P::AMN ? kit * astep : k0b;  // A's and B's soffsets
+    const int k0bb = P::BMN ? kit * bstep : k0b;
     if (left >= P::BK * 2) {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16, va[j], k0b, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16, va[j], k0ba, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
                                                  vb[j], k0bb, 0, 0);
       }
@@ -426,9 +448,10 @@ struct HLoader {
 #pragma unroll
       for (int j = 0; j < P::LOADS; ++j) {
         const bool ok = chunk(j) * 16 < left;
-        const bool okb = P::BMN ? (krow0 + j * P::BRPL) * 2 < left : ok;
+        const bool oka = P::AMN ? krow_ok(j, left) : ok;
+        const bool okb = P::BMN ? krow_ok(j, left) : ok;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_vptr)(smem + abase + j * 1024), 16,
-                                                 ok ? va[j] : kOOB, k0b, 0, 0);
+                                                 oka ? va[j] : kOOB, k0ba, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_vptr)(smem + bbase + j * 1024), 16,
                                                  okb ? vb[j] : kOOB, k0bb, 0, 0);
       }
@@ -472,18 +495,39 @@ __device__ __forceinline__ void h_frag_one(int stage, int sub, int wm, int wn, i
   const int lane = threadIdx.x & 63;
   const int As = P::a_off(stage), Bs = P::b_off(stage);
   const int c = sub * 2 + (lane >> 5);
-  if (q < P::NB && P::BMN) {
-    // lane 16 g + j addresses the four values (k, n .. n + 3) with
-    // k = 16 sub + 8 (g / 2) + j / 4 and n = 16 (g % 2) + 4 (j % 4) within
-    // the block; the transposing read hands lane 16 g + i the values
-    // (k0 .. k0 + 3, n0 + i) of its 16-lane group.  A second read 4 rows
-    // further completes the eight k of the k-contiguous fragment.
+  if ((q < P::NB && P::BMN) || (q >= P::NB && P::AMN)) {
+    // lane 16 g + j addresses the four values (k, x .. x + 3) with
+    // k = 16 sub + 8 (g / 2) + j / 4 and x = 16 (g % 2) + 4 (j % 4) within
+    // the 32-wide block (x: n for B, m for A); the transposing read hands
+    // lane 16 g + i the values (k0 .. k0 + 3, x0 + i) of its 16-lane group.
+    // A second read 4 rows further completes the eight k of the
+    // k-contiguous fragment.
+    //
+    // Chunk (32 blk + xl) / 8 of k-row k sits at position 4 (blk ^ (k & 3))
+    // + xl / 8 (blk: the 32-wide block within the tile, xl < 32), so the
+    // address is the lane's part, bits outside 6..8, plus 64 (blk ^ (k & 3))
+    // in bits 6..8: one lane base XORed with 64 blk for every block, so
+    // that the blocks of a wave share one address register.  The LDS
+    // address of the stage (whose bits are all above bit 8) is added first;
+    // the XOR is an explicit instruction at each read, which the compiler
+    // cannot hoist out of the loop into one register per block.
     const int g = lane >> 4, j = lane & 15;
-    const int n = wn * P::WTN + q * 32 + 16 * (g & 1) + 4 * (j & 3);
-    const int k = sub * 16 + 8 * (g >> 1) + (j >> 2);
-    const int off = Bs + k * P::BROW + (P::bpos(k, n >> 3) << 4) + (n & 4) * 2;
-    const v4s_t lo = ds_read_tr16(off), hi = ds_read_tr16(off + 4 * P::BROW);
-    F.b[q] = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    const int kl = 8 * (g >> 1) + (j >> 2), xl = 16 * (g & 1) + 4 * (j & 3);
+    const int lp = kl * P::MNROW + (xl >> 3) * 16 + (xl & 4) * 2 + 64 * (kl & 3);
+    const int blk = q < P::NB ? wn * (P::WTN / 32) + q : wm * (P::WTM / 32) + (q - P::NB);
+    static_assert(P::MNROW >= 512 || P::BN / 32 <= 4, "block bits below the k-row bits");
+    static_assert(P::A_BYTES % (16 * P::MNROW) == 0 && P::B_BYTES % (16 * P::MNROW) == 0,
+                  "stage bases above the lane part");
+    const int base = lds_addr(smem) + (q < P::NB ? Bs : As) + lp;
+    int xb;
+    asm volatile("v_xor_b32 %0, %1, %2" : "=v"(xb) : "s"(64 * blk), "v"(base));
+    const int addr = xb + sub * 16 * P::MNROW;
+    const v4s_t lo = ds_read_tr16_abs(addr), hi = ds_read_tr16_abs(addr + 4 * P::MNROW);
+    const V8 v = __builtin_bit_cast(V8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    if (q < P::NB)
+      F.b[q] = v;
+    else
+      F.a[q - P::NB] = v;
   } else if (q < P::NB) {
     const int row = wn * P::WTN + q * 32 + (lane & 31);
     F.b[q] = *reinterpret_cast<const V8 *>(smem + Bs + row * P::ROW + ((c ^ P::swz(row)) << 4));
@@ -1879,34 +1923,38 @@ static const void *ngemm_entry(int inst) {
   }
 }
 
-template <int DT, int TILE, bool BMN>
+template <int DT, int TILE, bool BMN, bool AMN>
 static const void *hgemm_entry_bz(bool beta_zero) {
   using namespace dev;
-  using P = HPolicy<DT, TILE, (TILE == 256 ? 8 : 4), BMN>;
+  using P = HPolicy<DT, TILE, (TILE == 256 ? 8 : 4), BMN, AMN>;
   return beta_zero ? reinterpret_cast<const void *>(&hgemm_kernel<P, true>)
                    : reinterpret_cast<const void *>(&hgemm_kernel<P, false>);
 }
 
 template <int DT, int TILE>
-static const void *hgemm_entry_b(bool beta_zero, bool b_mn) {
-  return b_mn ? hgemm_entry_bz<DT, TILE, true>(beta_zero) : hgemm_entry_bz<DT, TILE, false>(beta_zero);
+static const void *hgemm_entry_b(bool beta_zero, bool b_mn, bool a_mn) {
+  if (a_mn)
+    return b_mn ? hgemm_entry_bz<DT, TILE, true, true>(beta_zero) : hgemm_entry_bz<DT, TILE, false, true>(beta_zero);
+  return b_mn ? hgemm_entry_bz<DT, TILE, true, false>(beta_zero) : hgemm_entry_bz<DT, TILE, false, false>(beta_zero);
 }
 
-// b_mn: B read n-contiguous (instances 0 and 1 only)
-static const void *hgemm_entry(int dtype, int inst, bool beta_zero, bool b_mn) {
+// b_mn / a_mn: B read n-contiguous / A read m-contiguous (instances 0 and 1)
+static const void *hgemm_entry(int dtype, int inst, bool beta_zero, bool b_mn, bool a_mn) {
   if (inst >= 2) return dtype == SK_F16 ? ngemm_entry<SK_F16>(inst) : ngemm_entry<SK_BF16>(inst);
   if (inst == 1)
-    return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 128>(beta_zero, b_mn) : hgemm_entry_b<SK_BF16, 128>(beta_zero, b_mn);
-  return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 256>(beta_zero, b_mn) : hgemm_entry_b<SK_BF16, 256>(beta_zero, b_mn);
+    return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 128>(beta_zero, b_mn, a_mn)
+                           : hgemm_entry_b<SK_BF16, 128>(beta_zero, b_mn, a_mn);
+  return dtype == SK_F16 ? hgemm_entry_b<SK_F16, 256>(beta_zero, b_mn, a_mn)
+                         : hgemm_entry_b<SK_BF16, 256>(beta_zero, b_mn, a_mn);
 }
 
 int launch_gemm(const Plan &p, const KernelArgs &a, hipStream_t stream) {
   dim3 grid(p.grid), block(p.cfg.threads);
   const int vec_ok = c_vec_ok(a, p.dtype) ? 1 : 0;
   const size_t lds = p.cfg.lds_bytes;
-  if (p.dtype != SK_F32 && !a.a_kmajor) return (int)hipErrorInvalidValue;  // A is always k-contiguous here
-  if (p.dtype != SK_F32 && !a.b_kmajor && p.cfg.inst >= 2) return (int)hipErrorInvalidValue;
-  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst, a.beta == 0.f, !a.b_kmajor)
+  // the narrow instance reads k-contiguous operands only
+  if (p.dtype != SK_F32 && (!a.a_kmajor || !a.b_kmajor) && p.cfg.inst >= 2) return (int)hipErrorInvalidValue;
+  const void *f = p.dtype != SK_F32 ? hgemm_entry(p.dtype, p.cfg.inst, a.beta == 0.f, !a.b_kmajor, !a.a_kmajor)
                                     : sgemm_entry(p.cfg.inst, a.a_kmajor != 0, a.b_kmajor != 0, a.abft != 0);
   void *params[] = {const_cast<KernelArgs *>(&a), const_cast<int *>(&vec_ok)};
   return (int)hipLaunchKernel(f, grid, block, params, lds, stream);
@@ -1977,10 +2025,10 @@ int kernel_occupancy(int dtype, bool abft, int inst, int *blocks_per_cu) {
       if (o < nb) nb = o;
     }
   } else {
-    // both beta forms and both orders of B: the smaller occupancy
+    // both beta forms and both orders of A and of B: the smaller occupancy
     nb = 1 << 20;
-    for (int v = 0; v < 4 && e == hipSuccess; ++v) {
-      const void *f = hgemm_entry(dtype, inst, (v & 1) != 0, inst < 2 && (v & 2) != 0);
+    for (int v = 0; v < 8 && e == hipSuccess; ++v) {
+      const void *f = hgemm_entry(dtype, inst, (v & 1) != 0, inst < 2 && (v & 2) != 0, inst < 2 && (v & 4) != 0);
       e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, c.lds_bytes);
       int o = 0;
       if (e == hipSuccess) e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&o, f, c.threads, c.lds_bytes);

@@ -80,9 +80,9 @@ bool operand_direct(int dtype, bool kmajor, const void *ptr, int64_t ld, int64_t
   if (ld % vec != 0) return false;
   if (kmajor && k % vec != 0) return false;  // a 128-bit chunk never straddles k
   if (dtype != SK_F32 && !kmajor) {
-    // HGEMM reads an n-contiguous B in place on the 256 and 128 instances:
-    // whole 128-bit chunks along n, and byte offsets over all of k that fit
-    // a 31-bit buffer offset
+    // HGEMM reads an m-contiguous A or n-contiguous B in place on the 256
+    // and 128 instances: whole 128-bit chunks along m or n, and byte offsets
+    // over all of k that fit a 31-bit buffer offset
     if (!mn_ok || mn % vec != 0) return false;
     if ((k + 64) * ld * es + 1024 >= 0x7FFFFFFF) return false;
   }
@@ -242,7 +242,7 @@ static int plan_inst(const sk_gemm_desc &d, const sk_options &o, int inst, int s
   P.r = (int)(P.tiles % slots);
   const bool a_kmajor = d.layout == SK_A_ROW_B_ROW || d.layout == SK_A_ROW_B_COL;
   const bool b_kmajor = d.layout == SK_A_ROW_B_COL || d.layout == SK_A_COL_B_COL;
-  P.pack_a = !operand_direct(d.dtype, a_kmajor, d.A, d.lda, d.k, d.m, false);
+  P.pack_a = !operand_direct(d.dtype, a_kmajor, d.A, d.lda, d.k, d.m, inst < 2);
   P.pack_b = !operand_direct(d.dtype, b_kmajor, d.B, d.ldb, d.k, d.n, inst < 2);
   if (P.tiles == 0 || P.ipt == 0) {  // nothing to decompose (quick-return paths)
     P.schedule = SK_SCHED_DP;
