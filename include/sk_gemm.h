@@ -58,11 +58,12 @@ typedef enum { SK_F32 = 0, SK_F16 = 1, SK_BF16 = 2 } sk_dtype;
  * SK_A_ROW_B_COL keeps both operands contiguous along k.  Operands are read
  * in place when the base is 16-byte aligned, the leading dimension a
  * multiple of 16 bytes, and: for a k-contiguous operand, k a multiple of 16
- * bytes of elements; fp32, either order; fp16/bf16 A, k-contiguous only;
- * fp16/bf16 B stored n-contiguous (row-major), n a multiple of 8,
- * 2 (k + 64) ldb + 1024 below 2^31 - 1 (bytes) and the LARGE or SMALL tile
- * instance (transposed in LDS).  Any other operand is repacked into a k-contiguous copy first (see
- * sk_gemm_ex). */
+ * bytes of elements; fp32, either order; fp16/bf16 A stored m-contiguous
+ * (column-major) or B stored n-contiguous (row-major): m (A) or n (B) a
+ * multiple of 8, 2 (k + 64) ld + 1024 below 2^31 - 1 (bytes) and the LARGE
+ * or SMALL tile instance (transposed in LDS; NARROW reads k-contiguous
+ * operands only).  Any other operand is repacked into a k-contiguous copy
+ * first (see sk_gemm_ex). */
 typedef enum {
   SK_A_ROW_B_ROW = 0,
   SK_A_ROW_B_COL = 1,
