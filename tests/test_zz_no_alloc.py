@@ -35,12 +35,16 @@ def _both(c: Case, opts, alpha=1.0, beta=0.0):
 
 # (m, n, k, dtype, layout, options, alpha, beta): a forced Stream-K grid
 # (partials in the scratch), the XCD-aware split on both fp16/bf16 tiles,
-# fp32 with a split, matrix-vector products with chunk sums in the scratch
+# mn-contiguous fp16 operands, fp32 with a split, matrix-vector products
+# with chunk sums in the scratch
 CASES = [
     ("fp16 forced grid 200", (1000, 900, 3000, sk.F16, sk.A_ROW_B_COL), dict(forced_grid=200), 1.0, 0.0),
     ("bf16 xcd large tile", (256 * 17, 256 * 16, 1024, sk.BF16, sk.A_ROW_B_COL),
      dict(schedule=sk.SCHED_XCD_ALIGNED, tile=sk.TILE_LARGE), 1.0, 0.0),
     ("fp16 auto small tile", (1000, 1000, 5000, sk.F16, sk.A_ROW_B_COL), dict(tile=sk.TILE_SMALL), 0.5, 1.0),
+    # m-contiguous A and n-contiguous B read in place (m and n stay
+    # multiples of 8 after the shrink)
+    ("fp16 mn-contiguous operands", (1032, 1008, 3000, sk.F16, sk.A_COL_B_ROW), dict(forced_grid=100), 1.0, 1.0),
     ("fp32 forced grid 7", (520, 600, 3000, sk.F32, sk.A_ROW_B_ROW), dict(forced_grid=7), 1.0, 1.0),
     ("fp32 auto", (3000, 2960, 200, sk.F32, sk.A_ROW_B_ROW), {}, 1.0, 0.0),
     ("fp32 small tile", (1024, 1000, 1024, sk.F32, sk.A_ROW_B_ROW), dict(tile=sk.TILE_SMALL), 1.0, 1.0),
