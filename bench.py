@@ -291,9 +291,11 @@ def skinny_shapes(S, count=8, min_tmin_us=20.0):
 def skinny_leg(torch, sk, S, min_ms=20.0):
     """Skinny fp16 GEMMs (A row-major, B column-major, alpha=1, beta=0) under
     AUTO, on the narrow-m tile (Stream-K, XCD-aware split) and data-parallel
-    on the 256x256 tile, each timed as R launches back to back between one
-    event pair (at least `min_ms` per measurement, host enqueue hidden behind
-    a spin kernel).  Bytes = 2(mk + kn + mn), read and written once each."""
+    on the 256x256 tile, and under AUTO with the same B buffer taken as
+    row-major (n-contiguous: `x @ W` with W stored k x n), each timed as R
+    launches back to back between one event pair (at least `min_ms` per
+    measurement, host enqueue hidden behind a spin kernel).  Bytes =
+    2(mk + kn + mn), read and written once each."""
     out = []
     g = torch.Generator(device="cuda")
     g.manual_seed(S.SEED_SWEEP)
@@ -302,18 +304,20 @@ def skinny_leg(torch, sk, S, min_ms=20.0):
         B = torch.randn(k * n, generator=g, device="cuda").to(torch.float16)
         C = torch.empty(m * n, device="cuda", dtype=torch.float16)
         d = sk.make_desc(m, n, k, 1.0, A, k, B, k, 0.0, C, n, sk.F16, sk.A_ROW_B_COL)
+        d_brow = sk.make_desc(m, n, k, 1.0, A, k, B, n, 0.0, C, n, sk.F16, sk.A_ROW_B_ROW)
         by = 2.0 * (m * k + k * n + m * n)
         fl = 2.0 * m * n * k
         tmin = max(fl / (PEAK_TFLOPS["f16"] * 1e6), by / (PEAK_HBM_GBS * 1e3))
         row = {"shape": [m, n, k], "bytes": int(by), "tmin_us": round(tmin, 2)}
-        for name, opts in (("auto", sk.make_options()),
-                           ("narrow", sk.make_options(tile=sk.TILE_NARROW)),
-                           ("dp", sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE))):
-            us, R, _ = back_to_back_us(torch, lambda: sk.gemm_ex(d, opts), min_ms=min_ms)
-            p = sk.plan_query(d, opts)
+        for name, dd, opts in (("auto", d, sk.make_options()),
+                               ("narrow", d, sk.make_options(tile=sk.TILE_NARROW)),
+                               ("dp", d, sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE)),
+                               ("auto_b_row", d_brow, sk.make_options())):
+            us, R, _ = back_to_back_us(torch, lambda: sk.gemm_ex(dd, opts), min_ms=min_ms)
+            p = sk.plan_query(dd, opts)
             row[name] = {"us": round(us, 2), "GB_s": round(by / us / 1e3, 1), "tflops": round(fl / us / 1e6, 1),
                          "util": round(tmin / us, 4), "tile": [int(p.tile_m), int(p.tile_n)], "grid": int(p.grid),
-                         "schedule": int(p.schedule), "launches": R}
+                         "schedule": int(p.schedule), "packs": int(p.packs), "launches": R}
         out.append(row)
         del A, B, C
     return out
