@@ -10,14 +10,15 @@ import functools
 import numpy as np
 import pytest
 
+import oracle
 import sk_synth as S
 import work_centric_decomposition_amd as sk
 
 pytestmark = pytest.mark.gpu
 
 torch = pytest.importorskip("torch")
-from gemm_check import (TOL, Case, decode, rel_err, sampled_err, split_tiles,  # noqa: E402
-                        tile_sample_indices, to_dev)
+from gemm_check import (TOL, Case, decode, from_dev, rel_err, sampled_err,  # noqa: E402
+                        split_tiles, tile_sample_indices, to_dev)
 
 DTYPES = [sk.F32, sk.F16, sk.BF16]
 LAYOUTS = [sk.A_ROW_B_ROW, sk.A_ROW_B_COL, sk.A_COL_B_ROW, sk.A_COL_B_COL]
@@ -184,6 +185,46 @@ def test_mn_contiguous_bitwise_equal_to_k_contiguous(dtype, tile, layout):
             torch.cuda.synchronize()
             got2 = c.result()
             assert np.array_equal(got1.view(np.uint8), got2.view(np.uint8)), (m, n, k, kw)
+
+
+@pytest.mark.parametrize("layout", [sk.A_ROW_B_ROW, sk.A_COL_B_ROW])
+def test_mn_contiguous_offsets_at_the_31_bit_limit(layout):
+    """mn-contiguous operands whose k-rows span almost 2^31 bytes, the most
+    the in-place read takes (2 (k + 64) ld + 1024 below 2^31 - 1): the
+    buffer offsets of the last k-rows sit just under 2^31.  The leading
+    dimension is padded far beyond m and n, the padding holds NaN (never
+    read: chunks at or past m or n are fetched out of range), and every
+    128 x 128 output tile and split tile is checked against the oracle on
+    the compact matrices.  A leading dimension 8 elements longer crosses the
+    limit and the operand is repacked instead."""
+    dtype, m, n, k, ld = sk.F16, 1024, 1024, 65464, 16384
+    assert 2 * (k + 64) * ld + 1024 < 2 ** 31 - 1 < 2 * (k + 64) * (ld + 8) + 1024
+    a_col = layout == sk.A_COL_B_ROW
+    _say("case 31-bit offsets", layout, m, n, k, ld)
+    A = S.matrix(41, S.STREAM_A, m, k, dtype, "normal", "col" if a_col else "row", None, 1 / np.sqrt(k))
+    B = S.matrix(41, S.STREAM_B, k, n, dtype, "normal", "row")
+
+    def padded(host, outer, contig):
+        t = torch.full(((outer - 1) * ld + contig,), float("nan"), dtype=torch.float16, device="cuda")
+        t.as_strided((outer, contig), (ld, 1)).copy_(to_dev(host, dtype).view(outer, contig))
+        return t
+
+    dA, lda = (padded(A, k, m), ld) if a_col else (to_dev(A, dtype), k)
+    dB, ldb = padded(B, k, n), ld
+    dC = torch.zeros(m * n, dtype=torch.float16, device="cuda")
+    d = sk.make_desc(m, n, k, 1.0, dA, lda, dB, ldb, 0.0, dC, n, dtype, layout)
+    p = sk.plan_query(d)
+    assert p.packs == 0
+    sk.gemm_ex(d, None)
+    torch.cuda.synchronize()
+    got = from_dev(dC, dtype).reshape(m, n)
+    rows, cols = tile_sample_indices(m, n, 31, split=split_tiles(p), split_tm=p.tile_m, split_tn=p.tile_n,
+                                     tiles_n=p.tiles_n)
+    ref, bound = oracle.gemm_entries(m, n, k, 1.0, A, m if a_col else k, B, n, 0.0, None, n, dtype, layout,
+                                     rows, cols)
+    assert sampled_err(got, dtype, rows, cols, ref, bound) <= TOL[dtype]
+    d8 = sk.make_desc(m, n, k, 1.0, dA, lda, dB, ld + 8, 0.0, dC, n, dtype, layout)
+    assert sk.plan_query(d8).packs & 2
 
 
 # ------------------------------------------------ the narrow-m instance
