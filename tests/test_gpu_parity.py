@@ -483,18 +483,21 @@ def test_sgemm_square_sweep_sampled(nsq):
 
 
 @pytest.mark.parametrize("dtype", [sk.F16, sk.BF16])
-def test_hgemm_8192_sampled(dtype):
-    """8192^3, A row-major and B column-major (both k-contiguous), entries
-    N(0,1)/sqrt(k), alpha=1 beta=0, fp32 accumulation.  Every 128 x 128
-    output tile (4096 of them) is checked at its first and last rows and
-    columns and two more entries; Freivalds as a supplement."""
-    _say("case hgemm 8192", dtype)
+@pytest.mark.parametrize("layout", [sk.A_ROW_B_COL, sk.A_COL_B_ROW])
+def test_hgemm_8192_sampled(dtype, layout):
+    """8192^3, A row-major and B column-major (both k-contiguous), and A
+    column-major and B row-major (both read in place mn-contiguous, through
+    transposing LDS reads), entries N(0,1)/sqrt(k), alpha=1 beta=0, fp32
+    accumulation.  Every 128 x 128 output tile (4096 of them) is checked at
+    its first and last rows and columns and two more entries; Freivalds as a
+    supplement."""
+    _say("case hgemm 8192", dtype, layout)
     n = 8192
-    c = Case(n, n, n, dtype, sk.A_ROW_B_COL, S.SEED_HGEMM_LARGE, dist="normal",
+    c = Case(n, n, n, dtype, layout, S.SEED_HGEMM_LARGE, dist="normal",
              scale=1 / np.sqrt(n), with_c=False)
     got = c.run(1.0, 0.0)
-    p = sk.plan_query(sk.make_desc(n, n, n, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype,
-                                   sk.A_ROW_B_COL))
+    p = sk.plan_query(sk.make_desc(n, n, n, 1, c.dA, c.lda, c.dB, c.ldb, 0, c.dC, c.ldc, dtype, layout))
+    assert p.packs == 0
     rows, cols = tile_sample_indices(n, n, 8192 + dtype, split=split_tiles(p), split_tm=p.tile_m,
                                      split_tn=p.tile_n, tiles_n=p.tiles_n)
     ref, bound = c.reference_entries(rows, cols)
