@@ -21,7 +21,11 @@
  *    sk_layout; C is always row-major (element (i, j) at C[i * ldc + j]).
  *    Leading dimensions are in elements.  Row-major A needs lda >= k,
  *    column-major A needs lda >= m; row-major B needs ldb >= n, column-major
- *    B needs ldb >= k; ldc >= n.
+ *    B needs ldb >= k; ldc >= n.  A column-major C (element (i, j) at
+ *    C[j * ldc + i]) is the row-major n x m matrix C^T = B^T A^T: call with
+ *    m and n swapped, B's pointer and leading dimension as the first operand
+ *    and A's as the second, and each operand's storage order flipped (B
+ *    column-major becomes a row-major first operand, and so on).
  *  - A, B and C are device pointers owned by the caller; the library never
  *    frees them.  A and B are read only; C is read only when beta != 0.
  *  - Calls are asynchronous: work is enqueued on `stream` (0 = the default

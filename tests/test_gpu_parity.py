@@ -227,6 +227,30 @@ def test_mn_contiguous_offsets_at_the_31_bit_limit(layout):
     assert sk.plan_query(d8).packs & 2
 
 
+# storage order of the first and second operands of C^T = B^T A^T
+_SWAPPED = {sk.A_ROW_B_ROW: sk.A_COL_B_COL, sk.A_ROW_B_COL: sk.A_ROW_B_COL,
+            sk.A_COL_B_ROW: sk.A_COL_B_ROW, sk.A_COL_B_COL: sk.A_ROW_B_ROW}
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_column_major_c_by_transposition(dtype, layout):
+    """A column-major C computed as the row-major C^T = B^T A^T, as the
+    header describes (m and n swapped, B first, each storage order flipped),
+    against the oracle's C, with beta != 0 reading the column-major C_in."""
+    for (m, n, k) in [(300, 520, 200), (520, 264, 1000)]:
+        _say("case column-major C", dtype, layout, m, n, k)
+        c = Case(m, n, k, dtype, layout, 500 + m + layout)
+        cin = _storage(c.Cin, m, n, c.ldc)
+        dCt = to_dev(np.ascontiguousarray(cin.T).reshape(-1), dtype)  # element (i, j) at j * m + i
+        rc = sk.gemm(n, m, k, 0.75, c.dB, c.ldb, c.dA, c.lda, 1.25, dCt, m, dtype, _SWAPPED[layout])
+        assert rc == sk.OK
+        torch.cuda.synchronize()
+        got = from_dev(dCt, dtype).reshape(n, m).T
+        ref, bound = c.reference(0.75, 1.25)
+        assert rel_err(np.ascontiguousarray(got), dtype, ref, bound) <= TOL[dtype], (m, n, k)
+
+
 # ------------------------------------------------ the narrow-m instance
 
 # m, n, k, layout, pad, alpha, beta: every row-block count (BM = 64, 128,
