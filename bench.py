@@ -291,7 +291,8 @@ def skinny_shapes(S, count=8, min_tmin_us=20.0):
 def skinny_leg(torch, sk, S, min_ms=20.0):
     """Skinny fp16 GEMMs (A row-major, B column-major, alpha=1, beta=0) under
     AUTO, on the narrow-m tile (Stream-K, XCD-aware split) and data-parallel
-    on the 256x256 tile, and under AUTO with the same B buffer taken as
+    on the 256x256 tile, on each tile instance forced (AUTO's schedule), and
+    under AUTO and each forced instance with the same B buffer taken as
     row-major (n-contiguous: `x @ W` with W stored k x n), each timed as R
     launches back to back between one event pair (at least `min_ms` per
     measurement, host enqueue hidden behind a spin kernel).  Bytes =
@@ -312,7 +313,11 @@ def skinny_leg(torch, sk, S, min_ms=20.0):
         for name, dd, opts in (("auto", d, sk.make_options()),
                                ("narrow", d, sk.make_options(tile=sk.TILE_NARROW)),
                                ("dp", d, sk.make_options(schedule=sk.SCHED_DP, tile=sk.TILE_LARGE)),
-                               ("auto_b_row", d_brow, sk.make_options())):
+                               ("large", d, sk.make_options(tile=sk.TILE_LARGE)),
+                               ("small", d, sk.make_options(tile=sk.TILE_SMALL)),
+                               ("auto_b_row", d_brow, sk.make_options()),
+                               ("large_b_row", d_brow, sk.make_options(tile=sk.TILE_LARGE)),
+                               ("small_b_row", d_brow, sk.make_options(tile=sk.TILE_SMALL))):
             us, R, _ = back_to_back_us(torch, lambda: sk.gemm_ex(dd, opts), min_ms=min_ms)
             p = sk.plan_query(dd, opts)
             row[name] = {"us": round(us, 2), "GB_s": round(by / us / 1e3, 1), "tflops": round(fl / us / 1e6, 1),
