@@ -46,7 +46,7 @@ SWEEP = [1024, 2048, 3072, 4096, 5120, 6144]
 # reports null until the counters are taken again.
 KERNEL_SOURCES = ("work_centric_decomposition_amd/csrc/sk_kernels.hip",
                   "work_centric_decomposition_amd/csrc/sk_internal.h")
-TRAFFIC = {"kernel_hash": "870f4ac925f0f30e",
+TRAFFIC = {"kernel_hash": "8feefbd6b145e4fd",
            # mean over the six launches of one step (1024^3 ... 6144^3)
            "sgemm-sweep": 1170550910,
            # fp16 8192^3 launch

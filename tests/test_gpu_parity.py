@@ -89,13 +89,17 @@ def test_repacked_operands_buffers_grow_and_shrink_between_calls(dtype):
     repack one or both operands (fp16/bf16: any mn-contiguous operand; fp32:
     a leading dimension that is not a multiple of four), each against the
     oracle; the tile edges of the 64 x 64 transposes are exercised by ragged
-    m, n and k."""
+    m, n and k, and the source is read 16, 8, 4 or 2 bytes at a time as its
+    rows' alignment allows."""
     if dtype == sk.F32:
         runs = [(130, 70, 77, sk.A_ROW_B_ROW, 1), (1000, 1500, 700, sk.A_COL_B_ROW, 3),
-                (300, 130, 65, sk.A_COL_B_COL, 1)]
+                (300, 130, 65, sk.A_COL_B_COL, 1), (131, 66, 94, sk.A_COL_B_ROW, 1)]
     else:
         runs = [(130, 70, 77, sk.A_ROW_B_ROW, 0), (1000, 1500, 700, sk.A_COL_B_ROW, 0),
-                (300, 130, 65, sk.A_COL_B_COL, 5), (257, 513, 129, sk.A_ROW_B_ROW, 3)]
+                (300, 130, 65, sk.A_COL_B_COL, 5), (257, 513, 129, sk.A_ROW_B_ROW, 3),
+                # source rows 8-byte aligned (A: k = 300, B: n = 1004) and
+                # 4-byte aligned (A: m = 258, B: k = 138), not 16
+                (200, 1004, 300, sk.A_ROW_B_ROW, 0), (258, 130, 138, sk.A_COL_B_COL, 0)]
     for (m, n, k, layout, pad) in runs:
         _say("case repack", dtype, m, n, k, layout, pad)
         c = Case(m, n, k, dtype, layout, 60 + m + layout, pad=pad)

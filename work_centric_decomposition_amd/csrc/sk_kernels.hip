@@ -1630,14 +1630,15 @@ __global__ void scale_kernel(int64_t m, int64_t n, float beta, void *C, int64_t 
 // Repack: dst[r * ldd + l] = src(r, l) for l < k, 0 for k <= l < ldd, rows
 // r < rows; src(r, l) is src[r * lds + l] (k-major) or src[l * lds + r]
 // (mn-major).  One workgroup per 64 x 64 block, 16 bytes per lane on both
-// sides where the operands allow it (vec_src: the source base is 16-byte
-// aligned and lds a multiple of the elements in 16 bytes; the destination
-// always is): a k-major source is copied row by row; an mn-major one is
+// sides where the operands allow it (the destination always does; the
+// source is read in pieces of src_align bytes, 16, 8, 4 or the element
+// size: the largest power of two dividing both its base address and its
+// row pitch): a k-major source is copied row by row; an mn-major one is
 // transposed through LDS -- loaded along r into tile rows of l (rows of 64
 // elements plus 8 bytes, so that the element reads of the store side fall
 // at most two to a bank), and read back along l.
 template <typename U>
-__global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, int src_kmajor, int vec_src,
+__global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, int src_kmajor, int src_align,
                                                    int64_t rows, int64_t k, U *dst, int64_t ldd) {
   constexpr int EPV = 16 / sizeof(U);         // elements per 16-byte vector
   constexpr int VPR = 64 / EPV;              // vectors per 64-element row
@@ -1647,7 +1648,24 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
   union Vec {
     u4_t v;
     u2_t h[2];
+    uint32_t w[4];
     U e[EPV];
+  };
+  // one whole 16-byte vector of the source at p (every element in range),
+  // in pieces of src_align bytes
+  auto load_vec = [src_align](const U *p, Vec &x) {
+    if (src_align >= 16) {
+      x.v = *reinterpret_cast<const u4_t *>(p);
+    } else if (src_align == 8) {
+      x.h[0] = reinterpret_cast<const u2_t *>(p)[0];
+      x.h[1] = reinterpret_cast<const u2_t *>(p)[1];
+    } else if (src_align == 4) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) x.w[q] = reinterpret_cast<const uint32_t *>(p)[q];
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPV; ++e) x.e[e] = p[e];
+    }
   };
   const int64_t r0 = (int64_t)blockIdx.y * 64, l0 = (int64_t)blockIdx.x * 64;
   const int t = threadIdx.x, vi = t % VPR, ri = t / VPR;
@@ -1657,8 +1675,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
       const int64_t r = r0 + p + ri;
       if (r >= rows || l >= ldd) continue;
       Vec x;
-      if (vec_src && l + EPV <= k) {
-        x.v = *reinterpret_cast<const u4_t *>(src + r * lds + l);
+      if (l + EPV <= k) {
+        load_vec(src + r * lds + l, x);
       } else {
 #pragma unroll
         for (int e = 0; e < EPV; ++e) x.e[e] = l + e < k ? src[r * lds + l + e] : U(0);
@@ -1676,8 +1694,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const U *src, int64_t lds, in
     const int li = p + ri;
     const int64_t ll = l0 + li, r = r0 + vi * EPV;
     Vec x;
-    if (ll < k && vec_src && r + EPV <= rows) {
-      x.v = *reinterpret_cast<const u4_t *>(src + ll * lds + r);
+    if (ll < k && r + EPV <= rows) {
+      load_vec(src + ll * lds + r, x);
     } else {
 #pragma unroll
       for (int e = 0; e < EPV; ++e) x.e[e] = ll < k && r + e < rows ? src[ll * lds + r + e] : U(0);
@@ -1981,14 +1999,18 @@ int launch_pack(int dtype, const void *src, int64_t lds, bool src_kmajor, int64_
   // the kernel writes 16-byte vectors into dst: 16-byte aligned rows of it
   const int es = dtype == SK_F32 ? 4 : 2;
   if (reinterpret_cast<uintptr_t>(dst) % 16 != 0 || (ldd * es) % 16 != 0) return (int)hipErrorInvalidValue;
-  const int vec_src = reinterpret_cast<uintptr_t>(src) % 16 == 0 && (lds * es) % 16 == 0 ? 1 : 0;
+  // the largest of 16, 8, 4 bytes dividing the source's base and row pitch,
+  // else the element size
+  int src_align = 16;
+  while (src_align > es && (reinterpret_cast<uintptr_t>(src) % src_align != 0 || (lds * es) % src_align != 0))
+    src_align /= 2;
   if (dtype == SK_F32)
     hipLaunchKernelGGL(dev::pack_kernel<uint32_t>, grid, block, 0, stream,
-                       static_cast<const uint32_t *>(src), lds, src_kmajor ? 1 : 0, vec_src, rows, k,
+                       static_cast<const uint32_t *>(src), lds, src_kmajor ? 1 : 0, src_align, rows, k,
                        static_cast<uint32_t *>(dst), ldd);
   else
     hipLaunchKernelGGL(dev::pack_kernel<uint16_t>, grid, block, 0, stream,
-                       static_cast<const uint16_t *>(src), lds, src_kmajor ? 1 : 0, vec_src, rows, k,
+                       static_cast<const uint16_t *>(src), lds, src_kmajor ? 1 : 0, src_align, rows, k,
                        static_cast<uint16_t *>(dst), ldd);
   return (int)hipGetLastError();
 }
