@@ -331,15 +331,18 @@ def skinny_leg(torch, sk, S, min_ms=20.0):
 def measured_peaks(torch, sk, reps=5):
     """The machine's own sustained rates (libskmb.so, include/sk_microbench.h):
     MFMA issue rate per type with two waves on every SIMD (8 independent MFMAs
-    per round, 20000 rounds per launch) and the HBM read rate of a 4 GiB
-    buffer; each the best of `reps` launches after two warm-up launches, HIP
-    events on the launch stream."""
+    per round, 20000 rounds per launch), the HBM read rate of a 4 GiB buffer
+    and the LDS read rate with eight waves per CU (16-byte and transposing
+    8-byte reads); each the best of `reps` launches after two warm-up
+    launches, HIP events on the launch stream."""
     import ctypes
     mb = ctypes.CDLL(os.path.join(os.path.dirname(sk.LIB_PATH), "libskmb.so"))
     mb.skmb_mfma.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     mb.skmb_mfma.restype = ctypes.c_int
     mb.skmb_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
     mb.skmb_read.restype = ctypes.c_int
+    mb.skmb_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    mb.skmb_lds.restype = ctypes.c_int
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     stream = torch.cuda.current_stream()
     sp = ctypes.c_void_p(stream.cuda_stream)
@@ -370,6 +373,20 @@ def measured_peaks(torch, sk, reps=5):
     ms = best_ms(lambda: mb.skmb_read(ctypes.c_void_p(buf.data_ptr()), nbytes, rgrid,
                                       ctypes.c_void_p(rsink.data_ptr()), sp))
     res["hbm_read_GB_s"] = round(nbytes / (ms * 1e-3) / 1e9, 1)
+    # LDS read rate, eight waves per CU: 16-byte reads and 8-byte transposing
+    # reads; per CU in bytes per nanosecond (bytes per clock = that / GHz)
+    # (and per clock, at the core clock sampled while the same launches repeat)
+    lrounds = 20000
+    for mode, name, per in ((0, "lds_read", 1024), (1, "lds_tr_read", 512)):
+        launch = lambda: mb.skmb_lds(mode, lrounds, grid, ctypes.c_void_p(rsink.data_ptr()), sp)  # noqa: E731
+        ms = best_ms(launch)
+        tot = grid * 4 * lrounds * 8 * per
+        res[f"{name}_TB_s"] = round(tot / (ms * 1e-3) / 1e12, 1)
+        res[f"{name}_B_per_ns_per_cu"] = round(tot / (ms * 1e-3) / 1e9 / cus, 1)
+        clk = sample_clock(torch, lambda _: launch())
+        if clk:
+            res[f"{name}_clock_mhz"] = clk["median"]
+            res[f"{name}_B_per_clk_per_cu"] = round(tot / (ms * 1e-3) / cus / (clk["median"] * 1e6), 1)
     del buf
     torch.cuda.empty_cache()
     return res

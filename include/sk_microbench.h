@@ -39,6 +39,18 @@ int skmb_mfma(int dtype, int rounds, int grid, float *sink, hipStream_t stream);
  * Returns hipErrorInvalidValue for misaligned or non-positive sizes. */
 int skmb_read(const void *src, int64_t bytes, int grid, uint32_t *sink, hipStream_t stream);
 
+/* LDS read rate: `grid` workgroups of 256 threads (4 waves), each filling
+ * 32 KiB of LDS and then running `rounds` rounds of 8 reads per wave:
+ *   mode 0: 16 bytes per lane (1 KiB per read instruction, conflict-free),
+ *   mode 1: 8 bytes per lane by the transposing read ds_read_b64_tr_b16
+ *           (512 bytes per instruction),
+ * so one launch reads grid * 4 * rounds * 8 * (1024 or 512) bytes of LDS.
+ * Two workgroups per CU (grid = 2 x CUs) put eight waves on every CU, as the
+ * 256 x 256 GEMM kernel runs.  `sink` (device, grid * 256 uint32,
+ * caller-owned) receives each thread's XOR of what it read.  Returns
+ * hipErrorInvalidValue for an unknown mode or non-positive sizes. */
+int skmb_lds(int mode, int rounds, int grid, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -27,7 +27,7 @@ def test_measurement_library_exports_what_its_header_declares():
     import re
     hdr = open(os.path.join(os.path.dirname(sk.HEADER_PATH), "sk_microbench.h")).read()
     names = re.findall(r"^int (skmb_\w+)\(", hdr, re.M)
-    assert set(names) == {"skmb_mfma", "skmb_read"}
+    assert set(names) == {"skmb_mfma", "skmb_read", "skmb_lds"}
     mb = ctypes.CDLL(os.path.join(os.path.dirname(sk.LIB_PATH), "libskmb.so"))
     for name in names:
         assert hasattr(mb, name), name
@@ -36,6 +36,9 @@ def test_measurement_library_exports_what_its_header_declares():
     assert mb.skmb_mfma(3, 10, 1, 16, None) != 0  # unknown type
     assert mb.skmb_mfma(1, 0, 1, 16, None) != 0   # no rounds
     assert mb.skmb_read(16, 24, 1, 16, None) != 0  # not a multiple of 16 bytes
+    mb.skmb_lds.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    assert mb.skmb_lds(2, 10, 1, 16, None) != 0  # unknown mode
+    assert mb.skmb_lds(0, 0, 1, 16, None) != 0   # no rounds
 
 
 def _desc(m, n, k, dtype=sk.F16, layout=sk.A_ROW_B_COL):

@@ -1,6 +1,7 @@
-// sk_microbench.hip -- kernels that measure the MFMA issue rate and the HBM
-// read rate this MI355X sustains (include/sk_microbench.h).  Built into
-// libskmb.so, apart from the GEMM library.
+// sk_microbench.hip -- kernels that measure the MFMA issue rate, the HBM
+// read rate and the LDS read rate this MI355X sustains
+// (include/sk_microbench.h).  Built into libskmb.so, apart from the GEMM
+// library.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -13,6 +14,9 @@ typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef float f16v_t __attribute__((ext_vector_type(16)));
 typedef unsigned int u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u2_t __attribute__((ext_vector_type(2)));
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t *lds_v4s_t;
 
 // A value in [-1, 1) from a hash of (lane, j, e): operands that differ from
 // one MFMA to the next, so the datapath toggles as it does on real data (a
@@ -104,7 +108,52 @@ __global__ __launch_bounds__(256) void read_kernel(const u4_t *src, int64_t n16,
   sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x[0] ^ x[1] ^ x[2] ^ x[3];
 }
 
+// LDS read rate: each workgroup fills 32 KiB of LDS, then every wave runs
+// `rounds` rounds of 8 reads over it: MODE 0 reads 16 bytes per lane (1 KiB
+// per instruction, lanes in order: no bank conflicts), MODE 1 reads 8 bytes
+// per lane with the transposing read ds_read_b64_tr_b16 (512 bytes per
+// instruction, lanes in order).  The round's offsets change from round to
+// round and a compiler barrier between rounds keeps every read in the loop.
+__device__ __attribute__((always_inline)) inline v4s_t tr_read(lds_v4s_t __restrict__ p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(p);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void lds_kernel(int rounds, uint32_t *sink) {
+  __shared__ __attribute__((aligned(16))) uint32_t buf[8192];
+  for (int i = threadIdx.x; i < 8192; i += 256) buf[i] = (uint32_t)i * 2654435761u;
+  __syncthreads();
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const char *base = reinterpret_cast<const char *>(buf);
+  uint32_t x = 0;
+  for (int r = 0; r < rounds; ++r) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int blk = (r * 8 + u + w * 8) & 31;  // one of 32 blocks of 1 KiB
+      if constexpr (MODE == 0) {
+        const u4_t v = *reinterpret_cast<const u4_t *>(base + blk * 1024 + lane * 16);
+        x ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      } else {
+        const v4s_t v = tr_read((lds_v4s_t)(__attribute__((address_space(3))) void *)(base + blk * 1024 + lane * 8));
+        const u2_t b = __builtin_bit_cast(u2_t, v);  // the same XOR work per byte as mode 0
+        x ^= b[0] ^ b[1];
+      }
+    }
+    asm volatile("" ::: "memory");
+  }
+  sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = x;
+}
+
 }  // namespace
+
+extern "C" int skmb_lds(int mode, int rounds, int grid, uint32_t *sink, hipStream_t stream) {
+  if (rounds <= 0 || grid <= 0 || !sink || mode < 0 || mode > 1) return (int)hipErrorInvalidValue;
+  if (mode == 0)
+    hipLaunchKernelGGL(lds_kernel<0>, dim3(grid), dim3(256), 0, stream, rounds, sink);
+  else
+    hipLaunchKernelGGL(lds_kernel<1>, dim3(grid), dim3(256), 0, stream, rounds, sink);
+  return (int)hipGetLastError();
+}
 
 extern "C" int skmb_mfma(int dtype, int rounds, int grid, float *sink, hipStream_t stream) {
   if (rounds <= 0 || rounds % 4 || grid <= 0 || !sink || dtype < 0 || dtype > 2) return (int)hipErrorInvalidValue;
