@@ -41,6 +41,28 @@ def test_measurement_library_exports_what_its_header_declares():
     assert mb.skmb_lds(0, 0, 1, 16, None) != 0   # no rounds
 
 
+def test_calls_fail_loudly_without_the_library():
+    """With libskgemm.so absent, importing the package still works (the build
+    needs that) but the first call through the ABI raises ImportError: there
+    is no fallback path.  Run in a fresh interpreter so that this process's
+    loaded library is not reused."""
+    import os
+    import subprocess
+    import sys
+    code = ("import work_centric_decomposition_amd as sk\n"
+            "sk.LIB_PATH = '/nonexistent/libskgemm.so'\n"
+            "d = sk.make_desc(8, 8, 8, 1.0, 16, 8, 16, 8, 0.0, 16, 8, sk.F32, 0)\n"
+            "try:\n"
+            "    sk.plan_query(d, None, 256)\n"
+            "except ImportError as e:\n"
+            "    print('raised:', e)\n"
+            "else:\n"
+            "    print('no error')\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    out = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=120)
+    assert "raised:" in out.stdout and "is not built" in out.stdout, out.stdout + out.stderr
+
+
 def _desc(m, n, k, dtype=sk.F16, layout=sk.A_ROW_B_COL):
     # aligned fake pointers: the planner only inspects their alignment
     return sk.make_desc(m, n, k, 1.0, 1 << 20, k if layout in (0, 1) else m, 1 << 21,
