@@ -114,10 +114,12 @@ def test_repacked_operands_buffers_grow_and_shrink_between_calls(dtype):
 
 # m, n, k, pad, alpha, beta: m and n multiples of 8 but of neither tile size
 # (ragged last tiles), or not multiples of 8 (those operands repacked), k
-# below one iteration and below one 16-byte chunk, several iterations with a
-# tail of k-rows, padded leading dimensions, alpha and beta applied
+# below one iteration and below one 16-byte chunk (down to a single k-row),
+# several iterations with a tail of k-rows, padded leading dimensions, alpha
+# and beta applied
 MN_CASES = [(296, 520, 200, 0, 1.0, 0.0), (513, 264, 1000, 8, 0.5, -1.5), (64, 2048, 64, 0, 1.0, 1.0),
-            (256, 256, 5, 0, 1.0, 0.0), (264, 136, 4100, 16, 1.0, 0.0), (1000, 1000, 1000, 0, 0.75, 1.25)]
+            (256, 256, 5, 0, 1.0, 0.0), (264, 136, 4100, 16, 1.0, 0.0), (1000, 1000, 1000, 0, 0.75, 1.25),
+            (96, 136, 1, 0, 1.0, 0.5)]
 
 
 def _expected_packs(c):
