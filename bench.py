@@ -224,14 +224,17 @@ def library_gemm(torch, sk, S, steps, warmup):
 # form)
 GEMV_SHAPES = [(1, 16384, 16384, "f16", 1), (16384, 1, 16384, "f16", 1), (1, 16384, 16384, "f32", 1),
                (1, 1, 1 << 24, "f32", 1), (1, 16384, 16384, "f16", 0), (16384, 1, 16384, "f16", 3),
-               (1, 16384, 16384, "f32", 0), (8, 16384, 16384, "f16", 1), (8, 16384, 16384, "f32", 1)]
+               (1, 16384, 16384, "f32", 0), (8, 16384, 16384, "f16", 1), (8, 16384, 16384, "f32", 1),
+               (8, 16384, 16384, "f16", 0)]
 
 
 def gemv_leg(torch, sk, S, reps=20):
     """Matrix-vector products through the even split of dot products (AUTO
-    picks it for m == 1 or n == 1): per-launch time queued behind a spin
-    kernel, bytes = the matrix, the vector and the output once each, against
-    the 8 TB/s HBM peak; torch.matmul on the same operands for context."""
+    picks it for m == 1 or n == 1), and a few vectors at once (the multi form
+    when both operands are k-contiguous, else the tiled kernels, form
+    "tiled"): per-launch time queued behind a spin kernel, bytes = the
+    matrix, the vectors and the output once each, against the 8 TB/s HBM
+    peak; torch.matmul on the same operands for context."""
     import statistics
     dts = {"f16": (sk.F16, torch.float16, 2), "f32": (sk.F32, torch.float32, 4)}
     spin = _spin_cycles(torch, 300e-6)
@@ -263,7 +266,8 @@ def gemv_leg(torch, sk, S, reps=20):
         by = es * (m * k + k * n + m * n)
         out.append({"shape": [m, n, k], "dtype": name, "layout": ["A row, B row", "A row, B col", "A col, B row",
                                                                   "A col, B col"][layout],
-                    "form": "multi" if p.tile_m > 0 else ("axpy" if p.tile_n > 0 else "dot"),
+                    "form": ("tiled" if p.schedule != sk.SCHED_GEMV_SPLIT else
+                             "multi" if p.tile_m > 0 else ("axpy" if p.tile_n > 0 else "dot")),
                     "schedule": int(p.schedule),
                     "chunks": int(p.sk_blocks), "grid": int(p.grid), "us": round(us, 2),
                     "GB_s": round(by / us / 1e3, 1), "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBS, 4),
